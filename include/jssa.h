@@ -1,0 +1,196 @@
+/*
+ * jssa.h — C ABI of the MI355X (gfx950) token-level sparse decode library.
+ *
+ * One decode step of Joint Subspace Sparse Attention, as described in
+ * "Joint Subspace Sparse Attention for Efficient Long-Context Decoding"
+ * (paperlayer.ai summary of arXiv 2610.19026v1; cited below as "JSSA
+ * summary" with its section or figure):
+ *
+ *   1. every cached token is scored in a shared low-rank query-key subspace
+ *      using a projected-key cache Kp = K P (Figure 1, sections 3.1, 3.2, 3.4);
+ *   2. each (sequence, KV head) keeps its own top-k positions (Figure 1,
+ *      section 1, appendix A.3, section E.3);
+ *   3. the query heads of each KV head attend over those positions, reading
+ *      the original full-dimensional K/V rows in place from the standard GQA
+ *      cache, with no gather buffer and one launch for all heads (section 3.3).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers: every array argument is a DEVICE pointer, allocated and owned by
+ *   the caller.  The library never allocates or frees memory and keeps no
+ *   state between calls.  The descriptor itself is a HOST pointer read during
+ *   the call only.
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ *   stream).  Every call only enqueues work on it and returns without
+ *   synchronising.
+ * Errors: arguments are validated on the host before anything is enqueued;
+ *   a failing check returns a negative jssa_status and enqueues nothing.  A
+ *   failed kernel launch returns JSSA_ERR_HIP.  Values that live in device
+ *   memory (seq_lens, pos) are not visible to the host: kernels clamp
+ *   seq_lens[b] to [0, t_max] and skip appended rows beyond t_max.
+ * Workspace: entry points that take `ws` need at least
+ *   jssa_workspace_bytes(desc, op) bytes, 256-byte aligned, that were zeroed
+ *   once (jssa_workspace_init) before first use.  Every call leaves the
+ *   counters in the workspace zeroed again, so one workspace may be reused by
+ *   calls serialised on one stream; concurrent calls need distinct workspaces.
+ * Layouts (row-major, innermost last):
+ *   q         [B, Hq, d_k]               dtype kv_dtype
+ *   k_cache   [B, t_max, Hkv, d_k]       dtype kv_dtype
+ *   v_cache   [B, t_max, Hkv, d_v]       dtype kv_dtype  (MLA: unused; V is
+ *                                        the first d_v columns of each K row)
+ *   P         [Hkv, d_k, rank]           float32, orthonormal columns
+ *   kp_cache  [B, Hkv, t_max, rank]      dtype kp_dtype
+ *   seq_lens  [B]                        int32, tokens cached per sequence
+ *   scores    [B, Hkv, t_max]            float32
+ *   idx       [B, Hkv, topk + window]    int32
+ *   n_sel     [B, Hkv]                   int32
+ *   out       [B, Hq, d_v]               dtype out_dtype
+ *   lse       [B, Hq]                    float32 (natural log), may be NULL
+ * Query head hq belongs to KV head hq / G, G = Hq / Hkv.  Every base pointer
+ * must be 16-byte aligned.
+ */
+#ifndef JSSA_H
+#define JSSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define JSSA_ABI_VERSION 1
+
+typedef enum {
+  JSSA_OK = 0,
+  JSSA_ERR_INVALID_ARG = -1,  /* null pointer, inconsistent sizes, bad enum */
+  JSSA_ERR_UNSUPPORTED = -2,  /* valid but not built: shape/dtype combination */
+  JSSA_ERR_WORKSPACE = -3,    /* workspace missing, too small or misaligned */
+  JSSA_ERR_MISALIGNED = -4,   /* a data pointer is not 16-byte aligned */
+  JSSA_ERR_HIP = -5           /* a HIP launch failed */
+} jssa_status;
+
+typedef enum { JSSA_F32 = 0, JSSA_BF16 = 1 } jssa_dtype;
+
+/* How a KV head reduces the subspace scores of its G query heads.
+ * MAX: s_t = max_g (q_g P).Kp_t.  MEAN: s_t = mean_g (q_g P).Kp_t, which is
+ * the JSSA summary's group-mean query (Figure 1, sections 3.1 and 3.2). */
+typedef enum { JSSA_REDUCE_MAX = 0, JSSA_REDUCE_MEAN = 1 } jssa_reduce;
+
+/* GQA: standard [B, T, Hkv, d] K and V caches.  MLA: one shared latent row
+ * per token (Hkv = 1); the value is the first d_v columns of that row and
+ * selection yields one index set per sequence (JSSA summary section 3.3). */
+typedef enum { JSSA_LAYOUT_GQA = 0, JSSA_LAYOUT_MLA = 1 } jssa_layout;
+
+typedef enum {
+  JSSA_OP_TOPK = 1,    /* jssa_topk */
+  JSSA_OP_ATTN = 2,    /* jssa_indexed_attn */
+  JSSA_OP_DECODE = 3,  /* jssa_decode */
+  JSSA_OP_DENSE = 4    /* jssa_dense_decode */
+} jssa_op;
+
+typedef struct {
+  int32_t batch;       /* B >= 1 */
+  int32_t n_q_heads;   /* Hq, a multiple of n_kv_heads */
+  int32_t n_kv_heads;  /* Hkv */
+  int32_t d_k;         /* query/key head dim (GQA: 64 or 128; MLA: 576) */
+  int32_t d_v;         /* value head dim (GQA: == d_k; MLA: 512) */
+  int32_t rank;        /* scoring rank r (16, 32 or 64) */
+  int32_t t_max;       /* cache capacity in tokens, 1 .. 2^24 */
+  int32_t topk;        /* budget k >= 0 */
+  int32_t window;      /* W >= 0 trailing tokens always attended; k + W >= 1 */
+  int32_t kv_dtype;    /* jssa_dtype of q, K and V */
+  int32_t kp_dtype;    /* jssa_dtype of the projected-key cache */
+  int32_t out_dtype;   /* jssa_dtype of the attention output */
+  int32_t reduce;      /* jssa_reduce */
+  int32_t layout;      /* jssa_layout */
+  float scale;         /* softmax scale applied to q.K, e.g. 1/sqrt(d_k) */
+} jssa_desc;
+
+/* Version of this ABI (JSSA_ABI_VERSION). */
+int32_t jssa_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* jssa_status_str(int32_t status);
+
+/* Checks a descriptor without touching the GPU: JSSA_OK if the library can
+ * run `op` (a jssa_op, or 0 for the append/score entry points) for it. */
+int32_t jssa_check_desc(const jssa_desc* desc, int32_t op);
+
+/* Bytes of workspace `op` needs for `desc` (0 if the descriptor is invalid). */
+size_t jssa_workspace_bytes(const jssa_desc* desc, int32_t op);
+
+/* Zero-fills a workspace (a fill kernel on `stream`, safe inside graph
+ * capture).  Needed once before a workspace's first use. */
+int32_t jssa_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Append and project (JSSA summary section E.1: each newly generated key is
+ * projected into the scoring cache; sections 3.1 and 3.4: the cache holds
+ * Kp = K P per KV head and is used only for scoring).
+ * For b < B and j < n_new, with t = pos[b] + j (rows with t >= t_max are
+ * skipped):
+ *   k_cache[b,t,h,:] = k_new[b,j,h,:]; v_cache[b,t,h,:] = v_new[b,j,h,:]
+ *   kp_cache[b,h,t,i] = round(sum_d k_cache[b,t,h,d] * P[h,d,i])
+ * accumulated in fp32 and rounded to kp_dtype (bf16: nearest-even).
+ * k_new/v_new are [B, n_new, Hkv, d] (GQA) or [B, n_new, 1, d_k] (MLA, no v).
+ * If k_new is NULL the rows are already in the cache and only the projection
+ * is done (bulk prefill of the scoring cache); v_new is then ignored.
+ * pos: int32 [B] device array of first positions. */
+int32_t jssa_append_kv(const jssa_desc* desc, const void* k_new, const void* v_new, int32_t n_new,
+                       const int32_t* pos, const float* P, void* k_cache, void* v_cache,
+                       void* kp_cache, void* stream);
+
+/* Subspace scores (JSSA summary Figure 1 and section 3.1): for every
+ * candidate t < seq_lens[b] - window,
+ *   scores[b,h,t] = reduce_g sum_i (q[b,h*G+g,:] P[h])[i] * kp_cache[b,h,t,i]
+ * with the projected query kept in fp32.  Entries t >= seq_lens[b] - window
+ * are not written. */
+int32_t jssa_score(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
+                   const int32_t* seq_lens, float* scores, void* stream);
+
+/* Per-(sequence, KV head) selection (JSSA summary Figure 1, section 3.1,
+ * appendix A.3): among the candidates t < T_b - W (T_b = seq_lens[b]) keep
+ * the min(k, T_b - W) largest scores, ties to the lower index, NaN below every
+ * number, -0.0 equal to +0.0; then append the window T_b-W .. T_b-1.
+ * idx[b,h,:] lists the selected candidates in ascending order followed by the
+ * window; n_sel[b,h] = min(k, max(T_b-W,0)) + min(W, T_b).  Entries past
+ * n_sel are not written.  Exact: the result is a function of the fp32 score
+ * bits only.  Workspace op JSSA_OP_TOPK. */
+int32_t jssa_topk(const jssa_desc* desc, const float* scores, const int32_t* seq_lens,
+                  int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream);
+
+/* Gather-free indexed attention (JSSA summary section 3.3): for each query
+ * head hq (KV head h = hq / G) over the n_sel[b,h] tokens idx[b,h,:],
+ *   out[b,hq,:] = sum_t softmax_t(scale * q[b,hq].K[b,t,h]) V[b,t,h,:]
+ *   lse[b,hq]   = log sum_t exp(scale * q[b,hq].K[b,t,h])
+ * reading each selected K/V row in place once for all G query heads; fp32
+ * accumulation; index chunks merged by a log-sum-exp combine.  n_sel = 0
+ * gives out = 0 and lse = -inf.  Indices should lie in [0, t_max); others are
+ * clamped into that range.
+ * Workspace op JSSA_OP_ATTN. */
+int32_t jssa_indexed_attn(const jssa_desc* desc, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* idx, const int32_t* n_sel,
+                          void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* One fused sparse decode step: jssa_score -> jssa_topk -> jssa_indexed_attn
+ * (JSSA summary Figure 1 and section E.1) with intermediates in the
+ * workspace.  idx_out / n_sel_out may be NULL; when given they receive the
+ * selection.  The new token is expected to be appended (jssa_append_kv)
+ * before this call.  Workspace op JSSA_OP_DECODE. */
+int32_t jssa_decode(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
+                    const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                    void* out, float* lse, int32_t* idx_out, int32_t* n_sel_out,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Full-KV decode attention over all t < seq_lens[b] (the comparison path of
+ * JSSA summary section 4.5), same outputs as jssa_indexed_attn.
+ * Workspace op JSSA_OP_DENSE. */
+int32_t jssa_dense_decode(const jssa_desc* desc, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* seq_lens, void* out, float* lse,
+                          void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JSSA_H */

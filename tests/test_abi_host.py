@@ -1,0 +1,120 @@
+"""The C-ABI library: it loads, exports every function include/jssa.h declares,
+and rejects bad arguments on the host before touching the GPU (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import token_level_sparse_dim_amd as J
+from token_level_sparse_dim_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "jssa.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(jssa_[a-z_]+)\s*\(", src)))
+
+
+def _desc(**kw):
+    base = dict(batch=2, n_q_heads=32, n_kv_heads=8, d_k=128, d_v=128, rank=32, t_max=8192,
+                topk=256, window=0, kv_dtype=J.BF16, kp_dtype=J.BF16, out_dtype=J.F32,
+                reduce=J.REDUCE_MAX, layout=J.LAYOUT_GQA, scale=128 ** -0.5)
+    base.update(kw)
+    return J.Desc(**base)
+
+
+def test_library_exports_every_declared_function():
+    names = _declared()
+    assert len(names) >= 11
+    lib = J.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, n
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_abi_version_and_status_strings():
+    assert J.abi_version() == 1
+    lib = J.lib()
+    assert lib.jssa_status_str(0) == b"JSSA_OK"
+    for code, name in _lib.STATUS.items():
+        assert lib.jssa_status_str(code).decode() == name
+    assert lib.jssa_status_str(-99) == b"JSSA_ERR_UNKNOWN"
+
+
+def test_struct_layout_matches_header():
+    # 14 int32 fields and one float, no padding
+    assert ctypes.sizeof(_lib.CDesc) == 15 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 0),
+    (dict(n_q_heads=30), -1),           # Hq not a multiple of Hkv
+    (dict(batch=0), -1),
+    (dict(t_max=0), -1),
+    (dict(t_max=(1 << 24) + 1), -1),
+    (dict(topk=-1), -1),
+    (dict(kv_dtype=7), -1),
+    (dict(reduce=5), -1),
+    (dict(scale=float("nan")), -1),
+    (dict(rank=48), -2),                # not built
+    (dict(d_k=96, d_v=96), -2),
+    (dict(d_v=64), -2),
+    (dict(n_q_heads=48, n_kv_heads=3), -2),  # G = 16
+    (dict(rank=256, d_k=128), -1),     # rank > d_k
+])
+def test_descriptor_validation(kw, status):
+    assert J.check_desc(_desc(**kw), J.OP_DECODE) == status
+
+
+def test_selection_needs_a_budget_or_window():
+    d = _desc(topk=0, window=0)
+    assert J.check_desc(d, J.OP_TOPK) == -1
+    assert J.check_desc(d, J.OP_DENSE) == 0
+    assert J.check_desc(_desc(topk=0, window=16), J.OP_DECODE) == 0
+
+
+def test_workspace_sizes():
+    d = _desc()
+    for op in (J.OP_TOPK, J.OP_ATTN, J.OP_DECODE, J.OP_DENSE):
+        n = J.workspace_bytes(d, op)
+        assert n > 0 and n % 256 == 0
+    assert J.workspace_bytes(d, J.OP_DECODE) > J.workspace_bytes(d, J.OP_TOPK)
+    assert J.workspace_bytes(_desc(n_q_heads=30), J.OP_DECODE) == 0
+    assert J.workspace_bytes(d, 99) == 0
+
+
+def _fake(n=1):
+    return [ctypes.c_void_p(4096 * (i + 1)) for i in range(n)]
+
+
+def test_entry_points_reject_bad_arguments_before_launch():
+    lib = J.lib()
+    d = _desc().c()
+    p = _fake(12)
+    null = None
+    # null required pointers
+    assert lib.jssa_score(d, null, *p[:4], null) == -1
+    assert lib.jssa_topk(d, *p[:4], null, 0, null) == -3            # workspace missing
+    assert lib.jssa_topk(d, *p[:4], ctypes.c_void_p(4096), 16, null) == -3  # too small
+    assert lib.jssa_topk(d, *p[:4], ctypes.c_void_p(4096 + 16), 1 << 40, null) == -3  # misaligned ws
+    assert lib.jssa_indexed_attn(d, *p[:5], null, null, null, 0, null) == -1
+    assert lib.jssa_decode(d, *p[:6], null, null, null, null, null, 0, null) == -1
+    assert lib.jssa_dense_decode(d, null, *p[:4], null, null, 0, null) == -1
+    assert lib.jssa_append_kv(d, *p[:2], -1, *p[2:7], null) == -1
+    # misaligned data pointers
+    odd = ctypes.c_void_p(4096 + 2)
+    assert lib.jssa_score(d, odd, *p[:4], null) == -4
+    assert lib.jssa_decode(d, *p[:5], odd, p[6], null, null, null, p[7], 1 << 40, null) == -4
+    # invalid descriptor wins over everything else
+    bad = _desc(n_q_heads=30).c()
+    assert lib.jssa_decode(bad, *p[:7], null, null, null, p[7], 1 << 40, null) == -1
+    assert lib.jssa_score(None, *p[:5], null) == -1
+    # workspace init argument checks
+    assert lib.jssa_workspace_init(None, 64, None) == -1
+    assert lib.jssa_workspace_init(ctypes.c_void_p(4096 + 8), 64, None) == -3
+    assert lib.jssa_workspace_init(None, 0, None) == 0  # nothing to do

@@ -1,0 +1,128 @@
+"""MI355X (gfx950) token-level sparse decode attention: Python binding.
+
+Thin wrappers with the C ABI's names (``include/jssa.h``).  Tensors are
+device tensors owned by the caller; the functions pass their pointers and the
+current HIP stream to ``libjssa.so`` and raise :class:`JssaError` on a
+non-zero status.  PyTorch provides device memory and streams only.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import (BF16, F32, LAYOUT_GQA, LAYOUT_MLA, OP_ATTN, OP_DECODE, OP_DENSE, OP_TOPK,
+                   REDUCE_MAX, REDUCE_MEAN, Desc, JssaError, call, lib)
+
+__all__ = [
+    "Desc", "JssaError", "F32", "BF16", "REDUCE_MAX", "REDUCE_MEAN", "LAYOUT_GQA", "LAYOUT_MLA",
+    "OP_TOPK", "OP_ATTN", "OP_DECODE", "OP_DENSE", "lib", "abi_version", "check_desc",
+    "workspace_bytes", "workspace", "append_kv", "append_projection", "score", "topk", "indexed_attn", "decode",
+    "dense_decode",
+]
+
+_TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def abi_version() -> int:
+    return int(lib().jssa_abi_version())
+
+
+def check_desc(desc: Desc, op: int = 0) -> int:
+    """Status the library reports for ``desc`` and ``op`` (0 = append/score)."""
+    d = desc.c()
+    return int(lib().jssa_check_desc(d, op))
+
+
+def workspace_bytes(desc: Desc, op: int) -> int:
+    d = desc.c()
+    return int(lib().jssa_workspace_bytes(d, op))
+
+
+def workspace(desc: Desc, op: int, device="cuda", stream=None) -> torch.Tensor:
+    """A zero-initialised workspace for ``op`` (a uint8 device tensor)."""
+    n = workspace_bytes(desc, op)
+    if n == 0:
+        raise JssaError("jssa_workspace_bytes", -1)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    call("jssa_workspace_init", _ptr(ws, torch.uint8, "ws"), n, _stream(stream))
+    return ws
+
+
+def append_kv(desc: Desc, k_new, v_new, pos, P, k_cache, v_cache, kp_cache, stream=None):
+    """``jssa_append_kv``: write new K/V rows ``[B, n_new, Hkv, d]`` at ``pos`` and
+    project their keys into the scoring cache."""
+    kv, kp = _TORCH_DTYPE[desc.kv_dtype], _TORCH_DTYPE[desc.kp_dtype]
+    n_new = k_new.shape[1]
+    call("jssa_append_kv", desc.c(), _ptr(k_new, kv, "k_new"), _ptr(v_new, kv, "v_new"), int(n_new),
+         _ptr(pos, torch.int32, "pos"), _ptr(P, torch.float32, "P"), _ptr(k_cache, kv, "k_cache"),
+         _ptr(v_cache, kv, "v_cache"), _ptr(kp_cache, kp, "kp_cache"), _stream(stream))
+
+
+def append_projection(desc: Desc, n_new: int, pos, P, k_cache, kp_cache, stream=None):
+    """``jssa_append_kv`` with ``k_new = NULL``: project ``n_new`` cached rows from ``pos``."""
+    kv, kp = _TORCH_DTYPE[desc.kv_dtype], _TORCH_DTYPE[desc.kp_dtype]
+    call("jssa_append_kv", desc.c(), None, None, int(n_new), _ptr(pos, torch.int32, "pos"),
+         _ptr(P, torch.float32, "P"), _ptr(k_cache, kv, "k_cache"), None,
+         _ptr(kp_cache, kp, "kp_cache"), _stream(stream))
+
+
+def score(desc: Desc, q, P, kp_cache, seq_lens, scores, stream=None):
+    """``jssa_score``: subspace scores of every candidate token."""
+    call("jssa_score", desc.c(), _ptr(q, _TORCH_DTYPE[desc.kv_dtype], "q"), _ptr(P, torch.float32, "P"),
+         _ptr(kp_cache, _TORCH_DTYPE[desc.kp_dtype], "kp_cache"), _ptr(seq_lens, torch.int32, "seq_lens"),
+         _ptr(scores, torch.float32, "scores"), _stream(stream))
+
+
+def topk(desc: Desc, scores, seq_lens, idx, n_sel, ws, stream=None):
+    """``jssa_topk``: exact per-(sequence, KV head) selection plus the window."""
+    call("jssa_topk", desc.c(), _ptr(scores, torch.float32, "scores"), _ptr(seq_lens, torch.int32, "seq_lens"),
+         _ptr(idx, torch.int32, "idx"), _ptr(n_sel, torch.int32, "n_sel"), _ptr(ws, torch.uint8, "ws"),
+         ws.numel(), _stream(stream))
+
+
+def indexed_attn(desc: Desc, q, k_cache, v_cache, idx, n_sel, out, lse, ws, stream=None):
+    """``jssa_indexed_attn``: gather-free attention over the selected rows."""
+    kv = _TORCH_DTYPE[desc.kv_dtype]
+    call("jssa_indexed_attn", desc.c(), _ptr(q, kv, "q"), _ptr(k_cache, kv, "k_cache"),
+         _ptr(v_cache, kv, "v_cache"), _ptr(idx, torch.int32, "idx"), _ptr(n_sel, torch.int32, "n_sel"),
+         _ptr(out, _TORCH_DTYPE[desc.out_dtype], "out"), _ptr(lse, torch.float32, "lse"),
+         _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream))
+
+
+def decode(desc: Desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, ws,
+           idx_out=None, n_sel_out=None, stream=None):
+    """``jssa_decode``: score -> top-k -> indexed attention in one call."""
+    kv = _TORCH_DTYPE[desc.kv_dtype]
+    call("jssa_decode", desc.c(), _ptr(q, kv, "q"), _ptr(P, torch.float32, "P"),
+         _ptr(kp_cache, _TORCH_DTYPE[desc.kp_dtype], "kp_cache"), _ptr(k_cache, kv, "k_cache"),
+         _ptr(v_cache, kv, "v_cache"), _ptr(seq_lens, torch.int32, "seq_lens"),
+         _ptr(out, _TORCH_DTYPE[desc.out_dtype], "out"), _ptr(lse, torch.float32, "lse"),
+         _ptr(idx_out, torch.int32, "idx_out"), _ptr(n_sel_out, torch.int32, "n_sel_out"),
+         _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream))
+
+
+def dense_decode(desc: Desc, q, k_cache, v_cache, seq_lens, out, lse, ws, stream=None):
+    """``jssa_dense_decode``: full-KV decode attention (comparison path)."""
+    kv = _TORCH_DTYPE[desc.kv_dtype]
+    call("jssa_dense_decode", desc.c(), _ptr(q, kv, "q"), _ptr(k_cache, kv, "k_cache"),
+         _ptr(v_cache, kv, "v_cache"), _ptr(seq_lens, torch.int32, "seq_lens"),
+         _ptr(out, _TORCH_DTYPE[desc.out_dtype], "out"), _ptr(lse, torch.float32, "lse"),
+         _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream))

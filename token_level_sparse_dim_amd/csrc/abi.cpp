@@ -1,0 +1,242 @@
+// Host side of the C ABI declared in include/jssa.h: argument validation,
+// workspace sizing and launch sequencing.  No entry point allocates, frees or
+// synchronises; every check happens before the first launch.
+#include <math.h>
+#include <string.h>
+
+#include "jssa_internal.hpp"
+
+using jssa::Workspace;
+
+namespace {
+
+constexpr size_t kAlignWs = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t to_status(hipError_t e) { return e == hipSuccess ? JSSA_OK : JSSA_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Attention chunking: aim for about 2048 workgroups over the whole launch.
+void attn_chunking(int rows, int64_t n_max, bool indexed, int* chunk, int* n_chunks) {
+  const int64_t lo = indexed ? 64 : 256;
+  const int64_t hi = indexed ? 1024 : 8192;
+  int64_t c = (n_max * rows + 2047) / 2048;
+  c = (c + 63) / 64 * 64;
+  if (c < lo) c = lo;
+  if (c > hi) c = hi;
+  *chunk = int(c);
+  *n_chunks = int((n_max + c - 1) / c);
+  if (*n_chunks < 1) *n_chunks = 1;
+}
+
+}  // namespace
+
+namespace jssa {
+
+// Validation shared by every entry point.  op: 0 = append/score, else a jssa_op.
+static int32_t check(const jssa_desc* d, int op) {
+  if (!d) return JSSA_ERR_INVALID_ARG;
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1) return JSSA_ERR_INVALID_ARG;
+  if (d->n_q_heads % d->n_kv_heads != 0) return JSSA_ERR_INVALID_ARG;
+  if (d->t_max < 1 || d->t_max > kMaxSelTiles * kSelTile) return JSSA_ERR_INVALID_ARG;
+  if (d->topk < 0 || d->window < 0) return JSSA_ERR_INVALID_ARG;
+  const bool selects = op == JSSA_OP_TOPK || op == JSSA_OP_ATTN || op == JSSA_OP_DECODE;
+  if (selects && int64_t(d->topk) + d->window < 1) return JSSA_ERR_INVALID_ARG;
+  if (int64_t(d->topk) + d->window > (int64_t(1) << 30)) return JSSA_ERR_INVALID_ARG;
+  if (d->kv_dtype != JSSA_F32 && d->kv_dtype != JSSA_BF16) return JSSA_ERR_INVALID_ARG;
+  if (d->kp_dtype != JSSA_F32 && d->kp_dtype != JSSA_BF16) return JSSA_ERR_INVALID_ARG;
+  if (d->out_dtype != JSSA_F32 && d->out_dtype != JSSA_BF16) return JSSA_ERR_INVALID_ARG;
+  if (d->reduce != JSSA_REDUCE_MAX && d->reduce != JSSA_REDUCE_MEAN) return JSSA_ERR_INVALID_ARG;
+  if (d->layout != JSSA_LAYOUT_GQA && d->layout != JSSA_LAYOUT_MLA) return JSSA_ERR_INVALID_ARG;
+  if (!isfinite(d->scale)) return JSSA_ERR_INVALID_ARG;
+  if (d->d_k < 1 || d->d_v < 1 || d->rank < 1 || d->rank > d->d_k) return JSSA_ERR_INVALID_ARG;
+  if (d->rank != 16 && d->rank != 32 && d->rank != 64) return JSSA_ERR_UNSUPPORTED;
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if (d->layout == JSSA_LAYOUT_MLA) return JSSA_ERR_UNSUPPORTED;
+  if (d->d_k != d->d_v) return JSSA_ERR_UNSUPPORTED;
+  if (d->d_k != 64 && d->d_k != 128) return JSSA_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return JSSA_ERR_UNSUPPORTED;
+  return JSSA_OK;
+}
+
+bool workspace_layout(const jssa_desc& d, int op, Workspace* ws) {
+  if (check(&d, op) != JSSA_OK) return false;
+  *ws = Workspace();
+  const size_t rows = size_t(d.batch) * d.n_kv_heads;
+  const int G = d.n_q_heads / d.n_kv_heads;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, kAlignWs);
+    return at;
+  };
+  ws->n_sel_tiles = (d.t_max + kSelTile - 1) / kSelTile;
+  ws->row_state = take(rows * kRowStateWords * 4);
+  if (op == JSSA_OP_TOPK || op == JSSA_OP_DECODE) {
+    ws->hist1 = take(rows * kDigit1Bins * 4);
+    ws->tile_gt = take(rows * ws->n_sel_tiles * 4);
+    ws->tile_off = take(rows * ws->n_sel_tiles * 4);
+    ws->cand = take(rows * size_t(d.t_max) * 8);
+  }
+  if (op == JSSA_OP_ATTN || op == JSSA_OP_DECODE || op == JSSA_OP_DENSE) {
+    const bool indexed = op != JSSA_OP_DENSE;
+    const int64_t n_max = indexed ? int64_t(d.topk) + d.window : d.t_max;
+    attn_chunking(int(rows), n_max, indexed, &ws->chunk, &ws->n_chunks);
+    ws->part_acc = take(rows * ws->n_chunks * size_t(G) * d.d_v * 4);
+    ws->part_ml = take(rows * ws->n_chunks * size_t(G) * 2 * 4);
+  }
+  if (op == JSSA_OP_DECODE) {
+    ws->scores = take(rows * size_t(d.t_max) * 4);
+    ws->idx = take(rows * (size_t(d.topk) + d.window) * 4);
+    ws->n_sel = take(rows * 4);
+  }
+  ws->total = off;
+  return true;
+}
+
+static int32_t check_ws(const jssa_desc& d, int op, void* ws, size_t ws_bytes, Workspace* lay) {
+  if (!workspace_layout(d, op, lay)) return JSSA_ERR_INVALID_ARG;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlignWs) != 0 || ws_bytes < lay->total)
+    return JSSA_ERR_WORKSPACE;
+  return JSSA_OK;
+}
+
+}  // namespace jssa
+
+using namespace jssa;
+
+#define JSSA_TRY(expr)            \
+  do {                            \
+    const int32_t st_ = (expr);   \
+    if (st_ != JSSA_OK) return st_; \
+  } while (0)
+
+extern "C" {
+
+int32_t jssa_abi_version(void) { return JSSA_ABI_VERSION; }
+
+const char* jssa_status_str(int32_t s) {
+  switch (s) {
+    case JSSA_OK: return "JSSA_OK";
+    case JSSA_ERR_INVALID_ARG: return "JSSA_ERR_INVALID_ARG";
+    case JSSA_ERR_UNSUPPORTED: return "JSSA_ERR_UNSUPPORTED";
+    case JSSA_ERR_WORKSPACE: return "JSSA_ERR_WORKSPACE";
+    case JSSA_ERR_MISALIGNED: return "JSSA_ERR_MISALIGNED";
+    case JSSA_ERR_HIP: return "JSSA_ERR_HIP";
+  }
+  return "JSSA_ERR_UNKNOWN";
+}
+
+int32_t jssa_check_desc(const jssa_desc* desc, int32_t op) {
+  if (op < 0 || op > JSSA_OP_DENSE) return JSSA_ERR_INVALID_ARG;
+  return check(desc, op);
+}
+
+size_t jssa_workspace_bytes(const jssa_desc* desc, int32_t op) {
+  if (!desc || op < JSSA_OP_TOPK || op > JSSA_OP_DENSE) return 0;
+  Workspace w;
+  if (!workspace_layout(*desc, op, &w)) return 0;
+  return w.total;
+}
+
+int32_t jssa_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws && ws_bytes) return JSSA_ERR_INVALID_ARG;
+  if (ws && (reinterpret_cast<uintptr_t>(ws) % 256) != 0) return JSSA_ERR_WORKSPACE;
+  return to_status(launch_zero(ws, ws_bytes, as_stream(stream)));
+}
+
+int32_t jssa_append_kv(const jssa_desc* desc, const void* k_new, const void* v_new, int32_t n_new,
+                       const int32_t* pos, const float* P, void* k_cache, void* v_cache,
+                       void* kp_cache, void* stream) {
+  JSSA_TRY(check(desc, 0));
+  if (n_new < 0) return JSSA_ERR_INVALID_ARG;
+  if (!pos || !P || !k_cache || !kp_cache) return JSSA_ERR_INVALID_ARG;
+  const bool mla = desc->layout == JSSA_LAYOUT_MLA;
+  if (k_new && !mla && (!v_new || !v_cache)) return JSSA_ERR_INVALID_ARG;
+  if (!aligned16(P) || !aligned16(k_cache) || !aligned16(kp_cache) || !aligned16(pos) ||
+      (k_new && !aligned16(k_new)) || (v_new && !aligned16(v_new)) || (v_cache && !aligned16(v_cache)))
+    return JSSA_ERR_MISALIGNED;
+  if (n_new == 0) return JSSA_OK;
+  return to_status(launch_append(*desc, k_new, v_new, n_new, pos, P, k_cache, v_cache, kp_cache,
+                                 as_stream(stream)));
+}
+
+int32_t jssa_score(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
+                   const int32_t* seq_lens, float* scores, void* stream) {
+  JSSA_TRY(check(desc, 0));
+  if (!q || !P || !kp_cache || !seq_lens || !scores) return JSSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(P) || !aligned16(kp_cache) || !aligned16(seq_lens) || !aligned16(scores))
+    return JSSA_ERR_MISALIGNED;
+  Workspace none;
+  return to_status(launch_score(*desc, q, P, kp_cache, seq_lens, scores, nullptr, none, as_stream(stream)));
+}
+
+int32_t jssa_topk(const jssa_desc* desc, const float* scores, const int32_t* seq_lens,
+                  int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {
+  JSSA_TRY(check(desc, JSSA_OP_TOPK));
+  if (!scores || !seq_lens || !idx || !n_sel) return JSSA_ERR_INVALID_ARG;
+  if (!aligned16(scores) || !aligned16(seq_lens) || !aligned16(idx) || !aligned16(n_sel))
+    return JSSA_ERR_MISALIGNED;
+  Workspace lay;
+  JSSA_TRY(check_ws(*desc, JSSA_OP_TOPK, ws, ws_bytes, &lay));
+  return to_status(launch_topk(*desc, scores, seq_lens, idx, n_sel, static_cast<char*>(ws), lay, false,
+                               as_stream(stream)));
+}
+
+int32_t jssa_indexed_attn(const jssa_desc* desc, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* idx, const int32_t* n_sel,
+                          void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  JSSA_TRY(check(desc, JSSA_OP_ATTN));
+  if (!q || !k_cache || !v_cache || !idx || !n_sel || !out) return JSSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(idx) ||
+      !aligned16(n_sel) || !aligned16(out) || (lse && !aligned16(lse)))
+    return JSSA_ERR_MISALIGNED;
+  Workspace lay;
+  JSSA_TRY(check_ws(*desc, JSSA_OP_ATTN, ws, ws_bytes, &lay));
+  return to_status(launch_attention(*desc, q, k_cache, v_cache, idx, n_sel, nullptr, out, lse,
+                                    static_cast<char*>(ws), lay, as_stream(stream)));
+}
+
+int32_t jssa_decode(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
+                    const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                    void* out, float* lse, int32_t* idx_out, int32_t* n_sel_out,
+                    void* ws, size_t ws_bytes, void* stream) {
+  JSSA_TRY(check(desc, JSSA_OP_DECODE));
+  if (!q || !P || !kp_cache || !k_cache || !v_cache || !seq_lens || !out) return JSSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(P) || !aligned16(kp_cache) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(seq_lens) || !aligned16(out) || (lse && !aligned16(lse)) ||
+      (idx_out && !aligned16(idx_out)) || (n_sel_out && !aligned16(n_sel_out)))
+    return JSSA_ERR_MISALIGNED;
+  Workspace lay;
+  JSSA_TRY(check_ws(*desc, JSSA_OP_DECODE, ws, ws_bytes, &lay));
+  char* base = static_cast<char*>(ws);
+  float* scores = reinterpret_cast<float*>(base + lay.scores);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + lay.idx);
+  int32_t* n_sel = n_sel_out ? n_sel_out : reinterpret_cast<int32_t*>(base + lay.n_sel);
+  hipStream_t s = as_stream(stream);
+  hipError_t e = launch_score(*desc, q, P, kp_cache, seq_lens, scores, base, lay, s);
+  if (e == hipSuccess) e = launch_topk(*desc, scores, seq_lens, idx, n_sel, base, lay, true, s);
+  if (e == hipSuccess)
+    e = launch_attention(*desc, q, k_cache, v_cache, idx, n_sel, nullptr, out, lse, base, lay, s);
+  return to_status(e);
+}
+
+int32_t jssa_dense_decode(const jssa_desc* desc, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* seq_lens, void* out, float* lse,
+                          void* ws, size_t ws_bytes, void* stream) {
+  JSSA_TRY(check(desc, JSSA_OP_DENSE));
+  if (!q || !k_cache || !v_cache || !seq_lens || !out) return JSSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(seq_lens) ||
+      !aligned16(out) || (lse && !aligned16(lse)))
+    return JSSA_ERR_MISALIGNED;
+  Workspace lay;
+  JSSA_TRY(check_ws(*desc, JSSA_OP_DENSE, ws, ws_bytes, &lay));
+  return to_status(launch_attention(*desc, q, k_cache, v_cache, nullptr, nullptr, seq_lens, out, lse,
+                                    static_cast<char*>(ws), lay, as_stream(stream)));
+}
+
+}  // extern "C"

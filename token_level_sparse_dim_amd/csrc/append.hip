@@ -1,0 +1,130 @@
+// Append new K/V rows and project keys into the scoring cache (JSSA summary
+// section E.1: each newly generated key is projected; sections 3.1 and 3.4:
+// the scoring-only cache holds Kp = K P per KV head).  One lane per token:
+// the lane walks its key row in 16-byte pieces and accumulates the rank-R
+// projection in fp32; the basis rows are wave-uniform, so they come through
+// the scalar cache.
+#include "jssa_device.hpp"
+#include "jssa_internal.hpp"
+
+namespace jssa {
+
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* pos;
+  const float* P;
+  void* k_cache;
+  void* v_cache;
+  void* kp;
+  int n_new, Hkv, d_k, d_v, t_max;
+  int mla;
+};
+
+template <int KVT, int KPT, int R>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  constexpr int EB = Elem<KVT>::bytes;
+  constexpr int EPL = Elem<KVT>::per16;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= a.n_new) return;
+  const int t = a.pos[b] + j;
+  if (t < 0 || t >= a.t_max) return;
+
+  char* kc = reinterpret_cast<char*>(a.k_cache);
+  const size_t crow = ((size_t(b) * a.t_max + t) * a.Hkv + h) * a.d_k * EB;
+  const char* src;
+  if (a.k_new) {
+    const char* kn = reinterpret_cast<const char*>(a.k_new);
+    src = kn + ((size_t(b) * a.n_new + j) * a.Hkv + h) * a.d_k * EB;
+    for (int o = 0; o < a.d_k * EB; o += 16) *reinterpret_cast<uint4*>(kc + crow + o) = load16(src + o);
+    if (!a.mla && a.v_new) {
+      const char* vn = reinterpret_cast<const char*>(a.v_new);
+      const char* vs = vn + ((size_t(b) * a.n_new + j) * a.Hkv + h) * a.d_v * EB;
+      char* vc = reinterpret_cast<char*>(a.v_cache) + ((size_t(b) * a.t_max + t) * a.Hkv + h) * a.d_v * EB;
+      for (int o = 0; o < a.d_v * EB; o += 16) *reinterpret_cast<uint4*>(vc + o) = load16(vs + o);
+    }
+  } else {
+    src = kc + crow;
+  }
+
+  float acc[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) acc[i] = 0.f;
+  const float* Ph = a.P + size_t(h) * a.d_k * R;
+  for (int d0 = 0; d0 < a.d_k; d0 += EPL) {
+    float kv[EPL];
+    unpack16<KVT>(load16(src + size_t(d0) * EB), kv);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float* Pr = Ph + size_t(d0 + e) * R;
+#pragma unroll
+      for (int i = 0; i < R; ++i) acc[i] = fmaf(kv[e], Pr[i], acc[i]);
+    }
+  }
+
+  char* kprow = reinterpret_cast<char*>(a.kp) + ((size_t(b) * a.Hkv + h) * a.t_max + t) * R * Elem<KPT>::bytes;
+  if constexpr (KPT == 1) {
+#pragma unroll
+    for (int i = 0; i < R; i += 8) {
+      uint4 w;
+      w.x = uint32_t(f32_to_bf16_rne(acc[i + 0])) | (uint32_t(f32_to_bf16_rne(acc[i + 1])) << 16);
+      w.y = uint32_t(f32_to_bf16_rne(acc[i + 2])) | (uint32_t(f32_to_bf16_rne(acc[i + 3])) << 16);
+      w.z = uint32_t(f32_to_bf16_rne(acc[i + 4])) | (uint32_t(f32_to_bf16_rne(acc[i + 5])) << 16);
+      w.w = uint32_t(f32_to_bf16_rne(acc[i + 6])) | (uint32_t(f32_to_bf16_rne(acc[i + 7])) << 16);
+      *reinterpret_cast<uint4*>(kprow + i * 2) = w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < R; i += 4)
+      *reinterpret_cast<float4*>(kprow + i * 4) = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
+  }
+}
+
+template <int KVT, int KPT>
+static hipError_t dispatch_append_r(const AppendArgs& args, int r, dim3 grid, hipStream_t s) {
+  switch (r) {
+    case 16: hipLaunchKernelGGL((append_kernel<KVT, KPT, 16>), grid, dim3(256), 0, s, args); break;
+    case 32: hipLaunchKernelGGL((append_kernel<KVT, KPT, 32>), grid, dim3(256), 0, s, args); break;
+    case 64: hipLaunchKernelGGL((append_kernel<KVT, KPT, 64>), grid, dim3(256), 0, s, args); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const jssa_desc& d, const void* k_new, const void* v_new, int n_new,
+                         const int32_t* pos, const float* P, void* k_cache, void* v_cache,
+                         void* kp_cache, hipStream_t s) {
+  AppendArgs a;
+  a.k_new = k_new; a.v_new = v_new; a.pos = pos; a.P = P;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.kp = kp_cache;
+  a.n_new = n_new; a.Hkv = d.n_kv_heads; a.d_k = d.d_k; a.d_v = d.d_v; a.t_max = d.t_max;
+  a.mla = d.layout == JSSA_LAYOUT_MLA;
+  dim3 grid((n_new + 255) / 256, d.n_kv_heads, d.batch);
+  const bool kvb = d.kv_dtype == JSSA_BF16, kpb = d.kp_dtype == JSSA_BF16;
+  if (kvb && kpb) return dispatch_append_r<1, 1>(a, d.rank, grid, s);
+  if (kvb && !kpb) return dispatch_append_r<1, 0>(a, d.rank, grid, s);
+  if (!kvb && kpb) return dispatch_append_r<0, 1>(a, d.rank, grid, s);
+  return dispatch_append_r<0, 0>(a, d.rank, grid, s);
+}
+
+// Workspace zero-fill: a kernel rather than a memset so that it can be
+// captured in a graph.
+__global__ __launch_bounds__(256) void zero_kernel(char* p, size_t bytes) {
+  const size_t n16 = bytes / 16;
+  const size_t stride = size_t(gridDim.x) * 256;
+  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += stride)
+    reinterpret_cast<uint4*>(p)[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (blockIdx.x == 0 && threadIdx.x < (bytes & 15)) p[n16 * 16 + threadIdx.x] = 0;
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  size_t blocks = (bytes / 16 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(zero_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, reinterpret_cast<char*>(p), bytes);
+  return hipGetLastError();
+}
+
+}  // namespace jssa

@@ -1,0 +1,226 @@
+// Subspace score scan (JSSA summary Figure 1, sections 3.1 and E.1): every
+// candidate token of every (sequence, KV head) is scored against the
+// projected queries of the head's group, reading the projected-key cache once
+// with coalesced 16-byte loads.  Optionally builds the first radix digit
+// histogram of the scores for selection, so that selection needs no extra
+// pass over the scores for it.
+#include "jssa_device.hpp"
+#include "jssa_internal.hpp"
+#include "select_common.hpp"
+
+namespace jssa {
+
+struct ScoreArgs {
+  const void* q;
+  const float* P;
+  const void* kp;
+  const int32_t* seq_lens;
+  float* scores;
+  uint32_t* hist1;      // null: no histogram
+  uint32_t* row_state;
+  int Hq, Hkv, G, d_k, t_max, topk, window, q_dtype;
+};
+
+// One workgroup (4 waves) per kScoreTile candidate tokens of one (b, h) row.
+// Each token's projected key (R elements) is spread over LPT = R*bytes/16
+// lanes; each lane holds the matching slice of the G projected queries in
+// registers, and the per-head dot products are completed with DPP sums.
+// GE = G for the group max, 1 for the group mean.
+template <int KPT, int R, int GE>
+__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+  constexpr int EB = Elem<KPT>::bytes;
+  constexpr int EPL = Elem<KPT>::per16;
+  constexpr int LPT = R / EPL;
+  constexpr int TPW = 64 / LPT;
+  constexpr int U = 4;
+  constexpr int PER_ITER = 4 * TPW * U;
+  static_assert(LPT >= 1 && LPT <= 16 && (LPT & (LPT - 1)) == 0, "lanes per token");
+
+  __shared__ uint32_t s_hist[kDigit1Bins];
+  __shared__ float s_qp[8 * 64];
+  __shared__ uint32_t s_scan[256];
+  __shared__ uint32_t s_out[2];
+
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int row = b * a.Hkv + h;
+  int Tb;
+  const int n_cand = candidates_of(a.seq_lens, b, a.t_max, a.window, &Tb);
+  const int t0 = tile * kScoreTile;
+  if (t0 >= n_cand) return;
+  const bool do_hist = a.hist1 != nullptr && a.topk > 0 && a.topk < n_cand;
+
+  if (do_hist)
+    for (int i = threadIdx.x; i < kDigit1Bins; i += 256) s_hist[i] = 0u;
+
+  // projected queries of the group, fp32: qp[g][i] = sum_d q[b, hG+g, d] P[h, d, i]
+  const int G = a.G;
+  for (int j = threadIdx.x; j < G * R; j += 256) {
+    const int g = j / R, i = j - g * R;
+    const size_t qoff = (size_t(b) * a.Hq + size_t(h) * G + g) * a.d_k;
+    const float* Pc = a.P + size_t(h) * a.d_k * R + i;
+    float acc = 0.f;
+    for (int d = 0; d < a.d_k; ++d) acc = fmaf(load_elem(a.q, qoff + d, a.q_dtype), Pc[size_t(d) * R], acc);
+    s_qp[j] = acc;
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p = lane % LPT, tw = lane / LPT;
+  float qreg[GE][EPL];
+  if constexpr (GE == 1) {
+    const float invG = 1.0f / float(G);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float s = 0.f;
+      for (int g = 0; g < G; ++g) s += s_qp[g * R + p * EPL + e];
+      qreg[0][e] = s * invG;
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < GE; ++g)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qreg[g][e] = s_qp[g * R + p * EPL + e];
+  }
+
+  const char* kp_row = reinterpret_cast<const char*>(a.kp) + size_t(row) * a.t_max * R * EB;
+  float* srow = a.scores + size_t(row) * a.t_max;
+  const int t_end = min(t0 + kScoreTile, n_cand);
+
+  for (int base = t0; base < t_end; base += PER_ITER) {
+    uint4 v[U];
+    int tok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      tok[u] = base + (wave * U + u) * TPW + tw;
+      if (tok[u] < t_end)
+        v[u] = load16(kp_row + (size_t(tok[u]) * R + p * EPL) * EB);
+      else
+        v[u] = make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kv[EPL];
+      unpack16<KPT>(v[u], kv);
+      float best;
+#pragma unroll
+      for (int g = 0; g < GE; ++g) {
+        float dsum = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dsum = fmaf(qreg[g][e], kv[e], dsum);
+        dsum = group_sum<LPT>(dsum);
+        best = (g == 0) ? dsum : fmaxf(best, dsum);
+      }
+      if (p == 0 && tok[u] < t_end) {
+        srow[tok[u]] = best;
+        if (do_hist) atomicAdd(&s_hist[score_key(best) >> (32 - kDigit1Bits)], 1u);
+      }
+    }
+  }
+
+  if (!do_hist) return;
+  __syncthreads();
+  uint32_t* g_hist = a.hist1 + size_t(row) * kDigit1Bins;
+  for (int i = threadIdx.x; i < kDigit1Bins; i += 256) {
+    const uint32_t c = s_hist[i];
+    if (c) atomicAdd(&g_hist[i], c);
+  }
+  uint32_t* g_state = a.row_state + size_t(row) * kRowStateWords;
+  const uint32_t n_tiles = uint32_t((n_cand + kScoreTile - 1) / kScoreTile);
+  if (!last_arrival(&g_state[RS_TICKET_SCORE], n_tiles)) return;
+  finish_first_digit(g_hist, g_state, s_hist, s_scan, s_out, uint32_t(a.topk));
+}
+
+// First-digit histogram of caller-provided fp32 scores (the stand-alone
+// selection entry point), one workgroup per kSelTile keys of a row.
+struct HistArgs {
+  const float* scores;
+  const int32_t* seq_lens;
+  uint32_t* hist1;
+  uint32_t* row_state;
+  int Hkv, t_max, topk, window;
+};
+
+__global__ __launch_bounds__(256) void hist_kernel(HistArgs a) {
+  __shared__ uint32_t s_hist[kDigit1Bins];
+  __shared__ uint32_t s_scan[256];
+  __shared__ uint32_t s_out[2];
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int row = b * a.Hkv + h;
+  int Tb;
+  const int n_cand = candidates_of(a.seq_lens, b, a.t_max, a.window, &Tb);
+  const int t0 = tile * kSelTile;
+  if (t0 >= n_cand || a.topk <= 0 || a.topk >= n_cand) return;
+  for (int i = threadIdx.x; i < kDigit1Bins; i += 256) s_hist[i] = 0u;
+  __syncthreads();
+  const float* srow = a.scores + size_t(row) * a.t_max;
+  const int t_end = min(t0 + kSelTile, n_cand);
+  for (int t = t0 + threadIdx.x; t < t_end; t += 256)
+    atomicAdd(&s_hist[score_key(srow[t]) >> (32 - kDigit1Bits)], 1u);
+  __syncthreads();
+  uint32_t* g_hist = a.hist1 + size_t(row) * kDigit1Bins;
+  for (int i = threadIdx.x; i < kDigit1Bins; i += 256) {
+    const uint32_t c = s_hist[i];
+    if (c) atomicAdd(&g_hist[i], c);
+  }
+  uint32_t* g_state = a.row_state + size_t(row) * kRowStateWords;
+  const uint32_t n_tiles = uint32_t((n_cand + kSelTile - 1) / kSelTile);
+  if (!last_arrival(&g_state[RS_TICKET_SCORE], n_tiles)) return;
+  finish_first_digit(g_hist, g_state, s_hist, s_scan, s_out, uint32_t(a.topk));
+}
+
+// ---- launchers ----------------------------------------------------------------------
+template <int KPT, int R, int GE>
+static hipError_t launch_score_t(const ScoreArgs& args, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((score_kernel<KPT, R, GE>), grid, dim3(256), 0, s, args);
+  return hipGetLastError();
+}
+
+template <int KPT, int R>
+static hipError_t dispatch_ge(const ScoreArgs& args, int ge, dim3 grid, hipStream_t s) {
+  switch (ge) {
+    case 1: return launch_score_t<KPT, R, 1>(args, grid, s);
+    case 2: return launch_score_t<KPT, R, 2>(args, grid, s);
+    case 4: return launch_score_t<KPT, R, 4>(args, grid, s);
+    case 8: return launch_score_t<KPT, R, 8>(args, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int KPT>
+static hipError_t dispatch_r(const ScoreArgs& args, int r, int ge, dim3 grid, hipStream_t s) {
+  switch (r) {
+    case 16: return dispatch_ge<KPT, 16>(args, ge, grid, s);
+    case 32: return dispatch_ge<KPT, 32>(args, ge, grid, s);
+    case 64: return dispatch_ge<KPT, 64>(args, ge, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_score(const jssa_desc& d, const void* q, const float* P, const void* kp,
+                        const int32_t* seq_lens, float* scores, char* ws_base, const Workspace& ws,
+                        hipStream_t s) {
+  ScoreArgs a;
+  a.q = q; a.P = P; a.kp = kp; a.seq_lens = seq_lens; a.scores = scores;
+  a.hist1 = ws_base ? reinterpret_cast<uint32_t*>(ws_base + ws.hist1) : nullptr;
+  a.row_state = ws_base ? reinterpret_cast<uint32_t*>(ws_base + ws.row_state) : nullptr;
+  a.Hq = d.n_q_heads; a.Hkv = d.n_kv_heads; a.G = d.n_q_heads / d.n_kv_heads;
+  a.d_k = d.d_k; a.t_max = d.t_max; a.topk = d.topk; a.window = d.window; a.q_dtype = d.kv_dtype;
+  const int ge = (d.reduce == JSSA_REDUCE_MEAN) ? 1 : a.G;
+  dim3 grid((d.t_max + kScoreTile - 1) / kScoreTile, d.n_kv_heads, d.batch);
+  if (d.kp_dtype == JSSA_BF16) return dispatch_r<1>(a, d.rank, ge, grid, s);
+  return dispatch_r<0>(a, d.rank, ge, grid, s);
+}
+
+hipError_t launch_hist(const jssa_desc& d, const float* scores, const int32_t* seq_lens,
+                       char* ws_base, const Workspace& ws, hipStream_t s) {
+  HistArgs a;
+  a.scores = scores; a.seq_lens = seq_lens;
+  a.hist1 = reinterpret_cast<uint32_t*>(ws_base + ws.hist1);
+  a.row_state = reinterpret_cast<uint32_t*>(ws_base + ws.row_state);
+  a.Hkv = d.n_kv_heads; a.t_max = d.t_max; a.topk = d.topk; a.window = d.window;
+  dim3 grid((d.t_max + kSelTile - 1) / kSelTile, d.n_kv_heads, d.batch);
+  hipLaunchKernelGGL(hist_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace jssa
