@@ -15,7 +15,7 @@ from ._lib import (BF16, F32, LAYOUT_GQA, LAYOUT_MLA, OP_ATTN, OP_DECODE, OP_DEN
 __all__ = [
     "Desc", "JssaError", "F32", "BF16", "REDUCE_MAX", "REDUCE_MEAN", "LAYOUT_GQA", "LAYOUT_MLA",
     "OP_TOPK", "OP_ATTN", "OP_DECODE", "OP_DENSE", "lib", "abi_version", "check_desc",
-    "workspace_bytes", "workspace", "append_kv", "append_projection", "score", "topk", "indexed_attn", "decode",
+    "workspace_bytes", "workspace", "append_kv", "append_projection", "score", "topk", "indexed_attn", "decode", "decode_profiled",
     "dense_decode",
 ]
 
@@ -117,6 +117,25 @@ def decode(desc: Desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, ws,
          _ptr(out, _TORCH_DTYPE[desc.out_dtype], "out"), _ptr(lse, torch.float32, "lse"),
          _ptr(idx_out, torch.int32, "idx_out"), _ptr(n_sel_out, torch.int32, "n_sel_out"),
          _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream))
+
+
+def decode_profiled(desc: Desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, ws, events,
+                    idx_out=None, n_sel_out=None, stream=None):
+    """``jssa_decode_profiled``: ``jssa_decode`` recording five stage events
+    (``torch.cuda.Event(enable_timing=True)``, each already recorded once so that
+    it exists): before scoring, after scoring, after selection resolution, after
+    index emission, after attention."""
+    import ctypes
+    if len(events) != 5:
+        raise ValueError("five events are needed")
+    arr = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    kv = _TORCH_DTYPE[desc.kv_dtype]
+    call("jssa_decode_profiled", desc.c(), _ptr(q, kv, "q"), _ptr(P, torch.float32, "P"),
+         _ptr(kp_cache, _TORCH_DTYPE[desc.kp_dtype], "kp_cache"), _ptr(k_cache, kv, "k_cache"),
+         _ptr(v_cache, kv, "v_cache"), _ptr(seq_lens, torch.int32, "seq_lens"),
+         _ptr(out, _TORCH_DTYPE[desc.out_dtype], "out"), _ptr(lse, torch.float32, "lse"),
+         _ptr(idx_out, torch.int32, "idx_out"), _ptr(n_sel_out, torch.int32, "n_sel_out"),
+         _ptr(ws, torch.uint8, "ws"), ws.numel(), arr, _stream(stream))
 
 
 def dense_decode(desc: Desc, q, k_cache, v_cache, seq_lens, out, lse, ws, stream=None):

@@ -57,5 +57,17 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+
+def source_digest(name: str) -> str:
+    """Short content hash of one kernel source plus the shared headers (used to
+    tell whether a stored counter measurement still describes the current kernel)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in (name, "jssa_device.hpp", "jssa_internal.hpp", "select_common.hpp"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

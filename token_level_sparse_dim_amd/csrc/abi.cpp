@@ -201,16 +201,19 @@ int32_t jssa_indexed_attn(const jssa_desc* desc, const void* q, const void* k_ca
                                     static_cast<char*>(ws), lay, as_stream(stream)));
 }
 
-int32_t jssa_decode(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
-                    const void* k_cache, const void* v_cache, const int32_t* seq_lens,
-                    void* out, float* lse, int32_t* idx_out, int32_t* n_sel_out,
-                    void* ws, size_t ws_bytes, void* stream) {
+static int32_t decode_impl(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
+                           const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                           void* out, float* lse, int32_t* idx_out, int32_t* n_sel_out,
+                           void* ws, size_t ws_bytes, void* const* ev, void* stream) {
   JSSA_TRY(check(desc, JSSA_OP_DECODE));
   if (!q || !P || !kp_cache || !k_cache || !v_cache || !seq_lens || !out) return JSSA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(P) || !aligned16(kp_cache) || !aligned16(k_cache) ||
       !aligned16(v_cache) || !aligned16(seq_lens) || !aligned16(out) || (lse && !aligned16(lse)) ||
       (idx_out && !aligned16(idx_out)) || (n_sel_out && !aligned16(n_sel_out)))
     return JSSA_ERR_MISALIGNED;
+  if (ev)
+    for (int i = 0; i < 5; ++i)
+      if (!ev[i]) return JSSA_ERR_INVALID_ARG;
   Workspace lay;
   JSSA_TRY(check_ws(*desc, JSSA_OP_DECODE, ws, ws_bytes, &lay));
   char* base = static_cast<char*>(ws);
@@ -218,11 +221,35 @@ int32_t jssa_decode(const jssa_desc* desc, const void* q, const float* P, const 
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + lay.idx);
   int32_t* n_sel = n_sel_out ? n_sel_out : reinterpret_cast<int32_t*>(base + lay.n_sel);
   hipStream_t s = as_stream(stream);
-  hipError_t e = launch_score(*desc, q, P, kp_cache, seq_lens, scores, base, lay, s);
-  if (e == hipSuccess) e = launch_topk(*desc, scores, seq_lens, idx, n_sel, base, lay, true, s);
+  auto mark = [&](int i) { return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
+  hipError_t e = mark(0);
+  if (e == hipSuccess) e = launch_score(*desc, q, P, kp_cache, seq_lens, scores, base, lay, s);
+  if (e == hipSuccess) e = mark(1);
+  if (e == hipSuccess)
+    e = launch_topk(*desc, scores, seq_lens, idx, n_sel, base, lay, true, s,
+                    ev ? static_cast<hipEvent_t>(ev[2]) : nullptr);
+  if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess)
     e = launch_attention(*desc, q, k_cache, v_cache, idx, n_sel, nullptr, out, lse, base, lay, s);
+  if (e == hipSuccess) e = mark(4);
   return to_status(e);
+}
+
+int32_t jssa_decode(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
+                    const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                    void* out, float* lse, int32_t* idx_out, int32_t* n_sel_out,
+                    void* ws, size_t ws_bytes, void* stream) {
+  return decode_impl(desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, idx_out, n_sel_out,
+                     ws, ws_bytes, nullptr, stream);
+}
+
+int32_t jssa_decode_profiled(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
+                             const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                             void* out, float* lse, int32_t* idx_out, int32_t* n_sel_out,
+                             void* ws, size_t ws_bytes, void* const* stage_events, void* stream) {
+  if (!stage_events) return JSSA_ERR_INVALID_ARG;
+  return decode_impl(desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, idx_out, n_sel_out,
+                     ws, ws_bytes, stage_events, stream);
 }
 
 int32_t jssa_dense_decode(const jssa_desc* desc, const void* q, const void* k_cache,

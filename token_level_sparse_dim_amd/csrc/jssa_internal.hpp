@@ -77,7 +77,7 @@ hipError_t launch_hist(const jssa_desc& d, const float* scores, const int32_t* s
 // exact resolution, emission of indices in ascending order plus the window.
 hipError_t launch_topk(const jssa_desc& d, const float* scores, const int32_t* seq_lens,
                        int32_t* idx, int32_t* n_sel, char* ws_base, const Workspace& ws,
-                       bool hist_done, hipStream_t s);
+                       bool hist_done, hipStream_t s, hipEvent_t after_select = nullptr);
 
 // Attention over idx (indexed) or over every cached token (idx == nullptr).
 hipError_t launch_attention(const jssa_desc& d, const void* q, const void* k_cache,

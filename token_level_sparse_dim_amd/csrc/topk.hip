@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void emit_kernel(SelArgs a) {
 // ---- launcher -------------------------------------------------------------------------
 hipError_t launch_topk(const jssa_desc& d, const float* scores, const int32_t* seq_lens,
                        int32_t* idx, int32_t* n_sel, char* ws_base, const Workspace& ws,
-                       bool hist_done, hipStream_t s) {
+                       bool hist_done, hipStream_t s, hipEvent_t after_select) {
   if (!hist_done) {
     hipError_t e = launch_hist(d, scores, seq_lens, ws_base, ws, s);
     if (e != hipSuccess) return e;
@@ -230,6 +230,10 @@ hipError_t launch_topk(const jssa_desc& d, const float* scores, const int32_t* s
   hipLaunchKernelGGL(select_kernel, grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (after_select) {
+    e = hipEventRecord(after_select, s);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(emit_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
