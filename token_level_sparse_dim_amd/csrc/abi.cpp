@@ -78,6 +78,7 @@ bool workspace_layout(const jssa_desc& d, int op, Workspace* ws) {
   ws->row_state = take(rows * kRowStateWords * 4);
   if (op == JSSA_OP_TOPK || op == JSSA_OP_DECODE) {
     ws->hist1 = take(rows * kDigit1Bins * 4);
+    ws->hist2 = take(rows * 4096 * 4);
     ws->tile_gt = take(rows * ws->n_sel_tiles * 4);
     ws->tile_off = take(rows * ws->n_sel_tiles * 4);
     ws->cand = take(rows * size_t(d.t_max) * 8);

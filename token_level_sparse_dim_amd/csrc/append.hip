@@ -9,6 +9,8 @@
 
 namespace jssa {
 
+constexpr int kAppendRowsMax = 64;  // up to this many new rows: one workgroup per row
+
 struct AppendArgs {
   const void* k_new;
   const void* v_new;
@@ -81,8 +83,68 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 }
 
+// Few new rows (a decode step): one workgroup per (b, j, h) row; the rank-R
+// projection is split over 256 threads (R outputs x 256/R slices of d) with
+// the basis read coalesced and the key row staged in shared memory.
+template <int KVT, int KPT, int R>
+__global__ __launch_bounds__(256) void append_rows_kernel(AppendArgs a) {
+  constexpr int EB = Elem<KVT>::bytes;
+  constexpr int EPL = Elem<KVT>::per16;
+  constexpr int PARTS = 256 / R;
+  __shared__ float s_k[576];
+  __shared__ float s_part[256];
+  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int t = a.pos[b] + j;
+  if (t < 0 || t >= a.t_max) return;
+  char* kc = reinterpret_cast<char*>(a.k_cache);
+  const size_t crow = ((size_t(b) * a.t_max + t) * a.Hkv + h) * a.d_k * EB;
+  const char* src = kc + crow;
+  if (a.k_new) src = reinterpret_cast<const char*>(a.k_new) + ((size_t(b) * a.n_new + j) * a.Hkv + h) * a.d_k * EB;
+  const int n16 = a.d_k * EB / 16;
+  for (int c = threadIdx.x; c < n16; c += 256) {
+    const uint4 v = load16(src + size_t(c) * 16);
+    float f[EPL];
+    unpack16<KVT>(v, f);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s_k[c * EPL + e] = f[e];
+    if (a.k_new) *reinterpret_cast<uint4*>(kc + crow + size_t(c) * 16) = v;
+  }
+  if (a.k_new && !a.mla && a.v_new) {
+    const char* vs = reinterpret_cast<const char*>(a.v_new) + ((size_t(b) * a.n_new + j) * a.Hkv + h) * a.d_v * EB;
+    char* vc = reinterpret_cast<char*>(a.v_cache) + ((size_t(b) * a.t_max + t) * a.Hkv + h) * a.d_v * EB;
+    for (int c = threadIdx.x; c < a.d_v * EB / 16; c += 256)
+      *reinterpret_cast<uint4*>(vc + size_t(c) * 16) = load16(vs + size_t(c) * 16);
+  }
+  __syncthreads();
+  const int o = threadIdx.x % R, part = threadIdx.x / R;
+  const int dper = (a.d_k + PARTS - 1) / PARTS;
+  const int d0 = part * dper, d1 = min(a.d_k, d0 + dper);
+  const float* Pc = a.P + size_t(h) * a.d_k * R + o;
+  float acc = 0.f;
+  for (int d = d0; d < d1; ++d) acc = fmaf(s_k[d], Pc[size_t(d) * R], acc);
+  s_part[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x < R) {
+    float sum = 0.f;
+    for (int pp = 0; pp < PARTS; ++pp) sum += s_part[pp * R + threadIdx.x];
+    char* kprow = reinterpret_cast<char*>(a.kp) + ((size_t(b) * a.Hkv + h) * a.t_max + t) * R * Elem<KPT>::bytes;
+    if constexpr (KPT == 1) reinterpret_cast<uint16_t*>(kprow)[threadIdx.x] = f32_to_bf16_rne(sum);
+    else reinterpret_cast<float*>(kprow)[threadIdx.x] = sum;
+  }
+}
+
 template <int KVT, int KPT>
 static hipError_t dispatch_append_r(const AppendArgs& args, int r, dim3 grid, hipStream_t s) {
+  if (args.n_new <= kAppendRowsMax) {
+    dim3 g(args.n_new, grid.y, grid.z);
+    switch (r) {
+      case 16: hipLaunchKernelGGL((append_rows_kernel<KVT, KPT, 16>), g, dim3(256), 0, s, args); break;
+      case 32: hipLaunchKernelGGL((append_rows_kernel<KVT, KPT, 32>), g, dim3(256), 0, s, args); break;
+      case 64: hipLaunchKernelGGL((append_rows_kernel<KVT, KPT, 64>), g, dim3(256), 0, s, args); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (r) {
     case 16: hipLaunchKernelGGL((append_kernel<KVT, KPT, 16>), grid, dim3(256), 0, s, args); break;
     case 32: hipLaunchKernelGGL((append_kernel<KVT, KPT, 32>), grid, dim3(256), 0, s, args); break;

@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // merge the 4 waves -> this chunk's partial state
+  // merge the 4 waves -> this chunk's partial state, published for the combine
   float* pacc = a.part_acc + (size_t(row) * a.n_chunks + chunk_id) * G * D;
   float* pml = a.part_ml + (size_t(row) * a.n_chunks + chunk_id) * G * 2;
   for (int j = threadIdx.x; j < G * D; j += 256) {
@@ -202,8 +202,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       L = fmaf(s_l[w][g], sc, L);
       A = fmaf(s_acc[w][g][dd], sc, A);
     }
-    pacc[j] = A;
-    if (dd == 0) { pml[2 * g] = M; pml[2 * g + 1] = L; }
+    publish(&pacc[j], A);
+    if (dd == 0) { publish(&pml[2 * g], M); publish(&pml[2 * g + 1], L); }
   }
 
   // the last chunk of the row combines all chunks in a fixed order
@@ -212,16 +212,34 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   if (!last_arrival(ticket, n_chunks_row)) return;
   const float* racc = a.part_acc + size_t(row) * a.n_chunks * G * D;
   const float* rml = a.part_ml + size_t(row) * a.n_chunks * G * 2;
+  constexpr int CB = 8;  // chunks whose loads are issued together
   for (int j = threadIdx.x; j < G * D; j += 256) {
     const int g = j / D, dd = j - g * D;
     float M = -INFINITY;
-    for (uint32_t c = 0; c < n_chunks_row; ++c) M = fmaxf(M, rml[(c * G + g) * 2]);
+    for (uint32_t c0 = 0; c0 < n_chunks_row; c0 += CB) {
+      float mc[CB];
+#pragma unroll
+      for (int i = 0; i < CB; ++i)
+        mc[i] = (c0 + i < n_chunks_row) ? consume(&rml[((c0 + i) * G + g) * 2]) : -INFINITY;
+#pragma unroll
+      for (int i = 0; i < CB; ++i) M = fmaxf(M, mc[i]);
+    }
     float L = 0.f, A = 0.f;
-    for (uint32_t c = 0; c < n_chunks_row; ++c) {
-      const float mc = rml[(c * G + g) * 2];
-      const float w = (mc == -INFINITY) ? 0.f : fast_exp2(mc - M);
-      L = fmaf(rml[(c * G + g) * 2 + 1], w, L);
-      A = fmaf(racc[(size_t(c) * G + g) * D + dd], w, A);
+    for (uint32_t c0 = 0; c0 < n_chunks_row; c0 += CB) {
+      float mc[CB], lc[CB], ac[CB];
+#pragma unroll
+      for (int i = 0; i < CB; ++i) {
+        const bool ok = c0 + i < n_chunks_row;
+        mc[i] = ok ? consume(&rml[((c0 + i) * G + g) * 2]) : -INFINITY;
+        lc[i] = ok ? consume(&rml[((c0 + i) * G + g) * 2 + 1]) : 0.f;
+        ac[i] = ok ? consume(&racc[(size_t(c0 + i) * G + g) * D + dd]) : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < CB; ++i) {
+        const float w = (mc[i] == -INFINITY) ? 0.f : fast_exp2(mc[i] - M);
+        L = fmaf(lc[i], w, L);
+        A = fmaf(ac[i], w, A);
+      }
     }
     const float o = A / L;
     const size_t oi = (size_t(b) * a.Hq + size_t(h) * G + g) * D + dd;

@@ -95,42 +95,72 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// ---- last-workgroup ticket ----------------------------------------------------------
-// Every thread of the workgroup calls this after its global writes.  Returns
-// true in exactly one workgroup of the `expected` that share `counter`: the
-// last to arrive, which then sees every other workgroup's writes.  The counter
-// is reset to zero for the next call.
+// ---- cross-workgroup hand-off -------------------------------------------------------
+// Data one workgroup leaves for the last workgroup of its row is written with
+// device-scope atomic stores (`publish`, which write through to the level that
+// is coherent across XCDs) and read back with device-scope atomic loads
+// (`consume`).  That avoids a device-scope release fence, which on gfx950 would
+// write back the whole L2 of the XCD once per workgroup.
+__device__ __forceinline__ void publish(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void publish(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void publish(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float consume(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t consume(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t consume(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every thread of the workgroup calls this after its publish() stores and
+// device atomics.  It waits until they have completed, then takes a ticket;
+// returns true in exactly one of the `expected` workgroups sharing `counter`:
+// the last to arrive, which can then consume() everything the others
+// published.  The counter is reset to zero for the next call.
 __device__ __forceinline__ bool last_arrival(uint32_t* counter, uint32_t expected) {
   __shared__ uint32_t s_ticket;
-  __threadfence();  // release this thread's writes at device scope
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's memory operations have completed
   __syncthreads();
-  if (threadIdx.x == 0) s_ticket = atomicAdd(counter, 1u);
+  if (threadIdx.x == 0)
+    s_ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const bool last = (s_ticket == expected - 1);
-  if (last) {
-    __threadfence();  // acquire the other workgroups' writes
-    if (threadIdx.x == 0) atomicExch(counter, 0u);
-  }
+  if (last && threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return last;
 }
 
-// Block-wide exclusive prefix sum of one value per thread (blockDim.x == 256).
-// `tmp` is 256 words of shared memory; returns the exclusive prefix, and the
-// total through `total`.
+// Block-wide exclusive prefix sum of one value per thread (blockDim.x == 256):
+// a shuffle scan inside each wave, then the four wave totals through `tmp`
+// (at least 4 words of shared memory).  Returns the exclusive prefix and the
+// block total through `total`.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
-  const int t = threadIdx.x;
-  tmp[t] = v;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    uint32_t add = (t >= off) ? tmp[t - off] : 0u;
-    __syncthreads();
-    tmp[t] += add;
-    __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-  uint32_t incl = tmp[t];
-  *total = tmp[255];
+  if (lane == 63) tmp[wave] = x;
   __syncthreads();
-  return incl - v;
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t c = tmp[w];
+    before += (w < wave) ? c : 0u;
+    all += c;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
 }
 
 }  // namespace jssa

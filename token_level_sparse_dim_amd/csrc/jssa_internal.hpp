@@ -36,14 +36,15 @@ enum RowState : int {
 
 // ---- workspace layout ---------------------------------------------------------
 // Every region starts 256-byte aligned.  The zero-on-entry regions are
-// hist1, row_state (counter words) and nothing else; all other regions are
+// hist1, hist2 and the counter words of row_state; all other regions are
 // fully written before they are read within a call.
 struct Workspace {
-  size_t hist1 = 0;      // u32 [rows][kDigit1Bins]
+  size_t hist1 = 0;      // u32 [rows][kDigit1Bins]      (zero on entry and exit)
+  size_t hist2 = 0;      // u32 [rows][4096]             (zero on entry and exit)
   size_t row_state = 0;  // u32 [rows][kRowStateWords]
   size_t tile_gt = 0;    // u32 [rows][n_sel_tiles]
   size_t tile_off = 0;   // u32 [rows][n_sel_tiles]
-  size_t cand = 0;       // u32x2 [rows][t_max]  (key, index)
+  size_t cand = 0;       // u64 [rows][t_max]  (index << 32 | key)
   size_t part_acc = 0;   // f32 [rows][n_chunks][G][d_v]
   size_t part_ml = 0;    // f32 [rows][n_chunks][G][2]
   size_t scores = 0;     // f32 [rows][t_max]           (decode only)

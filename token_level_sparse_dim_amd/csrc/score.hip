@@ -21,11 +21,49 @@ struct ScoreArgs {
   int Hq, Hkv, G, d_k, t_max, topk, window, q_dtype;
 };
 
+// Projected queries of KV head h's group, fp32, into s_qp[g * R + i]:
+//   qp[g][i] = sum_d q[b, h*G + g, d] * P[h, d, i]
+// The query rows are staged in shared memory; the d-sum of each output is
+// split over several threads when G*R < 256 and the parts are added in a
+// fixed order.
+template <int R>
+__device__ void project_group_query(const void* q, int q_dtype, const float* P, int Hq, int d_k,
+                                    int G, int b, int h, float* s_q, float* s_part, float* s_qp) {
+  const size_t q0 = (size_t(b) * Hq + size_t(h) * G) * d_k;
+  for (int i = threadIdx.x; i < G * d_k; i += 256) s_q[i] = load_elem(q, q0 + i, q_dtype);
+  __syncthreads();
+  const int GR = G * R;
+  const int parts = GR >= 256 ? 1 : 256 / GR;
+  const int dper = d_k / parts;
+  const float* Ph = P + size_t(h) * d_k * R;
+  for (int j = threadIdx.x; j < GR * parts; j += 256) {
+    const int o = j % GR, part = j / GR;
+    const int g = o / R, i = o - g * R;
+    const float* qg = s_q + g * d_k;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int d = part * dper; d < (part + 1) * dper; d += 4) {
+      a0 = fmaf(qg[d + 0], Ph[size_t(d + 0) * R + i], a0);
+      a1 = fmaf(qg[d + 1], Ph[size_t(d + 1) * R + i], a1);
+      a2 = fmaf(qg[d + 2], Ph[size_t(d + 2) * R + i], a2);
+      a3 = fmaf(qg[d + 3], Ph[size_t(d + 3) * R + i], a3);
+    }
+    s_part[j] = (a0 + a1) + (a2 + a3);
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < GR; o += 256) {
+    float acc = 0.f;
+    for (int part = 0; part < parts; ++part) acc += s_part[part * GR + o];
+    s_qp[o] = acc;
+  }
+  __syncthreads();
+}
+
 // One workgroup (4 waves) per kScoreTile candidate tokens of one (b, h) row.
 // Each token's projected key (R elements) is spread over LPT = R*bytes/16
 // lanes; each lane holds the matching slice of the G projected queries in
 // registers, and the per-head dot products are completed with DPP sums.
-// GE = G for the group max, 1 for the group mean.
+// Loads are double-buffered: the next step's 16-byte vectors are in flight
+// while the current ones are scored.  GE = G for the group max, 1 for the mean.
 template <int KPT, int R, int GE>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   constexpr int EB = Elem<KPT>::bytes;
@@ -37,8 +75,10 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   static_assert(LPT >= 1 && LPT <= 16 && (LPT & (LPT - 1)) == 0, "lanes per token");
 
   __shared__ uint32_t s_hist[kDigit1Bins];
+  __shared__ float s_q[8 * 128];
+  __shared__ float s_part[512];
   __shared__ float s_qp[8 * 64];
-  __shared__ uint32_t s_scan[256];
+  __shared__ uint32_t s_scan[8];
   __shared__ uint32_t s_out[2];
 
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -48,32 +88,36 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   const int t0 = tile * kScoreTile;
   if (t0 >= n_cand) return;
   const bool do_hist = a.hist1 != nullptr && a.topk > 0 && a.topk < n_cand;
+  const int t_end = min(t0 + kScoreTile, n_cand);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p = lane % LPT, tw = lane / LPT;
+  const char* kp_row = reinterpret_cast<const char*>(a.kp) + size_t(row) * a.t_max * R * EB;
+  float* srow = a.scores + size_t(row) * a.t_max;
+
+  auto load_step = [&](int base, uint4* v) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int tok = base + (wave * U + u) * TPW + tw;
+      v[u] = (tok < t_end) ? load16(kp_row + (size_t(tok) * R + p * EPL) * EB) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  // first loads go out before the query projection
+  uint4 cur[U];
+  load_step(t0, cur);
 
   if (do_hist)
     for (int i = threadIdx.x; i < kDigit1Bins; i += 256) s_hist[i] = 0u;
-
-  // projected queries of the group, fp32: qp[g][i] = sum_d q[b, hG+g, d] P[h, d, i]
   const int G = a.G;
-  for (int j = threadIdx.x; j < G * R; j += 256) {
-    const int g = j / R, i = j - g * R;
-    const size_t qoff = (size_t(b) * a.Hq + size_t(h) * G + g) * a.d_k;
-    const float* Pc = a.P + size_t(h) * a.d_k * R + i;
-    float acc = 0.f;
-    for (int d = 0; d < a.d_k; ++d) acc = fmaf(load_elem(a.q, qoff + d, a.q_dtype), Pc[size_t(d) * R], acc);
-    s_qp[j] = acc;
-  }
-  __syncthreads();
+  project_group_query<R>(a.q, a.q_dtype, a.P, a.Hq, a.d_k, G, b, h, s_q, s_part, s_qp);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int p = lane % LPT, tw = lane / LPT;
   float qreg[GE][EPL];
   if constexpr (GE == 1) {
     const float invG = 1.0f / float(G);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      float s = 0.f;
-      for (int g = 0; g < G; ++g) s += s_qp[g * R + p * EPL + e];
-      qreg[0][e] = s * invG;
+      float sm = 0.f;
+      for (int g = 0; g < G; ++g) sm += s_qp[g * R + p * EPL + e];
+      qreg[0][e] = sm * invG;
     }
   } else {
 #pragma unroll
@@ -82,25 +126,15 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
       for (int e = 0; e < EPL; ++e) qreg[g][e] = s_qp[g * R + p * EPL + e];
   }
 
-  const char* kp_row = reinterpret_cast<const char*>(a.kp) + size_t(row) * a.t_max * R * EB;
-  float* srow = a.scores + size_t(row) * a.t_max;
-  const int t_end = min(t0 + kScoreTile, n_cand);
-
   for (int base = t0; base < t_end; base += PER_ITER) {
-    uint4 v[U];
-    int tok[U];
+    const int nb = base + PER_ITER;
+    uint4 nxt[U];
+    if (nb < t_end) load_step(nb, nxt);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      tok[u] = base + (wave * U + u) * TPW + tw;
-      if (tok[u] < t_end)
-        v[u] = load16(kp_row + (size_t(tok[u]) * R + p * EPL) * EB);
-      else
-        v[u] = make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
+      const int tok = base + (wave * U + u) * TPW + tw;
       float kv[EPL];
-      unpack16<KPT>(v[u], kv);
+      unpack16<KPT>(cur[u], kv);
       float best;
 #pragma unroll
       for (int g = 0; g < GE; ++g) {
@@ -110,10 +144,14 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         dsum = group_sum<LPT>(dsum);
         best = (g == 0) ? dsum : fmaxf(best, dsum);
       }
-      if (p == 0 && tok[u] < t_end) {
-        srow[tok[u]] = best;
+      if (p == 0 && tok < t_end) {
+        srow[tok] = best;
         if (do_hist) atomicAdd(&s_hist[score_key(best) >> (32 - kDigit1Bits)], 1u);
       }
+    }
+    if (nb < t_end) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
     }
   }
 
@@ -142,7 +180,7 @@ struct HistArgs {
 
 __global__ __launch_bounds__(256) void hist_kernel(HistArgs a) {
   __shared__ uint32_t s_hist[kDigit1Bins];
-  __shared__ uint32_t s_scan[256];
+  __shared__ uint32_t s_scan[8];
   __shared__ uint32_t s_out[2];
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int row = b * a.Hkv + h;

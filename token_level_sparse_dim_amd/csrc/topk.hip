@@ -23,9 +23,10 @@ struct SelArgs {
   int32_t* idx;
   int32_t* n_sel;
   uint32_t* row_state;
+  uint32_t* hist2;
   uint32_t* tile_gt;
   uint32_t* tile_off;
-  uint2* cand;
+  uint64_t* cand;  // (index << 32) | key
   int Hkv, t_max, topk, window, n_sel_tiles;
 };
 
@@ -33,10 +34,12 @@ __device__ __forceinline__ bool is_selected(uint32_t key, int t, uint32_t kstar,
   return key > kstar || (key == kstar && uint32_t(t) <= istar);
 }
 
+constexpr int kDigit2Bins = 4096;  // key bits 19..8
+
 __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
-  __shared__ uint32_t s_buf[2 * kSelTile];  // candidate (key, index) pairs, later histograms
-  __shared__ uint32_t s_cnt[kMaxSelTiles];  // per-tile selected counts (resolution only)
-  __shared__ uint32_t s_scan[256];
+  __shared__ uint64_t s_cand[kSelTile];        // this tile's candidates; later per-tile counts
+  __shared__ uint32_t s_hist[kDigit2Bins];     // digit-2 histogram; later digit 3 / index digits
+  __shared__ uint32_t s_scan[8];
   __shared__ uint32_t s_out[2];
   __shared__ uint32_t s_n, s_gt, s_base;
 
@@ -49,9 +52,11 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
   if (t0 >= n_cand) return;
   const int t_end = min(t0 + kSelTile, n_cand);
   uint32_t* g_state = a.row_state + size_t(row) * kRowStateWords;
+  uint32_t* g_hist2 = a.hist2 + size_t(row) * kDigit2Bins;
   const uint32_t D1 = g_state[RS_D1];
   const float* srow = a.scores + size_t(row) * a.t_max;
 
+  for (int i = threadIdx.x; i < kDigit2Bins; i += 256) s_hist[i] = 0u;
   if (threadIdx.x == 0) { s_n = 0u; s_gt = 0u; }
   __syncthreads();
   uint32_t gt = 0;
@@ -61,86 +66,92 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
     gt += (dg > D1);
     if (dg == D1) {
       const uint32_t slot = atomicAdd(&s_n, 1u);
-      s_buf[2 * slot] = key;
-      s_buf[2 * slot + 1] = uint32_t(t);
+      s_cand[slot] = (uint64_t(uint32_t(t)) << 32) | key;
+      atomicAdd(&s_hist[(key >> 8) & 0xfffu], 1u);
     }
   }
   atomicAdd(&s_gt, gt);
   __syncthreads();
   if (threadIdx.x == 0) {
     s_base = atomicAdd(&g_state[RS_CAND_COUNT], s_n);
-    a.tile_gt[size_t(row) * a.n_sel_tiles + tile] = s_gt;
+    publish(&a.tile_gt[size_t(row) * a.n_sel_tiles + tile], s_gt);
+  }
+  for (int i = threadIdx.x; i < kDigit2Bins; i += 256) {
+    const uint32_t c = s_hist[i];
+    if (c) atomicAdd(&g_hist2[i], c);
   }
   __syncthreads();
-  uint2* clist = a.cand + size_t(row) * a.t_max;
-  for (uint32_t j = threadIdx.x; j < s_n; j += 256)
-    clist[s_base + j] = make_uint2(s_buf[2 * j], s_buf[2 * j + 1]);
+  uint64_t* clist = a.cand + size_t(row) * a.t_max;
+  for (uint32_t j = threadIdx.x; j < s_n; j += 256) publish(&clist[s_base + j], s_cand[j]);
 
   const uint32_t n_tiles = uint32_t((n_cand + kSelTile - 1) / kSelTile);
   if (!last_arrival(&g_state[RS_TICKET_CAND], n_tiles)) return;
 
   // ---- resolution by the row's last workgroup ------------------------------------
-  const uint32_t C = __hip_atomic_load(&g_state[RS_CAND_COUNT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t C = consume(&g_state[RS_CAND_COUNT]);
   const uint32_t need1 = g_state[RS_NEED1];
-  uint32_t* hist = s_buf;
 
-  // digit 2: key bits 19..8
-  for (int i = threadIdx.x; i < 4096; i += 256) hist[i] = 0u;
+  // digit 2 (key bits 19..8) from the histogram every workgroup contributed to
+  for (int i = threadIdx.x; i < kDigit2Bins; i += 256) {
+    s_hist[i] = consume(&g_hist2[i]);
+    publish(&g_hist2[i], 0u);  // zero for the next call
+  }
   __syncthreads();
-  for (uint32_t j = threadIdx.x; j < C; j += 256) atomicAdd(&hist[(clist[j].x >> 8) & 0xfffu], 1u);
-  __syncthreads();
-  find_bin_from_top<16>(hist, need1, s_scan, s_out);
+  find_bin_from_top<kDigit2Bins / 256>(s_hist, need1, s_scan, s_out);
   const uint32_t D2 = s_out[0];
   const uint32_t need2 = need1 - s_out[1];
   __syncthreads();
 
-  // digit 3: key bits 7..0
-  for (int i = threadIdx.x; i < 256; i += 256) hist[i] = 0u;
+  // digit 3 (key bits 7..0) over the candidates in bin D2
+  if (threadIdx.x < 256) s_hist[threadIdx.x] = 0u;
   __syncthreads();
   for (uint32_t j = threadIdx.x; j < C; j += 256) {
-    const uint32_t key = clist[j].x;
-    if (((key >> 8) & 0xfffu) == D2) atomicAdd(&hist[key & 0xffu], 1u);
+    const uint32_t key = uint32_t(consume(&clist[j]));
+    if (((key >> 8) & 0xfffu) == D2) atomicAdd(&s_hist[key & 0xffu], 1u);
   }
   __syncthreads();
-  find_bin_from_top<1>(hist, need2, s_scan, s_out);
+  find_bin_from_top<1>(s_hist, need2, s_scan, s_out);
   const uint32_t D3 = s_out[0];
   const uint32_t m_ties = need2 - s_out[1];  // keys equal to K* still to take (lowest indices)
-  const uint32_t n_eq = hist[D3];
+  const uint32_t n_eq = s_hist[D3];
   const uint32_t kstar = (D1 << 20) | (D2 << 8) | D3;
   __syncthreads();
 
   uint32_t istar = 0x7fffffffu;
   if (m_ties < n_eq) {
     // the m_ties-th smallest index among keys equal to K*: index bits 23..12, then 11..0
-    for (int i = threadIdx.x; i < 4096; i += 256) hist[i] = 0u;
+    for (int i = threadIdx.x; i < 4096; i += 256) s_hist[i] = 0u;
     __syncthreads();
     for (uint32_t j = threadIdx.x; j < C; j += 256) {
-      const uint2 c = clist[j];
-      if (c.x == kstar) atomicAdd(&hist[c.y >> 12], 1u);
+      const uint64_t c = consume(&clist[j]);
+      if (uint32_t(c) == kstar) atomicAdd(&s_hist[uint32_t(c >> 32) >> 12], 1u);
     }
     __syncthreads();
-    find_bin_from_bottom<16>(hist, m_ties, s_scan, s_out);
+    find_bin_from_bottom<16>(s_hist, m_ties, s_scan, s_out);
     const uint32_t E1 = s_out[0];
     const uint32_t m2 = m_ties - s_out[1];
     __syncthreads();
-    for (int i = threadIdx.x; i < 4096; i += 256) hist[i] = 0u;
+    for (int i = threadIdx.x; i < 4096; i += 256) s_hist[i] = 0u;
     __syncthreads();
     for (uint32_t j = threadIdx.x; j < C; j += 256) {
-      const uint2 c = clist[j];
-      if (c.x == kstar && (c.y >> 12) == E1) atomicAdd(&hist[c.y & 0xfffu], 1u);
+      const uint64_t c = consume(&clist[j]);
+      const uint32_t t = uint32_t(c >> 32);
+      if (uint32_t(c) == kstar && (t >> 12) == E1) atomicAdd(&s_hist[t & 0xfffu], 1u);
     }
     __syncthreads();
-    find_bin_from_bottom<16>(hist, m2, s_scan, s_out);
+    find_bin_from_bottom<16>(s_hist, m2, s_scan, s_out);
     istar = (E1 << 12) | s_out[0];
     __syncthreads();
   }
 
   // per-tile selected counts -> exclusive offsets
-  for (uint32_t i = threadIdx.x; i < n_tiles; i += 256) s_cnt[i] = a.tile_gt[size_t(row) * a.n_sel_tiles + i];
+  uint32_t* s_cnt = reinterpret_cast<uint32_t*>(s_cand);  // kMaxSelTiles words fit in s_cand
+  for (uint32_t i = threadIdx.x; i < n_tiles; i += 256) s_cnt[i] = consume(&a.tile_gt[size_t(row) * a.n_sel_tiles + i]);
   __syncthreads();
   for (uint32_t j = threadIdx.x; j < C; j += 256) {
-    const uint2 c = clist[j];
-    if (is_selected(c.x, int(c.y), kstar, istar)) atomicAdd(&s_cnt[c.y / kSelTile], 1u);
+    const uint64_t c = consume(&clist[j]);
+    const uint32_t t = uint32_t(c >> 32);
+    if (is_selected(uint32_t(c), int(t), kstar, istar)) atomicAdd(&s_cnt[t / kSelTile], 1u);
   }
   __syncthreads();
   constexpr int PER = kMaxSelTiles / 256;
@@ -162,7 +173,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
     g_state[RS_KSTAR] = kstar;
     g_state[RS_ISTAR] = istar;
     g_state[RS_NSCAN] = total;
-    __hip_atomic_store(&g_state[RS_CAND_COUNT], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    publish(&g_state[RS_CAND_COUNT], 0u);
   }
 }
 
@@ -223,7 +234,8 @@ hipError_t launch_topk(const jssa_desc& d, const float* scores, const int32_t* s
   a.row_state = reinterpret_cast<uint32_t*>(ws_base + ws.row_state);
   a.tile_gt = reinterpret_cast<uint32_t*>(ws_base + ws.tile_gt);
   a.tile_off = reinterpret_cast<uint32_t*>(ws_base + ws.tile_off);
-  a.cand = reinterpret_cast<uint2*>(ws_base + ws.cand);
+  a.cand = reinterpret_cast<uint64_t*>(ws_base + ws.cand);
+  a.hist2 = reinterpret_cast<uint32_t*>(ws_base + ws.hist2);
   a.Hkv = d.n_kv_heads; a.t_max = d.t_max; a.topk = d.topk; a.window = d.window;
   a.n_sel_tiles = ws.n_sel_tiles;
   dim3 grid(ws.n_sel_tiles, d.n_kv_heads, d.batch);
