@@ -141,7 +141,7 @@ def main():
     log(f"sparse step: {ms_step * 1e3:.2f} us (events), {wall / args.steps * 1e6:.2f} us (wall)")
 
     # ---- per-stage breakdown from HIP events on the launch stream -------------------------------
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for row in evs:
         for e in row:
             e.record(stream)  # materialise the event objects
@@ -149,9 +149,9 @@ def main():
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
-    stage_ms = np.array([[row[j].elapsed_time(row[j + 1]) for j in range(4)] for row in evs])
+    stage_ms = np.array([[row[j].elapsed_time(row[j + 1]) for j in range(3)] for row in evs])
     stage_us = stage_ms.mean(axis=0) * 1e3
-    names = ["score_scan", "select_resolve", "emit_indices", "attention_combine"]
+    names = ["score_scan", "select_candidates", "resolve_attention"]
     log("stages (us): " + ", ".join(f"{n}={v:.2f}" for n, v in zip(names, stage_us)))
 
     # ---- bytes -------------------------------------------------------------------------------

@@ -182,12 +182,12 @@ int32_t jssa_decode(const jssa_desc* desc, const void* q, const float* P, const 
                     void* out, float* lse, int32_t* idx_out, int32_t* n_sel_out,
                     void* ws, size_t ws_bytes, void* stream);
 
-/* jssa_decode that also records five caller-created HIP events
+/* jssa_decode that also records four caller-created HIP events
  * (stage_events[i] is a hipEvent_t; the array is a host array) on `stream`:
- * [0] before scoring, [1] after scoring (with the first radix digit),
- * [2] after candidate resolution, [3] after index emission, [4] after
- * attention and the combine -- the per-component latency breakdown of
- * JSSA summary section E.1 (scan, selection, attention). */
+ * [0] before the score scan, [1] after it (scores and the first radix digit),
+ * [2] after the candidate pass of the selection, [3] after the resolve +
+ * attention launch -- the per-component latency breakdown of JSSA summary
+ * section E.1 (scan, selection, attention). */
 int32_t jssa_decode_profiled(const jssa_desc* desc, const void* q, const float* P,
                              const void* kp_cache, const void* k_cache, const void* v_cache,
                              const int32_t* seq_lens, void* out, float* lse, int32_t* idx_out,

@@ -121,14 +121,14 @@ def decode(desc: Desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, ws,
 
 def decode_profiled(desc: Desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, ws, events,
                     idx_out=None, n_sel_out=None, stream=None):
-    """``jssa_decode_profiled``: ``jssa_decode`` recording five stage events
+    """``jssa_decode_profiled``: ``jssa_decode`` recording four stage events
     (``torch.cuda.Event(enable_timing=True)``, each already recorded once so that
-    it exists): before scoring, after scoring, after selection resolution, after
-    index emission, after attention."""
+    it exists): before the score scan, after it, after the candidate pass,
+    after the resolve + attention launch."""
     import ctypes
-    if len(events) != 5:
-        raise ValueError("five events are needed")
-    arr = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    if len(events) != 4:
+        raise ValueError("four events are needed")
+    arr = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in events])
     kv = _TORCH_DTYPE[desc.kv_dtype]
     call("jssa_decode_profiled", desc.c(), _ptr(q, kv, "q"), _ptr(P, torch.float32, "P"),
          _ptr(kp_cache, _TORCH_DTYPE[desc.kp_dtype], "kp_cache"), _ptr(k_cache, kv, "k_cache"),

@@ -20,11 +20,14 @@ int32_t to_status(hipError_t e) { return e == hipSuccess ? JSSA_OK : JSSA_ERR_HI
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-// Attention chunking: aim for about 2048 workgroups over the whole launch.
+// Attention chunking: about 256 workgroups (one per CU) for the indexed path,
+// which measured best for 512-byte K/V rows on MI355X; about 1024 for the dense
+// path.  Chunks are multiples of 64 tokens.
 void attn_chunking(int rows, int64_t n_max, bool indexed, int* chunk, int* n_chunks) {
-  const int64_t lo = indexed ? 64 : 256;
+  const int64_t lo = indexed ? 128 : 256;
   const int64_t hi = indexed ? 1024 : 8192;
-  int64_t c = (n_max * rows + 2047) / 2048;
+  const int64_t target = indexed ? 256 : 1024;
+  int64_t c = (n_max * rows + target - 1) / target;
   c = (c + 63) / 64 * 64;
   if (c < lo) c = lo;
   if (c > hi) c = hi;
@@ -76,11 +79,12 @@ bool workspace_layout(const jssa_desc& d, int op, Workspace* ws) {
   };
   ws->n_sel_tiles = (d.t_max + kSelTile - 1) / kSelTile;
   ws->row_state = take(rows * kRowStateWords * 4);
+  ws->queue = take(kQueueWords * 4);
   if (op == JSSA_OP_TOPK || op == JSSA_OP_DECODE) {
     ws->hist1 = take(rows * kDigit1Bins * 4);
-    ws->hist2 = take(rows * 4096 * 4);
-    ws->tile_gt = take(rows * ws->n_sel_tiles * 4);
+    ws->tile_cnt = take(rows * ws->n_sel_tiles * 4);
     ws->tile_off = take(rows * ws->n_sel_tiles * 4);
+    ws->cand_base = take(rows * ws->n_sel_tiles * 4);
     ws->cand = take(rows * size_t(d.t_max) * 8);
   }
   if (op == JSSA_OP_ATTN || op == JSSA_OP_DECODE || op == JSSA_OP_DENSE) {
@@ -184,8 +188,14 @@ int32_t jssa_topk(const jssa_desc* desc, const float* scores, const int32_t* seq
     return JSSA_ERR_MISALIGNED;
   Workspace lay;
   JSSA_TRY(check_ws(*desc, JSSA_OP_TOPK, ws, ws_bytes, &lay));
-  return to_status(launch_topk(*desc, scores, seq_lens, idx, n_sel, static_cast<char*>(ws), lay, false,
-                               as_stream(stream)));
+  char* base = static_cast<char*>(ws);
+  hipStream_t s = as_stream(stream);
+  hipError_t e = launch_hist(*desc, scores, seq_lens, base, lay, s);
+  if (e == hipSuccess) e = launch_candidates(*desc, scores, seq_lens, base, lay, s);
+  if (e == hipSuccess)
+    e = launch_resolve_attend(*desc, true, false, nullptr, nullptr, nullptr, idx, n_sel, seq_lens, nullptr,
+                              nullptr, base, lay, s);
+  return to_status(e);
 }
 
 int32_t jssa_indexed_attn(const jssa_desc* desc, const void* q, const void* k_cache,
@@ -198,8 +208,9 @@ int32_t jssa_indexed_attn(const jssa_desc* desc, const void* q, const void* k_ca
     return JSSA_ERR_MISALIGNED;
   Workspace lay;
   JSSA_TRY(check_ws(*desc, JSSA_OP_ATTN, ws, ws_bytes, &lay));
-  return to_status(launch_attention(*desc, q, k_cache, v_cache, idx, n_sel, nullptr, out, lse,
-                                    static_cast<char*>(ws), lay, as_stream(stream)));
+  return to_status(launch_resolve_attend(*desc, false, true, q, k_cache, v_cache, const_cast<int32_t*>(idx),
+                                         const_cast<int32_t*>(n_sel), nullptr, out, lse,
+                                         static_cast<char*>(ws), lay, as_stream(stream)));
 }
 
 static int32_t decode_impl(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
@@ -213,7 +224,7 @@ static int32_t decode_impl(const jssa_desc* desc, const void* q, const float* P,
       (idx_out && !aligned16(idx_out)) || (n_sel_out && !aligned16(n_sel_out)))
     return JSSA_ERR_MISALIGNED;
   if (ev)
-    for (int i = 0; i < 5; ++i)
+    for (int i = 0; i < 4; ++i)
       if (!ev[i]) return JSSA_ERR_INVALID_ARG;
   Workspace lay;
   JSSA_TRY(check_ws(*desc, JSSA_OP_DECODE, ws, ws_bytes, &lay));
@@ -226,13 +237,12 @@ static int32_t decode_impl(const jssa_desc* desc, const void* q, const float* P,
   hipError_t e = mark(0);
   if (e == hipSuccess) e = launch_score(*desc, q, P, kp_cache, seq_lens, scores, base, lay, s);
   if (e == hipSuccess) e = mark(1);
+  if (e == hipSuccess) e = launch_candidates(*desc, scores, seq_lens, base, lay, s);
+  if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess)
-    e = launch_topk(*desc, scores, seq_lens, idx, n_sel, base, lay, true, s,
-                    ev ? static_cast<hipEvent_t>(ev[2]) : nullptr);
+    e = launch_resolve_attend(*desc, true, true, q, k_cache, v_cache, idx, n_sel, seq_lens, out, lse, base,
+                              lay, s);
   if (e == hipSuccess) e = mark(3);
-  if (e == hipSuccess)
-    e = launch_attention(*desc, q, k_cache, v_cache, idx, n_sel, nullptr, out, lse, base, lay, s);
-  if (e == hipSuccess) e = mark(4);
   return to_status(e);
 }
 
@@ -263,8 +273,8 @@ int32_t jssa_dense_decode(const jssa_desc* desc, const void* q, const void* k_ca
     return JSSA_ERR_MISALIGNED;
   Workspace lay;
   JSSA_TRY(check_ws(*desc, JSSA_OP_DENSE, ws, ws_bytes, &lay));
-  return to_status(launch_attention(*desc, q, k_cache, v_cache, nullptr, nullptr, seq_lens, out, lse,
-                                    static_cast<char*>(ws), lay, as_stream(stream)));
+  return to_status(launch_resolve_attend(*desc, false, true, q, k_cache, v_cache, nullptr, nullptr, seq_lens,
+                                         out, lse, static_cast<char*>(ws), lay, as_stream(stream)));
 }
 
 }  // extern "C"

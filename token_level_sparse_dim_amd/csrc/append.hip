@@ -121,6 +121,7 @@ __global__ __launch_bounds__(256) void append_rows_kernel(AppendArgs a) {
   const int d0 = part * dper, d1 = min(a.d_k, d0 + dper);
   const float* Pc = a.P + size_t(h) * a.d_k * R + o;
   float acc = 0.f;
+#pragma unroll 8
   for (int d = d0; d < d1; ++d) acc = fmaf(s_k[d], Pc[size_t(d) * R], acc);
   s_part[threadIdx.x] = acc;
   __syncthreads();

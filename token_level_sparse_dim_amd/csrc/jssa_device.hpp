@@ -36,6 +36,14 @@ __device__ __forceinline__ uint4 load16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// 16-byte load with the nontemporal hint: for data streamed once (the
+// projected-key scan, K/V rows), so it does not displace reusable lines.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_nt(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Scalar element load with a run-time dtype (prologues only).
 __device__ __forceinline__ float load_elem(const void* base, size_t i, int dt) {
   if (dt == 0) return reinterpret_cast<const float*>(base)[i];

@@ -12,39 +12,53 @@
 namespace jssa {
 
 // ---- tiling constants -------------------------------------------------------
-constexpr int kScoreTile = 4096;     // candidate tokens per score workgroup
-constexpr int kSelTile = 4096;       // keys per selection workgroup (must equal kScoreTile)
+// Compile-time tuning knobs (defaults are the measured choices on MI355X).
+#ifndef JSSA_SCORE_TILE
+#define JSSA_SCORE_TILE 4096
+#endif
+#ifndef JSSA_SCORE_UNROLL
+#define JSSA_SCORE_UNROLL 4
+#endif
+#ifndef JSSA_ATTN_UNROLL
+#define JSSA_ATTN_UNROLL 4
+#endif
+constexpr int kScoreTile = JSSA_SCORE_TILE;  // candidate tokens per score workgroup
+constexpr int kSelTile = 4096;               // keys per selection workgroup
 constexpr int kDigit1Bits = 12;      // first radix digit: key bits 31..20
 constexpr int kDigit1Bins = 1 << kDigit1Bits;
 constexpr int kMaxSelTiles = 4096;   // t_max <= kMaxSelTiles * kSelTile
 constexpr int kAttnBlock = 64;       // tokens per attention inner block (per workgroup pass)
 constexpr int kRowStateWords = 16;   // u32 words of per-row selection state
 
-// per-row selection state (u32 words)
+// per-row state (u32 words).  The tickets and the ready flag are zero on
+// entry and are left zero by every call.
 enum RowState : int {
-  RS_MODE = 0,        // 0: select, 1: take every candidate, 2: nothing to select
-  RS_D1 = 1,          // first-digit threshold bin
-  RS_NEED1 = 2,       // how many keys with digit == D1 are still needed
-  RS_KSTAR = 3,       // exact key of the k-th selected candidate
-  RS_ISTAR = 4,       // ties at KSTAR are taken for indices <= ISTAR
-  RS_NSCAN = 5,       // number of selected candidates
-  RS_CAND_COUNT = 6,  // running count of first-digit candidates (zero on entry/exit)
-  RS_TICKET_SCORE = 7,  // zero on entry/exit
-  RS_TICKET_CAND = 8,   // zero on entry/exit
-  RS_TICKET_ATTN = 9,   // zero on entry/exit
+  RS_D1 = 1,            // first-digit (key bits 31..20) threshold bin
+  RS_NEED1 = 2,         // keys still needed from bin D1 (k minus the count above it)
+  RS_KSTAR = 3,         // key of the k-th selected candidate
+  RS_ISTAR = 4,         // keys equal to KSTAR are selected for indices <= ISTAR
+  RS_NCAND = 5,         // candidates of the row (keys in or above bin D1)
+  RS_TICKET_SCORE = 7,  // arrivals of score / histogram workgroups
+  RS_READY = 8,         // selection of the row published (set by resolve, cleared by attention)
+  RS_TICKET_ATTN = 9,   // arrivals of attention chunks
 };
+
+// Work queue of the resolve + attention launch: [0] next item, [1] finished
+// items (both zero on entry and exit).
+constexpr int kQueueWords = 64;
 
 // ---- workspace layout ---------------------------------------------------------
 // Every region starts 256-byte aligned.  The zero-on-entry regions are
-// hist1, hist2 and the counter words of row_state; all other regions are
-// fully written before they are read within a call.
+// hist1, row_state and queue; all other regions are fully written before
+// they are read within a call.
 struct Workspace {
   size_t hist1 = 0;      // u32 [rows][kDigit1Bins]      (zero on entry and exit)
-  size_t hist2 = 0;      // u32 [rows][4096]             (zero on entry and exit)
   size_t row_state = 0;  // u32 [rows][kRowStateWords]
-  size_t tile_gt = 0;    // u32 [rows][n_sel_tiles]
-  size_t tile_off = 0;   // u32 [rows][n_sel_tiles]
-  size_t cand = 0;       // u64 [rows][t_max]  (index << 32 | key)
+  size_t queue = 0;      // u32 [kQueueWords]            (zero on entry and exit)
+  size_t tile_cnt = 0;   // u32 [rows][n_sel_tiles]      candidates per selection tile
+  size_t tile_off = 0;   // u32 [rows][n_sel_tiles]      first output position of each tile
+  size_t cand_base = 0;  // u32 [rows][n_sel_tiles]      first candidate of each tile (concatenated)
+  size_t cand = 0;       // u64 [rows][t_max]  (index << 32 | key), in tile slots of kSelTile
   size_t part_acc = 0;   // f32 [rows][n_chunks][G][d_v]
   size_t part_ml = 0;    // f32 [rows][n_chunks][G][2]
   size_t scores = 0;     // f32 [rows][t_max]           (decode only)
@@ -74,17 +88,20 @@ hipError_t launch_score(const jssa_desc& d, const void* q, const float* P, const
 hipError_t launch_hist(const jssa_desc& d, const float* scores, const int32_t* seq_lens,
                        char* ws_base, const Workspace& ws, hipStream_t s);
 
-// Selection from fp32 scores: histogram (unless `hist_done`), candidates and
-// exact resolution, emission of indices in ascending order plus the window.
-hipError_t launch_topk(const jssa_desc& d, const float* scores, const int32_t* seq_lens,
-                       int32_t* idx, int32_t* n_sel, char* ws_base, const Workspace& ws,
-                       bool hist_done, hipStream_t s, hipEvent_t after_select = nullptr);
+// Candidate pass of the selection: every key in or above the first-digit
+// threshold bin, written in token order to its tile's slot.
+hipError_t launch_candidates(const jssa_desc& d, const float* scores, const int32_t* seq_lens,
+                             char* ws_base, const Workspace& ws, hipStream_t s);
 
-// Attention over idx (indexed) or over every cached token (idx == nullptr).
-hipError_t launch_attention(const jssa_desc& d, const void* q, const void* k_cache,
-                            const void* v_cache, const int32_t* idx, const int32_t* n_sel,
-                            const int32_t* seq_lens, void* out, float* lse, char* ws_base,
-                            const Workspace& ws, hipStream_t s);
+// One launch with a work queue: a resolve item per row (exact k-th key, tie
+// cut, emission of idx / n_sel in ascending order plus the window), and, when
+// `attend`, the attention chunks of every row, each waiting for its row's
+// resolve.  Without `resolve`, idx / n_sel are inputs.  idx == nullptr with
+// `attend` and no `resolve` selects the dense path (every t < seq_lens[b]).
+hipError_t launch_resolve_attend(const jssa_desc& d, bool resolve, bool attend, const void* q,
+                                 const void* k_cache, const void* v_cache, int32_t* idx,
+                                 int32_t* n_sel, const int32_t* seq_lens, void* out, float* lse,
+                                 char* ws_base, const Workspace& ws, hipStream_t s);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   constexpr int EPL = Elem<KPT>::per16;
   constexpr int LPT = R / EPL;
   constexpr int TPW = 64 / LPT;
-  constexpr int U = 4;
+  constexpr int U = JSSA_SCORE_UNROLL;
   constexpr int PER_ITER = 4 * TPW * U;
   static_assert(LPT >= 1 && LPT <= 16 && (LPT & (LPT - 1)) == 0, "lanes per token");
 
@@ -94,16 +94,18 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   const char* kp_row = reinterpret_cast<const char*>(a.kp) + size_t(row) * a.t_max * R * EB;
   float* srow = a.scores + size_t(row) * a.t_max;
 
+  // Loads are issued without per-lane branches (tokens past the end re-read the
+  // last candidate and are discarded), so the compiler can keep the next
+  // step's loads in flight while the current step is scored.
   auto load_step = [&](int base, uint4* v) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int tok = base + (wave * U + u) * TPW + tw;
-      v[u] = (tok < t_end) ? load16(kp_row + (size_t(tok) * R + p * EPL) * EB) : make_uint4(0u, 0u, 0u, 0u);
+      const int tok = min(base + (wave * U + u) * TPW + tw, t_end - 1);
+      v[u] = load16_nt(kp_row + (size_t(tok) * R + p * EPL) * EB);
     }
   };
-  // first loads go out before the query projection
   uint4 cur[U];
-  load_step(t0, cur);
+  load_step(t0, cur);  // first loads go out before the query projection
 
   if (do_hist)
     for (int i = threadIdx.x; i < kDigit1Bins; i += 256) s_hist[i] = 0u;
@@ -127,9 +129,8 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   }
 
   for (int base = t0; base < t_end; base += PER_ITER) {
-    const int nb = base + PER_ITER;
     uint4 nxt[U];
-    if (nb < t_end) load_step(nb, nxt);
+    load_step(base + PER_ITER, nxt);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int tok = base + (wave * U + u) * TPW + tw;
@@ -149,10 +150,8 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         if (do_hist) atomicAdd(&s_hist[score_key(best) >> (32 - kDigit1Bits)], 1u);
       }
     }
-    if (nb < t_end) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-    }
+    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
   }
 
   if (!do_hist) return;
@@ -192,8 +191,13 @@ __global__ __launch_bounds__(256) void hist_kernel(HistArgs a) {
   __syncthreads();
   const float* srow = a.scores + size_t(row) * a.t_max;
   const int t_end = min(t0 + kSelTile, n_cand);
-  for (int t = t0 + threadIdx.x; t < t_end; t += 256)
-    atomicAdd(&s_hist[score_key(srow[t]) >> (32 - kDigit1Bits)], 1u);
+  constexpr int KPT_ = kSelTile / 256;
+  float v[KPT_];
+#pragma unroll
+  for (int i = 0; i < KPT_; ++i) v[i] = srow[min(t0 + i * 256 + int(threadIdx.x), t_end - 1)];
+#pragma unroll
+  for (int i = 0; i < KPT_; ++i)
+    if (t0 + i * 256 + int(threadIdx.x) < t_end) atomicAdd(&s_hist[score_key(v[i]) >> (32 - kDigit1Bits)], 1u);
   __syncthreads();
   uint32_t* g_hist = a.hist1 + size_t(row) * kDigit1Bins;
   for (int i = threadIdx.x; i < kDigit1Bins; i += 256) {

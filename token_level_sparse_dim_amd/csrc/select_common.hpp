@@ -73,6 +73,19 @@ __device__ __forceinline__ int candidates_of(const int32_t* seq_lens, int b, int
   return n > 0 ? n : 0;
 }
 
+constexpr int kKeysPerThread = kSelTile / 256;
+
+// Keys of one selection tile, round-major: thread x holds tokens t0 + i*256 + x
+// (coalesced loads, all issued before use).  Tokens past t_end repeat the last
+// key and must be masked by the caller.
+__device__ __forceinline__ void load_tile_keys(const float* srow, int t0, int t_end, uint32_t* key) {
+  float v[kKeysPerThread];
+#pragma unroll
+  for (int i = 0; i < kKeysPerThread; ++i) v[i] = srow[min(t0 + i * 256 + int(threadIdx.x), t_end - 1)];
+#pragma unroll
+  for (int i = 0; i < kKeysPerThread; ++i) key[i] = score_key(v[i]);
+}
+
 // Last workgroup of a row after the first-digit histogram: moves the global
 // histogram into `s_hist` (zeroing the global copy for the next call), finds
 // the first-digit threshold bin of the k-th largest key and stores it in the
