@@ -172,11 +172,19 @@ int32_t jssa_indexed_attn(const jssa_desc* desc, const void* q, const void* k_ca
                           const void* v_cache, const int32_t* idx, const int32_t* n_sel,
                           void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
-/* One fused sparse decode step: jssa_score -> jssa_topk -> jssa_indexed_attn
- * (JSSA summary Figure 1 and section E.1) with intermediates in the
- * workspace.  idx_out / n_sel_out may be NULL; when given they receive the
- * selection.  The new token is expected to be appended (jssa_append_kv)
- * before this call.  Workspace op JSSA_OP_DECODE. */
+/* One sparse decode step: the result of jssa_score -> jssa_topk ->
+ * jssa_indexed_attn (JSSA summary Figure 1 and section E.1), bit-identical in
+ * idx / n_sel, with intermediates in the workspace.  For the shapes with a
+ * fused build (bf16: d 128 rank 32 G 4, d 128 rank 64 G 1, d 64 rank 16 G 4;
+ * f32: d 64 rank 16 G 4, d 128 rank 32 G 2; GQA layout) it runs in two
+ * launches: a scan that scores every candidate and keeps, per tile, the
+ * tokens at or above a threshold taken from a strided sample of the row's
+ * scores, and a resolve + attention launch that selects exactly among them
+ * (re-selecting a row exactly in the rare case fewer than k tokens passed the
+ * threshold).  Other shapes run the stand-alone kernels in sequence.
+ * idx_out / n_sel_out may be NULL; when given they receive the selection.
+ * The new token is expected to be appended (jssa_append_kv) before this
+ * call.  Workspace op JSSA_OP_DECODE. */
 int32_t jssa_decode(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
                     const void* k_cache, const void* v_cache, const int32_t* seq_lens,
                     void* out, float* lse, int32_t* idx_out, int32_t* n_sel_out,
@@ -184,10 +192,10 @@ int32_t jssa_decode(const jssa_desc* desc, const void* q, const float* P, const 
 
 /* jssa_decode that also records four caller-created HIP events
  * (stage_events[i] is a hipEvent_t; the array is a host array) on `stream`:
- * [0] before the score scan, [1] after it (scores and the first radix digit),
- * [2] after the candidate pass of the selection, [3] after the resolve +
- * attention launch -- the per-component latency breakdown of JSSA summary
- * section E.1 (scan, selection, attention). */
+ * [0] before the score scan, [1] after it, [2] after the candidate pass of
+ * the selection (the same point as [1] where the scan emits the candidates
+ * itself), [3] after the resolve + attention launch -- the per-component
+ * latency breakdown of JSSA summary section E.1 (scan, selection, attention). */
 int32_t jssa_decode_profiled(const jssa_desc* desc, const void* q, const float* P,
                              const void* kp_cache, const void* k_cache, const void* v_cache,
                              const int32_t* seq_lens, void* out, float* lse, int32_t* idx_out,

@@ -121,13 +121,18 @@ def decode(desc: Desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, ws,
 
 def decode_profiled(desc: Desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, ws, events,
                     idx_out=None, n_sel_out=None, stream=None):
-    """``jssa_decode_profiled``: ``jssa_decode`` recording four stage events
-    (``torch.cuda.Event(enable_timing=True)``, each already recorded once so that
-    it exists): before the score scan, after it, after the candidate pass,
-    after the resolve + attention launch."""
+    """``jssa_decode_profiled``: the staged decode (score scan, candidate pass,
+    resolve + attention launch) recording four stage events
+    (``torch.cuda.Event(enable_timing=True)``): before the score scan, after it,
+    after the candidate pass, after the resolve + attention launch.  torch
+    creates an event on its first record, so unrecorded events are recorded
+    once here first."""
     import ctypes
     if len(events) != 4:
         raise ValueError("four events are needed")
+    for e in events:
+        if not e.cuda_event:
+            e.record(stream if stream is not None else torch.cuda.current_stream())
     arr = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in events])
     kv = _TORCH_DTYPE[desc.kv_dtype]
     call("jssa_decode_profiled", desc.c(), _ptr(q, kv, "q"), _ptr(P, torch.float32, "P"),

@@ -78,11 +78,19 @@ bool workspace_layout(const jssa_desc& d, int op, Workspace* ws) {
     return at;
   };
   ws->n_sel_tiles = (d.t_max + kSelTile - 1) / kSelTile;
+  int pipe_chunk = 0;
+  if (op == JSSA_OP_DECODE && pipeline_layout(d, &ws->pipe_ts, &ws->pipe_tiles, &pipe_chunk)) {
+    const int64_t n_max = int64_t(d.topk) + d.window;
+    ws->pipe = true;
+    ws->pipe_chunk = pipe_chunk;
+    ws->pipe_n_chunks = int((n_max + pipe_chunk - 1) / pipe_chunk);
+  }
+  const int cnt_tiles = ws->pipe_tiles > ws->n_sel_tiles ? ws->pipe_tiles : ws->n_sel_tiles;
   ws->row_state = take(rows * kRowStateWords * 4);
   ws->queue = take(kQueueWords * 4);
   if (op == JSSA_OP_TOPK || op == JSSA_OP_DECODE) {
     ws->hist1 = take(rows * kDigit1Bins * 4);
-    ws->tile_cnt = take(rows * ws->n_sel_tiles * 4);
+    ws->tile_cnt = take(rows * cnt_tiles * 4);
     ws->tile_off = take(rows * ws->n_sel_tiles * 4);
     ws->cand_base = take(rows * ws->n_sel_tiles * 4);
     ws->cand = take(rows * size_t(d.t_max) * 8);
@@ -91,8 +99,9 @@ bool workspace_layout(const jssa_desc& d, int op, Workspace* ws) {
     const bool indexed = op != JSSA_OP_DENSE;
     const int64_t n_max = indexed ? int64_t(d.topk) + d.window : d.t_max;
     attn_chunking(int(rows), n_max, indexed, &ws->chunk, &ws->n_chunks);
-    ws->part_acc = take(rows * ws->n_chunks * size_t(G) * d.d_v * 4);
-    ws->part_ml = take(rows * ws->n_chunks * size_t(G) * 2 * 4);
+    const int part_chunks = ws->pipe_n_chunks > ws->n_chunks ? ws->pipe_n_chunks : ws->n_chunks;
+    ws->part_acc = take(rows * part_chunks * size_t(G) * d.d_v * 4);
+    ws->part_ml = take(rows * part_chunks * size_t(G) * 2 * 4);
   }
   if (op == JSSA_OP_DECODE) {
     ws->scores = take(rows * size_t(d.t_max) * 4);
@@ -233,6 +242,9 @@ static int32_t decode_impl(const jssa_desc* desc, const void* q, const float* P,
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + lay.idx);
   int32_t* n_sel = n_sel_out ? n_sel_out : reinterpret_cast<int32_t*>(base + lay.n_sel);
   hipStream_t s = as_stream(stream);
+  if (lay.pipe)
+    return to_status(launch_pipeline(*desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, idx, n_sel,
+                                     base, lay, ev, s));
   auto mark = [&](int i) { return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
   hipError_t e = mark(0);
   if (e == hipSuccess) e = launch_score(*desc, q, P, kp_cache, seq_lens, scores, base, lay, s);

@@ -1,0 +1,423 @@
+// Attention core shared by the stand-alone attention launch (attn.hip) and the
+// fused decode pipeline (pipeline.hip): one chunk of one (sequence, KV head)
+// row, with an online-softmax state per chunk and a log-sum-exp combine by the
+// row's last chunk (JSSA summary section 3.3: every selected K/V row is read in
+// place once and used by all G query heads of its KV head).
+#pragma once
+
+#include "jssa_device.hpp"
+#include "jssa_internal.hpp"
+#include "resolve.hpp"
+
+namespace jssa {
+
+constexpr int kMaxIdxChunk = 1024;
+constexpr uint32_t kSpinLimit = 1u << 26;  // bounded wait (seconds): a broken invariant cannot hang
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int32_t* idx;  // input list (indexed attention) or the output list (after a resolve)
+  const int32_t* n_sel;
+  const int32_t* seq_lens;
+  void* out;
+  float* lse;
+  float* part_acc;
+  float* part_ml;
+  uint32_t* row_state;
+  uint32_t* queue;
+  int Hq, Hkv, t_max, idx_stride, chunk, n_chunks, out_dtype;
+  int n_resolve, n_items, attend;
+  float qscale;  // softmax scale * log2(e): logits are kept in base 2
+  ResolveArgs res;
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int G, int D, bool INDEXED, bool RESOLVE>
+struct AttnSmem {
+  int idx[INDEXED ? kMaxIdxChunk : 1];
+  float m[4][G], l[4][G];
+  float acc[4][G][D];
+  uint32_t tab[RESOLVE ? 2 * kMaxSelTiles : 1];  // tile tables of extract_range
+  uint32_t scan[8];
+};
+
+// The last workgroup of the launch resets the queue for the next call.
+__device__ __forceinline__ void finish_item(const AttnArgs& a) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(&a.queue[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == uint32_t(a.n_items) - 1u) {
+      __hip_atomic_store(&a.queue[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.queue[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// The last chunk of a row to finish: log-sum-exp merge of the row's non-empty
+// chunk partials (in chunk order) into out (and lse), or out = 0, lse = -inf
+// when the row attends over nothing.
+template <int D, int G>
+__device__ __forceinline__ void combine_chunks(const AttnArgs& a, int row, int b, int h, int n) {
+  const uint32_t n_live = uint32_t((n + a.chunk - 1) / a.chunk);
+  if (n_live == 0) {  // nothing attended: out = 0, lse = -inf
+    for (int j = threadIdx.x; j < G * D; j += 256) {
+      const size_t o = (size_t(b) * a.Hq + size_t(h) * G) * D + j;
+      if (a.out_dtype == JSSA_BF16) reinterpret_cast<uint16_t*>(a.out)[o] = 0;
+      else reinterpret_cast<float*>(a.out)[o] = 0.f;
+    }
+    if (a.lse && threadIdx.x < G) a.lse[size_t(b) * a.Hq + h * G + threadIdx.x] = -INFINITY;
+    return;
+  }
+  const float* racc = a.part_acc + size_t(row) * a.n_chunks * G * D;
+  const float* rml = a.part_ml + size_t(row) * a.n_chunks * G * 2;
+  constexpr int CB = 8;  // chunks whose loads are issued together
+  for (int j = threadIdx.x; j < G * D; j += 256) {
+    const int g = j / D, dd = j - g * D;
+    float M = -INFINITY;
+    for (uint32_t cb = 0; cb < n_live; cb += CB) {
+      float mc[CB];
+#pragma unroll
+      for (int i = 0; i < CB; ++i)
+        mc[i] = (cb + i < n_live) ? consume(&rml[((cb + i) * G + g) * 2]) : -INFINITY;
+#pragma unroll
+      for (int i = 0; i < CB; ++i) M = fmaxf(M, mc[i]);
+    }
+    float L = 0.f, A = 0.f;
+    for (uint32_t cb = 0; cb < n_live; cb += CB) {
+      float mc[CB], lc[CB], ac[CB];
+#pragma unroll
+      for (int i = 0; i < CB; ++i) {
+        const bool ok = cb + i < n_live;
+        mc[i] = ok ? consume(&rml[((cb + i) * G + g) * 2]) : -INFINITY;
+        lc[i] = ok ? consume(&rml[((cb + i) * G + g) * 2 + 1]) : 0.f;
+        ac[i] = ok ? consume(&racc[(size_t(cb + i) * G + g) * D + dd]) : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < CB; ++i) {
+        const float w = (mc[i] == -INFINITY) ? 0.f : fast_exp2(mc[i] - M);
+        L = fmaf(lc[i], w, L);
+        A = fmaf(ac[i], w, A);
+      }
+    }
+    const float o = A / L;
+    const size_t oi = (size_t(b) * a.Hq + size_t(h) * G + g) * D + dd;
+    if (a.out_dtype == JSSA_BF16) reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_rne(o);
+    else reinterpret_cast<float*>(a.out)[oi] = o;
+    if (dd == 0 && a.lse) a.lse[size_t(b) * a.Hq + h * G + g] = (M + __log2f(L)) * kLn2;
+  }
+}
+
+// One chunk of one row: positions [chunk_id*chunk, ...) of the row's n
+// tokens; for the indexed path their token indices are already in S.idx.
+// RESET_READY: the row's last chunk also clears the row's ready flag (the
+// chunks waited for it).  Smem provides idx[], m[4][G], l[4][G], acc[4][G][D].
+// Returns true in the one workgroup of the row that merged the chunks.
+template <int KVT, int D, int G, bool INDEXED, bool RESET_READY, int U = JSSA_ATTN_UNROLL, typename Smem>
+__device__ bool attend_chunk(const AttnArgs& a, Smem& S, int row, int b, int h, int chunk_id, int n) {
+  constexpr int EB = Elem<KVT>::bytes;
+  constexpr int EPL = Elem<KVT>::per16;
+  constexpr int LR = D / EPL;   // lanes per K/V row
+  constexpr int RPW = 64 / LR;  // rows per wave per load
+  constexpr int NS = 4 * RPW;   // token streams per workgroup
+  // U: tokens per stream per step
+  static_assert(LR >= 4 && LR <= 32, "row split");
+
+  const int c0 = chunk_id * a.chunk;
+  const int cnt = c0 < n ? min(c0 + a.chunk, n) - c0 : 0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* pacc = a.part_acc + (size_t(row) * a.n_chunks + chunk_id) * G * D;
+  float* pml = a.part_ml + (size_t(row) * a.n_chunks + chunk_id) * G * 2;
+
+  if (cnt > 0) {
+    const int p = lane % LR, sidx = wave * RPW + lane / LR;
+    float qreg[G][EPL];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint4 raw = load16(reinterpret_cast<const char*>(a.q) +
+                               ((size_t(b) * a.Hq + size_t(h) * G + g) * D + p * EPL) * EB);
+      float tmp[EPL];
+      unpack16<KVT>(raw, tmp);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qreg[g][e] = tmp[e] * a.qscale;
+    }
+    float m[G], l[G], acc[G][EPL];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = -INFINITY;
+      l[g] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+    }
+    const char* kbase = reinterpret_cast<const char*>(a.k);
+    const char* vbase = reinterpret_cast<const char*>(a.v);
+    const size_t row_stride = size_t(a.Hkv) * D * EB;  // bytes between consecutive tokens
+    const size_t head_off = (size_t(b) * a.t_max * a.Hkv + h) * D * EB + size_t(p) * EPL * EB;
+    // K/V loads carry no per-lane branch (past-the-end streams re-read a valid
+    // row and are masked out), so the next step's rows stay in flight while the
+    // current ones are used.
+    auto row_off = [&](int i) {
+      const int ic = min(i, cnt - 1);
+      const int t = INDEXED ? min(max(S.idx[ic], 0), a.t_max - 1) : c0 + ic;  // indices are clamped
+      return head_off + size_t(t) * row_stride;
+    };
+    uint4 kn[U], vn[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t off = row_off(u * NS + sidx);
+      kn[u] = load16_nt(kbase + off);
+      vn[u] = load16_nt(vbase + off);
+    }
+    for (int i0 = 0; i0 < cnt; i0 += NS * U) {
+      uint4 kr[U], vr[U];
+      bool valid[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        kr[u] = kn[u];
+        vr[u] = vn[u];
+        valid[u] = i0 + u * NS + sidx < cnt;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const size_t off = row_off(i0 + NS * U + u * NS + sidx);
+        kn[u] = load16_nt(kbase + off);
+        vn[u] = load16_nt(vbase + off);
+      }
+      float lg[U][G];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float kf[EPL];
+        unpack16<KVT>(kr[u], kf);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) s = fmaf(qreg[g][e], kf[e], s);
+          s = group_sum<LR>(s);
+          lg[u][g] = valid[u] ? s : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float mx = lg[0][g];
+#pragma unroll
+        for (int u = 1; u < U; ++u) mx = fmaxf(mx, lg[u][g]);
+        const float mnew = fmaxf(m[g], mx);
+        if (mnew == -INFINITY) continue;
+        const float alpha = fast_exp2(m[g] - mnew);
+        l[g] *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+        m[g] = mnew;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float pu = fast_exp2(lg[u][g] - mnew);
+          l[g] += pu;
+          float vf[EPL];
+          unpack16<KVT>(vr[u], vf);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pu, vf[e], acc[g][e]);
+        }
+      }
+    }
+    // merge the RPW streams of each wave (rows LR lanes apart)
+#pragma unroll
+    for (int off = LR; off < 64; off <<= 1) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float mo = __shfl_xor(m[g], off);
+        const float lo = __shfl_xor(l[g], off);
+        const float M = fmaxf(m[g], mo);
+        const float a1 = (m[g] == -INFINITY) ? 0.f : fast_exp2(m[g] - M);
+        const float a2 = (mo == -INFINITY) ? 0.f : fast_exp2(mo - M);
+        l[g] = l[g] * a1 + lo * a2;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = acc[g][e] * a1 + __shfl_xor(acc[g][e], off) * a2;
+        m[g] = M;
+      }
+    }
+    if (lane < LR) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if (lane == 0) { S.m[wave][g] = m[g]; S.l[wave][g] = l[g]; }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) S.acc[wave][g][p * EPL + e] = acc[g][e];
+      }
+    }
+    __syncthreads();
+    // merge the 4 waves -> this chunk's partial state, published for the combine
+    for (int j = threadIdx.x; j < G * D; j += 256) {
+      const int g = j / D, dd = j - g * D;
+      float M = S.m[0][g];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) M = fmaxf(M, S.m[w][g]);
+      float L = 0.f, A = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float sc = (S.m[w][g] == -INFINITY) ? 0.f : fast_exp2(S.m[w][g] - M);
+        L = fmaf(S.l[w][g], sc, L);
+        A = fmaf(S.acc[w][g][dd], sc, A);
+      }
+      publish(&pacc[j], A);
+      if (dd == 0) { publish(&pml[2 * g], M); publish(&pml[2 * g + 1], L); }
+    }
+  }
+
+  // every chunk of the row arrives; the last one combines the non-empty chunks
+  uint32_t* rstate = a.row_state + size_t(row) * kRowStateWords;
+  if (!last_arrival(&rstate[RS_TICKET_ATTN], uint32_t(a.n_chunks))) return false;
+  if (RESET_READY && threadIdx.x == 0) publish(&rstate[RS_READY], 0u);  // every chunk has passed its wait
+  combine_chunks<D, G>(a, row, b, h, n);
+  return true;
+}
+
+// Two-pass variant for short chunks (the fused decode): every K and V row of
+// the chunk is requested at once (NL 16-byte loads of each per lane), then
+//   pass 1: base-2 logits of the G query heads -> shared memory; one wave per
+//           head finds the chunk's max m_g and sum l_g of exp2(logit - m_g)
+//           and turns the logits into those weights;
+//   pass 2: acc[g] = sum_t w[t][g] * V[t], summed over the row groups of a wave
+//           with shuffles and over the 4 waves through shared memory.
+// The chunk partial (m_g, l_g, acc[g]) is the one attend_chunk publishes, so
+// the same log-sum-exp combine finishes the row.  One chunk covers
+// CH = NL * 4 * RPW tokens (a.chunk must equal it).
+template <int KVT, int D, int G, int NL>
+struct Attn2Shape {
+  static constexpr int EB = Elem<KVT>::bytes;
+  static constexpr int EPL = Elem<KVT>::per16;
+  static constexpr int LR = D / EPL;   // lanes per K/V row
+  static constexpr int RPW = 64 / LR;  // rows per wave per load
+  static constexpr int CH = NL * 4 * RPW;
+};
+
+template <int KVT, int D, int G, int NL>
+struct Attn2Smem {
+  static constexpr int CH = Attn2Shape<KVT, D, G, NL>::CH;
+  int idx[CH];
+  float w[CH][G];      // logits, then weights
+  float ml[G][2];      // chunk max and sum of each head
+  float acc[4][G][D];  // per-wave partial outputs
+};
+
+template <int KVT, int D, int G, int NL, typename Smem>
+__device__ __forceinline__ bool attend_chunk_2pass(const AttnArgs& a, Smem& S, int row, int b, int h, int chunk_id, int n) {
+  using SH = Attn2Shape<KVT, D, G, NL>;
+  constexpr int EB = SH::EB, EPL = SH::EPL, LR = SH::LR, RPW = SH::RPW, CH = SH::CH;
+  static_assert(LR >= 4 && LR <= 32, "row split");
+  const int c0 = chunk_id * CH;
+  const int cnt = c0 < n ? min(c0 + CH, n) - c0 : 0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* pacc = a.part_acc + (size_t(row) * a.n_chunks + chunk_id) * G * D;
+  float* pml = a.part_ml + (size_t(row) * a.n_chunks + chunk_id) * G * 2;
+
+  if (cnt > 0) {
+    const int p = lane % LR, rsub = lane / LR;
+    const char* kbase = reinterpret_cast<const char*>(a.k);
+    const char* vbase = reinterpret_cast<const char*>(a.v);
+    const size_t row_stride = size_t(a.Hkv) * D * EB;
+    const size_t head_off = (size_t(b) * a.t_max * a.Hkv + h) * D * EB + size_t(p) * EPL * EB;
+    uint4 kr[NL], vr[NL];
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {  // rows past cnt re-read a valid row and get weight 0
+      const int r = (k * 4 + wave) * RPW + rsub;
+      const int t = min(max(S.idx[min(r, cnt - 1)], 0), a.t_max - 1);  // indices are clamped
+      const size_t off = head_off + size_t(t) * row_stride;
+      kr[k] = load16_nt(kbase + off);
+      vr[k] = load16_nt(vbase + off);
+    }
+    float qreg[G][EPL];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint4 raw = load16(reinterpret_cast<const char*>(a.q) +
+                               ((size_t(b) * a.Hq + size_t(h) * G + g) * D + p * EPL) * EB);
+      float tmp[EPL];
+      unpack16<KVT>(raw, tmp);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qreg[g][e] = tmp[e] * a.qscale;
+    }
+    // pass 1: logits
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int r = (k * 4 + wave) * RPW + rsub;
+      float kf[EPL];
+      unpack16<KVT>(kr[k], kf);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s = fmaf(qreg[g][e], kf[e], s);
+        s = group_sum<LR>(s);
+        if (p == 0) S.w[r][g] = (r < cnt) ? s : -INFINITY;
+      }
+    }
+    __syncthreads();
+    for (int g = wave; g < G; g += 4) {
+      float mx = -INFINITY;
+      for (int r = lane; r < CH; r += 64) mx = fmaxf(mx, S.w[r][g]);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      float sum = 0.f;
+      for (int r = lane; r < CH; r += 64) {
+        const float x = S.w[r][g];
+        const float wgt = (x == -INFINITY) ? 0.f : fast_exp2(x - mx);
+        S.w[r][g] = wgt;
+        sum += wgt;
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+      if (lane == 0) {
+        S.ml[g][0] = mx;
+        S.ml[g][1] = sum;
+      }
+    }
+    __syncthreads();
+    // pass 2: weighted V rows
+    float acc[G][EPL];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int r = (k * 4 + wave) * RPW + rsub;
+      float vf[EPL];
+      unpack16<KVT>(vr[k], vf);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float wgt = S.w[r][g];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(wgt, vf[e], acc[g][e]);
+      }
+    }
+#pragma unroll
+    for (int off = LR; off < 64; off <<= 1)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] += __shfl_xor(acc[g][e], off);
+    if (lane < LR) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) S.acc[wave][g][p * EPL + e] = acc[g][e];
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < G * D; j += 256) {
+      const int g = j / D, dd = j - g * D;
+      publish(&pacc[j], (S.acc[0][g][dd] + S.acc[1][g][dd]) + (S.acc[2][g][dd] + S.acc[3][g][dd]));
+      if (dd == 0) {
+        publish(&pml[2 * g], S.ml[g][0]);
+        publish(&pml[2 * g + 1], S.ml[g][1]);
+      }
+    }
+  }
+  uint32_t* rstate = a.row_state + size_t(row) * kRowStateWords;
+  if (!last_arrival(&rstate[RS_TICKET_ATTN], uint32_t(a.n_chunks))) return false;
+  combine_chunks<D, G>(a, row, b, h, n);
+  return true;
+}
+
+}  // namespace jssa

@@ -29,6 +29,7 @@ constexpr int kDigit1Bins = 1 << kDigit1Bits;
 constexpr int kMaxSelTiles = 4096;   // t_max <= kMaxSelTiles * kSelTile
 constexpr int kAttnBlock = 64;       // tokens per attention inner block (per workgroup pass)
 constexpr int kRowStateWords = 16;   // u32 words of per-row selection state
+constexpr int kMaxPipeChunk = 1024;  // attention chunk limit of the fused decode
 
 // per-row state (u32 words).  The tickets and the ready flag are zero on
 // entry and are left zero by every call.
@@ -68,6 +69,11 @@ struct Workspace {
   int n_chunks = 0;      // attention chunks per row
   int chunk = 0;         // tokens per attention chunk
   int n_sel_tiles = 0;
+  // fused decode (one persistent launch): available for the shapes it is built
+  // for; score items of pipe_ts tokens, pipe_tiles per row (tile_cnt and the
+  // candidate slots are shared with the staged path and sized for both)
+  bool pipe = false;
+  int pipe_ts = 0, pipe_tiles = 0, pipe_chunk = 0, pipe_n_chunks = 0;
 };
 
 // Layout for `op` (a jssa_op).  Returns false if the descriptor is invalid.
@@ -104,5 +110,18 @@ hipError_t launch_resolve_attend(const jssa_desc& d, bool resolve, bool attend, 
                                  char* ws_base, const Workspace& ws, hipStream_t s);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
+// Fused decode: whether a build exists for the descriptor's shape, its tile
+// size, tiles per row and attention chunk (tokens).
+bool pipeline_layout(const jssa_desc& d, int* ts, int* n_tiles, int* chunk);
+
+// The whole decode step in two launches (scan with sampled-threshold
+// candidate emission; resolve + attention); requires ws.pipe.  With `ev`
+// (four events): recorded before the scan, after it (twice: the candidate pass
+// is part of the scan) and after the resolve + attention launch.
+hipError_t launch_pipeline(const jssa_desc& d, const void* q, const float* P, const void* kp,
+                           const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
+                           float* lse, int32_t* idx, int32_t* n_sel, char* ws_base, const Workspace& ws,
+                           void* const* ev, hipStream_t s);
 
 }  // namespace jssa

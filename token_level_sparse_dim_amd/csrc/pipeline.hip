@@ -1,0 +1,846 @@
+// Sparse decode step in two launches (JSSA summary Figure 1 and section E.1:
+// subspace score scan, per-KV-head top-k selection, gather-free indexed
+// attention).
+//
+// Scan launch, one item per workgroup taken in ticket order:
+//   SAMPLE(row)     a candidate threshold L for the row from a strided sample
+//                   of its scores: a key far enough below the sample's estimate
+//                   of the k-th key that, with overwhelming probability, at
+//                   least k tokens score >= L.  Rows with nothing to choose
+//                   (every candidate taken, or none) get their index list here.
+//   SCORE(row, i)   scores run i of the row's tokens, streaming the
+//                   projected-key cache once, and writes the tokens scoring
+//                   >= L, in token order, to each tile's candidate slot.  Runs
+//                   are sized so that every item of the launch is resident at
+//                   once: a run streams long enough that its row's threshold
+//                   is known by the time it is needed.
+// Resolve + attention launch (the scan's output is read across the launch
+// boundary, on a GPU no longer saturated by the scan):
+//   RESOLVE(row)    the exact k-th key and tie cut among the row's candidates,
+//                   the ascending index list plus the window, n_sel.  If fewer
+//                   than k tokens reached L (the sample misled), the row is
+//                   redone exactly: its scores are recomputed, first for the
+//                   exact top radix digit of the k-th key, then to rewrite the
+//                   candidate slots from that digit.
+//   ATTN(row, c)    attention over chunk c of the row's index list once the
+//                   row is resolved; the row's last chunk merges the chunks.
+// Every wait is on an item handed out earlier in the same launch (a score run
+// on its row's sample, a chunk on its row's resolve) and is bounded in time.
+#include <math.h>
+
+#include <type_traits>
+
+#include "attn_core.hpp"
+#include "jssa_device.hpp"
+#include "jssa_internal.hpp"
+#include "score_core.hpp"
+#include "select_common.hpp"
+
+namespace jssa {
+
+constexpr int kPipeNit = 4;            // workgroup steps per tile
+constexpr int kPipeMaxItem = 8192;     // tokens per score item at most (whole tiles)
+constexpr int kPipeCandLds = 8192;     // candidates resolved in shared memory
+constexpr int kPipeMaxTiles = 2048;    // tiles per row
+constexpr int kPipeAttnNL = 8;         // K and V row loads per lane per attention chunk
+
+// per-row state word of the scan (zero on entry and exit): u64 at words 12-13,
+// (1 << 32) | L once the row's threshold is known
+constexpr int PW_L = 12;
+// queue words (PQ_ERR and PQ_FALLBACK are sticky diagnostics, the rest zero on entry and exit)
+enum PipeQueue : int { PQ_SCAN = 0, PQ_SCAN_EXIT = 1, PQ_ERR = 2, PQ_FALLBACK = 3, PQ_RA = 4, PQ_RA_EXIT = 5 };
+
+struct PipeArgs {
+  AttnArgs at;  // q, k, v, idx and n_sel (outputs), seq_lens, out, lse, partials, row_state, queue
+  const float* P;
+  const void* kp;
+  uint64_t* cand;      // [rows][t_max] candidate slots, ts entries per tile
+  uint32_t* tile_cnt;  // [rows][n_tiles]
+  int G, d_k, topk, window, q_dtype, ts, item, n_tiles, n_rows, items_per_row, n_main, n_attn;
+  uint64_t spin_ticks;  // wall-clock ticks after the launch's start when every wait gives up
+};
+
+__device__ __forceinline__ void flag_error(const PipeArgs& a) { publish(a.at.queue + PQ_ERR, 1u); }
+
+// Waits are bounded in time (a broken invariant ends the launch with the error
+// flag set instead of hanging it).
+__device__ __forceinline__ bool past(uint64_t deadline) { return wall_clock64() > deadline; }
+
+// The need-th largest key among n candidates ((index << 32) | key, read via
+// `get`), with the tie cut: exactly `need` candidates satisfy
+// key > K* or (key == K* and index <= I*).  Radix digits of 11, 11 and 10 bits
+// over shared-memory histograms (`hist`: 2048 words); ties by the index bits
+// 23..16, 15..8, 7..0.  1 <= need <= n.
+template <typename Get>
+__device__ void kth_cut(Get get, uint32_t n, uint32_t need, bool want_ties, uint32_t* hist,
+                        uint32_t* scan, uint32_t* out, uint32_t* kstar_out, uint32_t* istar_out) {
+  // digit A: bits 31..21
+  for (int i = threadIdx.x; i < 2048; i += 256) hist[i] = 0u;
+  __syncthreads();
+  for (uint32_t j = threadIdx.x; j < n; j += 256) atomicAdd(&hist[uint32_t(get(j)) >> 21], 1u);
+  __syncthreads();
+  find_bin_from_top<8>(hist, need, scan, out);
+  const uint32_t dA = out[0];
+  need -= out[1];
+  __syncthreads();
+  // digit B: bits 20..10
+  for (int i = threadIdx.x; i < 2048; i += 256) hist[i] = 0u;
+  __syncthreads();
+  for (uint32_t j = threadIdx.x; j < n; j += 256) {
+    const uint32_t key = uint32_t(get(j));
+    if ((key >> 21) == dA) atomicAdd(&hist[(key >> 10) & 0x7ffu], 1u);
+  }
+  __syncthreads();
+  find_bin_from_top<8>(hist, need, scan, out);
+  const uint32_t hi22 = (dA << 11) | out[0];
+  need -= out[1];
+  __syncthreads();
+  // digit C: bits 9..0
+  for (int i = threadIdx.x; i < 1024; i += 256) hist[i] = 0u;
+  __syncthreads();
+  for (uint32_t j = threadIdx.x; j < n; j += 256) {
+    const uint32_t key = uint32_t(get(j));
+    if ((key >> 10) == hi22) atomicAdd(&hist[key & 0x3ffu], 1u);
+  }
+  __syncthreads();
+  find_bin_from_top<4>(hist, need, scan, out);
+  const uint32_t dC = out[0];
+  const uint32_t m_ties = need - out[1];
+  const uint32_t n_eq = hist[dC];
+  const uint32_t kstar = (hi22 << 10) | dC;
+  __syncthreads();
+  uint32_t istar = 0xffffffffu;
+  if (want_ties && m_ties < n_eq) {
+    uint32_t prefix = 0, m = m_ties;
+    for (int shift = 16; shift >= 0; shift -= 8) {
+      hist[threadIdx.x] = 0u;
+      __syncthreads();
+      for (uint32_t j = threadIdx.x; j < n; j += 256) {
+        const uint64_t c = get(j);
+        const uint32_t t = uint32_t(c >> 32);
+        if (uint32_t(c) == kstar && (t >> (shift + 8)) == (prefix >> (shift + 8)))
+          atomicAdd(&hist[(t >> shift) & 0xffu], 1u);
+      }
+      __syncthreads();
+      find_bin_from_bottom<1>(hist, m, scan, out);
+      prefix |= out[0] << shift;
+      m -= out[1];
+      __syncthreads();
+    }
+    istar = prefix;
+  }
+  *kstar_out = kstar;
+  *istar_out = istar;
+}
+
+// Selection mode of sequence b: kk tokens to select among n_cand candidates.
+struct RowMode {
+  int Tb, n_cand, kk, nW;
+  __device__ bool select() const { return kk > 0 && kk < n_cand; }
+};
+__device__ __forceinline__ RowMode row_mode(const PipeArgs& a, int b) {
+  RowMode m;
+  m.n_cand = candidates_of(a.at.seq_lens, b, a.at.t_max, a.window, &m.Tb);
+  m.kk = a.topk < m.n_cand ? a.topk : m.n_cand;
+  m.nW = a.window < m.Tb ? a.window : m.Tb;
+  return m;
+}
+
+constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
+
+// Projection of the group's queries: the G query rows and P[h] (in chunks of
+// at most 4096 floats, rows of d in order) are staged in shared memory with all
+// loads of a chunk issued at once, then
+//   qp[g][i] = sum_d q[b, h*G + g, d] * P[h, d, i]
+// with the d-sum split over 256 / (G*R) threads, four running sums per thread
+// (d, d+1, d+2, d+3) carried across chunks, added as (s0 + s1) + (s2 + s3), and
+// the parts added in order: the arithmetic of the stand-alone score kernel.
+template <int D, int R, int G>
+struct QpSmem {
+  static constexpr int PCH = D * R <= 4096 ? D * R : 4096;  // floats of P per chunk
+  float P[PCH];
+  float q[G * D];
+  float part[256];
+  float qp[G * R];
+};
+
+template <int D, int R, int G>
+__device__ void project_query_staged(const PipeArgs& a, int b, int h, QpSmem<D, R, G>& sm) {
+  constexpr int PCH = QpSmem<D, R, G>::PCH;
+  constexpr int DCH = PCH / R;  // rows of d per chunk
+  constexpr int NCH = D / DCH;
+  constexpr int NP = PCH / 1024;           // 16-byte loads of a chunk per thread
+  constexpr int NQ = (G * D + 255) / 256;  // query elements per thread
+  constexpr int GR = G * R;
+  constexpr int PARTS = 256 / GR;
+  constexpr int DPER = D / PARTS;
+  static_assert(PCH % 1024 == 0 && GR <= 256 && DPER % 4 == 0 && DCH % 4 == 0, "staging shape");
+  const float* Ph = a.P + size_t(h) * D * R;
+  const size_t q0 = (size_t(b) * a.at.Hq + size_t(h) * G) * D;
+  float qv[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) qv[i] = load_elem(a.at.q, q0 + min(i * 256 + int(threadIdx.x), G * D - 1), a.q_dtype);
+  const int o = threadIdx.x % GR, part = threadIdx.x / GR;
+  const int g = o / R, i = o - g * R;
+  const int d_lo = part * DPER, d_hi = d_lo + DPER;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll 1
+  for (int c = 0; c < NCH; ++c) {
+    uint4 pv[NP];
+#pragma unroll
+    for (int k = 0; k < NP; ++k)
+      pv[k] = load16(reinterpret_cast<const uint4*>(Ph + size_t(c) * PCH) + k * 256 + threadIdx.x);
+    if (c > 0) __syncthreads();  // the previous chunk is no longer read
+#pragma unroll
+    for (int k = 0; k < NP; ++k) reinterpret_cast<uint4*>(sm.P)[k * 256 + threadIdx.x] = pv[k];
+    if (c == 0) {
+#pragma unroll
+      for (int k = 0; k < NQ; ++k)
+        if (k * 256 + int(threadIdx.x) < G * D) sm.q[k * 256 + threadIdx.x] = qv[k];
+    }
+    __syncthreads();
+    const float* qg = sm.q + g * D;
+    const int lo = max(d_lo, c * DCH), hi = min(d_hi, (c + 1) * DCH);
+    for (int d = lo; d < hi; d += 4) {
+      const int dl = d - c * DCH;
+      a0 = fmaf(qg[d + 0], sm.P[(dl + 0) * R + i], a0);
+      a1 = fmaf(qg[d + 1], sm.P[(dl + 1) * R + i], a1);
+      a2 = fmaf(qg[d + 2], sm.P[(dl + 2) * R + i], a2);
+      a3 = fmaf(qg[d + 3], sm.P[(dl + 3) * R + i], a3);
+    }
+  }
+  sm.part[threadIdx.x] = (a0 + a1) + (a2 + a3);
+  __syncthreads();
+  for (int j = threadIdx.x; j < GR; j += 256) {
+    float acc = 0.f;
+    for (int pp = 0; pp < PARTS; ++pp) acc += sm.part[pp * GR + j];
+    sm.qp[j] = acc;
+  }
+  __syncthreads();
+}
+
+template <int KPT, int R, int GE, int D, int G, int KVT>
+struct Pipe {
+  using S = ScanShape<KPT, R>;
+  static constexpr int TS = kPipeNit * S::PER_ITER;  // tokens per tile
+  static_assert(kPipeMaxItem % TS == 0, "score items are whole tiles");
+  static constexpr int NW = kPipeNit * S::U;  // keys per lane per tile
+  static constexpr int NSAMP = TS;            // sample size (one block of loads)
+  using Qp = QpSmem<D, R, G>;
+  using ASmem = Attn2Smem<KVT, D, G, kPipeAttnNL>;
+
+  struct SampleSmem {
+    Qp qp;
+    uint32_t keys[NSAMP];
+    uint32_t hist[2048];
+    uint32_t scan[8];
+    uint32_t out[2];
+  };
+  struct ScoreSmem {
+    union {
+      Qp qp;
+      uint32_t keys[kPipeMaxItem];  // keys of the item's tokens, token order
+    };
+    uint32_t l_key;
+  };
+  struct ResolveSmem {
+    uint32_t keys[kPipeCandLds];  // token indices of the candidates by ordinal
+    uint32_t tab[kPipeMaxTiles];  // candidate prefix per tile
+    uint32_t hist[2048];          // histograms of the cut
+    uint32_t scan[8];
+    uint32_t out[2];
+  };
+  static constexpr size_t kSmemScan = cmax(sizeof(SampleSmem), sizeof(ScoreSmem));
+  // the exact re-selection overlays ScoreSmem on ResolveSmem (its keys only on ResolveSmem::keys)
+  static constexpr size_t kSmemRA = cmax(cmax(sizeof(ResolveSmem), sizeof(ScoreSmem)), sizeof(ASmem));
+
+  static __device__ const char* kp_row(const PipeArgs& a, int row) {
+    return reinterpret_cast<const char*>(a.kp) + size_t(row) * a.at.t_max * R * S::EB;
+  }
+  static __device__ uint32_t* state(const PipeArgs& a, int row) {
+    return a.at.row_state + size_t(row) * kRowStateWords;
+  }
+  static __device__ uint64_t* l_word(const PipeArgs& a, int row) {
+    return reinterpret_cast<uint64_t*>(state(a, row) + PW_L);
+  }
+
+  // Rows with nothing to choose: every candidate (kk == n_cand) or none (kk == 0),
+  // plus the window (read by the next launch: plain stores).
+  static __device__ void resolve_trivial(const PipeArgs& a, int row, const RowMode& md) {
+    int32_t* out = a.at.idx + size_t(row) * a.at.idx_stride;
+    for (int j = threadIdx.x; j < md.nW; j += 256) out[md.kk + j] = md.Tb - md.nW + j;
+    for (int t = threadIdx.x; t < md.kk; t += 256) out[t] = t;
+    if (threadIdx.x == 0) const_cast<int32_t*>(a.at.n_sel)[row] = md.kk + md.nW;
+  }
+
+  // ---- SAMPLE -----------------------------------------------------------------------------
+  static __device__ __forceinline__ void sample(const PipeArgs& a, int row, SampleSmem& sm) {
+    const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
+    const RowMode md = row_mode(a, b);
+    if (!md.select()) {
+      resolve_trivial(a, row, md);
+      return;
+    }
+    uint32_t L = 0;  // every token is a candidate unless a sample allows a higher threshold
+    if (md.n_cand > kPipeCandLds) {
+      const int n_samp = NSAMP;  // n_cand > NSAMP here
+      const int stride = md.n_cand / n_samp;
+      const double E = double(n_samp) * md.kk / md.n_cand;  // expected sample tokens above the k-th score
+      const int m = int(ceil(E + 4.0 * sqrt(E) + 8.0));
+      if (m < n_samp) {
+        // the sampled projected keys are requested before the query projection
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int p = lane % S::LPT, tw = lane / S::LPT;
+        const char* kr = kp_row(a, row);
+        constexpr int HALF = kPipeNit / 2;  // steps per batch of loads
+        auto load_half = [&](int it0, uint4 (&v)[HALF][S::U]) {
+#pragma unroll
+          for (int it = 0; it < HALF; ++it)
+#pragma unroll
+            for (int u = 0; u < S::U; ++u) {
+              const int i = (it0 + it) * S::PER_ITER + (wave * S::U + u) * S::TPW + tw;
+              v[it][u] = load16_nt(kr + (size_t(i) * stride * R + p * S::EPL) * S::EB);
+            }
+        };
+        uint4 v[HALF][S::U];
+        load_half(0, v);
+        project_query_staged<D, R, G>(a, b, h, sm.qp);
+        float qreg[GE][S::EPL];
+        load_qreg<KPT, R, GE>([&](int i) { return sm.qp.qp[i]; }, G, qreg);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          uint4 w[HALF][S::U];
+          if (half == 0) load_half(HALF, w);
+#pragma unroll
+          for (int it = 0; it < HALF; ++it)
+#pragma unroll
+            for (int u = 0; u < S::U; ++u) {
+              const uint32_t key = score_key(score_of<KPT, R, GE>(v[it][u], qreg));
+              const int i = (half * HALF + it) * S::PER_ITER + (wave * S::U + u) * S::TPW + tw;
+              if (p == 0) sm.keys[i] = key;
+            }
+          if (half == 0) {
+#pragma unroll
+            for (int it = 0; it < HALF; ++it)
+#pragma unroll
+              for (int u = 0; u < S::U; ++u) v[it][u] = w[it][u];
+          }
+        }
+        __syncthreads();
+        uint32_t kstar, istar;
+        kth_cut([&](uint32_t j) { return uint64_t(sm.keys[j]); }, uint32_t(n_samp), uint32_t(m), false,
+                sm.hist, sm.scan, sm.out, &kstar, &istar);
+        L = kstar;
+      }
+    }
+    if (threadIdx.x == 0) publish(l_word(a, row), (uint64_t(1) << 32) | L);
+  }
+
+  // ---- SCORE ------------------------------------------------------------------------------
+  // Scores tokens [t_begin, t_end) of the row into keys[t - t_begin] (token
+  // order).  b0 holds the first step's loads, already issued.  Loads carry no
+  // per-lane branch (tokens past the end re-read the last one), so the next
+  // step's loads stay in flight while the current step is scored.
+  static __device__ void scan_keys(const char* kr, int t_begin, int t_end, const float (&qreg)[GE][S::EPL],
+                                   uint4 (&b0)[S::U], uint32_t* keys) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int p = lane % S::LPT, tw = lane / S::LPT;
+    const int n_steps = (t_end - t_begin + S::PER_ITER - 1) / S::PER_ITER;
+    for (int st = 0; st < n_steps; ++st) {
+      uint4 b1[S::U];
+      load_step(kr, t_begin + (st + 1) * S::PER_ITER, t_end, b1);
+#pragma unroll
+      for (int u = 0; u < S::U; ++u) {
+        const uint32_t key = score_key(score_of<KPT, R, GE>(b0[u], qreg));
+        if (p == 0) keys[st * S::PER_ITER + (wave * S::U + u) * S::TPW + tw] = key;
+      }
+#pragma unroll
+      for (int u = 0; u < S::U; ++u) b0[u] = b1[u];
+    }
+  }
+  static __device__ void load_step(const char* kr, int base, int t_end, uint4 (&v)[S::U]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int p = lane % S::LPT, tw = lane / S::LPT;
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      const int t = min(base + (wave * S::U + u) * S::TPW + tw, t_end - 1);
+      v[u] = load16_nt(kr + (size_t(t) * R + p * S::EPL) * S::EB);
+    }
+  }
+
+  // Writes the tokens of [t_begin, t_end) (whole tiles from t_begin) whose key
+  // in keys[] is >= thr to their tiles' candidate slots, in token order, and
+  // the tile counts (plain stores: read after the launch boundary, or by the
+  // workgroup that wrote them).  Each wave compacts whole tiles: lane l takes PL
+  // consecutive tokens and a wave scan gives the positions.
+  static __device__ void emit_keys(const PipeArgs& a, int row, int t_begin, int t_end, uint32_t thr,
+                                   const uint32_t* keys) {
+    constexpr int PL = TS / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n_sub = (t_end - t_begin + TS - 1) / TS;
+    const int tile0 = t_begin / TS;
+    for (int s = wave; s < n_sub; s += 4) {
+      const int t0 = t_begin + s * TS;
+      const int n_tok = min(TS, t_end - t0);
+      const uint32_t* kk = keys + s * TS + lane * PL;
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int k = 0; k < PL; ++k) cnt += (lane * PL + k < n_tok && kk[k] >= thr) ? 1u : 0u;
+      uint32_t incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      uint32_t pos = incl - cnt;
+      const uint32_t tot = __shfl(incl, 63);
+      uint64_t* slot = a.cand + size_t(row) * a.at.t_max + size_t(tile0 + s) * TS;
+#pragma unroll
+      for (int k = 0; k < PL; ++k) {
+        if (lane * PL + k < n_tok && kk[k] >= thr) {
+          slot[pos] = (uint64_t(uint32_t(t0 + lane * PL + k)) << 32) | kk[k];
+          ++pos;
+        }
+      }
+      if (lane == 0) a.tile_cnt[size_t(row) * a.n_tiles + tile0 + s] = tot;
+    }
+  }
+
+  static __device__ __forceinline__ void score_item(const PipeArgs& a, int row, int item, char* smem, uint64_t deadline) {
+    const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
+    const RowMode md = row_mode(a, b);
+    if (!md.select()) return;
+    const int t_begin = item * a.item;
+    if (t_begin >= md.n_cand) return;
+    const int t_end = min(t_begin + a.item, md.n_cand);
+    ScoreSmem& sm = *reinterpret_cast<ScoreSmem*>(smem);
+    const char* kr = kp_row(a, row);
+    uint4 b0[S::U];
+    load_step(kr, t_begin, t_end, b0);  // in flight during the query projection
+    uint64_t lw = 0;
+    if (threadIdx.x == 0) lw = consume(l_word(a, row));
+    project_query_staged<D, R, G>(a, b, h, sm.qp);
+    float qreg[GE][S::EPL];
+    load_qreg<KPT, R, GE>([&](int i) { return sm.qp.qp[i]; }, G, qreg);
+    __syncthreads();  // the projection's shared memory becomes the key buffer
+    scan_keys(kr, t_begin, t_end, qreg, b0, sm.keys);
+    // the row's threshold (its sample item was handed out before this item)
+    if (threadIdx.x == 0) {
+      while ((lw >> 32) == 0 && !past(deadline)) {
+        __builtin_amdgcn_s_sleep(1);
+        lw = consume(l_word(a, row));
+      }
+      if ((lw >> 32) == 0) flag_error(a);
+      sm.l_key = uint32_t(lw);
+    }
+    __syncthreads();
+    emit_keys(a, row, t_begin, t_end, sm.l_key, sm.keys);
+  }
+
+  // ---- RESOLVE (second launch) ------------------------------------------------------------
+  // Candidate counts of the row's tiles -> sm.tab (exclusive prefix); returns C.
+  static __device__ uint32_t count_candidates(const PipeArgs& a, int row, int n_tiles_row, ResolveSmem& sm) {
+    constexpr int PER = kPipeMaxTiles / 256;
+    const uint32_t* cnt = a.tile_cnt + size_t(row) * a.n_tiles;
+    uint32_t c[PER], local = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = int(threadIdx.x) * PER + j;
+      c[j] = (i < n_tiles_row) ? consume(&cnt[i]) : 0u;
+      local += c[j];
+    }
+    uint32_t C;
+    uint32_t run = block_exclusive_scan(local, sm.scan, &C);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      sm.tab[threadIdx.x * PER + j] = run;
+      run += c[j];
+    }
+    __syncthreads();
+    return C;
+  }
+
+  // The sampled threshold let fewer than kk tokens through: rebuild the row's
+  // candidate slots exactly (every key in or above the k-th key's top 11-bit
+  // bin), scanning the row twice: once for the histogram of that digit, once
+  // to write the candidates.
+  static __device__ __forceinline__ void exact_candidates(const PipeArgs& a, int row, const RowMode& md, char* smem) {
+    const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
+    ScoreSmem& ss = *reinterpret_cast<ScoreSmem*>(smem);
+    ResolveSmem& rs = *reinterpret_cast<ResolveSmem*>(smem);
+    project_query_staged<D, R, G>(a, b, h, ss.qp);
+    float qreg[GE][S::EPL];
+    load_qreg<KPT, R, GE>([&](int i) { return ss.qp.qp[i]; }, G, qreg);
+    for (int i = threadIdx.x; i < 2048; i += 256) rs.hist[i] = 0u;
+    __syncthreads();
+    const char* kr = kp_row(a, row);
+    for (int pass = 0; pass < 2; ++pass) {
+      uint32_t thr = 0;
+      if (pass == 1) {
+        find_bin_from_top<8>(rs.hist, uint32_t(md.kk), rs.scan, rs.out);
+        thr = rs.out[0] << 21;
+        __syncthreads();
+      }
+      for (int t_begin = 0; t_begin < md.n_cand; t_begin += kPipeMaxItem) {
+        const int t_end = min(t_begin + kPipeMaxItem, md.n_cand);
+        uint4 b0[S::U];
+        load_step(kr, t_begin, t_end, b0);
+        scan_keys(kr, t_begin, t_end, qreg, b0, ss.keys);
+        __syncthreads();
+        if (pass == 0) {
+          for (int i = threadIdx.x; i < t_end - t_begin; i += 256) atomicAdd(&rs.hist[ss.keys[i] >> 21], 1u);
+        } else {
+          emit_keys(a, row, t_begin, t_end, thr, ss.keys);
+        }
+        __syncthreads();
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(a.at.queue + PQ_FALLBACK, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  static __device__ __forceinline__ void resolve_select(const PipeArgs& a, int row, const RowMode& md, char* smem) {
+    ResolveSmem& sm = *reinterpret_cast<ResolveSmem*>(smem);
+    uint32_t* out = reinterpret_cast<uint32_t*>(a.at.idx + size_t(row) * a.at.idx_stride);
+    if (threadIdx.x == 0) *l_word(a, row) = 0;  // read again only by the next call's scan
+    for (int j = threadIdx.x; j < md.nW; j += 256) publish(&out[md.kk + j], uint32_t(md.Tb - md.nW + j));
+    if (threadIdx.x == 0)
+      publish(reinterpret_cast<uint32_t*>(const_cast<int32_t*>(a.at.n_sel) + row), uint32_t(md.kk + md.nW));
+    const int n_tiles_row = (md.n_cand + TS - 1) / TS;
+    uint32_t C = count_candidates(a, row, n_tiles_row, sm);
+    if (C < uint32_t(md.kk)) {
+      exact_candidates(a, row, md, smem);
+      C = count_candidates(a, row, n_tiles_row, sm);
+    }
+    // the slots were written by the scan launch, or by this workgroup's exact
+    // re-selection: plain loads see them
+    const uint64_t* slots = a.cand + size_t(row) * a.at.t_max;
+    auto global_cand = [&](uint32_t j) {
+      const uint32_t tile = last_le(sm.tab, uint32_t(n_tiles_row), j);
+      return slots[size_t(tile) * TS + (j - sm.tab[tile])];
+    };
+    uint32_t kstar, istar;
+    if (C <= uint32_t(kPipeCandLds)) {
+      // Thread x owns the contiguous run of candidate ordinals [j0, j1): their
+      // keys stay in registers for every pass of the cut, their token indices
+      // go to shared memory.  Candidates are in token order, so ranking equal
+      // keys by ordinal ranks them by token index.
+      constexpr int MAXPER = kPipeCandLds / 256;
+      constexpr int BATCH = 16;
+      const uint32_t per = (C + 255) / 256;
+      const uint32_t j0 = min(C, uint32_t(threadIdx.x) * per), j1 = min(C, j0 + per);
+      const int cnt = int(j1 - j0);
+      uint32_t kv[MAXPER];
+      {
+        uint32_t tile = cnt > 0 ? last_le(sm.tab, uint32_t(n_tiles_row), j0) : 0u;
+        uint32_t next = tile + 1 < uint32_t(n_tiles_row) ? sm.tab[tile + 1] : 0xffffffffu;
+#pragma unroll
+        for (int i0 = 0; i0 < MAXPER; i0 += BATCH) {
+          uint64_t v[BATCH];
+#pragma unroll
+          for (int u = 0; u < BATCH; ++u) {
+            const uint32_t j = j0 + uint32_t(i0 + u);
+            size_t off = 0;  // runs shorter than MAXPER re-read entry 0 (C >= 1) and ignore it
+            if (i0 + u < cnt) {
+              while (j >= next) {
+                ++tile;
+                next = tile + 1 < uint32_t(n_tiles_row) ? sm.tab[tile + 1] : 0xffffffffu;
+              }
+              off = size_t(tile) * TS + (j - sm.tab[tile]);
+            }
+            v[u] = slots[off];
+          }
+#pragma unroll
+          for (int u = 0; u < BATCH; ++u) {
+            kv[i0 + u] = uint32_t(v[u]);
+            if (i0 + u < cnt) sm.keys[j0 + i0 + u] = uint32_t(v[u] >> 32);  // token index of ordinal j
+          }
+        }
+      }
+      // radix digits of the key: bits 31..21, 20..10, 9..0
+      uint32_t need = uint32_t(md.kk), prefix = 0;
+      auto radix_pass = [&](auto sh_c, auto nb_c) {
+        constexpr int SH = decltype(sh_c)::value, NBITS = decltype(nb_c)::value, HI = SH + NBITS;
+        for (int i = threadIdx.x; i < (1 << NBITS); i += 256) sm.hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < MAXPER; ++i)
+          if (i < cnt && (HI >= 32 || (kv[i] >> (HI & 31)) == (prefix >> (HI & 31))))
+            atomicAdd(&sm.hist[(kv[i] >> SH) & ((1u << NBITS) - 1u)], 1u);
+        __syncthreads();
+        find_bin_from_top<(1 << NBITS) / 256>(sm.hist, need, sm.scan, sm.out);
+        prefix |= sm.out[0] << SH;
+        need -= sm.out[1];
+        __syncthreads();
+      };
+      radix_pass(std::integral_constant<int, 21>(), std::integral_constant<int, 11>());
+      radix_pass(std::integral_constant<int, 10>(), std::integral_constant<int, 11>());
+      radix_pass(std::integral_constant<int, 0>(), std::integral_constant<int, 10>());
+      kstar = prefix;
+      // ties: the `need` lowest ordinals among the keys equal to K* are taken
+      uint32_t eq = 0;
+#pragma unroll
+      for (int i = 0; i < MAXPER; ++i) eq += (i < cnt && kv[i] == kstar) ? 1u : 0u;
+      uint32_t n_eq;
+      const uint32_t eq_before = block_exclusive_scan(eq, sm.scan, &n_eq);
+      if (threadIdx.x == 0) sm.out[0] = 0xffffffffu;
+      __syncthreads();
+      if (need < n_eq && eq_before < need && need <= eq_before + eq) {
+        uint32_t seen = eq_before;
+#pragma unroll
+        for (int i = 0; i < MAXPER; ++i)
+          if (i < cnt && kv[i] == kstar && ++seen == need) sm.out[0] = j0 + uint32_t(i);
+      }
+      __syncthreads();
+      istar = sm.out[0];
+      // emission in token order
+      uint32_t mine = 0;
+#pragma unroll
+      for (int i = 0; i < MAXPER; ++i)
+        mine += (i < cnt && (kv[i] > kstar || (kv[i] == kstar && j0 + uint32_t(i) <= istar))) ? 1u : 0u;
+      uint32_t total;
+      uint32_t pos = block_exclusive_scan(mine, sm.scan, &total);
+#pragma unroll
+      for (int i = 0; i < MAXPER; ++i) {
+        if (i < cnt && (kv[i] > kstar || (kv[i] == kstar && j0 + uint32_t(i) <= istar))) {
+          if (pos < uint32_t(md.kk)) publish(&out[pos], sm.keys[j0 + i]);
+          ++pos;
+        }
+      }
+    } else {
+      // more candidates than shared memory holds: every pass reads them in place
+      kth_cut(global_cand, C, uint32_t(md.kk), true, sm.hist, sm.scan, sm.out, &kstar, &istar);
+      const uint32_t per = (C + 255) / 256;
+      const uint32_t j0 = threadIdx.x * per, j1 = min(C, j0 + per);
+      uint32_t mine = 0;
+      for (uint32_t j = j0; j < j1; ++j) mine += passes(global_cand(j), kstar, istar);
+      uint32_t total;
+      uint32_t pos = block_exclusive_scan(mine, sm.scan, &total);
+      for (uint32_t j = j0; j < j1; ++j) {
+        const uint64_t c = global_cand(j);
+        if (passes(c, kstar, istar)) {
+          if (pos < uint32_t(md.kk)) publish(&out[pos], uint32_t(c >> 32));
+          ++pos;
+        }
+      }
+    }
+    // the index list and n_sel are complete before the row is marked resolved
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) publish(&state(a, row)[RS_READY], 1u);
+  }
+
+  // ---- ATTN -------------------------------------------------------------------------------
+  static __device__ __forceinline__ void attend(const PipeArgs& a, int row, int chunk, ASmem& S_, uint64_t deadline) {
+    const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
+    const bool selects = row_mode(a, b).select();
+    uint32_t* ready = &state(a, row)[RS_READY];
+    if (selects && threadIdx.x == 0) {  // its resolve item was handed out before this chunk
+      int backoff = 1;
+      while (consume(ready) == 0u && !past(deadline)) {
+        for (int i = 0; i < backoff; ++i) __builtin_amdgcn_s_sleep(16);
+        backoff = backoff < 8 ? 2 * backoff : 8;
+      }
+      if (consume(ready) == 0u) flag_error(a);
+    }
+    __syncthreads();
+    int n = int(consume(reinterpret_cast<const uint32_t*>(a.at.n_sel + row)));
+    n = n < 0 ? 0 : (n > a.at.idx_stride ? a.at.idx_stride : n);
+    const int c0 = chunk * a.at.chunk;
+    const int cnt = c0 < n ? min(c0 + a.at.chunk, n) - c0 : 0;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.at.idx + size_t(row) * a.at.idx_stride + c0);
+    for (int i = threadIdx.x; i < cnt; i += 256) S_.idx[i] = int(consume(&src[i]));
+    __syncthreads();
+    // the chunk that merges the row clears its ready flag (every chunk has passed its wait)
+    if (attend_chunk_2pass<KVT, D, G, kPipeAttnNL>(a.at, S_, row, b, h, chunk, n) && selects && threadIdx.x == 0)
+      publish(ready, 0u);
+  }
+};
+
+// Resets the launch's ticket words once every workgroup has left.
+__device__ __forceinline__ void leave(uint32_t* queue, int ticket_word, int exit_word) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(queue + exit_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == gridDim.x - 1) {
+      __hip_atomic_store(queue + ticket_word, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(queue + exit_word, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+__device__ __forceinline__ int take_ticket(uint32_t* word) {
+  __shared__ int s_t;
+  if (threadIdx.x == 0) s_t = int(__hip_atomic_fetch_add(word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  __syncthreads();
+  return s_t;
+}
+
+// Scan launch: samples first, then the score runs row by row.
+template <int KPT, int R, int GE, int D, int G, int KVT>
+__global__ __launch_bounds__(256, 3) void scan_kernel(PipeArgs a) {
+  using Pp = Pipe<KPT, R, GE, D, G, KVT>;
+  __shared__ __align__(16) char smem[Pp::kSmemScan];
+  const uint64_t deadline = wall_clock64() + a.spin_ticks;
+  const int t = take_ticket(a.at.queue + PQ_SCAN);
+  if (t < a.n_rows) {
+    Pp::sample(a, t, *reinterpret_cast<typename Pp::SampleSmem*>(smem));
+  } else if (t < a.n_main) {
+    const int r = (t - a.n_rows) / a.items_per_row;
+    Pp::score_item(a, r, t - a.n_rows - r * a.items_per_row, smem, deadline);
+  }
+  leave(a.at.queue, PQ_SCAN, PQ_SCAN_EXIT);
+}
+
+// Resolve + attention launch: the rows' resolves first, then the attention
+// chunks row by row.
+template <int KPT, int R, int GE, int D, int G, int KVT>
+__global__ __launch_bounds__(256, 3) void resolve_attend_kernel(PipeArgs a) {
+  using Pp = Pipe<KPT, R, GE, D, G, KVT>;
+  __shared__ __align__(16) char smem[Pp::kSmemRA];
+  const uint64_t deadline = wall_clock64() + a.spin_ticks;
+  const int t = take_ticket(a.at.queue + PQ_RA);
+  if (t < a.n_rows) {
+    const RowMode md = row_mode(a, t / a.at.Hkv);
+    if (md.select()) Pp::resolve_select(a, t, md, smem);
+  } else if (t < a.n_rows + a.n_attn) {
+    const int c = t - a.n_rows;
+    Pp::attend(a, c / a.at.n_chunks, c % a.at.n_chunks, *reinterpret_cast<typename Pp::ASmem*>(smem), deadline);
+  }
+  leave(a.at.queue, PQ_RA, PQ_RA_EXIT);
+}
+
+// ---- host side ------------------------------------------------------------------------------
+// Shapes with a fused build: (kv/kp dtype, d, rank, G).  Others run the staged launches.
+struct PipeShape {
+  int dt, d, r, g;
+};
+static const PipeShape kPipeShapes[] = {
+    {JSSA_BF16, 128, 32, 4}, {JSSA_BF16, 128, 64, 1}, {JSSA_BF16, 64, 16, 4},
+    {JSSA_F32, 64, 16, 4},   {JSSA_F32, 128, 32, 2},
+};
+
+static int scan_tile_tokens(int dt, int r) {
+  const int per16 = dt == JSSA_BF16 ? 8 : 4;
+  return kPipeNit * 4 * (64 / (r / per16)) * JSSA_SCORE_UNROLL;
+}
+
+bool pipeline_layout(const jssa_desc& d, int* ts, int* n_tiles, int* chunk) {
+  const int G = d.n_q_heads / d.n_kv_heads;
+  bool ok = false;
+  for (const PipeShape& s : kPipeShapes)
+    ok |= (d.kv_dtype == s.dt && d.kp_dtype == s.dt && d.d_k == s.d && d.rank == s.r && G == s.g);
+  if (!ok || d.layout != JSSA_LAYOUT_GQA) return false;
+  *ts = scan_tile_tokens(d.kp_dtype, d.rank);
+  *n_tiles = (d.t_max + *ts - 1) / *ts;
+  const int per16 = d.kv_dtype == JSSA_BF16 ? 8 : 4;
+  *chunk = kPipeAttnNL * 4 * (64 / (d.d_k / per16));  // the two-pass attention chunk
+  return *n_tiles <= kPipeMaxTiles;
+}
+
+// Ticks of the device wall clock in 4 seconds (the bound on every wait).
+static uint64_t wait_ticks() {
+  static uint64_t ticks[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 400000000ull;
+  if (ticks[dev] == 0) {
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz < 1) khz = 100000;
+    ticks[dev] = uint64_t(khz) * 1000ull * 4ull;
+  }
+  return ticks[dev];
+}
+
+// Compute units of the current device (cached per device).
+static int compute_units() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <int KPT, int R, int GE, int D, int G, int KVT>
+static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
+  using Pp = Pipe<KPT, R, GE, D, G, KVT>;
+  if (Pp::TS != a.ts || Attn2Shape<KVT, D, G, kPipeAttnNL>::CH != a.at.chunk) return hipErrorInvalidValue;
+  // score runs sized so that the samples and every score run of the scan are
+  // resident at once: each run streams long enough for its row's threshold to
+  // be known when it needs it, and the rows finish their scans together
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_kernel<KPT, R, GE, D, G, KVT>, 256, 0) != hipSuccess ||
+        n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  const int resident = per_cu * compute_units();
+  const int per_row = resident > 2 * a.n_rows ? (resident - a.n_rows) / a.n_rows : 1;
+  int item = (a.at.t_max + per_row - 1) / per_row;
+  item = (item + Pp::TS - 1) / Pp::TS * Pp::TS;
+  a.item = item < Pp::TS ? Pp::TS : (item > kPipeMaxItem ? kPipeMaxItem : item);
+  a.items_per_row = (a.at.t_max + a.item - 1) / a.item;
+  a.n_main = a.n_rows + a.n_rows * a.items_per_row;
+  auto mark = [&](int i) { return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
+  hipError_t e = mark(0);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((scan_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_main), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess || (e = mark(2)) != hipSuccess) return e;
+  hipLaunchKernelGGL((resolve_attend_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_rows + a.n_attn), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return mark(3);
+}
+
+template <int DT, int D, int R, int G>
+static hipError_t launch_pipe_reduce(const PipeArgs& a, bool mean, void* const* ev, hipStream_t s) {
+  if (mean) return launch_pipe_t<DT, R, 1, D, G, DT>(a, ev, s);
+  return launch_pipe_t<DT, R, G, D, G, DT>(a, ev, s);
+}
+
+hipError_t launch_pipeline(const jssa_desc& d, const void* q, const float* P, const void* kp,
+                           const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
+                           float* lse, int32_t* idx, int32_t* n_sel, char* ws_base, const Workspace& ws,
+                           void* const* ev, hipStream_t s) {
+  if (!ws.pipe) return hipErrorInvalidValue;
+  PipeArgs a{};
+  AttnArgs& at = a.at;
+  at.q = q; at.k = k_cache; at.v = v_cache; at.idx = idx; at.n_sel = n_sel; at.seq_lens = seq_lens;
+  at.out = out; at.lse = lse;
+  at.part_acc = reinterpret_cast<float*>(ws_base + ws.part_acc);
+  at.part_ml = reinterpret_cast<float*>(ws_base + ws.part_ml);
+  at.row_state = reinterpret_cast<uint32_t*>(ws_base + ws.row_state);
+  at.queue = reinterpret_cast<uint32_t*>(ws_base + ws.queue);
+  at.Hq = d.n_q_heads; at.Hkv = d.n_kv_heads; at.t_max = d.t_max;
+  at.idx_stride = d.topk + d.window; at.chunk = ws.pipe_chunk; at.n_chunks = ws.pipe_n_chunks;
+  at.out_dtype = d.out_dtype; at.qscale = d.scale * kLog2e;
+  at.n_resolve = 0; at.attend = 1;
+  a.P = P; a.kp = kp;
+  a.cand = reinterpret_cast<uint64_t*>(ws_base + ws.cand);
+  a.tile_cnt = reinterpret_cast<uint32_t*>(ws_base + ws.tile_cnt);
+  a.G = d.n_q_heads / d.n_kv_heads; a.d_k = d.d_k; a.topk = d.topk; a.window = d.window;
+  a.q_dtype = d.kv_dtype; a.ts = ws.pipe_ts; a.n_tiles = ws.pipe_tiles;
+  a.n_rows = d.batch * d.n_kv_heads;
+  a.n_attn = a.n_rows * ws.pipe_n_chunks;
+  a.spin_ticks = wait_ticks();
+  const int G = a.G;
+  const bool mean = d.reduce == JSSA_REDUCE_MEAN;
+  if (d.kv_dtype == JSSA_BF16) {
+    if (d.d_k == 128 && d.rank == 32 && G == 4) return launch_pipe_reduce<1, 128, 32, 4>(a, mean, ev, s);
+    if (d.d_k == 128 && d.rank == 64 && G == 1) return launch_pipe_reduce<1, 128, 64, 1>(a, mean, ev, s);
+    if (d.d_k == 64 && d.rank == 16 && G == 4) return launch_pipe_reduce<1, 64, 16, 4>(a, mean, ev, s);
+  } else {
+    if (d.d_k == 64 && d.rank == 16 && G == 4) return launch_pipe_reduce<0, 64, 16, 4>(a, mean, ev, s);
+    if (d.d_k == 128 && d.rank == 32 && G == 2) return launch_pipe_reduce<0, 128, 32, 2>(a, mean, ev, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace jssa

@@ -6,6 +6,7 @@
 // pass over the scores for it.
 #include "jssa_device.hpp"
 #include "jssa_internal.hpp"
+#include "score_core.hpp"
 #include "select_common.hpp"
 
 namespace jssa {
@@ -21,43 +22,6 @@ struct ScoreArgs {
   int Hq, Hkv, G, d_k, t_max, topk, window, q_dtype;
 };
 
-// Projected queries of KV head h's group, fp32, into s_qp[g * R + i]:
-//   qp[g][i] = sum_d q[b, h*G + g, d] * P[h, d, i]
-// The query rows are staged in shared memory; the d-sum of each output is
-// split over several threads when G*R < 256 and the parts are added in a
-// fixed order.
-template <int R>
-__device__ void project_group_query(const void* q, int q_dtype, const float* P, int Hq, int d_k,
-                                    int G, int b, int h, float* s_q, float* s_part, float* s_qp) {
-  const size_t q0 = (size_t(b) * Hq + size_t(h) * G) * d_k;
-  for (int i = threadIdx.x; i < G * d_k; i += 256) s_q[i] = load_elem(q, q0 + i, q_dtype);
-  __syncthreads();
-  const int GR = G * R;
-  const int parts = GR >= 256 ? 1 : 256 / GR;
-  const int dper = d_k / parts;
-  const float* Ph = P + size_t(h) * d_k * R;
-  for (int j = threadIdx.x; j < GR * parts; j += 256) {
-    const int o = j % GR, part = j / GR;
-    const int g = o / R, i = o - g * R;
-    const float* qg = s_q + g * d_k;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int d = part * dper; d < (part + 1) * dper; d += 4) {
-      a0 = fmaf(qg[d + 0], Ph[size_t(d + 0) * R + i], a0);
-      a1 = fmaf(qg[d + 1], Ph[size_t(d + 1) * R + i], a1);
-      a2 = fmaf(qg[d + 2], Ph[size_t(d + 2) * R + i], a2);
-      a3 = fmaf(qg[d + 3], Ph[size_t(d + 3) * R + i], a3);
-    }
-    s_part[j] = (a0 + a1) + (a2 + a3);
-  }
-  __syncthreads();
-  for (int o = threadIdx.x; o < GR; o += 256) {
-    float acc = 0.f;
-    for (int part = 0; part < parts; ++part) acc += s_part[part * GR + o];
-    s_qp[o] = acc;
-  }
-  __syncthreads();
-}
-
 // One workgroup (4 waves) per kScoreTile candidate tokens of one (b, h) row.
 // Each token's projected key (R elements) is spread over LPT = R*bytes/16
 // lanes; each lane holds the matching slice of the G projected queries in
@@ -66,13 +30,8 @@ __device__ void project_group_query(const void* q, int q_dtype, const float* P, 
 // while the current ones are scored.  GE = G for the group max, 1 for the mean.
 template <int KPT, int R, int GE>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
-  constexpr int EB = Elem<KPT>::bytes;
-  constexpr int EPL = Elem<KPT>::per16;
-  constexpr int LPT = R / EPL;
-  constexpr int TPW = 64 / LPT;
-  constexpr int U = JSSA_SCORE_UNROLL;
-  constexpr int PER_ITER = 4 * TPW * U;
-  static_assert(LPT >= 1 && LPT <= 16 && (LPT & (LPT - 1)) == 0, "lanes per token");
+  using S = ScanShape<KPT, R>;
+  constexpr int EB = S::EB, EPL = S::EPL, LPT = S::LPT, TPW = S::TPW, U = S::U, PER_ITER = S::PER_ITER;
 
   __shared__ uint32_t s_hist[kDigit1Bins];
   __shared__ float s_q[8 * 128];
@@ -113,20 +72,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   project_group_query<R>(a.q, a.q_dtype, a.P, a.Hq, a.d_k, G, b, h, s_q, s_part, s_qp);
 
   float qreg[GE][EPL];
-  if constexpr (GE == 1) {
-    const float invG = 1.0f / float(G);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float sm = 0.f;
-      for (int g = 0; g < G; ++g) sm += s_qp[g * R + p * EPL + e];
-      qreg[0][e] = sm * invG;
-    }
-  } else {
-#pragma unroll
-    for (int g = 0; g < GE; ++g)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) qreg[g][e] = s_qp[g * R + p * EPL + e];
-  }
+  load_qreg<KPT, R, GE>([&](int i) { return s_qp[i]; }, G, qreg);
 
   for (int base = t0; base < t_end; base += PER_ITER) {
     uint4 nxt[U];
@@ -134,17 +80,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int tok = base + (wave * U + u) * TPW + tw;
-      float kv[EPL];
-      unpack16<KPT>(cur[u], kv);
-      float best;
-#pragma unroll
-      for (int g = 0; g < GE; ++g) {
-        float dsum = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) dsum = fmaf(qreg[g][e], kv[e], dsum);
-        dsum = group_sum<LPT>(dsum);
-        best = (g == 0) ? dsum : fmaxf(best, dsum);
-      }
+      const float best = score_of<KPT, R, GE>(cur[u], qreg);
       if (p == 0 && tok < t_end) {
         srow[tok] = best;
         if (do_hist) atomicAdd(&s_hist[score_key(best) >> (32 - kDigit1Bits)], 1u);
