@@ -1,8 +1,8 @@
-// Sparse decode step in two launches (JSSA summary Figure 1 and section E.1:
-// subspace score scan, per-KV-head top-k selection, gather-free indexed
+// Sparse decode step in three launches (JSSA summary Figure 1 and section
+// E.1: subspace score scan, per-KV-head top-k selection, gather-free indexed
 // attention).
 //
-// Scan launch, one item per workgroup taken in ticket order:
+// Scan launch, items taken in ticket order:
 //   SAMPLE(row)     a candidate threshold L for the row from a strided sample
 //                   of its scores: a key far enough below the sample's estimate
 //                   of the k-th key that, with overwhelming probability, at
@@ -11,21 +11,19 @@
 //   SCORE(row, i)   scores run i of the row's tokens, streaming the
 //                   projected-key cache once, and writes the tokens scoring
 //                   >= L, in token order, to each tile's candidate slot.  Runs
-//                   are sized so that every item of the launch is resident at
-//                   once: a run streams long enough that its row's threshold
-//                   is known by the time it is needed.
-// Resolve + attention launch (the scan's output is read across the launch
-// boundary, on a GPU no longer saturated by the scan):
-//   RESOLVE(row)    the exact k-th key and tie cut among the row's candidates,
-//                   the ascending index list plus the window, n_sel.  If fewer
-//                   than k tokens reached L (the sample misled), the row is
-//                   redone exactly: its scores are recomputed, first for the
-//                   exact top radix digit of the k-th key, then to rewrite the
-//                   candidate slots from that digit.
-//   ATTN(row, c)    attention over chunk c of the row's index list once the
-//                   row is resolved; the row's last chunk merges the chunks.
-// Every wait is on an item handed out earlier in the same launch (a score run
-// on its row's sample, a chunk on its row's resolve) and is bounded in time.
+//                   are sized so that one run per resident workgroup covers
+//                   the rows: a run streams long enough that its row's
+//                   threshold is known by the time it is needed.
+// Resolve launch, one workgroup per row: the exact k-th key and tie cut among
+//   the row's candidates, the ascending index list plus the window, n_sel.  If
+//   fewer than k tokens reached L (the sample misled), the row is redone
+//   exactly: its scores are recomputed, first for the exact top radix digit of
+//   the k-th key, then to rewrite the candidate slots from that digit.
+// Attention launch, one workgroup per chunk of a row's index list; the row's
+//   last chunk merges the chunks.
+// Data passes between launches through plain stores and loads; the only wait
+// inside a launch is a score run's on its row's sample (an earlier ticket),
+// bounded in time.
 #include <math.h>
 
 #include <type_traits>
@@ -48,7 +46,7 @@ constexpr int kPipeAttnNL = 8;         // K and V row loads per lane per attenti
 // (1 << 32) | L once the row's threshold is known
 constexpr int PW_L = 12;
 // queue words (PQ_ERR and PQ_FALLBACK are sticky diagnostics, the rest zero on entry and exit)
-enum PipeQueue : int { PQ_SCAN = 0, PQ_SCAN_EXIT = 1, PQ_ERR = 2, PQ_FALLBACK = 3, PQ_RA = 4, PQ_RA_EXIT = 5 };
+enum PipeQueue : int { PQ_SCAN = 0, PQ_SCAN_EXIT = 1, PQ_ERR = 2, PQ_FALLBACK = 3 };
 
 struct PipeArgs {
   AttnArgs at;  // q, k, v, idx and n_sel (outputs), seq_lens, out, lse, partials, row_state, queue
@@ -56,7 +54,8 @@ struct PipeArgs {
   const void* kp;
   uint64_t* cand;      // [rows][t_max] candidate slots, ts entries per tile
   uint32_t* tile_cnt;  // [rows][n_tiles]
-  int G, d_k, topk, window, q_dtype, ts, item, n_tiles, n_rows, items_per_row, n_main, n_attn;
+  int G, d_k, topk, window, q_dtype, ts, n_tiles, n_rows, n_main, n_attn;
+  int item, n_big, n_small;  // score runs: n_big runs of `item` tokens per row, then n_small single tiles
   uint64_t spin_ticks;  // wall-clock ticks after the launch's start when every wait gives up
 };
 
@@ -252,7 +251,7 @@ struct Pipe {
   };
   static constexpr size_t kSmemScan = cmax(sizeof(SampleSmem), sizeof(ScoreSmem));
   // the exact re-selection overlays ScoreSmem on ResolveSmem (its keys only on ResolveSmem::keys)
-  static constexpr size_t kSmemRA = cmax(cmax(sizeof(ResolveSmem), sizeof(ScoreSmem)), sizeof(ASmem));
+  static constexpr size_t kSmemResolve = cmax(sizeof(ResolveSmem), sizeof(ScoreSmem));
 
   static __device__ const char* kp_row(const PipeArgs& a, int row) {
     return reinterpret_cast<const char*>(a.kp) + size_t(row) * a.at.t_max * R * S::EB;
@@ -406,13 +405,14 @@ struct Pipe {
     }
   }
 
-  static __device__ __forceinline__ void score_item(const PipeArgs& a, int row, int item, char* smem, uint64_t deadline) {
+  // Scores tokens [t_begin, t_begin + len) of the row (whole tiles from t_begin).
+  static __device__ __forceinline__ void score_item(const PipeArgs& a, int row, int t_begin, int len, char* smem,
+                                                    uint64_t deadline) {
     const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
     const RowMode md = row_mode(a, b);
     if (!md.select()) return;
-    const int t_begin = item * a.item;
     if (t_begin >= md.n_cand) return;
-    const int t_end = min(t_begin + a.item, md.n_cand);
+    const int t_end = min(t_begin + len, md.n_cand);
     ScoreSmem& sm = *reinterpret_cast<ScoreSmem*>(smem);
     const char* kr = kp_row(a, row);
     uint4 b0[S::U];
@@ -505,9 +505,8 @@ struct Pipe {
     ResolveSmem& sm = *reinterpret_cast<ResolveSmem*>(smem);
     uint32_t* out = reinterpret_cast<uint32_t*>(a.at.idx + size_t(row) * a.at.idx_stride);
     if (threadIdx.x == 0) *l_word(a, row) = 0;  // read again only by the next call's scan
-    for (int j = threadIdx.x; j < md.nW; j += 256) publish(&out[md.kk + j], uint32_t(md.Tb - md.nW + j));
-    if (threadIdx.x == 0)
-      publish(reinterpret_cast<uint32_t*>(const_cast<int32_t*>(a.at.n_sel) + row), uint32_t(md.kk + md.nW));
+    for (int j = threadIdx.x; j < md.nW; j += 256) out[md.kk + j] = uint32_t(md.Tb - md.nW + j);
+    if (threadIdx.x == 0) const_cast<int32_t*>(a.at.n_sel)[row] = md.kk + md.nW;
     const int n_tiles_row = (md.n_cand + TS - 1) / TS;
     uint32_t C = count_candidates(a, row, n_tiles_row, sm);
     if (C < uint32_t(md.kk)) {
@@ -528,7 +527,7 @@ struct Pipe {
       // go to shared memory.  Candidates are in token order, so ranking equal
       // keys by ordinal ranks them by token index.
       constexpr int MAXPER = kPipeCandLds / 256;
-      constexpr int BATCH = 16;
+      constexpr int BATCH = MAXPER;  // every load of the run in one round trip
       const uint32_t per = (C + 255) / 256;
       const uint32_t j0 = min(C, uint32_t(threadIdx.x) * per), j1 = min(C, j0 + per);
       const int cnt = int(j1 - j0);
@@ -559,25 +558,48 @@ struct Pipe {
           }
         }
       }
-      // radix digits of the key: bits 31..21, 20..10, 9..0
-      uint32_t need = uint32_t(md.kk), prefix = 0;
-      auto radix_pass = [&](auto sh_c, auto nb_c) {
-        constexpr int SH = decltype(sh_c)::value, NBITS = decltype(nb_c)::value, HI = SH + NBITS;
-        for (int i = threadIdx.x; i < (1 << NBITS); i += 256) sm.hist[i] = 0u;
+      // Radix digits of d = key - (smallest candidate key): the candidates sit
+      // in a narrow band at the top, so digits of the key itself would pile
+      // them into a few bins.  Passes of 11 bits from the top set bit of the
+      // largest d down.
+      uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+      for (int i = 0; i < MAXPER; ++i)
+        if (i < cnt) {
+          kmin = min(kmin, kv[i]);
+          kmax = max(kmax, kv[i]);
+        }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), off)));
+        kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), off)));
+      }
+      if ((threadIdx.x & 63) == 0) {
+        sm.scan[threadIdx.x >> 6] = kmin;
+        sm.scan[4 + (threadIdx.x >> 6)] = kmax;
+      }
+      __syncthreads();
+      kmin = min(min(sm.scan[0], sm.scan[1]), min(sm.scan[2], sm.scan[3]));
+      kmax = max(max(sm.scan[4], sm.scan[5]), max(sm.scan[6], sm.scan[7]));
+      __syncthreads();
+      const int nbits = kmax > kmin ? 32 - __clz(kmax - kmin) : 1;
+      uint32_t need = uint32_t(md.kk), prefix = 0;  // prefix: the digits of d* found so far
+      for (int hi = nbits; hi > 0; hi -= 11) {
+        const int sh = hi > 11 ? hi - 11 : 0;
+        for (int i = threadIdx.x; i < 2048; i += 256) sm.hist[i] = 0u;
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < MAXPER; ++i)
-          if (i < cnt && (HI >= 32 || (kv[i] >> (HI & 31)) == (prefix >> (HI & 31))))
-            atomicAdd(&sm.hist[(kv[i] >> SH) & ((1u << NBITS) - 1u)], 1u);
+        for (int i = 0; i < MAXPER; ++i) {
+          const uint32_t dv = kv[i] - kmin;
+          if (i < cnt && (hi >= 32 || (dv >> hi) == (prefix >> hi))) atomicAdd(&sm.hist[(dv >> sh) & 0x7ffu], 1u);
+        }
         __syncthreads();
-        find_bin_from_top<(1 << NBITS) / 256>(sm.hist, need, sm.scan, sm.out);
-        prefix |= sm.out[0] << SH;
+        find_bin_from_top<8>(sm.hist, need, sm.scan, sm.out);
+        prefix |= sm.out[0] << sh;
         need -= sm.out[1];
         __syncthreads();
-      };
-      radix_pass(std::integral_constant<int, 21>(), std::integral_constant<int, 11>());
-      radix_pass(std::integral_constant<int, 10>(), std::integral_constant<int, 11>());
-      radix_pass(std::integral_constant<int, 0>(), std::integral_constant<int, 10>());
+      }
+      prefix += kmin;
       kstar = prefix;
       // ties: the `need` lowest ordinals among the keys equal to K* are taken
       uint32_t eq = 0;
@@ -605,7 +627,7 @@ struct Pipe {
 #pragma unroll
       for (int i = 0; i < MAXPER; ++i) {
         if (i < cnt && (kv[i] > kstar || (kv[i] == kstar && j0 + uint32_t(i) <= istar))) {
-          if (pos < uint32_t(md.kk)) publish(&out[pos], sm.keys[j0 + i]);
+          if (pos < uint32_t(md.kk)) out[pos] = sm.keys[j0 + i];
           ++pos;
         }
       }
@@ -621,41 +643,24 @@ struct Pipe {
       for (uint32_t j = j0; j < j1; ++j) {
         const uint64_t c = global_cand(j);
         if (passes(c, kstar, istar)) {
-          if (pos < uint32_t(md.kk)) publish(&out[pos], uint32_t(c >> 32));
+          if (pos < uint32_t(md.kk)) out[pos] = uint32_t(c >> 32);
           ++pos;
         }
       }
     }
-    // the index list and n_sel are complete before the row is marked resolved
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0) publish(&state(a, row)[RS_READY], 1u);
   }
 
   // ---- ATTN -------------------------------------------------------------------------------
-  static __device__ __forceinline__ void attend(const PipeArgs& a, int row, int chunk, ASmem& S_, uint64_t deadline) {
+  static __device__ __forceinline__ void attend(const PipeArgs& a, int row, int chunk, ASmem& S_) {
     const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
-    const bool selects = row_mode(a, b).select();
-    uint32_t* ready = &state(a, row)[RS_READY];
-    if (selects && threadIdx.x == 0) {  // its resolve item was handed out before this chunk
-      int backoff = 1;
-      while (consume(ready) == 0u && !past(deadline)) {
-        for (int i = 0; i < backoff; ++i) __builtin_amdgcn_s_sleep(16);
-        backoff = backoff < 8 ? 2 * backoff : 8;
-      }
-      if (consume(ready) == 0u) flag_error(a);
-    }
-    __syncthreads();
-    int n = int(consume(reinterpret_cast<const uint32_t*>(a.at.n_sel + row)));
-    n = n < 0 ? 0 : (n > a.at.idx_stride ? a.at.idx_stride : n);
+    // the chunk's index entries and n_sel (written by the previous launch) in one round trip
     const int c0 = chunk * a.at.chunk;
-    const int cnt = c0 < n ? min(c0 + a.at.chunk, n) - c0 : 0;
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.at.idx + size_t(row) * a.at.idx_stride + c0);
-    for (int i = threadIdx.x; i < cnt; i += 256) S_.idx[i] = int(consume(&src[i]));
+    const int32_t* src = a.at.idx + size_t(row) * a.at.idx_stride;
+    for (int i = threadIdx.x; i < a.at.chunk; i += 256) S_.idx[i] = src[min(c0 + i, a.at.idx_stride - 1)];
+    int n = a.at.n_sel[row];
+    n = n < 0 ? 0 : (n > a.at.idx_stride ? a.at.idx_stride : n);
     __syncthreads();
-    // the chunk that merges the row clears its ready flag (every chunk has passed its wait)
-    if (attend_chunk_2pass<KVT, D, G, kPipeAttnNL>(a.at, S_, row, b, h, chunk, n) && selects && threadIdx.x == 0)
-      publish(ready, 0u);
+    attend_chunk_2pass<KVT, D, G, kPipeAttnNL>(a.at, S_, row, b, h, chunk, n);
   }
 };
 
@@ -672,45 +677,70 @@ __device__ __forceinline__ void leave(uint32_t* queue, int ticket_word, int exit
   }
 }
 
+// A ticket for the whole workgroup (callers are between barriers, so s_t is
+// not read while it is rewritten).
 __device__ __forceinline__ int take_ticket(uint32_t* word) {
   __shared__ int s_t;
   if (threadIdx.x == 0) s_t = int(__hip_atomic_fetch_add(word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   __syncthreads();
-  return s_t;
+  const int t = s_t;
+  __syncthreads();
+  return t;
 }
 
-// Scan launch: samples first, then the score runs row by row.
+// Scan launch: tickets in order are the samples, one long score run per
+// resident workgroup (long enough that its row's threshold is known when it
+// finishes), then single-tile runs that balance the end.  A workgroup keeps
+// taking tickets until none are left.
 template <int KPT, int R, int GE, int D, int G, int KVT>
 __global__ __launch_bounds__(256, 3) void scan_kernel(PipeArgs a) {
   using Pp = Pipe<KPT, R, GE, D, G, KVT>;
   __shared__ __align__(16) char smem[Pp::kSmemScan];
   const uint64_t deadline = wall_clock64() + a.spin_ticks;
-  const int t = take_ticket(a.at.queue + PQ_SCAN);
-  if (t < a.n_rows) {
+  const int n_big_all = a.n_rows * a.n_big;
+  int t = take_ticket(a.at.queue + PQ_SCAN);
+  if (t < a.n_rows) {  // samples come first, outside the loop of score runs
     Pp::sample(a, t, *reinterpret_cast<typename Pp::SampleSmem*>(smem));
-  } else if (t < a.n_main) {
-    const int r = (t - a.n_rows) / a.items_per_row;
-    Pp::score_item(a, r, t - a.n_rows - r * a.items_per_row, smem, deadline);
+    __syncthreads();
+    t = take_ticket(a.at.queue + PQ_SCAN);
+  }
+  while (t < a.n_main) {
+    int r, t_begin, len;
+    if (t < a.n_rows + n_big_all) {
+      const int i = t - a.n_rows;
+      r = i / a.n_big;
+      t_begin = (i - r * a.n_big) * a.item;
+      len = a.item;
+    } else {
+      const int i = t - a.n_rows - n_big_all;
+      r = i / a.n_small;
+      t_begin = a.n_big * a.item + (i - r * a.n_small) * Pp::TS;
+      len = Pp::TS;
+    }
+    Pp::score_item(a, r, t_begin, len, smem, deadline);
+    __syncthreads();
+    t = take_ticket(a.at.queue + PQ_SCAN);
   }
   leave(a.at.queue, PQ_SCAN, PQ_SCAN_EXIT);
 }
 
-// Resolve + attention launch: the rows' resolves first, then the attention
-// chunks row by row.
+// Resolve launch: one workgroup per (sequence, KV head) row.
 template <int KPT, int R, int GE, int D, int G, int KVT>
-__global__ __launch_bounds__(256, 3) void resolve_attend_kernel(PipeArgs a) {
+__global__ __launch_bounds__(256, 1) void resolve_kernel(PipeArgs a) {
   using Pp = Pipe<KPT, R, GE, D, G, KVT>;
-  __shared__ __align__(16) char smem[Pp::kSmemRA];
-  const uint64_t deadline = wall_clock64() + a.spin_ticks;
-  const int t = take_ticket(a.at.queue + PQ_RA);
-  if (t < a.n_rows) {
-    const RowMode md = row_mode(a, t / a.at.Hkv);
-    if (md.select()) Pp::resolve_select(a, t, md, smem);
-  } else if (t < a.n_rows + a.n_attn) {
-    const int c = t - a.n_rows;
-    Pp::attend(a, c / a.at.n_chunks, c % a.at.n_chunks, *reinterpret_cast<typename Pp::ASmem*>(smem), deadline);
-  }
-  leave(a.at.queue, PQ_RA, PQ_RA_EXIT);
+  __shared__ __align__(16) char smem[Pp::kSmemResolve];
+  const int row = blockIdx.x;
+  const RowMode md = row_mode(a, row / a.at.Hkv);
+  if (md.select()) Pp::resolve_select(a, row, md, smem);
+}
+
+// Attention launch: one workgroup per chunk of a row's index list; the row's
+// last chunk to finish merges the chunks.
+template <int KPT, int R, int GE, int D, int G, int KVT>
+__global__ __launch_bounds__(256, 3) void attend_kernel(PipeArgs a) {
+  using Pp = Pipe<KPT, R, GE, D, G, KVT>;
+  __shared__ __align__(16) char smem[sizeof(typename Pp::ASmem)];
+  Pp::attend(a, blockIdx.x / a.at.n_chunks, blockIdx.x % a.at.n_chunks, *reinterpret_cast<typename Pp::ASmem*>(smem));
 }
 
 // ---- host side ------------------------------------------------------------------------------
@@ -771,9 +801,10 @@ template <int KPT, int R, int GE, int D, int G, int KVT>
 static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
   using Pp = Pipe<KPT, R, GE, D, G, KVT>;
   if (Pp::TS != a.ts || Attn2Shape<KVT, D, G, kPipeAttnNL>::CH != a.at.chunk) return hipErrorInvalidValue;
-  // score runs sized so that the samples and every score run of the scan are
-  // resident at once: each run streams long enough for its row's threshold to
-  // be known when it needs it, and the rows finish their scans together
+  // score runs sized so that the samples and one run per resident workgroup
+  // cover every row: each run streams long enough that its row's threshold is
+  // known when it finishes, and the rows finish their scans together (per-run
+  // overhead makes short runs for balancing a loss)
   static int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
@@ -783,18 +814,23 @@ static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
     per_cu = n;
   }
   const int resident = per_cu * compute_units();
+  const int n_tiles_max = (a.at.t_max + Pp::TS - 1) / Pp::TS;
   const int per_row = resident > 2 * a.n_rows ? (resident - a.n_rows) / a.n_rows : 1;
-  int item = (a.at.t_max + per_row - 1) / per_row;
-  item = (item + Pp::TS - 1) / Pp::TS * Pp::TS;
-  a.item = item < Pp::TS ? Pp::TS : (item > kPipeMaxItem ? kPipeMaxItem : item);
-  a.items_per_row = (a.at.t_max + a.item - 1) / a.item;
-  a.n_main = a.n_rows + a.n_rows * a.items_per_row;
+  int big_tiles = (n_tiles_max + per_row - 1) / per_row;
+  if (big_tiles > kPipeMaxItem / Pp::TS) big_tiles = kPipeMaxItem / Pp::TS;
+  a.item = big_tiles * Pp::TS;
+  a.n_big = (n_tiles_max + big_tiles - 1) / big_tiles;
+  a.n_small = 0;
+  a.n_main = a.n_rows + a.n_rows * a.n_big;
+  const int grid = resident < a.n_main ? resident : a.n_main;
   auto mark = [&](int i) { return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
   hipError_t e = mark(0);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((scan_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_main), dim3(256), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess || (e = mark(2)) != hipSuccess) return e;
-  hipLaunchKernelGGL((resolve_attend_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_rows + a.n_attn), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((scan_kernel<KPT, R, GE, D, G, KVT>), dim3(grid), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess) return e;
+  hipLaunchKernelGGL((resolve_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_rows), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess) return e;
+  hipLaunchKernelGGL((attend_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_attn), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return mark(3);
 }
