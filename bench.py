@@ -13,8 +13,12 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
 value = decode steps/s, plus effective HBM GB/s (projected-key bytes +
 selected K/V bytes per step) and its fraction of the 8 TB/s peak, the
 per-stage breakdown from HIP events, the roofline of the dominant kernel
-(the score scan), the dense full-KV decode on the same inputs, and the CPU
-oracle timed on a bounded sample on the host cores.
+(the projected-key scan), the dense full-KV decode on the same inputs, and the
+CPU oracle timed on a bounded sample on the host cores.
+
+``--calibrate-copy MB`` instead runs a plain device-to-device copy of MB
+mebibytes a few times and exits: the known-size kernel whose hardware byte
+counters scale those of the scan kernel.
 """
 from __future__ import annotations
 
@@ -48,7 +52,20 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense full-KV comparison")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                    help="only run a device copy of MB MiB (counter calibration) and exit")
     return ap.parse_args()
+
+
+def calibrate_copy(mib):
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
 
 
 def main():
@@ -62,6 +79,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import token_level_sparse_dim_amd as J
     from synth import WORKLOADS, generate, scaled
@@ -151,7 +172,9 @@ def main():
     torch.cuda.synchronize()
     stage_ms = np.array([[row[j].elapsed_time(row[j + 1]) for j in range(3)] for row in evs])
     stage_us = stage_ms.mean(axis=0) * 1e3
-    names = ["score_scan", "select_candidates", "resolve_attention"]
+    # fused build: scan (+ candidate emission), resolve, attention launches;
+    # staged build: score scan, candidate pass, resolve + attention launch
+    names = ["scan", "select", "attention"]
     log("stages (us): " + ", ".join(f"{n}={v:.2f}" for n, v in zip(names, stage_us)))
 
     # ---- bytes -------------------------------------------------------------------------------
@@ -167,13 +190,13 @@ def main():
     achieved = kp_bytes / (score_us * 1e-6) / 1e9
 
     traffic = None
-    tpath = os.path.join(ROOT, "profiles", f"score_kernel_{args.workload}_traffic.json")
+    tpath = os.path.join(ROOT, "profiles", f"scan_kernel_{args.workload}_traffic.json")
     if os.path.exists(tpath):
         try:
             with open(tpath) as f:
                 rec = json.load(f)
             from token_level_sparse_dim_amd.build import source_digest
-            if rec.get("source_digest") == source_digest("score.hip") and rec.get("topk") == w.topk:
+            if rec.get("source_digest") == source_digest("pipeline.hip") and rec.get("topk") == w.topk:
                 traffic = rec.get("hbm_bytes_per_launch")
         except Exception as exc:  # a stale or unreadable record reads as unmeasured
             log(f"traffic record ignored: {exc}")
@@ -190,7 +213,7 @@ def main():
         "eff_bytes_per_step": eff_bytes, "eff_GBps": round(eff_gbps, 1),
         "pct_peak": round(100.0 * eff_gbps / HBM_PEAK_GBPS, 2),
         "stages_us": {n: round(float(v), 2) for n, v in zip(names, stage_us)},
-        "roofline": {"kernel": "score_kernel (projected-key scan)", "bound": "hbm",
+        "roofline": {"kernel": "scan_kernel (projected-key scan + candidate emission)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "bytes_per_launch": kp_bytes, "avg_launch_us": round(score_us, 2)},

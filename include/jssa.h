@@ -191,11 +191,12 @@ int32_t jssa_decode(const jssa_desc* desc, const void* q, const float* P, const 
                     void* ws, size_t ws_bytes, void* stream);
 
 /* jssa_decode that also records four caller-created HIP events
- * (stage_events[i] is a hipEvent_t; the array is a host array) on `stream`:
- * [0] before the score scan, [1] after it, [2] after the candidate pass of
- * the selection (the same point as [1] where the scan emits the candidates
- * itself), [3] after the resolve + attention launch -- the per-component
- * latency breakdown of JSSA summary section E.1 (scan, selection, attention). */
+ * (stage_events[i] is a hipEvent_t; the array is a host array) on `stream`,
+ * around its launches -- the per-component latency breakdown of JSSA summary
+ * section E.1 (scan, selection, attention).  Fused build: [0] before the scan
+ * (which also writes the candidates), [1] after it, [2] after the resolve,
+ * [3] after the attention.  Other shapes: [0] before the score scan, [1] after
+ * it, [2] after the candidate pass, [3] after the resolve + attention. */
 int32_t jssa_decode_profiled(const jssa_desc* desc, const void* q, const float* P,
                              const void* kp_cache, const void* k_cache, const void* v_cache,
                              const int32_t* seq_lens, void* out, float* lse, int32_t* idx_out,

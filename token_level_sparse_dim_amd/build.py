@@ -63,7 +63,8 @@ def source_digest(name: str) -> str:
     tell whether a stored counter measurement still describes the current kernel)."""
     import hashlib
     h = hashlib.sha256()
-    for f in (name, "jssa_device.hpp", "jssa_internal.hpp", "select_common.hpp"):
+    for f in (name, "jssa_device.hpp", "jssa_internal.hpp", "select_common.hpp", "score_core.hpp",
+              "attn_core.hpp", "resolve.hpp"):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
