@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define JSSA_ABI_VERSION 1
+#define JSSA_ABI_VERSION 2
 
 typedef enum {
   JSSA_OK = 0,
@@ -79,14 +79,18 @@ typedef enum { JSSA_REDUCE_MAX = 0, JSSA_REDUCE_MEAN = 1 } jssa_reduce;
 
 /* GQA: standard [B, T, Hkv, d] K and V caches.  MLA: one shared latent row
  * per token (Hkv = 1); the value is the first d_v columns of that row and
- * selection yields one index set per sequence (JSSA summary section 3.3). */
+ * selection yields one index set per sequence (JSSA summary section 3.3).
+ * MLA builds: d_k = 576, d_v = 512, rank 32 or 64, Hq = 64 or 128, bf16 q,
+ * K and Kp; both contractions of scoring and attention run on the matrix
+ * cores.  v_cache is unused and may be NULL. */
 typedef enum { JSSA_LAYOUT_GQA = 0, JSSA_LAYOUT_MLA = 1 } jssa_layout;
 
 typedef enum {
   JSSA_OP_TOPK = 1,    /* jssa_topk */
   JSSA_OP_ATTN = 2,    /* jssa_indexed_attn */
   JSSA_OP_DECODE = 3,  /* jssa_decode */
-  JSSA_OP_DENSE = 4    /* jssa_dense_decode */
+  JSSA_OP_DENSE = 4,   /* jssa_dense_decode */
+  JSSA_OP_SCORE = 5    /* jssa_score */
 } jssa_op;
 
 typedef struct {
@@ -144,9 +148,14 @@ int32_t jssa_append_kv(const jssa_desc* desc, const void* k_new, const void* v_n
  * candidate t < seq_lens[b] - window,
  *   scores[b,h,t] = reduce_g sum_i (q[b,h*G+g,:] P[h])[i] * kp_cache[b,h,t,i]
  * with the projected query kept in fp32.  Entries t >= seq_lens[b] - window
- * are not written. */
+ * are not written.  MLA: the projected queries are fp32 and enter the
+ * matrix-core product as two bf16 terms (hi = nearest bf16, lo = nearest
+ * bf16 of the remainder), so |error| <= 2^-17 * sum_i |qp_i Kp_i| per head;
+ * MEAN projects the mean of the Hq queries.
+ * Workspace op JSSA_OP_SCORE: MLA descriptors need it (the projected-query
+ * fragments); GQA descriptors do not use it and may pass NULL. */
 int32_t jssa_score(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
-                   const int32_t* seq_lens, float* scores, void* stream);
+                   const int32_t* seq_lens, float* scores, void* ws, size_t ws_bytes, void* stream);
 
 /* Per-(sequence, KV head) selection (JSSA summary Figure 1, section 3.1,
  * appendix A.3): among the candidates t < T_b - W (T_b = seq_lens[b]) keep
@@ -166,7 +175,10 @@ int32_t jssa_topk(const jssa_desc* desc, const float* scores, const int32_t* seq
  * reading each selected K/V row in place once for all G query heads; fp32
  * accumulation; index chunks merged by a log-sum-exp combine.  n_sel = 0
  * gives out = 0 and lse = -inf.  Indices should lie in [0, t_max); others are
- * clamped into that range.
+ * clamped into that range.  MLA: all Hq heads share the one index set per
+ * sequence; the value is the first d_v columns of the selected row; q.K and
+ * P V run on the matrix cores with fp32 accumulation and the probabilities
+ * entered as bf16 hi + lo terms (about 16 significant bits).
  * Workspace op JSSA_OP_ATTN. */
 int32_t jssa_indexed_attn(const jssa_desc* desc, const void* q, const void* k_cache,
                           const void* v_cache, const int32_t* idx, const int32_t* n_sel,
@@ -181,7 +193,9 @@ int32_t jssa_indexed_attn(const jssa_desc* desc, const void* q, const void* k_ca
  * tokens at or above a threshold taken from a strided sample of the row's
  * scores, and a resolve + attention launch that selects exactly among them
  * (re-selecting a row exactly in the rare case fewer than k tokens passed the
- * threshold).  Other shapes run the stand-alone kernels in sequence.
+ * threshold).  Other shapes run the stand-alone kernels in sequence (MLA:
+ * query projection, score scan with the first-digit histogram, candidate
+ * pass, resolve, attention, chunk merge).
  * idx_out / n_sel_out may be NULL; when given they receive the selection.
  * The new token is expected to be appended (jssa_append_kv) before this
  * call.  Workspace op JSSA_OP_DECODE. */

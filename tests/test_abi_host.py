@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert J.abi_version() == 1
+    assert J.abi_version() == 2
     lib = J.lib()
     assert lib.jssa_status_str(0) == b"JSSA_OK"
     for code, name in _lib.STATUS.items():
@@ -80,7 +80,7 @@ def test_selection_needs_a_budget_or_window():
 
 def test_workspace_sizes():
     d = _desc()
-    for op in (J.OP_TOPK, J.OP_ATTN, J.OP_DECODE, J.OP_DENSE):
+    for op in (J.OP_TOPK, J.OP_ATTN, J.OP_DECODE, J.OP_DENSE, J.OP_SCORE):
         n = J.workspace_bytes(d, op)
         assert n > 0 and n % 256 == 0
     assert J.workspace_bytes(d, J.OP_DECODE) > J.workspace_bytes(d, J.OP_TOPK)
@@ -98,7 +98,7 @@ def test_entry_points_reject_bad_arguments_before_launch():
     p = _fake(12)
     null = None
     # null required pointers
-    assert lib.jssa_score(d, null, *p[:4], null) == -1
+    assert lib.jssa_score(d, null, *p[:4], null, 0, null) == -1
     assert lib.jssa_topk(d, *p[:4], null, 0, null) == -3            # workspace missing
     assert lib.jssa_topk(d, *p[:4], ctypes.c_void_p(4096), 16, null) == -3  # too small
     assert lib.jssa_topk(d, *p[:4], ctypes.c_void_p(4096 + 16), 1 << 40, null) == -3  # misaligned ws
@@ -108,13 +108,67 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.jssa_append_kv(d, *p[:2], -1, *p[2:7], null) == -1
     # misaligned data pointers
     odd = ctypes.c_void_p(4096 + 2)
-    assert lib.jssa_score(d, odd, *p[:4], null) == -4
+    assert lib.jssa_score(d, odd, *p[:4], null, 0, null) == -4
     assert lib.jssa_decode(d, *p[:5], odd, p[6], null, null, null, p[7], 1 << 40, null) == -4
     # invalid descriptor wins over everything else
     bad = _desc(n_q_heads=30).c()
     assert lib.jssa_decode(bad, *p[:7], null, null, null, p[7], 1 << 40, null) == -1
-    assert lib.jssa_score(None, *p[:5], null) == -1
+    assert lib.jssa_score(None, *p[:5], null, 0, null) == -1
     # workspace init argument checks
     assert lib.jssa_workspace_init(None, 64, None) == -1
     assert lib.jssa_workspace_init(ctypes.c_void_p(4096 + 8), 64, None) == -3
     assert lib.jssa_workspace_init(None, 0, None) == 0  # nothing to do
+
+
+def _mla(**kw):
+    base = dict(batch=8, n_q_heads=128, n_kv_heads=1, d_k=576, d_v=512, rank=64, t_max=131072,
+                topk=2048, window=0, layout=J.LAYOUT_MLA, scale=576 ** -0.5)
+    base.update(kw)
+    return _desc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 0),
+    (dict(rank=32), 0),
+    (dict(n_q_heads=64), 0),
+    (dict(reduce=J.REDUCE_MEAN), 0),
+    (dict(n_kv_heads=2, n_q_heads=128), -1),  # one latent row per token
+    (dict(d_v=640), -1),                      # the value is a prefix of the row
+    (dict(rank=16), -2),
+    (dict(n_q_heads=96), -2),
+    (dict(d_k=512, d_v=448), -2),
+    (dict(kv_dtype=J.F32, kp_dtype=J.F32), -2),
+    (dict(kp_dtype=J.F32), -2),
+])
+def test_mla_descriptor_validation(kw, status):
+    for op in (J.OP_DECODE, J.OP_SCORE, J.OP_ATTN, J.OP_DENSE, 0):
+        assert J.check_desc(_mla(**kw), op) == status, op
+
+
+def test_mla_workspace_holds_query_fragments_and_partials():
+    d = _mla()
+    # projected-query fragments: B x (Hq/16 M-tiles) x (r/32 steps) x (hi, lo) x 1 KiB
+    frag = 8 * 8 * 2 * 2 * 1024
+    assert J.workspace_bytes(d, J.OP_SCORE) >= frag
+    assert J.workspace_bytes(_mla(reduce=J.REDUCE_MEAN), J.OP_SCORE) < J.workspace_bytes(d, J.OP_SCORE)
+    # attention partials: fp32 [B][chunks][Hq][512] for at least one chunk
+    assert J.workspace_bytes(d, J.OP_ATTN) >= 8 * 128 * 512 * 4
+    assert J.workspace_bytes(d, J.OP_DECODE) > J.workspace_bytes(d, J.OP_SCORE) + J.workspace_bytes(d, J.OP_ATTN)
+
+
+def test_mla_entry_points_accept_null_v_cache_and_need_a_score_workspace():
+    lib = J.lib()
+    d = _mla().c()
+    p = _fake(12)
+    null = None
+    # MLA scoring needs the workspace (the projected-query fragments)
+    assert lib.jssa_score(d, *p[:5], null, 0, null) == -3
+    assert lib.jssa_score(d, *p[:5], ctypes.c_void_p(4096), 64, null) == -3
+    # v_cache is unused for MLA: a NULL v_cache passes the pointer checks and
+    # the call fails on the missing workspace instead
+    assert lib.jssa_indexed_attn(d, p[0], p[1], null, p[2], p[3], p[4], null, null, 0, null) == -3
+    assert lib.jssa_dense_decode(d, p[0], p[1], null, p[2], p[3], null, null, 0, null) == -3
+    assert lib.jssa_decode(d, *p[:4], null, p[4], p[5], null, null, null, null, 0, null) == -3
+    # GQA still requires v_cache
+    g = _desc().c()
+    assert lib.jssa_dense_decode(g, p[0], p[1], null, p[2], p[3], null, null, 0, null) == -1

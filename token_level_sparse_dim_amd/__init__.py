@@ -9,12 +9,12 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import (BF16, F32, LAYOUT_GQA, LAYOUT_MLA, OP_ATTN, OP_DECODE, OP_DENSE, OP_TOPK,
+from ._lib import (BF16, F32, LAYOUT_GQA, LAYOUT_MLA, OP_ATTN, OP_DECODE, OP_DENSE, OP_SCORE, OP_TOPK,
                    REDUCE_MAX, REDUCE_MEAN, Desc, JssaError, call, lib)
 
 __all__ = [
     "Desc", "JssaError", "F32", "BF16", "REDUCE_MAX", "REDUCE_MEAN", "LAYOUT_GQA", "LAYOUT_MLA",
-    "OP_TOPK", "OP_ATTN", "OP_DECODE", "OP_DENSE", "lib", "abi_version", "check_desc",
+    "OP_TOPK", "OP_ATTN", "OP_DECODE", "OP_DENSE", "OP_SCORE", "lib", "abi_version", "check_desc",
     "workspace_bytes", "workspace", "append_kv", "append_projection", "score", "topk", "indexed_attn", "decode", "decode_profiled",
     "dense_decode",
 ]
@@ -84,11 +84,13 @@ def append_projection(desc: Desc, n_new: int, pos, P, k_cache, kp_cache, stream=
          _ptr(kp_cache, kp, "kp_cache"), _stream(stream))
 
 
-def score(desc: Desc, q, P, kp_cache, seq_lens, scores, stream=None):
-    """``jssa_score``: subspace scores of every candidate token."""
+def score(desc: Desc, q, P, kp_cache, seq_lens, scores, ws=None, stream=None):
+    """``jssa_score``: subspace scores of every candidate token.  ``ws`` is the
+    JSSA_OP_SCORE workspace; MLA descriptors need one (GQA ones ignore it)."""
+    wsp, wsn = (None, 0) if ws is None else (_ptr(ws, torch.uint8, "ws"), ws.numel())
     call("jssa_score", desc.c(), _ptr(q, _TORCH_DTYPE[desc.kv_dtype], "q"), _ptr(P, torch.float32, "P"),
          _ptr(kp_cache, _TORCH_DTYPE[desc.kp_dtype], "kp_cache"), _ptr(seq_lens, torch.int32, "seq_lens"),
-         _ptr(scores, torch.float32, "scores"), _stream(stream))
+         _ptr(scores, torch.float32, "scores"), wsp, wsn, _stream(stream))
 
 
 def topk(desc: Desc, scores, seq_lens, idx, n_sel, ws, stream=None):

@@ -16,7 +16,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjssa.so
 F32, BF16 = 0, 1
 REDUCE_MAX, REDUCE_MEAN = 0, 1
 LAYOUT_GQA, LAYOUT_MLA = 0, 1
-OP_TOPK, OP_ATTN, OP_DECODE, OP_DENSE = 1, 2, 3, 4
+OP_TOPK, OP_ATTN, OP_DECODE, OP_DENSE, OP_SCORE = 1, 2, 3, 4, 5
 
 STATUS = {0: "JSSA_OK", -1: "JSSA_ERR_INVALID_ARG", -2: "JSSA_ERR_UNSUPPORTED",
           -3: "JSSA_ERR_WORKSPACE", -4: "JSSA_ERR_MISALIGNED", -5: "JSSA_ERR_HIP"}
@@ -40,7 +40,8 @@ SIGNATURES = {
     "jssa_workspace_init": (_i32, [_c_void_p, _size_t, _c_void_p]),
     "jssa_append_kv": (_i32, [_PDESC, _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p,
                               _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
-    "jssa_score": (_i32, [_PDESC, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "jssa_score": (_i32, [_PDESC, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                          _size_t, _c_void_p]),
     "jssa_topk": (_i32, [_PDESC, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t,
                          _c_void_p]),
     "jssa_indexed_attn": (_i32, [_PDESC, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,

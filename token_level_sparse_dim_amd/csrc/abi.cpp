@@ -36,6 +36,21 @@ void attn_chunking(int rows, int64_t n_max, bool indexed, int* chunk, int* n_chu
   if (*n_chunks < 1) *n_chunks = 1;
 }
 
+// MLA attention chunking: workgroups are (sequence, 32-head group, chunk);
+// about 256 of them for the indexed path (one per CU: each holds a whole CU's
+// registers) and 1024 for the dense path.  Chunks are multiples of 64 rows.
+void mla_chunking(int batch, int groups, int64_t n_max, bool indexed, int* chunk, int* n_chunks) {
+  const int64_t target = indexed ? 256 : 1024;
+  const int64_t hi = indexed ? 2048 : 8192;
+  int64_t c = (n_max * batch * groups + target - 1) / target;
+  c = (c + 63) / 64 * 64;
+  if (c < 64) c = 64;
+  if (c > hi) c = hi;
+  *chunk = int(c);
+  *n_chunks = int((n_max + c - 1) / c);
+  if (*n_chunks < 1) *n_chunks = 1;
+}
+
 }  // namespace
 
 namespace jssa {
@@ -59,7 +74,15 @@ static int32_t check(const jssa_desc* d, int op) {
   if (d->d_k < 1 || d->d_v < 1 || d->rank < 1 || d->rank > d->d_k) return JSSA_ERR_INVALID_ARG;
   if (d->rank != 16 && d->rank != 32 && d->rank != 64) return JSSA_ERR_UNSUPPORTED;
   const int G = d->n_q_heads / d->n_kv_heads;
-  if (d->layout == JSSA_LAYOUT_MLA) return JSSA_ERR_UNSUPPORTED;
+  if (d->layout == JSSA_LAYOUT_MLA) {
+    // one latent row per token, the value is a prefix of it
+    if (d->n_kv_heads != 1 || d->d_v > d->d_k) return JSSA_ERR_INVALID_ARG;
+    if (d->d_k != kMlaDk || d->d_v != kMlaDv) return JSSA_ERR_UNSUPPORTED;
+    if (d->rank != 32 && d->rank != 64) return JSSA_ERR_UNSUPPORTED;
+    if (d->kv_dtype != JSSA_BF16 || d->kp_dtype != JSSA_BF16) return JSSA_ERR_UNSUPPORTED;
+    if (d->n_q_heads != 64 && d->n_q_heads != 128) return JSSA_ERR_UNSUPPORTED;
+    return JSSA_OK;
+  }
   if (d->d_k != d->d_v) return JSSA_ERR_UNSUPPORTED;
   if (d->d_k != 64 && d->d_k != 128) return JSSA_ERR_UNSUPPORTED;
   if (G != 1 && G != 2 && G != 4 && G != 8) return JSSA_ERR_UNSUPPORTED;
@@ -77,6 +100,7 @@ bool workspace_layout(const jssa_desc& d, int op, Workspace* ws) {
     off = align_up(off + bytes, kAlignWs);
     return at;
   };
+  const bool mla = d.layout == JSSA_LAYOUT_MLA;
   ws->n_sel_tiles = (d.t_max + kSelTile - 1) / kSelTile;
   int pipe_chunk = 0;
   if (op == JSSA_OP_DECODE && pipeline_layout(d, &ws->pipe_ts, &ws->pipe_tiles, &pipe_chunk)) {
@@ -98,7 +122,8 @@ bool workspace_layout(const jssa_desc& d, int op, Workspace* ws) {
   if (op == JSSA_OP_ATTN || op == JSSA_OP_DECODE || op == JSSA_OP_DENSE) {
     const bool indexed = op != JSSA_OP_DENSE;
     const int64_t n_max = indexed ? int64_t(d.topk) + d.window : d.t_max;
-    attn_chunking(int(rows), n_max, indexed, &ws->chunk, &ws->n_chunks);
+    if (mla) mla_chunking(d.batch, d.n_q_heads / kMlaHeadGroup, n_max, indexed, &ws->chunk, &ws->n_chunks);
+    else attn_chunking(int(rows), n_max, indexed, &ws->chunk, &ws->n_chunks);
     const int part_chunks = ws->pipe_n_chunks > ws->n_chunks ? ws->pipe_n_chunks : ws->n_chunks;
     ws->part_acc = take(rows * part_chunks * size_t(G) * d.d_v * 4);
     ws->part_ml = take(rows * part_chunks * size_t(G) * 2 * 4);
@@ -107,6 +132,10 @@ bool workspace_layout(const jssa_desc& d, int op, Workspace* ws) {
     ws->scores = take(rows * size_t(d.t_max) * 4);
     ws->idx = take(rows * (size_t(d.topk) + d.window) * 4);
     ws->n_sel = take(rows * 4);
+  }
+  if (mla && (op == JSSA_OP_SCORE || op == JSSA_OP_DECODE)) {
+    const size_t mt = d.reduce == JSSA_REDUCE_MEAN ? 1 : size_t(d.n_q_heads) / 16;
+    ws->qfrag = take(size_t(d.batch) * mt * (d.rank / 32) * 2 * 64 * 16);
   }
   ws->total = off;
   return true;
@@ -146,12 +175,12 @@ const char* jssa_status_str(int32_t s) {
 }
 
 int32_t jssa_check_desc(const jssa_desc* desc, int32_t op) {
-  if (op < 0 || op > JSSA_OP_DENSE) return JSSA_ERR_INVALID_ARG;
+  if (op < 0 || op > JSSA_OP_SCORE) return JSSA_ERR_INVALID_ARG;
   return check(desc, op);
 }
 
 size_t jssa_workspace_bytes(const jssa_desc* desc, int32_t op) {
-  if (!desc || op < JSSA_OP_TOPK || op > JSSA_OP_DENSE) return 0;
+  if (!desc || op < JSSA_OP_TOPK || op > JSSA_OP_SCORE) return 0;
   Workspace w;
   if (!workspace_layout(*desc, op, &w)) return 0;
   return w.total;
@@ -180,11 +209,17 @@ int32_t jssa_append_kv(const jssa_desc* desc, const void* k_new, const void* v_n
 }
 
 int32_t jssa_score(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
-                   const int32_t* seq_lens, float* scores, void* stream) {
-  JSSA_TRY(check(desc, 0));
+                   const int32_t* seq_lens, float* scores, void* ws, size_t ws_bytes, void* stream) {
+  JSSA_TRY(check(desc, JSSA_OP_SCORE));
   if (!q || !P || !kp_cache || !seq_lens || !scores) return JSSA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(P) || !aligned16(kp_cache) || !aligned16(seq_lens) || !aligned16(scores))
     return JSSA_ERR_MISALIGNED;
+  if (desc->layout == JSSA_LAYOUT_MLA) {
+    Workspace lay;
+    JSSA_TRY(check_ws(*desc, JSSA_OP_SCORE, ws, ws_bytes, &lay));
+    return to_status(launch_mla_score(*desc, q, P, kp_cache, seq_lens, scores, false, static_cast<char*>(ws),
+                                      lay, as_stream(stream)));
+  }
   Workspace none;
   return to_status(launch_score(*desc, q, P, kp_cache, seq_lens, scores, nullptr, none, as_stream(stream)));
 }
@@ -211,12 +246,16 @@ int32_t jssa_indexed_attn(const jssa_desc* desc, const void* q, const void* k_ca
                           const void* v_cache, const int32_t* idx, const int32_t* n_sel,
                           void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   JSSA_TRY(check(desc, JSSA_OP_ATTN));
-  if (!q || !k_cache || !v_cache || !idx || !n_sel || !out) return JSSA_ERR_INVALID_ARG;
+  const bool mla = desc->layout == JSSA_LAYOUT_MLA;
+  if (!q || !k_cache || (!mla && !v_cache) || !idx || !n_sel || !out) return JSSA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(idx) ||
       !aligned16(n_sel) || !aligned16(out) || (lse && !aligned16(lse)))
     return JSSA_ERR_MISALIGNED;
   Workspace lay;
   JSSA_TRY(check_ws(*desc, JSSA_OP_ATTN, ws, ws_bytes, &lay));
+  if (mla)
+    return to_status(launch_mla_attend(*desc, q, k_cache, idx, n_sel, nullptr, out, lse, static_cast<char*>(ws),
+                                       lay, as_stream(stream)));
   return to_status(launch_resolve_attend(*desc, false, true, q, k_cache, v_cache, const_cast<int32_t*>(idx),
                                          const_cast<int32_t*>(n_sel), nullptr, out, lse,
                                          static_cast<char*>(ws), lay, as_stream(stream)));
@@ -227,7 +266,8 @@ static int32_t decode_impl(const jssa_desc* desc, const void* q, const float* P,
                            void* out, float* lse, int32_t* idx_out, int32_t* n_sel_out,
                            void* ws, size_t ws_bytes, void* const* ev, void* stream) {
   JSSA_TRY(check(desc, JSSA_OP_DECODE));
-  if (!q || !P || !kp_cache || !k_cache || !v_cache || !seq_lens || !out) return JSSA_ERR_INVALID_ARG;
+  const bool mla = desc->layout == JSSA_LAYOUT_MLA;
+  if (!q || !P || !kp_cache || !k_cache || (!mla && !v_cache) || !seq_lens || !out) return JSSA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(P) || !aligned16(kp_cache) || !aligned16(k_cache) ||
       !aligned16(v_cache) || !aligned16(seq_lens) || !aligned16(out) || (lse && !aligned16(lse)) ||
       (idx_out && !aligned16(idx_out)) || (n_sel_out && !aligned16(n_sel_out)))
@@ -247,6 +287,18 @@ static int32_t decode_impl(const jssa_desc* desc, const void* q, const float* P,
                                      base, lay, ev, s));
   auto mark = [&](int i) { return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
   hipError_t e = mark(0);
+  if (mla) {
+    if (e == hipSuccess) e = launch_mla_score(*desc, q, P, kp_cache, seq_lens, scores, true, base, lay, s);
+    if (e == hipSuccess) e = mark(1);
+    if (e == hipSuccess) e = launch_candidates(*desc, scores, seq_lens, base, lay, s);
+    if (e == hipSuccess) e = mark(2);
+    if (e == hipSuccess)
+      e = launch_resolve_attend(*desc, true, false, nullptr, nullptr, nullptr, idx, n_sel, seq_lens, nullptr,
+                                nullptr, base, lay, s);
+    if (e == hipSuccess) e = launch_mla_attend(*desc, q, k_cache, idx, n_sel, nullptr, out, lse, base, lay, s);
+    if (e == hipSuccess) e = mark(3);
+    return to_status(e);
+  }
   if (e == hipSuccess) e = launch_score(*desc, q, P, kp_cache, seq_lens, scores, base, lay, s);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = launch_candidates(*desc, scores, seq_lens, base, lay, s);
@@ -279,12 +331,16 @@ int32_t jssa_dense_decode(const jssa_desc* desc, const void* q, const void* k_ca
                           const void* v_cache, const int32_t* seq_lens, void* out, float* lse,
                           void* ws, size_t ws_bytes, void* stream) {
   JSSA_TRY(check(desc, JSSA_OP_DENSE));
-  if (!q || !k_cache || !v_cache || !seq_lens || !out) return JSSA_ERR_INVALID_ARG;
+  const bool mla = desc->layout == JSSA_LAYOUT_MLA;
+  if (!q || !k_cache || (!mla && !v_cache) || !seq_lens || !out) return JSSA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(seq_lens) ||
       !aligned16(out) || (lse && !aligned16(lse)))
     return JSSA_ERR_MISALIGNED;
   Workspace lay;
   JSSA_TRY(check_ws(*desc, JSSA_OP_DENSE, ws, ws_bytes, &lay));
+  if (mla)
+    return to_status(launch_mla_attend(*desc, q, k_cache, nullptr, nullptr, seq_lens, out, lse,
+                                       static_cast<char*>(ws), lay, as_stream(stream)));
   return to_status(launch_resolve_attend(*desc, false, true, q, k_cache, v_cache, nullptr, nullptr, seq_lens,
                                          out, lse, static_cast<char*>(ws), lay, as_stream(stream)));
 }

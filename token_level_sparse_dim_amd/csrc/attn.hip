@@ -145,6 +145,7 @@ hipError_t launch_resolve_attend(const jssa_desc& d, bool resolve, bool attend, 
   const int G = d.n_q_heads / d.n_kv_heads;
   dim3 grid(a.n_items);
   if (!attend && !resolve) return hipSuccess;
+  if (!attend) return launch_attn_t<1, 128, 1>(a, indexed, resolve, grid, s);  // emission only: no K/V access
   if (d.kv_dtype == JSSA_BF16) {
     if (d.d_k == 128) return dispatch_g<1, 128>(a, G, indexed, resolve, grid, s);
     if (d.d_k == 64) return dispatch_g<1, 64>(a, G, indexed, resolve, grid, s);

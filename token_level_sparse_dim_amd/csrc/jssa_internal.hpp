@@ -30,6 +30,11 @@ constexpr int kMaxSelTiles = 4096;   // t_max <= kMaxSelTiles * kSelTile
 constexpr int kAttnBlock = 64;       // tokens per attention inner block (per workgroup pass)
 constexpr int kRowStateWords = 16;   // u32 words of per-row selection state
 constexpr int kMaxPipeChunk = 1024;  // attention chunk limit of the fused decode
+// MLA layout: shared latent rows of kMlaDk elements, values = first kMlaDv
+constexpr int kMlaDk = 576;
+constexpr int kMlaDv = 512;
+constexpr int kMlaScoreTile = 2048;  // candidate tokens per MLA score workgroup
+constexpr int kMlaHeadGroup = 32;    // query heads per MLA attention workgroup
 
 // per-row state (u32 words).  The tickets and the ready flag are zero on
 // entry and are left zero by every call.
@@ -65,6 +70,7 @@ struct Workspace {
   size_t scores = 0;     // f32 [rows][t_max]           (decode only)
   size_t idx = 0;        // i32 [rows][k+W]             (decode only)
   size_t n_sel = 0;      // i32 [rows]                  (decode only)
+  size_t qfrag = 0;      // bf16 projected-query MFMA fragments (MLA score)
   size_t total = 0;
   int n_chunks = 0;      // attention chunks per row
   int chunk = 0;         // tokens per attention chunk
@@ -110,6 +116,18 @@ hipError_t launch_resolve_attend(const jssa_desc& d, bool resolve, bool attend, 
                                  char* ws_base, const Workspace& ws, hipStream_t s);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
+// MLA scoring on the matrix cores: query projection into ws.qfrag, then the
+// score scan; with `hist` also the first-digit histogram and threshold state.
+hipError_t launch_mla_score(const jssa_desc& d, const void* q, const float* P, const void* kp,
+                            const int32_t* seq_lens, float* scores, bool hist, char* ws_base,
+                            const Workspace& ws, hipStream_t s);
+
+// MLA attention over idx / n_sel (idx == nullptr: every t < seq_lens[b]) in
+// chunks of ws.chunk rows, then the log-sum-exp merge of the chunks.
+hipError_t launch_mla_attend(const jssa_desc& d, const void* q, const void* k_cache, const int32_t* idx,
+                             const int32_t* n_sel, const int32_t* seq_lens, void* out, float* lse,
+                             char* ws_base, const Workspace& ws, hipStream_t s);
 
 // Fused decode: whether a build exists for the descriptor's shape, its tile
 // size, tiles per row and attention chunk (tokens).
