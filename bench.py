@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="ctx128k",
-                    choices=["tiny", "llama8b_32k", "ctx128k", "hybrid_ragged"])
+                    choices=["tiny", "llama8b_32k", "ctx128k", "hybrid_ragged", "mla"])
     ap.add_argument("--topk", type=int, default=None, help="override the budget k")
     ap.add_argument("--reduce", default="max", choices=["max", "mean"])
     ap.add_argument("--sets", type=int, default=2, help="independent input sets rotated per step")
@@ -100,7 +100,8 @@ def main():
     reduce = J.REDUCE_MAX if args.reduce == "max" else J.REDUCE_MEAN
     desc = J.Desc(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, d_k=w.d_k, d_v=w.d_v,
                   rank=w.rank, t_max=w.t_max, topk=w.topk, window=w.window, kv_dtype=dt, kp_dtype=dt,
-                  out_dtype=J.F32, reduce=reduce, scale=w.scale)
+                  out_dtype=J.F32, reduce=reduce, layout=J.LAYOUT_MLA if w.mla else J.LAYOUT_GQA,
+                  scale=w.scale)
 
     def up(x):
         if x.dtype == np.uint16:
@@ -113,7 +114,8 @@ def main():
     for si in range(args.sets):
         t0 = time.time()
         inp = generate(w, seed=w.seed + 100 * si)
-        s = {k: up(inp[k]) for k in ("q", "P", "k_cache", "v_cache", "seq_lens")}
+        s = {k: up(inp[k]) for k in ("q", "P", "k_cache", "seq_lens")}
+        s["v_cache"] = None if w.mla else up(inp["v_cache"])  # MLA: the value is a prefix of K
         s["kp"] = torch.empty((w.batch, w.n_kv_heads, w.t_max, w.rank), dtype=tdt, device=dev)
         J.append_projection(desc, w.t_max, torch.zeros(w.batch, dtype=torch.int32, device=dev),
                             s["P"], s["k_cache"], s["kp"])
@@ -122,12 +124,14 @@ def main():
         kn = rng.standard_normal((w.batch, 1, w.n_kv_heads, w.d_k)).astype(np.float32)
         vn = rng.standard_normal((w.batch, 1, w.n_kv_heads, w.d_v)).astype(np.float32)
         s["k_new"] = up(kn).to(tdt)
-        s["v_new"] = up(vn).to(tdt)
+        s["v_new"] = None if w.mla else up(vn).to(tdt)
         s["pos"] = (s["seq_lens"] - 1).contiguous()
         sets.append(s)
         if si == 0:
-            host0 = {"q": inp["q"][:1], "P": inp["P"], "k_cache": inp["k_cache"][:1].copy(),
-                     "v_cache": inp["v_cache"][:1].copy(), "seq_lens": inp["seq_lens"].copy()}
+            k0 = inp["k_cache"][:1].copy()
+            host0 = {"q": inp["q"][:1], "P": inp["P"], "k_cache": k0,
+                     "v_cache": k0[..., :w.d_v] if w.mla else inp["v_cache"][:1].copy(),
+                     "seq_lens": inp["seq_lens"].copy()}
         del inp
         log(f"input set {si}: generated and resident in {time.time() - t0:.1f}s")
     torch.cuda.synchronize()
@@ -172,9 +176,9 @@ def main():
     torch.cuda.synchronize()
     stage_ms = np.array([[row[j].elapsed_time(row[j + 1]) for j in range(3)] for row in evs])
     stage_us = stage_ms.mean(axis=0) * 1e3
-    # fused build: scan (+ candidate emission), resolve, attention launches;
-    # staged build: score scan, candidate pass, resolve + attention launch
-    names = ["scan", "select", "attention"]
+    # GQA fused build: scan (+ candidate emission), resolve, attention launches;
+    # MLA: score scan, candidate pass, resolve + attention + chunk merge
+    names = ["score_scan", "candidates", "resolve+attention"] if w.mla else ["scan", "select", "attention"]
     log("stages (us): " + ", ".join(f"{n}={v:.2f}" for n, v in zip(names, stage_us)))
 
     # ---- bytes -------------------------------------------------------------------------------
@@ -183,20 +187,23 @@ def main():
     n_sel = np.minimum(w.window, L) + np.minimum(w.topk, n_cand)
     eb = 2 if dt == J.BF16 else 4
     kp_bytes = int(n_cand.sum()) * w.n_kv_heads * w.rank * eb
-    sel_bytes = int(n_sel.sum()) * w.n_kv_heads * (w.d_k + w.d_v) * eb
+    row_bytes = w.d_k * eb if w.mla else (w.d_k + w.d_v) * eb  # MLA: a latent row is read once
+    sel_bytes = int(n_sel.sum()) * w.n_kv_heads * row_bytes
     eff_bytes = kp_bytes + sel_bytes
     eff_gbps = eff_bytes / (ms_step * 1e-3) / 1e9
     score_us = float(stage_us[0])
     achieved = kp_bytes / (score_us * 1e-6) / 1e9
 
     traffic = None
-    tpath = os.path.join(ROOT, "profiles", f"scan_kernel_{args.workload}_traffic.json")
+    kname = "mla_score_kernel" if w.mla else "scan_kernel"
+    tpath = os.path.join(ROOT, "profiles", f"{kname}_{args.workload}_traffic.json")
     if os.path.exists(tpath):
         try:
             with open(tpath) as f:
                 rec = json.load(f)
             from token_level_sparse_dim_amd.build import source_digest
-            if rec.get("source_digest") == source_digest("pipeline.hip") and rec.get("topk") == w.topk:
+            src = "mla.hip" if w.mla else "pipeline.hip"
+            if rec.get("source_digest") == source_digest(src) and rec.get("topk") == w.topk:
                 traffic = rec.get("hbm_bytes_per_launch")
         except Exception as exc:  # a stale or unreadable record reads as unmeasured
             log(f"traffic record ignored: {exc}")
@@ -207,13 +214,15 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if dt == J.BF16 else "f32", "data": "synthetic (seeded, resident in HBM)",
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.n_q_heads,
-                   "kv_heads": w.n_kv_heads, "head_dim": w.d_k, "rank": w.rank, "context": w.t_max,
+                   "kv_heads": w.n_kv_heads, "head_dim": w.d_k, "value_dim": w.d_v,
+                   "layout": "mla" if w.mla else "gqa", "rank": w.rank, "context": w.t_max,
                    "topk": w.topk, "window": w.window, "reduce": args.reduce,
                    "step": "append new token + fused sparse decode", "input_sets": args.sets},
         "eff_bytes_per_step": eff_bytes, "eff_GBps": round(eff_gbps, 1),
         "pct_peak": round(100.0 * eff_gbps / HBM_PEAK_GBPS, 2),
         "stages_us": {n: round(float(v), 2) for n, v in zip(names, stage_us)},
-        "roofline": {"kernel": "scan_kernel (projected-key scan + candidate emission)", "bound": "hbm",
+        "roofline": {"kernel": "mla_score_kernel (MFMA projected-key scan + histogram)" if w.mla
+                     else "scan_kernel (projected-key scan + candidate emission)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "bytes_per_launch": kp_bytes, "avg_launch_us": round(score_us, 2)},
@@ -234,7 +243,7 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         dense_ms = e0.elapsed_time(e1) / nd
-        dense_bytes = int(L.sum()) * w.n_kv_heads * (w.d_k + w.d_v) * eb
+        dense_bytes = int(L.sum()) * w.n_kv_heads * row_bytes
         result["dense"] = {"ms_per_step": round(dense_ms, 5),
                            "GBps": round(dense_bytes / (dense_ms * 1e-3) / 1e9, 1),
                            "speedup_sparse_vs_dense": round(dense_ms / ms_step, 3)}

@@ -217,8 +217,10 @@ int32_t jssa_score(const jssa_desc* desc, const void* q, const float* P, const v
   if (desc->layout == JSSA_LAYOUT_MLA) {
     Workspace lay;
     JSSA_TRY(check_ws(*desc, JSSA_OP_SCORE, ws, ws_bytes, &lay));
-    return to_status(launch_mla_score(*desc, q, P, kp_cache, seq_lens, scores, false, static_cast<char*>(ws),
-                                      lay, as_stream(stream)));
+    char* base = static_cast<char*>(ws);
+    hipError_t e = launch_mla_qproj(*desc, q, P, base, lay, as_stream(stream));
+    if (e == hipSuccess) e = launch_mla_scan(*desc, kp_cache, seq_lens, scores, false, base, lay, as_stream(stream));
+    return to_status(e);
   }
   Workspace none;
   return to_status(launch_score(*desc, q, P, kp_cache, seq_lens, scores, nullptr, none, as_stream(stream)));
@@ -286,9 +288,10 @@ static int32_t decode_impl(const jssa_desc* desc, const void* q, const float* P,
     return to_status(launch_pipeline(*desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, idx, n_sel,
                                      base, lay, ev, s));
   auto mark = [&](int i) { return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
-  hipError_t e = mark(0);
   if (mla) {
-    if (e == hipSuccess) e = launch_mla_score(*desc, q, P, kp_cache, seq_lens, scores, true, base, lay, s);
+    hipError_t e = launch_mla_qproj(*desc, q, P, base, lay, s);
+    if (e == hipSuccess) e = mark(0);
+    if (e == hipSuccess) e = launch_mla_scan(*desc, kp_cache, seq_lens, scores, true, base, lay, s);
     if (e == hipSuccess) e = mark(1);
     if (e == hipSuccess) e = launch_candidates(*desc, scores, seq_lens, base, lay, s);
     if (e == hipSuccess) e = mark(2);
@@ -299,6 +302,7 @@ static int32_t decode_impl(const jssa_desc* desc, const void* q, const float* P,
     if (e == hipSuccess) e = mark(3);
     return to_status(e);
   }
+  hipError_t e = mark(0);
   if (e == hipSuccess) e = launch_score(*desc, q, P, kp_cache, seq_lens, scores, base, lay, s);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = launch_candidates(*desc, scores, seq_lens, base, lay, s);

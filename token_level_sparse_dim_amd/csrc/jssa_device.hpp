@@ -44,6 +44,21 @@ __device__ __forceinline__ uint4 load16_nt(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// ---- matrix cores ------------------------------------------------------------------
+// v_mfma_f32_16x16x32_bf16 (wave64): lane l supplies row m = l % 16 of A and
+// column n = l % 16 of B, each with the eight contraction indices
+// 8 (l / 16) .. 8 (l / 16) + 7 (element j of the 16-byte operand = index
+// 8 (l / 16) + j); it receives column n = l % 16, rows 4 (l / 16) .. +3 of
+// the 16 x 16 fp32 result.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ u32x4_t as_u32x4(const uint4& v) { return u32x4_t{v.x, v.y, v.z, v.w}; }
+
 // Scalar element load with a run-time dtype (prologues only).
 __device__ __forceinline__ float load_elem(const void* base, size_t i, int dt) {
   if (dt == 0) return reinterpret_cast<const float*>(base)[i];
@@ -56,6 +71,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x0040u);
   u += 0x7fffu + ((u >> 16) & 1u);
   return uint16_t(u >> 16);
+}
+
+// x as a sum of N bfloat16 terms, each the nearest bf16 to what the earlier
+// terms leave (every remainder is exact in fp32).  N = 2 keeps about 16
+// significant bits of x, N = 3 all 24.
+template <int N>
+__device__ __forceinline__ void split_bf16_terms(float x, uint16_t (&t)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    t[i] = f32_to_bf16_rne(x);
+    x -= __uint_as_float(uint32_t(t[i]) << 16);
+  }
 }
 
 // ---- cross-lane reductions --------------------------------------------------------

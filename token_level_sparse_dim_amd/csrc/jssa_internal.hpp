@@ -117,11 +117,13 @@ hipError_t launch_resolve_attend(const jssa_desc& d, bool resolve, bool attend, 
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
-// MLA scoring on the matrix cores: query projection into ws.qfrag, then the
-// score scan; with `hist` also the first-digit histogram and threshold state.
-hipError_t launch_mla_score(const jssa_desc& d, const void* q, const float* P, const void* kp,
-                            const int32_t* seq_lens, float* scores, bool hist, char* ws_base,
-                            const Workspace& ws, hipStream_t s);
+// MLA scoring on the matrix cores: the query projection into ws.qfrag, then
+// the score scan that reads it; with `hist` the scan also builds the
+// first-digit histogram and threshold state.
+hipError_t launch_mla_qproj(const jssa_desc& d, const void* q, const float* P, char* ws_base, const Workspace& ws,
+                            hipStream_t s);
+hipError_t launch_mla_scan(const jssa_desc& d, const void* kp, const int32_t* seq_lens, float* scores, bool hist,
+                           char* ws_base, const Workspace& ws, hipStream_t s);
 
 // MLA attention over idx / n_sel (idx == nullptr: every t < seq_lens[b]) in
 // chunks of ws.chunk rows, then the log-sum-exp merge of the chunks.

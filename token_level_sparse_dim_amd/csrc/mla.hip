@@ -16,23 +16,12 @@
 //    head, and O += P V_sel, with P split into bf16 hi + lo terms in the same
 //    way (V is exact in bf16).
 //
-// Operand layout of v_mfma_f32_16x16x32_bf16 (wave64): lane l supplies row
-// m = l % 16 of A and column n = l % 16 of B, each with the eight contraction
-// indices 8 (l / 16) .. 8 (l / 16) + 7; it receives column n = l % 16, rows
-// 4 (l / 16) .. 4 (l / 16) + 3 of the 16 x 16 result.
+// (Operand layout of v_mfma_f32_16x16x32_bf16: see mfma16 in jssa_device.hpp.)
 #include "jssa_device.hpp"
 #include "jssa_internal.hpp"
 #include "select_common.hpp"
 
 namespace jssa {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
 
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ __forceinline__ u32x4_t ld16_nt(const void* p) {
@@ -43,8 +32,10 @@ __device__ __forceinline__ float mla_exp2(float x) { return __builtin_amdgcn_exp
 
 // fp32 -> (hi, lo) bf16 pair with hi = rne(x), lo = rne(x - hi); x - hi is exact.
 __device__ __forceinline__ void split_bf16(float x, uint16_t* hi, uint16_t* lo) {
-  *hi = f32_to_bf16_rne(x);
-  *lo = f32_to_bf16_rne(x - bf16_to_f32(*hi));
+  uint16_t t[2];
+  split_bf16_terms<2>(x, t);
+  *hi = t[0];
+  *lo = t[1];
 }
 
 // =====================================================================================
@@ -543,41 +534,50 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(MlaAttnArgs a) {
 }
 
 // ---- launchers -----------------------------------------------------------------------------
-hipError_t launch_mla_score(const jssa_desc& d, const void* q, const float* P, const void* kp,
-                            const int32_t* seq_lens, float* scores, bool hist, char* ws_base,
-                            const Workspace& ws, hipStream_t s) {
-  const bool mean = d.reduce == JSSA_REDUCE_MEAN;
+static MlaQArgs qproj_args(const jssa_desc& d, const void* q, const float* P, char* ws_base, const Workspace& ws) {
   MlaQArgs qa;
   qa.q = reinterpret_cast<const uint16_t*>(q);
   qa.P = P;
   qa.qf = reinterpret_cast<uint16_t*>(ws_base + ws.qfrag);
   qa.Hq = d.n_q_heads;
-  qa.MT = mean ? 1 : d.n_q_heads / 16;
+  qa.MT = d.reduce == JSSA_REDUCE_MEAN ? 1 : d.n_q_heads / 16;
+  return qa;
+}
+
+hipError_t launch_mla_qproj(const jssa_desc& d, const void* q, const float* P, char* ws_base, const Workspace& ws,
+                            hipStream_t s) {
+  const MlaQArgs qa = qproj_args(d, q, P, ws_base, ws);
+  const bool mean = d.reduce == JSSA_REDUCE_MEAN;
+  if (d.rank == 64) {
+    if (mean) hipLaunchKernelGGL(mla_qproj_mean_kernel<64>, dim3(1, d.batch), dim3(256), 0, s, qa);
+    else hipLaunchKernelGGL(mla_qproj_kernel<64>, dim3(d.n_q_heads / 4, d.batch), dim3(256), 0, s, qa);
+  } else {
+    if (mean) hipLaunchKernelGGL(mla_qproj_mean_kernel<32>, dim3(1, d.batch), dim3(256), 0, s, qa);
+    else hipLaunchKernelGGL(mla_qproj_kernel<32>, dim3(d.n_q_heads / 8, d.batch), dim3(256), 0, s, qa);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_scan(const jssa_desc& d, const void* kp, const int32_t* seq_lens, float* scores, bool hist,
+                           char* ws_base, const Workspace& ws, hipStream_t s) {
+  const bool mean = d.reduce == JSSA_REDUCE_MEAN;
   MlaScoreArgs sa;
-  sa.qf = qa.qf; sa.kp = kp; sa.seq_lens = seq_lens; sa.scores = scores;
+  sa.qf = reinterpret_cast<const uint16_t*>(ws_base + ws.qfrag);
+  sa.kp = kp; sa.seq_lens = seq_lens; sa.scores = scores;
   sa.hist1 = hist ? reinterpret_cast<uint32_t*>(ws_base + ws.hist1) : nullptr;
   sa.row_state = hist ? reinterpret_cast<uint32_t*>(ws_base + ws.row_state) : nullptr;
-  sa.t_max = d.t_max; sa.topk = d.topk; sa.window = d.window; sa.MT = qa.MT;
-  const dim3 sgrid((d.t_max + kMlaScoreTile - 1) / kMlaScoreTile, d.batch);
-  const int mtw = d.n_q_heads / 64;
+  sa.t_max = d.t_max; sa.topk = d.topk; sa.window = d.window;
+  sa.MT = mean ? 1 : d.n_q_heads / 16;
+  const dim3 grid((d.t_max + kMlaScoreTile - 1) / kMlaScoreTile, d.batch);
+  const bool two = d.n_q_heads / 64 == 2;
   if (d.rank == 64) {
-    if (mean) {
-      hipLaunchKernelGGL(mla_qproj_mean_kernel<64>, dim3(1, d.batch), dim3(256), 0, s, qa);
-      hipLaunchKernelGGL((mla_score_kernel<64, 1, true>), sgrid, dim3(256), 0, s, sa);
-    } else {
-      hipLaunchKernelGGL(mla_qproj_kernel<64>, dim3(d.n_q_heads / 4, d.batch), dim3(256), 0, s, qa);
-      if (mtw == 2) hipLaunchKernelGGL((mla_score_kernel<64, 2, false>), sgrid, dim3(256), 0, s, sa);
-      else hipLaunchKernelGGL((mla_score_kernel<64, 1, false>), sgrid, dim3(256), 0, s, sa);
-    }
+    if (mean) hipLaunchKernelGGL((mla_score_kernel<64, 1, true>), grid, dim3(256), 0, s, sa);
+    else if (two) hipLaunchKernelGGL((mla_score_kernel<64, 2, false>), grid, dim3(256), 0, s, sa);
+    else hipLaunchKernelGGL((mla_score_kernel<64, 1, false>), grid, dim3(256), 0, s, sa);
   } else {
-    if (mean) {
-      hipLaunchKernelGGL(mla_qproj_mean_kernel<32>, dim3(1, d.batch), dim3(256), 0, s, qa);
-      hipLaunchKernelGGL((mla_score_kernel<32, 1, true>), sgrid, dim3(256), 0, s, sa);
-    } else {
-      hipLaunchKernelGGL(mla_qproj_kernel<32>, dim3(d.n_q_heads / 8, d.batch), dim3(256), 0, s, qa);
-      if (mtw == 2) hipLaunchKernelGGL((mla_score_kernel<32, 2, false>), sgrid, dim3(256), 0, s, sa);
-      else hipLaunchKernelGGL((mla_score_kernel<32, 1, false>), sgrid, dim3(256), 0, s, sa);
-    }
+    if (mean) hipLaunchKernelGGL((mla_score_kernel<32, 1, true>), grid, dim3(256), 0, s, sa);
+    else if (two) hipLaunchKernelGGL((mla_score_kernel<32, 2, false>), grid, dim3(256), 0, s, sa);
+    else hipLaunchKernelGGL((mla_score_kernel<32, 1, false>), grid, dim3(256), 0, s, sa);
   }
   return hipGetLastError();
 }

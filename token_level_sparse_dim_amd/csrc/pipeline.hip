@@ -2,7 +2,7 @@
 // E.1: subspace score scan, per-KV-head top-k selection, gather-free indexed
 // attention).
 //
-// Scan launch, items taken in ticket order:
+// Scan launch, items in order (workgroup i takes items i, i + grid, ...):
 //   SAMPLE(row)     a candidate threshold L for the row from a strided sample
 //                   of its scores: a key far enough below the sample's estimate
 //                   of the k-th key that, with overwhelming probability, at
@@ -22,8 +22,8 @@
 // Attention launch, one workgroup per chunk of a row's index list; the row's
 //   last chunk merges the chunks.
 // Data passes between launches through plain stores and loads; the only wait
-// inside a launch is a score run's on its row's sample (an earlier ticket),
-// bounded in time.
+// inside a launch is a score run's on its row's sample (an item of a lower
+// workgroup index), bounded in time.
 #include <math.h>
 
 #include <type_traits>
@@ -45,8 +45,8 @@ constexpr int kPipeAttnNL = 8;         // K and V row loads per lane per attenti
 // per-row state word of the scan (zero on entry and exit): u64 at words 12-13,
 // (1 << 32) | L once the row's threshold is known
 constexpr int PW_L = 12;
-// queue words (PQ_ERR and PQ_FALLBACK are sticky diagnostics, the rest zero on entry and exit)
-enum PipeQueue : int { PQ_SCAN = 0, PQ_SCAN_EXIT = 1, PQ_ERR = 2, PQ_FALLBACK = 3 };
+// queue words: sticky diagnostics (a missing threshold; exact re-selections)
+enum PipeQueue : int { PQ_ERR = 2, PQ_FALLBACK = 3 };
 
 struct PipeArgs {
   AttnArgs at;  // q, k, v, idx and n_sel (outputs), seq_lens, out, lse, partials, row_state, queue
@@ -154,6 +154,9 @@ constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
 // with the d-sum split over 256 / (G*R) threads, four running sums per thread
 // (d, d+1, d+2, d+3) carried across chunks, added as (s0 + s1) + (s2 + s3), and
 // the parts added in order: the arithmetic of the stand-alone score kernel.
+// `issued()` runs right after the loads of the first chunk are issued: loads
+// the caller issues there complete after the projection's own (memory
+// operations complete in order), so the projection never waits for them.
 template <int D, int R, int G>
 struct QpSmem {
   static constexpr int PCH = D * R <= 4096 ? D * R : 4096;  // floats of P per chunk
@@ -163,8 +166,8 @@ struct QpSmem {
   float qp[G * R];
 };
 
-template <int D, int R, int G>
-__device__ void project_query_staged(const PipeArgs& a, int b, int h, QpSmem<D, R, G>& sm) {
+template <int D, int R, int G, typename F>
+__device__ __forceinline__ void project_query_staged(const PipeArgs& a, int b, int h, QpSmem<D, R, G>& sm, F issued) {
   constexpr int PCH = QpSmem<D, R, G>::PCH;
   constexpr int DCH = PCH / R;  // rows of d per chunk
   constexpr int NCH = D / DCH;
@@ -189,6 +192,7 @@ __device__ void project_query_staged(const PipeArgs& a, int b, int h, QpSmem<D, 
 #pragma unroll
     for (int k = 0; k < NP; ++k)
       pv[k] = load16(reinterpret_cast<const uint4*>(Ph + size_t(c) * PCH) + k * 256 + threadIdx.x);
+    if (c == 0) issued();
     if (c > 0) __syncthreads();  // the previous chunk is no longer read
 #pragma unroll
     for (int k = 0; k < NP; ++k) reinterpret_cast<uint4*>(sm.P)[k * 256 + threadIdx.x] = pv[k];
@@ -288,8 +292,6 @@ struct Pipe {
       const int m = int(ceil(E + 4.0 * sqrt(E) + 8.0));
       if (m < n_samp) {
         // the sampled projected keys are requested before the query projection
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-        const int p = lane % S::LPT, tw = lane / S::LPT;
         const char* kr = kp_row(a, row);
         constexpr int HALF = kPipeNit / 2;  // steps per batch of loads
         auto load_half = [&](int it0, uint4 (&v)[HALF][S::U]) {
@@ -297,27 +299,23 @@ struct Pipe {
           for (int it = 0; it < HALF; ++it)
 #pragma unroll
             for (int u = 0; u < S::U; ++u) {
-              const int i = (it0 + it) * S::PER_ITER + (wave * S::U + u) * S::TPW + tw;
-              v[it][u] = load16_nt(kr + (size_t(i) * stride * R + p * S::EPL) * S::EB);
+              const int i = (it0 + it) * S::PER_ITER + slot_token<KPT, R>(u);
+              v[it][u] = load16_nt(kr + size_t(i) * stride * R * S::EB + slot_byte<KPT, R>(u));
             }
         };
         uint4 v[HALF][S::U];
-        load_half(0, v);
-        project_query_staged<D, R, G>(a, b, h, sm.qp);
-        float qreg[GE][S::EPL];
-        load_qreg<KPT, R, GE>([&](int i) { return sm.qp.qp[i]; }, G, qreg);
+        project_query_staged<D, R, G>(a, b, h, sm.qp, [&] { load_half(0, v); });
+        QFrag<KPT, R, GE> qf;
+        load_qfrag<KPT, R, GE>([&](int i) { return sm.qp.qp[i]; }, G, qf);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           uint4 w[HALF][S::U];
           if (half == 0) load_half(HALF, w);
 #pragma unroll
-          for (int it = 0; it < HALF; ++it)
-#pragma unroll
-            for (int u = 0; u < S::U; ++u) {
-              const uint32_t key = score_key(score_of<KPT, R, GE>(v[it][u], qreg));
-              const int i = (half * HALF + it) * S::PER_ITER + (wave * S::U + u) * S::TPW + tw;
-              if (p == 0) sm.keys[i] = key;
-            }
+          for (int it = 0; it < HALF; ++it) {
+            const int i0 = (half * HALF + it) * S::PER_ITER;
+            score_loads<KPT, R, GE>(v[it], qf, G, [&](int toff, float sc) { sm.keys[i0 + toff] = score_key(sc); });
+          }
           if (half == 0) {
 #pragma unroll
             for (int it = 0; it < HALF; ++it)
@@ -340,68 +338,55 @@ struct Pipe {
   // order).  b0 holds the first step's loads, already issued.  Loads carry no
   // per-lane branch (tokens past the end re-read the last one), so the next
   // step's loads stay in flight while the current step is scored.
-  static __device__ void scan_keys(const char* kr, int t_begin, int t_end, const float (&qreg)[GE][S::EPL],
+  static __device__ void scan_keys(const char* kr, int t_begin, int t_end, const QFrag<KPT, R, GE>& qf,
                                    uint4 (&b0)[S::U], uint32_t* keys) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int p = lane % S::LPT, tw = lane / S::LPT;
     const int n_steps = (t_end - t_begin + S::PER_ITER - 1) / S::PER_ITER;
     for (int st = 0; st < n_steps; ++st) {
       uint4 b1[S::U];
       load_step(kr, t_begin + (st + 1) * S::PER_ITER, t_end, b1);
-#pragma unroll
-      for (int u = 0; u < S::U; ++u) {
-        const uint32_t key = score_key(score_of<KPT, R, GE>(b0[u], qreg));
-        if (p == 0) keys[st * S::PER_ITER + (wave * S::U + u) * S::TPW + tw] = key;
-      }
+      uint32_t* kst = keys + st * S::PER_ITER;
+      score_loads<KPT, R, GE>(b0, qf, G, [&](int toff, float sc) { kst[toff] = score_key(sc); });
 #pragma unroll
       for (int u = 0; u < S::U; ++u) b0[u] = b1[u];
     }
   }
   static __device__ void load_step(const char* kr, int base, int t_end, uint4 (&v)[S::U]) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int p = lane % S::LPT, tw = lane / S::LPT;
 #pragma unroll
     for (int u = 0; u < S::U; ++u) {
-      const int t = min(base + (wave * S::U + u) * S::TPW + tw, t_end - 1);
-      v[u] = load16_nt(kr + (size_t(t) * R + p * S::EPL) * S::EB);
+      const int t = min(base + slot_token<KPT, R>(u), t_end - 1);
+      v[u] = load16_nt(kr + size_t(t) * R * S::EB + slot_byte<KPT, R>(u));
     }
   }
 
   // Writes the tokens of [t_begin, t_end) (whole tiles from t_begin) whose key
   // in keys[] is >= thr to their tiles' candidate slots, in token order, and
   // the tile counts (plain stores: read after the launch boundary, or by the
-  // workgroup that wrote them).  Each wave compacts whole tiles: lane l takes PL
-  // consecutive tokens and a wave scan gives the positions.
+  // workgroup that wrote them).  Each wave compacts whole tiles in rounds of 64
+  // tokens (lane l takes token 64 k + l of round k, so the key reads are
+  // conflict-free); a ballot per round gives the positions.
   static __device__ void emit_keys(const PipeArgs& a, int row, int t_begin, int t_end, uint32_t thr,
                                    const uint32_t* keys) {
     constexpr int PL = TS / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n_sub = (t_end - t_begin + TS - 1) / TS;
     const int tile0 = t_begin / TS;
+    const unsigned long long below = (1ull << lane) - 1ull;
     for (int s = wave; s < n_sub; s += 4) {
       const int t0 = t_begin + s * TS;
       const int n_tok = min(TS, t_end - t0);
-      const uint32_t* kk = keys + s * TS + lane * PL;
-      uint32_t cnt = 0;
-#pragma unroll
-      for (int k = 0; k < PL; ++k) cnt += (lane * PL + k < n_tok && kk[k] >= thr) ? 1u : 0u;
-      uint32_t incl = cnt;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
-      uint32_t pos = incl - cnt;
-      const uint32_t tot = __shfl(incl, 63);
+      const uint32_t* kk = keys + s * TS;
       uint64_t* slot = a.cand + size_t(row) * a.at.t_max + size_t(tile0 + s) * TS;
+      uint32_t pos = 0;
 #pragma unroll
       for (int k = 0; k < PL; ++k) {
-        if (lane * PL + k < n_tok && kk[k] >= thr) {
-          slot[pos] = (uint64_t(uint32_t(t0 + lane * PL + k)) << 32) | kk[k];
-          ++pos;
-        }
+        const int i = k * 64 + lane;
+        const uint32_t key = kk[i];
+        const bool take = i < n_tok && key >= thr;
+        const unsigned long long m = __ballot(take);
+        if (take) slot[pos + uint32_t(__popcll(m & below))] = (uint64_t(uint32_t(t0 + i)) << 32) | key;
+        pos += uint32_t(__popcll(m));
       }
-      if (lane == 0) a.tile_cnt[size_t(row) * a.n_tiles + tile0 + s] = tot;
+      if (lane == 0) a.tile_cnt[size_t(row) * a.n_tiles + tile0 + s] = pos;
     }
   }
 
@@ -416,14 +401,15 @@ struct Pipe {
     ScoreSmem& sm = *reinterpret_cast<ScoreSmem*>(smem);
     const char* kr = kp_row(a, row);
     uint4 b0[S::U];
-    load_step(kr, t_begin, t_end, b0);  // in flight during the query projection
     uint64_t lw = 0;
-    if (threadIdx.x == 0) lw = consume(l_word(a, row));
-    project_query_staged<D, R, G>(a, b, h, sm.qp);
-    float qreg[GE][S::EPL];
-    load_qreg<KPT, R, GE>([&](int i) { return sm.qp.qp[i]; }, G, qreg);
+    project_query_staged<D, R, G>(a, b, h, sm.qp, [&] {
+      load_step(kr, t_begin, t_end, b0);  // in flight during the query projection
+      if (threadIdx.x == 0) lw = consume(l_word(a, row));
+    });
+    QFrag<KPT, R, GE> qf;
+    load_qfrag<KPT, R, GE>([&](int i) { return sm.qp.qp[i]; }, G, qf);
     __syncthreads();  // the projection's shared memory becomes the key buffer
-    scan_keys(kr, t_begin, t_end, qreg, b0, sm.keys);
+    scan_keys(kr, t_begin, t_end, qf, b0, sm.keys);
     // the row's threshold (its sample item was handed out before this item)
     if (threadIdx.x == 0) {
       while ((lw >> 32) == 0 && !past(deadline)) {
@@ -468,9 +454,9 @@ struct Pipe {
     const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
     ScoreSmem& ss = *reinterpret_cast<ScoreSmem*>(smem);
     ResolveSmem& rs = *reinterpret_cast<ResolveSmem*>(smem);
-    project_query_staged<D, R, G>(a, b, h, ss.qp);
-    float qreg[GE][S::EPL];
-    load_qreg<KPT, R, GE>([&](int i) { return ss.qp.qp[i]; }, G, qreg);
+    project_query_staged<D, R, G>(a, b, h, ss.qp, [] {});
+    QFrag<KPT, R, GE> qf;
+    load_qfrag<KPT, R, GE>([&](int i) { return ss.qp.qp[i]; }, G, qf);
     for (int i = threadIdx.x; i < 2048; i += 256) rs.hist[i] = 0u;
     __syncthreads();
     const char* kr = kp_row(a, row);
@@ -485,7 +471,7 @@ struct Pipe {
         const int t_end = min(t_begin + kPipeMaxItem, md.n_cand);
         uint4 b0[S::U];
         load_step(kr, t_begin, t_end, b0);
-        scan_keys(kr, t_begin, t_end, qreg, b0, ss.keys);
+        scan_keys(kr, t_begin, t_end, qf, b0, ss.keys);
         __syncthreads();
         if (pass == 0) {
           for (int i = threadIdx.x; i < t_end - t_begin; i += 256) atomicAdd(&rs.hist[ss.keys[i] >> 21], 1u);
@@ -664,47 +650,30 @@ struct Pipe {
   }
 };
 
-// Resets the launch's ticket words once every workgroup has left.
-__device__ __forceinline__ void leave(uint32_t* queue, int ticket_word, int exit_word) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t done = __hip_atomic_fetch_add(queue + exit_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (done == gridDim.x - 1) {
-      __hip_atomic_store(queue + ticket_word, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(queue + exit_word, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-}
-
-// A ticket for the whole workgroup (callers are between barriers, so s_t is
-// not read while it is rewritten).
-__device__ __forceinline__ int take_ticket(uint32_t* word) {
-  __shared__ int s_t;
-  if (threadIdx.x == 0) s_t = int(__hip_atomic_fetch_add(word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  __syncthreads();
-  const int t = s_t;
-  __syncthreads();
-  return t;
-}
-
-// Scan launch: tickets in order are the samples, one long score run per
-// resident workgroup (long enough that its row's threshold is known when it
-// finishes), then single-tile runs that balance the end.  A workgroup keeps
-// taking tickets until none are left.
+// Scan launch: items in order are the samples (one per row), one long score
+// run per resident workgroup (long enough that its row's threshold is known
+// when it finishes), then single-tile runs that balance the end.  Workgroup i
+// takes items i, i + grid, i + 2 grid, ...: the samples go to the lowest
+// workgroup indices, which the dispatcher starts first, and no shared counter
+// is contended.  A score run waits for its row's threshold only after its
+// scan, under a deadline (a missing threshold is flagged, never waited for
+// forever).
 template <int KPT, int R, int GE, int D, int G, int KVT>
 __global__ __launch_bounds__(256, 3) void scan_kernel(PipeArgs a) {
   using Pp = Pipe<KPT, R, GE, D, G, KVT>;
   __shared__ __align__(16) char smem[Pp::kSmemScan];
   const uint64_t deadline = wall_clock64() + a.spin_ticks;
   const int n_big_all = a.n_rows * a.n_big;
-  int t = take_ticket(a.at.queue + PQ_SCAN);
-  if (t < a.n_rows) {  // samples come first, outside the loop of score runs
+  int t = blockIdx.x;
+  // at most one sample per workgroup (the grid covers every row), outside the
+  // loop of score runs: in a loop, each item type's invariants would stay live
+  // across the other's code
+  if (t < a.n_rows) {
     Pp::sample(a, t, *reinterpret_cast<typename Pp::SampleSmem*>(smem));
     __syncthreads();
-    t = take_ticket(a.at.queue + PQ_SCAN);
+    t += gridDim.x;
   }
-  while (t < a.n_main) {
+  for (; t < a.n_main; t += gridDim.x) {
     int r, t_begin, len;
     if (t < a.n_rows + n_big_all) {
       const int i = t - a.n_rows;
@@ -719,9 +688,7 @@ __global__ __launch_bounds__(256, 3) void scan_kernel(PipeArgs a) {
     }
     Pp::score_item(a, r, t_begin, len, smem, deadline);
     __syncthreads();
-    t = take_ticket(a.at.queue + PQ_SCAN);
   }
-  leave(a.at.queue, PQ_SCAN, PQ_SCAN_EXIT);
 }
 
 // Resolve launch: one workgroup per (sequence, KV head) row.
@@ -822,7 +789,8 @@ static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
   a.n_big = (n_tiles_max + big_tiles - 1) / big_tiles;
   a.n_small = 0;
   a.n_main = a.n_rows + a.n_rows * a.n_big;
-  const int grid = resident < a.n_main ? resident : a.n_main;
+  int grid = resident < a.n_main ? resident : a.n_main;
+  if (grid < a.n_rows) grid = a.n_rows;  // one sample per workgroup at most
   auto mark = [&](int i) { return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
   hipError_t e = mark(0);
   if (e != hipSuccess) return e;

@@ -23,15 +23,14 @@ struct ScoreArgs {
 };
 
 // One workgroup (4 waves) per kScoreTile candidate tokens of one (b, h) row.
-// Each token's projected key (R elements) is spread over LPT = R*bytes/16
-// lanes; each lane holds the matching slice of the G projected queries in
-// registers, and the per-head dot products are completed with DPP sums.
+// The scores of a step come from score_loads (score_core.hpp): on the matrix
+// cores for bf16 keys of rank 32 or 64, with DPP dot products otherwise.
 // Loads are double-buffered: the next step's 16-byte vectors are in flight
 // while the current ones are scored.  GE = G for the group max, 1 for the mean.
 template <int KPT, int R, int GE>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   using S = ScanShape<KPT, R>;
-  constexpr int EB = S::EB, EPL = S::EPL, LPT = S::LPT, TPW = S::TPW, U = S::U, PER_ITER = S::PER_ITER;
+  constexpr int EB = S::EB, U = S::U, PER_ITER = S::PER_ITER;
 
   __shared__ uint32_t s_hist[kDigit1Bins];
   __shared__ float s_q[8 * 128];
@@ -48,19 +47,17 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   if (t0 >= n_cand) return;
   const bool do_hist = a.hist1 != nullptr && a.topk > 0 && a.topk < n_cand;
   const int t_end = min(t0 + kScoreTile, n_cand);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int p = lane % LPT, tw = lane / LPT;
   const char* kp_row = reinterpret_cast<const char*>(a.kp) + size_t(row) * a.t_max * R * EB;
   float* srow = a.scores + size_t(row) * a.t_max;
 
   // Loads are issued without per-lane branches (tokens past the end re-read the
   // last candidate and are discarded), so the compiler can keep the next
   // step's loads in flight while the current step is scored.
-  auto load_step = [&](int base, uint4* v) {
+  auto load_step = [&](int base, uint4 (&v)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int tok = min(base + (wave * U + u) * TPW + tw, t_end - 1);
-      v[u] = load16_nt(kp_row + (size_t(tok) * R + p * EPL) * EB);
+      const int tok = min(base + slot_token<KPT, R>(u), t_end - 1);
+      v[u] = load16_nt(kp_row + size_t(tok) * R * EB + slot_byte<KPT, R>(u));
     }
   };
   uint4 cur[U];
@@ -71,21 +68,19 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   const int G = a.G;
   project_group_query<R>(a.q, a.q_dtype, a.P, a.Hq, a.d_k, G, b, h, s_q, s_part, s_qp);
 
-  float qreg[GE][EPL];
-  load_qreg<KPT, R, GE>([&](int i) { return s_qp[i]; }, G, qreg);
+  QFrag<KPT, R, GE> qf;
+  load_qfrag<KPT, R, GE>([&](int i) { return s_qp[i]; }, G, qf);
 
   for (int base = t0; base < t_end; base += PER_ITER) {
     uint4 nxt[U];
     load_step(base + PER_ITER, nxt);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int tok = base + (wave * U + u) * TPW + tw;
-      const float best = score_of<KPT, R, GE>(cur[u], qreg);
-      if (p == 0 && tok < t_end) {
+    score_loads<KPT, R, GE>(cur, qf, G, [&](int toff, float best) {
+      const int tok = base + toff;
+      if (tok < t_end) {
         srow[tok] = best;
         if (do_hist) atomicAdd(&s_hist[score_key(best) >> (32 - kDigit1Bits)], 1u);
       }
-    }
+    });
 #pragma unroll
     for (int u = 0; u < U; ++u) cur[u] = nxt[u];
   }

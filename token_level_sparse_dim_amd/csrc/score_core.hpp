@@ -3,11 +3,20 @@
 // token is scored with the projected queries of its KV head's group against
 // the projected-key cache).
 //
-// Layout of the scan: a token's projected key (R elements) is spread over
-// LPT = R*bytes/16 lanes (one 16-byte load each); each lane keeps the matching
-// slice of the group's projected queries in registers and the per-head dot
-// products are completed with DPP sums.  A wave covers TPW = 64/LPT tokens
-// per load, a workgroup step covers PER_ITER = 4 waves x U loads.
+// Layout of the scan: every lane issues U 16-byte loads of projected keys per
+// workgroup step; a wave load covers TPW = 64/LPT whole tokens (LPT =
+// R*bytes/16 lanes per token) and a step PER_ITER = 4 waves x U x TPW tokens.
+//
+// Two ways to form the scores, chosen by shape:
+//  * matrix cores (bf16 keys, R = 32 or 64): 16 tokens' keys are the B operand
+//    of v_mfma_f32_16x16x32_bf16 (lane l loads token l % 16, elements
+//    32 s + 8 (l / 16) .. +7 of K-step s); the A operand holds the group's
+//    projected queries (row g = query head g; row 0 = the group mean for the
+//    mean reduction), each fp32 coordinate split into three bf16 terms whose
+//    sum is the coordinate, so the products see the full fp32 query;
+//  * vector ALU (other shapes): each lane keeps its slice of the projected
+//    queries in registers and the per-head dot products are completed with
+//    DPP sums.
 #pragma once
 
 #include "jssa_device.hpp"
@@ -23,7 +32,39 @@ struct ScanShape {
   static constexpr int TPW = 64 / LPT;
   static constexpr int U = JSSA_SCORE_UNROLL;
   static constexpr int PER_ITER = 4 * TPW * U;
+  static constexpr bool MF = KPT == 1 && (R == 32 || R == 64);  // matrix-core scoring
+  static constexpr int KS = R / 32;                             // K-steps per token (MF)
   static_assert(LPT >= 1 && LPT <= 16 && (LPT & (LPT - 1)) == 0, "lanes per token");
+  static_assert(!MF || U % KS == 0, "a wave's loads cover whole 16-token groups");
+};
+
+constexpr int kQTerms = 3;  // bf16 terms per fp32 query coordinate (matrix-core scoring)
+
+// Token (offset within a workgroup step) and byte (within the token's row) of
+// this lane's u-th load.
+template <int KPT, int R>
+__device__ __forceinline__ int slot_token(int u) {
+  using S = ScanShape<KPT, R>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if constexpr (S::MF) return (wave * (S::U / S::KS) + u / S::KS) * 16 + (lane & 15);
+  else return (wave * S::U + u) * S::TPW + lane / S::LPT;
+}
+template <int KPT, int R>
+__device__ __forceinline__ int slot_byte(int u) {
+  using S = ScanShape<KPT, R>;
+  const int lane = threadIdx.x & 63;
+  if constexpr (S::MF) return (32 * (u % S::KS) + 8 * (lane >> 4)) * 2;
+  else return (lane % S::LPT) * 16;
+}
+
+// The group's projected queries as the scan uses them.
+template <int KPT, int R, int GE, bool MF = ScanShape<KPT, R>::MF>
+struct QFrag {
+  float q[GE][ScanShape<KPT, R>::EPL];  // this lane's slice (vector ALU)
+};
+template <int KPT, int R, int GE>
+struct QFrag<KPT, R, GE, true> {
+  u32x4_t a[R / 32][kQTerms];  // A-operand fragments, one per K-step and term
 };
 
 // Projected queries of KV head h's group, fp32, into s_qp[g * R + i]:
@@ -105,63 +146,80 @@ __device__ __forceinline__ float score_of(const uint4& raw, const float (&qreg)[
   return best;
 }
 
-// Scores NIT workgroup steps of logical tokens [i0, i0 + NIT*PER_ITER): logical
-// token i is cached token tok(i) (clamped to a valid token by the caller) and
-// is real when i < i_end.  key[it][u] receives the order-preserving key of
-// logical token i0 + it*PER_ITER + (wave*U + u)*TPW + tw in every lane of its
-// group.  Loads are double-buffered across steps and issued without per-lane
-// branches.
-template <int KPT, int R, int GE, int NIT, typename Tok>
-__device__ __forceinline__ void score_steps(const char* kp_row, Tok tok, int i0, int i_end,
-                                            const float (&qreg)[GE][ScanShape<KPT, R>::EPL],
-                                            uint32_t (&key)[NIT][ScanShape<KPT, R>::U]) {
+// Projected queries (fp32, element g * R + i read through `ld`) into the
+// scan's form.  Matrix cores: row m of the A operand is query head m (rows
+// >= G are zero) or, for the mean (GE = 1), row 0 is the group mean formed as
+// in load_qreg; each coordinate becomes kQTerms bf16 terms.
+template <int KPT, int R, int GE, typename Ld>
+__device__ __forceinline__ void load_qfrag(Ld ld, int G, QFrag<KPT, R, GE>& qf) {
   using S = ScanShape<KPT, R>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int p = lane % S::LPT, tw = lane / S::LPT;
-  auto load_step = [&](int it, uint4* v) {
+  if constexpr (S::MF) {
+    const int lane = threadIdx.x & 63, m = lane & 15, kg = lane >> 4;
+    const float invG = 1.0f / float(G);
 #pragma unroll
-    for (int u = 0; u < S::U; ++u) {
-      const int i = min(i0 + it * S::PER_ITER + (wave * S::U + u) * S::TPW + tw, i_end - 1);
-      v[u] = load16_nt(kp_row + (size_t(tok(i)) * R + p * S::EPL) * S::EB);
+    for (int s = 0; s < S::KS; ++s) {
+      uint16_t t[8][kQTerms];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = 32 * s + 8 * kg + j;
+        float x = 0.f;
+        if constexpr (GE == 1) {
+          if (m == 0) {
+            float sm = 0.f;
+            for (int g = 0; g < G; ++g) sm += ld(g * R + i);
+            x = sm * invG;
+          }
+        } else {
+          if (m < G) x = ld(m * R + i);
+        }
+        split_bf16_terms<kQTerms>(x, t[j]);
+      }
+#pragma unroll
+      for (int k = 0; k < kQTerms; ++k)
+        qf.a[s][k] = u32x4_t{uint32_t(t[0][k]) | (uint32_t(t[1][k]) << 16), uint32_t(t[2][k]) | (uint32_t(t[3][k]) << 16),
+                             uint32_t(t[4][k]) | (uint32_t(t[5][k]) << 16), uint32_t(t[6][k]) | (uint32_t(t[7][k]) << 16)};
     }
-  };
-  uint4 cur[S::U];
-  load_step(0, cur);
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    uint4 nxt[S::U];
-    if (it + 1 < NIT) load_step(it + 1, nxt);
-#pragma unroll
-    for (int u = 0; u < S::U; ++u) key[it][u] = score_key(score_of<KPT, R, GE>(cur[u], qreg));
-    if (it + 1 < NIT) {
-#pragma unroll
-      for (int u = 0; u < S::U; ++u) cur[u] = nxt[u];
-    }
+  } else {
+    load_qreg<KPT, R, GE>(ld, G, qf.q);
   }
 }
 
-// Same keys as score_steps, but every load of the NIT steps is issued before
-// the first one is used: for scattered, latency-bound reads (a strided sample
-// of a row) where one round trip per NIT steps beats one per step.
-template <int KPT, int R, int GE, int NIT, typename Tok>
-__device__ __forceinline__ void score_block(const char* kp_row, Tok tok, int i0, int i_end,
-                                            const float (&qreg)[GE][ScanShape<KPT, R>::EPL],
-                                            uint32_t (&key)[NIT][ScanShape<KPT, R>::U]) {
+// Scores of the tokens of one workgroup step from this lane's U loads
+// (v[u] holds the 16 bytes at slot_token(u) / slot_byte(u)).  Calls
+// emit(token offset within the step, score) once per token, in one lane.
+// MAX over the G heads (GE = G) or the group-mean query (GE = 1).
+template <int KPT, int R, int GE, typename F>
+__device__ __forceinline__ void score_loads(const uint4 (&v)[ScanShape<KPT, R>::U], const QFrag<KPT, R, GE>& qf,
+                                            int G, F emit) {
   using S = ScanShape<KPT, R>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int p = lane % S::LPT, tw = lane / S::LPT;
-  uint4 v[NIT][S::U];
+  const int lane = threadIdx.x & 63;
+  if constexpr (S::MF) {
+    const int kg = lane >> 4;
 #pragma unroll
-  for (int it = 0; it < NIT; ++it)
+    for (int q = 0; q < S::U / S::KS; ++q) {
+      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < S::KS; ++s)
+#pragma unroll
+        for (int k = 0; k < kQTerms; ++k) c = mfma16(qf.a[s][k], as_u32x4(v[q * S::KS + s]), c);
+      // result lane: token lane % 16, rows (query heads) 4 kg .. 4 kg + 3
+      float best = c[0];
+      if constexpr (GE > 1) {
+#pragma unroll
+        for (int i = 1; i < 4; ++i)
+          if (4 * kg + i < G) best = fmaxf(best, c[i]);
+        if (G > 4) best = fmaxf(best, __shfl_xor(best, 16));
+      }
+      if (lane < 16) emit(slot_token<KPT, R>(q * S::KS), best);
+    }
+  } else {
+    const int p = lane % S::LPT;
 #pragma unroll
     for (int u = 0; u < S::U; ++u) {
-      const int i = min(i0 + it * S::PER_ITER + (wave * S::U + u) * S::TPW + tw, i_end - 1);
-      v[it][u] = load16_nt(kp_row + (size_t(tok(i)) * R + p * S::EPL) * S::EB);
+      const float best = score_of<KPT, R, GE>(v[u], qf.q);
+      if (p == 0) emit(slot_token<KPT, R>(u), best);
     }
-#pragma unroll
-  for (int it = 0; it < NIT; ++it)
-#pragma unroll
-    for (int u = 0; u < S::U; ++u) key[it][u] = score_key(score_of<KPT, R, GE>(v[it][u], qreg));
+  }
 }
 
 }  // namespace jssa
