@@ -188,12 +188,12 @@ int32_t jssa_indexed_attn(const jssa_desc* desc, const void* q, const void* k_ca
  * jssa_indexed_attn (JSSA summary Figure 1 and section E.1), bit-identical in
  * idx / n_sel, with intermediates in the workspace.  For the shapes with a
  * fused build (bf16: d 128 rank 32 G 4, d 128 rank 64 G 1, d 64 rank 16 G 4;
- * f32: d 64 rank 16 G 4, d 128 rank 32 G 2; GQA layout) it runs in two
+ * f32: d 64 rank 16 G 4, d 128 rank 32 G 2; GQA layout) it runs in four
  * launches: a scan that scores every candidate and keeps, per tile, the
  * tokens at or above a threshold taken from a strided sample of the row's
- * scores, and a resolve + attention launch that selects exactly among them
- * (re-selecting a row exactly in the rare case fewer than k tokens passed the
- * threshold).  Other shapes run the stand-alone kernels in sequence (MLA:
+ * scores; a resolve that selects exactly among them (re-selecting a row
+ * exactly in the rare case fewer than k tokens passed the threshold); the
+ * attention over chunks of the selection; the merge of the chunks.  Other shapes run the stand-alone kernels in sequence (MLA:
  * query projection, score scan with the first-digit histogram, candidate
  * pass, resolve, attention, chunk merge).
  * idx_out / n_sel_out may be NULL; when given they receive the selection.

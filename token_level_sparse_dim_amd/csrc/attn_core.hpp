@@ -12,6 +12,7 @@
 namespace jssa {
 
 constexpr int kMaxIdxChunk = 1024;
+constexpr int kCombineBatch = 64;  // chunks whose merge weights are staged together
 constexpr uint32_t kSpinLimit = 1u << 26;  // bounded wait (seconds): a broken invariant cannot hang
 
 struct AttnArgs {
@@ -37,6 +38,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 template <int G, int D, bool INDEXED, bool RESOLVE>
 struct AttnSmem {
+  static_assert(4 * G * D >= kCombineBatch * G + 2 * G, "combine scratch fits in acc");
   int idx[INDEXED ? kMaxIdxChunk : 1];
   float m[4][G], l[4][G];
   float acc[4][G][D];
@@ -59,10 +61,17 @@ __device__ __forceinline__ void finish_item(const AttnArgs& a) {
 
 // The last chunk of a row to finish: log-sum-exp merge of the row's non-empty
 // chunk partials (in chunk order) into out (and lse), or out = 0, lse = -inf
-// when the row attends over nothing.
+// when the row attends over nothing.  Two rounds of loads: one wave per head
+// reads every chunk's (max, sum) at once and forms the head's global max M,
+// the chunk weights exp2(m_c - M) and the total L; then every thread reads the
+// partial outputs of its elements for all chunks of a batch at once.  sw:
+// shared scratch of kCombineBatch * G + 2 * G floats, free at this point.
+
 template <int D, int G>
-__device__ __forceinline__ void combine_chunks(const AttnArgs& a, int row, int b, int h, int n) {
-  const uint32_t n_live = uint32_t((n + a.chunk - 1) / a.chunk);
+__device__ __forceinline__ void combine_chunks(const AttnArgs& a, int row, int b, int h, int n, float* sw) {
+  const int n_live = (n + a.chunk - 1) / a.chunk;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int PER = (G * D + 255) / 256;  // output elements per thread
   if (n_live == 0) {  // nothing attended: out = 0, lse = -inf
     for (int j = threadIdx.x; j < G * D; j += 256) {
       const size_t o = (size_t(b) * a.Hq + size_t(h) * G) * D + j;
@@ -74,40 +83,65 @@ __device__ __forceinline__ void combine_chunks(const AttnArgs& a, int row, int b
   }
   const float* racc = a.part_acc + size_t(row) * a.n_chunks * G * D;
   const float* rml = a.part_ml + size_t(row) * a.n_chunks * G * 2;
-  constexpr int CB = 8;  // chunks whose loads are issued together
-  for (int j = threadIdx.x; j < G * D; j += 256) {
-    const int g = j / D, dd = j - g * D;
+  float* sM = sw;
+  float* sL = sw + G;
+  float* sW = sw + 2 * G;  // [kCombineBatch][G]
+  // global max of each head
+  for (int g = wave; g < G; g += 4) {
     float M = -INFINITY;
-    for (uint32_t cb = 0; cb < n_live; cb += CB) {
-      float mc[CB];
+    for (int c = lane; c < n_live; c += 64) M = fmaxf(M, consume(&rml[(c * G + g) * 2]));
 #pragma unroll
-      for (int i = 0; i < CB; ++i)
-        mc[i] = (cb + i < n_live) ? consume(&rml[((cb + i) * G + g) * 2]) : -INFINITY;
-#pragma unroll
-      for (int i = 0; i < CB; ++i) M = fmaxf(M, mc[i]);
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if (lane == 0) {
+      sM[g] = M;
+      sL[g] = 0.f;
     }
-    float L = 0.f, A = 0.f;
-    for (uint32_t cb = 0; cb < n_live; cb += CB) {
-      float mc[CB], lc[CB], ac[CB];
+  }
+  __syncthreads();
+  float acc[PER];
 #pragma unroll
-      for (int i = 0; i < CB; ++i) {
-        const bool ok = cb + i < n_live;
-        mc[i] = ok ? consume(&rml[((cb + i) * G + g) * 2]) : -INFINITY;
-        lc[i] = ok ? consume(&rml[((cb + i) * G + g) * 2 + 1]) : 0.f;
-        ac[i] = ok ? consume(&racc[(size_t(cb + i) * G + g) * D + dd]) : 0.f;
+  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  for (int cb = 0; cb < n_live; cb += kCombineBatch) {
+    const int nb = min(kCombineBatch, n_live - cb);
+    for (int g = wave; g < G; g += 4) {
+      float lw = 0.f;
+      if (lane < nb) {
+        const int c = cb + lane;
+        const float m = consume(&rml[(c * G + g) * 2]), l = consume(&rml[(c * G + g) * 2 + 1]);
+        const float w = (m == -INFINITY) ? 0.f : fast_exp2(m - sM[g]);
+        sW[lane * G + g] = w;
+        lw = w * l;
       }
 #pragma unroll
-      for (int i = 0; i < CB; ++i) {
-        const float w = (mc[i] == -INFINITY) ? 0.f : fast_exp2(mc[i] - M);
-        L = fmaf(lc[i], w, L);
-        A = fmaf(ac[i], w, A);
+      for (int off = 32; off >= 1; off >>= 1) lw += __shfl_xor(lw, off);
+      if (lane == 0) sL[g] += lw;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int j = k * 256 + int(threadIdx.x);
+      if (j < G * D) {
+        const int g = j / D;
+        float v[kCombineBatch];
+#pragma unroll
+        for (int c = 0; c < kCombineBatch; ++c) v[c] = c < nb ? consume(&racc[size_t(cb + c) * G * D + j]) : 0.f;
+#pragma unroll
+        for (int c = 0; c < kCombineBatch; ++c)
+          if (c < nb) acc[k] = fmaf(sW[c * G + g], v[c], acc[k]);
       }
     }
-    const float o = A / L;
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int j = k * 256 + int(threadIdx.x);
+    if (j >= G * D) continue;
+    const int g = j / D, dd = j - g * D;
+    const float o = acc[k] / sL[g];
     const size_t oi = (size_t(b) * a.Hq + size_t(h) * G + g) * D + dd;
     if (a.out_dtype == JSSA_BF16) reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_rne(o);
     else reinterpret_cast<float*>(a.out)[oi] = o;
-    if (dd == 0 && a.lse) a.lse[size_t(b) * a.Hq + h * G + g] = (M + __log2f(L)) * kLn2;
+    if (dd == 0 && a.lse) a.lse[size_t(b) * a.Hq + h * G + g] = (sM[g] + __log2f(sL[g])) * kLn2;
   }
 }
 
@@ -270,7 +304,7 @@ __device__ bool attend_chunk(const AttnArgs& a, Smem& S, int row, int b, int h, 
   uint32_t* rstate = a.row_state + size_t(row) * kRowStateWords;
   if (!last_arrival(&rstate[RS_TICKET_ATTN], uint32_t(a.n_chunks))) return false;
   if (RESET_READY && threadIdx.x == 0) publish(&rstate[RS_READY], 0u);  // every chunk has passed its wait
-  combine_chunks<D, G>(a, row, b, h, n);
+  combine_chunks<D, G>(a, row, b, h, n, &S.acc[0][0][0]);
   return true;
 }
 
@@ -295,6 +329,7 @@ struct Attn2Shape {
 
 template <int KVT, int D, int G, int NL>
 struct Attn2Smem {
+  static_assert(4 * G * D >= kCombineBatch * G + 2 * G, "combine scratch fits in acc");
   static constexpr int CH = Attn2Shape<KVT, D, G, NL>::CH;
   int idx[CH];
   float w[CH][G];      // logits, then weights
@@ -302,7 +337,10 @@ struct Attn2Smem {
   float acc[4][G][D];  // per-wave partial outputs
 };
 
-template <int KVT, int D, int G, int NL, typename Smem>
+// MERGE: the row's last chunk merges the partials here (device-scope hand-off
+// through a ticket); otherwise the partials are written with plain stores for
+// a later launch (merge_rows) to merge.
+template <int KVT, int D, int G, int NL, bool MERGE = true, typename Smem>
 __device__ __forceinline__ bool attend_chunk_2pass(const AttnArgs& a, Smem& S, int row, int b, int h, int chunk_id, int n) {
   using SH = Attn2Shape<KVT, D, G, NL>;
   constexpr int EB = SH::EB, EPL = SH::EPL, LR = SH::LR, RPW = SH::RPW, CH = SH::CH;
@@ -407,17 +445,69 @@ __device__ __forceinline__ bool attend_chunk_2pass(const AttnArgs& a, Smem& S, i
     __syncthreads();
     for (int j = threadIdx.x; j < G * D; j += 256) {
       const int g = j / D, dd = j - g * D;
-      publish(&pacc[j], (S.acc[0][g][dd] + S.acc[1][g][dd]) + (S.acc[2][g][dd] + S.acc[3][g][dd]));
+      const float v = (S.acc[0][g][dd] + S.acc[1][g][dd]) + (S.acc[2][g][dd] + S.acc[3][g][dd]);
+      if (MERGE) publish(&pacc[j], v);
+      else pacc[j] = v;
       if (dd == 0) {
-        publish(&pml[2 * g], S.ml[g][0]);
-        publish(&pml[2 * g + 1], S.ml[g][1]);
+        if (MERGE) {
+          publish(&pml[2 * g], S.ml[g][0]);
+          publish(&pml[2 * g + 1], S.ml[g][1]);
+        } else {
+          pml[2 * g] = S.ml[g][0];
+          pml[2 * g + 1] = S.ml[g][1];
+        }
       }
     }
   }
+  if (!MERGE) return false;
   uint32_t* rstate = a.row_state + size_t(row) * kRowStateWords;
   if (!last_arrival(&rstate[RS_TICKET_ATTN], uint32_t(a.n_chunks))) return false;
-  combine_chunks<D, G>(a, row, b, h, n);
+  combine_chunks<D, G>(a, row, b, h, n, &S.acc[0][0][0]);
   return true;
+}
+
+// Merge of one (row, head) in a launch after the chunks' (plain-stored)
+// partials: thread dd owns output element dd; every chunk's max, sum and
+// partial are read in batches of kMergeBatch loads issued together, folded
+// into a running log-sum-exp in chunk order.  blockDim.x == D.
+constexpr int kMergeBatch = 16;
+
+template <int D, int G>
+__device__ __forceinline__ void merge_rows(const AttnArgs& a, int row, int g, int n) {
+  const int b = row / a.Hkv, h = row - b * a.Hkv;
+  const int dd = threadIdx.x;
+  const int n_live = (n + a.chunk - 1) / a.chunk;
+  const size_t oi = (size_t(b) * a.Hq + size_t(h) * G + g) * D + dd;
+  float M = -INFINITY, L = 0.f, A = 0.f;
+  const float* racc = a.part_acc + size_t(row) * a.n_chunks * G * D + size_t(g) * D + dd;
+  const float* rml = a.part_ml + size_t(row) * a.n_chunks * G * 2 + size_t(g) * 2;
+  for (int c0 = 0; c0 < n_live; c0 += kMergeBatch) {
+    float m[kMergeBatch], l[kMergeBatch], v[kMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const bool ok = c0 + i < n_live;
+      m[i] = ok ? rml[size_t(c0 + i) * G * 2] : -INFINITY;
+      l[i] = ok ? rml[size_t(c0 + i) * G * 2 + 1] : 0.f;
+      v[i] = ok ? racc[size_t(c0 + i) * G * D] : 0.f;
+    }
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) Mb = fmaxf(Mb, m[i]);
+    const float sc = (M == -INFINITY) ? 0.f : fast_exp2(M - Mb);
+    L *= sc;
+    A *= sc;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const float w = (m[i] == -INFINITY) ? 0.f : fast_exp2(m[i] - Mb);
+      L = fmaf(w, l[i], L);
+      A = fmaf(w, v[i], A);
+    }
+    M = Mb;
+  }
+  const float o = n_live > 0 ? A / L : 0.f;
+  if (a.out_dtype == JSSA_BF16) reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_rne(o);
+  else reinterpret_cast<float*>(a.out)[oi] = o;
+  if (dd == 0 && a.lse) a.lse[size_t(b) * a.Hq + h * G + g] = n_live > 0 ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
 
 }  // namespace jssa

@@ -135,10 +135,10 @@ hipError_t launch_mla_attend(const jssa_desc& d, const void* q, const void* k_ca
 // size, tiles per row and attention chunk (tokens).
 bool pipeline_layout(const jssa_desc& d, int* ts, int* n_tiles, int* chunk);
 
-// The whole decode step in two launches (scan with sampled-threshold
-// candidate emission; resolve + attention); requires ws.pipe.  With `ev`
-// (four events): recorded before the scan, after it (twice: the candidate pass
-// is part of the scan) and after the resolve + attention launch.
+// The whole decode step in four launches (scan with sampled-threshold
+// candidate emission; resolve; attention chunks; chunk merge); requires
+// ws.pipe.  With `ev` (four events): recorded before the scan, after it, after
+// the resolve and after the merge.
 hipError_t launch_pipeline(const jssa_desc& d, const void* q, const float* P, const void* kp,
                            const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
                            float* lse, int32_t* idx, int32_t* n_sel, char* ws_base, const Workspace& ws,

@@ -1,4 +1,4 @@
-// Sparse decode step in three launches (JSSA summary Figure 1 and section
+// Sparse decode step in four launches (JSSA summary Figure 1 and section
 // E.1: subspace score scan, per-KV-head top-k selection, gather-free indexed
 // attention).
 //
@@ -19,8 +19,9 @@
 //   fewer than k tokens reached L (the sample misled), the row is redone
 //   exactly: its scores are recomputed, first for the exact top radix digit of
 //   the k-th key, then to rewrite the candidate slots from that digit.
-// Attention launch, one workgroup per chunk of a row's index list; the row's
-//   last chunk merges the chunks.
+// Attention launch, one workgroup per chunk of a row's index list, then a
+//   merge launch (one workgroup per row and query head) that combines the
+//   chunks' partials.
 // Data passes between launches through plain stores and loads; the only wait
 // inside a launch is a score run's on its row's sample (an item of a lower
 // workgroup index), bounded in time.
@@ -646,7 +647,12 @@ struct Pipe {
     int n = a.at.n_sel[row];
     n = n < 0 ? 0 : (n > a.at.idx_stride ? a.at.idx_stride : n);
     __syncthreads();
-    attend_chunk_2pass<KVT, D, G, kPipeAttnNL>(a.at, S_, row, b, h, chunk, n);
+    attend_chunk_2pass<KVT, D, G, kPipeAttnNL, false>(a.at, S_, row, b, h, chunk, n);
+  }
+  static __device__ __forceinline__ void merge(const PipeArgs& a, int row, int g) {
+    int n = a.at.n_sel[row];
+    n = n < 0 ? 0 : (n > a.at.idx_stride ? a.at.idx_stride : n);
+    merge_rows<D, G>(a.at, row, g, n);
   }
 };
 
@@ -701,13 +707,20 @@ __global__ __launch_bounds__(256, 1) void resolve_kernel(PipeArgs a) {
   if (md.select()) Pp::resolve_select(a, row, md, smem);
 }
 
-// Attention launch: one workgroup per chunk of a row's index list; the row's
-// last chunk to finish merges the chunks.
+// Attention launch: one workgroup per chunk of a row's index list, each
+// leaving its partial for the merge launch.
 template <int KPT, int R, int GE, int D, int G, int KVT>
 __global__ __launch_bounds__(256, 3) void attend_kernel(PipeArgs a) {
   using Pp = Pipe<KPT, R, GE, D, G, KVT>;
   __shared__ __align__(16) char smem[sizeof(typename Pp::ASmem)];
   Pp::attend(a, blockIdx.x / a.at.n_chunks, blockIdx.x % a.at.n_chunks, *reinterpret_cast<typename Pp::ASmem*>(smem));
+}
+
+// Merge launch: one workgroup of D threads per (row, query head).
+template <int KPT, int R, int GE, int D, int G, int KVT>
+__global__ __launch_bounds__(D) void merge_kernel(PipeArgs a) {
+  using Pp = Pipe<KPT, R, GE, D, G, KVT>;
+  Pp::merge(a, blockIdx.x / G, blockIdx.x % G);
 }
 
 // ---- host side ------------------------------------------------------------------------------
@@ -799,6 +812,8 @@ static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
   hipLaunchKernelGGL((resolve_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_rows), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess) return e;
   hipLaunchKernelGGL((attend_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_attn), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((merge_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_rows * G), dim3(D), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return mark(3);
 }

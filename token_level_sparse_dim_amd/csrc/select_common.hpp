@@ -14,11 +14,13 @@ namespace jssa {
 template <int BPT>
 __device__ void find_bin_from_top(const uint32_t* hist, uint32_t need, uint32_t* scan_tmp,
                                   uint32_t* out) {
+  static_assert(BPT >= 1 && (BPT & (BPT - 1)) == 0, "bins per thread: a power of two");
   const int seg = 255 - int(threadIdx.x);  // thread 0 owns the highest segment
   if (threadIdx.x == 0) { out[0] = 0u; out[1] = 0u; }  // defined result even if need > total
   uint32_t sum = 0;
+  // bins summed from a per-thread rotation, so neighbouring lanes read different banks
 #pragma unroll
-  for (int j = 0; j < BPT; ++j) sum += hist[seg * BPT + j];
+  for (int j = 0; j < BPT; ++j) sum += hist[seg * BPT + ((j + int(threadIdx.x)) & (BPT - 1))];
   uint32_t total;
   const uint32_t above = block_exclusive_scan(sum, scan_tmp, &total);
   if (above < need && need <= above + sum) {
@@ -41,11 +43,12 @@ __device__ void find_bin_from_top(const uint32_t* hist, uint32_t need, uint32_t*
 template <int BPT>
 __device__ void find_bin_from_bottom(const uint32_t* hist, uint32_t need, uint32_t* scan_tmp,
                                      uint32_t* out) {
+  static_assert(BPT >= 1 && (BPT & (BPT - 1)) == 0, "bins per thread: a power of two");
   const int seg = int(threadIdx.x);
   if (threadIdx.x == 0) { out[0] = 0u; out[1] = 0u; }
   uint32_t sum = 0;
 #pragma unroll
-  for (int j = 0; j < BPT; ++j) sum += hist[seg * BPT + j];
+  for (int j = 0; j < BPT; ++j) sum += hist[seg * BPT + ((j + int(threadIdx.x)) & (BPT - 1))];
   uint32_t total;
   const uint32_t below = block_exclusive_scan(sum, scan_tmp, &total);
   if (below < need && need <= below + sum) {
