@@ -73,15 +73,24 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return uint16_t(u >> 16);
 }
 
-// x as a sum of N bfloat16 terms, each the nearest bf16 to what the earlier
-// terms leave (every remainder is exact in fp32).  N = 2 keeps about 16
-// significant bits of x, N = 3 all 24.
+// Two floats -> packed bfloat16 (x0 in bits 0..15), round to nearest even, in
+// one instruction (v_cvt_pk_bf16_f32).  For operands of the matrix cores.
+__device__ __forceinline__ uint32_t pack_bf16x2(float x0, float x1) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t h = {(__bf16)x0, (__bf16)x1};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// (x0, x1) as sums of N packed bfloat16 terms, each the nearest bf16 to what
+// the earlier terms leave (every remainder is exact in fp32).  N = 2 keeps
+// about 16 significant bits, N = 3 all 24.
 template <int N>
-__device__ __forceinline__ void split_bf16_terms(float x, uint16_t (&t)[N]) {
+__device__ __forceinline__ void split_bf16x2_terms(float x0, float x1, uint32_t (&w)[N]) {
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    t[i] = f32_to_bf16_rne(x);
-    x -= __uint_as_float(uint32_t(t[i]) << 16);
+    w[i] = pack_bf16x2(x0, x1);
+    x0 -= __uint_as_float(w[i] << 16);
+    x1 -= __uint_as_float(w[i] & 0xffff0000u);
   }
 }
 

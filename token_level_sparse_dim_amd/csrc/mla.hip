@@ -32,10 +32,10 @@ __device__ __forceinline__ float mla_exp2(float x) { return __builtin_amdgcn_exp
 
 // fp32 -> (hi, lo) bf16 pair with hi = rne(x), lo = rne(x - hi); x - hi is exact.
 __device__ __forceinline__ void split_bf16(float x, uint16_t* hi, uint16_t* lo) {
-  uint16_t t[2];
-  split_bf16_terms<2>(x, t);
-  *hi = t[0];
-  *lo = t[1];
+  uint32_t w[2];
+  split_bf16x2_terms<2>(x, 0.f, w);
+  *hi = uint16_t(w[0]);
+  *lo = uint16_t(w[1]);
 }
 
 // =====================================================================================
@@ -59,27 +59,43 @@ __device__ __forceinline__ size_t qfrag_at(int b, int MT, int mt, int m, int r, 
   return ((((size_t(b) * MT + mt) * KS + s) * 2 + split) * 64 + lane) * 8 + (kk & 7);
 }
 
-// MAX: one workgroup per 256 / R query heads; thread (head, r) accumulates
-// q[head] . P[:, r] over the 576 coordinates (q staged in shared memory).
+// MAX: one wave per (16 query heads, 16 projection coordinates), on the
+// matrix cores: A = the bf16 query rows (exact), B = P[:, 16 coordinates]
+// split into bf16 hi + lo terms, so qp = q P_hi + q P_lo with fp32
+// accumulation (|P - P_hi - P_lo| <= 2^-17 |P|).  All loads are issued
+// before the first product.
 template <int R>
-__global__ __launch_bounds__(256) void mla_qproj_kernel(MlaQArgs a) {
-  constexpr int HPB = 256 / R;
-  __shared__ float s_q[HPB][kMlaDk];
-  const int b = blockIdx.y, h0 = blockIdx.x * HPB;
-  for (int i = threadIdx.x; i < HPB * kMlaDk; i += 256) {
-    const int hl = i / kMlaDk, j = i - hl * kMlaDk;
-    s_q[hl][j] = bf16_to_f32(a.q[(size_t(b) * a.Hq + h0 + hl) * kMlaDk + j]);
+__global__ __launch_bounds__(64) void mla_qproj_kernel(MlaQArgs a) {
+  constexpr int KS = kMlaDk / 32;
+  const int mt = blockIdx.x, nt = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x, g = lane >> 4, n16 = lane & 15;
+  const uint16_t* qrow = a.q + (size_t(b) * a.Hq + 16 * mt + n16) * kMlaDk + 8 * g;
+  const float* pcol = a.P + 16 * nt + n16;
+  u32x4_t qa[KS];
+  float pv[KS][8];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    qa[s] = ld16(qrow + 32 * s);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pv[s][j] = pcol[size_t(32 * s + 8 * g + j) * R];
   }
-  __syncthreads();
-  const int hl = threadIdx.x / R, r = threadIdx.x % R;
-  float acc = 0.f;
-#pragma unroll 8
-  for (int j = 0; j < kMlaDk; ++j) acc = fmaf(s_q[hl][j], a.P[j * R + r], acc);
-  const int h = h0 + hl;
-  uint16_t hi, lo;
-  split_bf16(acc, &hi, &lo);
-  a.qf[qfrag_at<R>(b, a.MT, h >> 4, h & 15, r, 0)] = hi;
-  a.qf[qfrag_at<R>(b, a.MT, h >> 4, h & 15, r, 1)] = lo;
+  f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    uint32_t w[4][2];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split_bf16x2_terms<2>(pv[s][2 * e], pv[s][2 * e + 1], w[e]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) c = mfma16(qa[s], u32x4_t{w[0][k], w[1][k], w[2][k], w[3][k]}, c);
+  }
+  // result lane: coordinate 16 nt + n16, query heads 16 mt + 4 g + i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint16_t hi, lo;
+    split_bf16(c[i], &hi, &lo);
+    a.qf[qfrag_at<R>(b, a.MT, mt, 4 * g + i, 16 * nt + n16, 0)] = hi;
+    a.qf[qfrag_at<R>(b, a.MT, mt, 4 * g + i, 16 * nt + n16, 1)] = lo;
+  }
 }
 
 // MEAN: the group-mean query (1/Hq) sum_h q_h, projected once (linearity:
@@ -288,29 +304,37 @@ __global__ __launch_bounds__(256, 2) void mla_score_kernel(MlaScoreArgs a) {
 
 // =====================================================================================
 // Attention over the selected latent rows.  One workgroup per (sequence, group
-// of 32 query heads, chunk of the index list), in sub-blocks of 64 rows:
+// of 32 query heads, chunk of the index list), in sub-blocks of 64 rows.  The
+// head group's queries and the chunk's row indices are staged in shared
+// memory once; the rows of sub-block j + 1 are loaded into registers while
+// sub-block j is processed:
 //
-//  1. wave w loads rows 16 w .. 16 w + 15 of the sub-block straight into
-//     A-operand registers (576 elements each) and computes S^T (16 rows x 32
-//     heads) against the head group's queries, held in B-operand registers;
-//  2. the first 512 elements of its rows (the values) go to shared memory
-//     transposed, token-contiguous per value column, as the B operand of P V
-//     needs them;
+//  1. wave w holds rows 16 w .. 16 w + 15 of the sub-block (576 elements each)
+//     as A operands and computes S^T (16 rows x 32 heads) against the queries
+//     (B operands read from shared memory);
+//  2. the first 512 elements of its rows (the values) are stored row-major in
+//     shared memory; the P V products read them back as B operands with the
+//     transposing ds_read_b64_tr_b16 (within a 16-lane group, lane i receives
+//     column i of the four rows that lanes 4 k + q address);
 //  3. per-head maxima are merged through shared memory; every wave forms the
-//     base-2 probabilities of its 16 rows, split into bf16 hi + lo, in
-//     shared memory;
+//     base-2 probabilities of its 16 rows, split into bf16 hi + lo, in shared
+//     memory;
 //  4. wave w accumulates O[32 heads x value columns 128 w .. 128 w + 127] +=
 //     P V over the 64 rows, after rescaling by the change of the running max.
 //
 // The chunk's unnormalised output, running max (base 2) and sum are written
 // as partials; mla_combine_kernel merges the chunks of a head.
 // =====================================================================================
-constexpr int kVtStride = 144;  // bytes per transposed value column: 64 rows + 16 B pad
-constexpr int kPStride = 144;   // bytes per probability row (one head): 64 rows + 16 B pad
+constexpr int kQStride = kMlaDk * 2 + 16;  // bytes per staged query row
+constexpr int kVStride = kMlaDv * 2 + 32;  // bytes per staged value row
+constexpr int kPStride = 144;              // bytes per probability row (one head): 64 rows + 16 B pad
+constexpr int kMlaMaxChunk = 2048;         // rows per attention chunk at most
 
 struct MlaAttnSmem {
-  char vt[kMlaDv * kVtStride];
+  char q[32 * kQStride];
+  char v[64 * kVStride];
   char p[2][32 * kPStride];
+  int idx[kMlaMaxChunk];
   float mx[4][32];
   float alpha[32];
 };
@@ -336,8 +360,24 @@ __device__ __forceinline__ int mla_row_count(const MlaAttnArgs& a, int b) {
   return n < 0 ? 0 : (n > hi ? hi : n);
 }
 
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
+
+// B fragment of P V for value columns n0 .. n0 + 15 and sub-block rows
+// 32 ks + 8 g .. + 7 (g = lane / 16): two transposing reads of 4 rows each.
+__device__ __forceinline__ u32x4_t vfrag(const char* sv, int ks, int n0) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15;
+  const char* base = sv + (32 * ks + 8 * g + (i >> 2)) * kVStride + (n0 + 4 * (i & 3)) * 2;
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t r0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(base)));
+  const u32x2_t r1 =
+      __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(base + 4 * kVStride)));
+  return u32x4_t{r0.x, r0.y, r1.x, r1.y};
+}
+
 template <bool INDEXED>
 __global__ __launch_bounds__(256, 1) void mla_attn_kernel(MlaAttnArgs a) {
+  constexpr int KS = kMlaDk / 32;
   __shared__ __align__(16) MlaAttnSmem S;
   const int chunk_id = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
   const int h0 = hg * 32;
@@ -347,25 +387,28 @@ __global__ __launch_bounds__(256, 1) void mla_attn_kernel(MlaAttnArgs a) {
   if (cnt == 0) return;  // never read by the combine
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, n16 = lane & 15;
 
-  // queries: B operand of S^T = K Q^T; column n = head h0 + 16 ht + n16
-  u32x4_t qfr[2][kMlaDk / 32];
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-    for (int s = 0; s < kMlaDk / 32; ++s)
-      qfr[ht][s] = ld16(a.q + (size_t(b) * a.Hq + h0 + 16 * ht + n16) * kMlaDk + 32 * s + 8 * g);
+  // the head group's queries and the chunk's row indices into shared memory
+  for (int u = threadIdx.x; u < 32 * (kMlaDk / 8); u += 256) {
+    const int hh = u / (kMlaDk / 8), c = u - hh * (kMlaDk / 8);
+    *reinterpret_cast<u32x4_t*>(S.q + hh * kQStride + c * 16) =
+        ld16(a.q + (size_t(b) * a.Hq + h0 + hh) * kMlaDk + c * 8);
+  }
+  if constexpr (INDEXED) {  // (the dense path's rows are c0 + p)
+    for (int i = threadIdx.x; i < cnt; i += 256) {
+      const int t = a.idx[size_t(b) * a.idx_stride + c0 + i];
+      S.idx[i] = t < 0 ? 0 : (t >= a.t_max ? a.t_max - 1 : t);
+    }
+  }
+  __syncthreads();
 
-  const int32_t* irow = INDEXED ? a.idx + size_t(b) * a.idx_stride + c0 : nullptr;
   const uint16_t* kvb = a.kv + size_t(b) * a.t_max * kMlaDk;
   // rows: A operand; row m = row 16 wave + n16 of the sub-block
-  u32x4_t kfr[kMlaDk / 32];
-  auto load_rows = [&](int sb) {
+  auto load_rows = [&](int sb, u32x4_t (&kf)[KS]) {
     const int p = min(sb * 64 + 16 * wave + n16, cnt - 1);
-    int t = INDEXED ? irow[p] : c0 + p;
-    t = t < 0 ? 0 : (t >= a.t_max ? a.t_max - 1 : t);
+    const int t = INDEXED ? S.idx[p] : c0 + p;
     const uint16_t* row = kvb + size_t(t) * kMlaDk + 8 * g;
 #pragma unroll
-    for (int s = 0; s < kMlaDk / 32; ++s) kfr[s] = ld16_nt(row + 32 * s);
+    for (int s = 0; s < KS; ++s) kf[s] = ld16_nt(row + 32 * s);
   };
 
   f32x4_t acc[2][8];
@@ -377,27 +420,28 @@ __global__ __launch_bounds__(256, 1) void mla_attn_kernel(MlaAttnArgs a) {
   const int n_sub = (cnt + 63) >> 6;
   const int tau = 16 * wave + n16;  // this lane's row within the sub-block (A layout)
 
-  load_rows(0);
-  for (int sb = 0; sb < n_sub; ++sb) {
+  // kf: this sub-block's rows; kn, loaded here for sub-block `next` once kf's
+  // products are issued, stays in flight through the rest of the step
+  auto step = [&](int sb, const u32x4_t (&kf)[KS], int next, u32x4_t (&kn)[KS]) {
     f32x4_t st[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    constexpr int QB = 3;  // K-steps whose query fragments are read together
 #pragma unroll
-    for (int s = 0; s < kMlaDk / 32; ++s) {
-      st[0] = mfma16(kfr[s], qfr[0][s], st[0]);
-      st[1] = mfma16(kfr[s], qfr[1][s], st[1]);
+    for (int s0 = 0; s0 < KS; s0 += QB) {
+      u32x4_t qb[QB][2];
+#pragma unroll
+      for (int u = 0; u < QB; ++u)
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) qb[u][ht] = ld16(S.q + (16 * ht + n16) * kQStride + (32 * (s0 + u) + 8 * g) * 2);
+#pragma unroll
+      for (int u = 0; u < QB; ++u)
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) st[ht] = mfma16(kf[s0 + u], qb[u][ht], st[ht]);
     }
-    __syncthreads();  // the previous sub-block's readers of vt, p and alpha are done
-    // values, transposed: column d holds rows 0..63 in 16-byte units of 8 rows;
-    // unit u of column d sits at position u ^ ((d / 8) % 8)
+    if (next < n_sub) load_rows(next, kn);
+    __syncthreads();  // the previous sub-block's readers of v, p and alpha are done
 #pragma unroll
-    for (int s = 0; s < kMlaDv / 32; ++s) {
-      const int d0 = 32 * s + 8 * g;
-      char* base = S.vt + d0 * kVtStride + 16 * ((tau >> 3) ^ ((d0 >> 3) & 7)) + 2 * (tau & 7);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t w = kfr[s][j >> 1];
-        *reinterpret_cast<uint16_t*>(base + j * kVtStride) = uint16_t((j & 1) ? (w >> 16) : (w & 0xffffu));
-      }
-    }
+    for (int s = 0; s < kMlaDv / 32; ++s)
+      *reinterpret_cast<u32x4_t*>(S.v + tau * kVStride + (32 * s + 8 * g) * 2) = kf[s];
     // logits in base 2; result lane holds head 16 ht + n16, rows 16 wave + 4 g + i
     const int pbase = sb * 64 + 16 * wave + 4 * g;
     float x[2][4];
@@ -410,26 +454,23 @@ __global__ __launch_bounds__(256, 1) void mla_attn_kernel(MlaAttnArgs a) {
       mw = fmaxf(mw, __shfl_xor(mw, 32));
       if (g == 0) S.mx[wave][16 * ht + n16] = mw;
     }
-    if (sb + 1 < n_sub) load_rows(sb + 1);  // the row registers are free again
     __syncthreads();
 
-    float m_new[2], alpha[2];
+    float alpha[2];
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
       const int hh = 16 * ht + n16;
       const float mb = fmaxf(fmaxf(S.mx[0][hh], S.mx[1][hh]), fmaxf(S.mx[2][hh], S.mx[3][hh]));
-      m_new[ht] = fmaxf(m_run[ht], mb);
-      alpha[ht] = mla_exp2(m_run[ht] - m_new[ht]);
-      uint16_t hi[4], lo[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) split_bf16(mla_exp2(x[ht][i] - m_new[ht]), &hi[i], &lo[i]);
+      const float m_new = fmaxf(m_run[ht], mb);
+      alpha[ht] = mla_exp2(m_run[ht] - m_new);
+      uint32_t w01[2], w23[2];
+      split_bf16x2_terms<2>(mla_exp2(x[ht][0] - m_new), mla_exp2(x[ht][1] - m_new), w01);
+      split_bf16x2_terms<2>(mla_exp2(x[ht][2] - m_new), mla_exp2(x[ht][3] - m_new), w23);
       const int off = hh * kPStride + (16 * wave + 4 * g) * 2;
-      *reinterpret_cast<uint2*>(S.p[0] + off) =
-          make_uint2(uint32_t(hi[0]) | (uint32_t(hi[1]) << 16), uint32_t(hi[2]) | (uint32_t(hi[3]) << 16));
-      *reinterpret_cast<uint2*>(S.p[1] + off) =
-          make_uint2(uint32_t(lo[0]) | (uint32_t(lo[1]) << 16), uint32_t(lo[2]) | (uint32_t(lo[3]) << 16));
+      *reinterpret_cast<uint2*>(S.p[0] + off) = make_uint2(w01[0], w23[0]);
+      *reinterpret_cast<uint2*>(S.p[1] + off) = make_uint2(w01[1], w23[1]);
       if (wave == 0 && g == 0) S.alpha[hh] = alpha[ht];
-      m_run[ht] = m_new[ht];
+      m_run[ht] = m_new;
     }
     __syncthreads();
 
@@ -459,18 +500,30 @@ __global__ __launch_bounds__(256, 1) void mla_attn_kernel(MlaAttnArgs a) {
         acc[mt][nt][3] *= al.w;
       }
     }
+    constexpr int VB = 4;  // value tiles whose fragments are read together
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const int d = 128 * wave + 16 * nt + n16;
-        const u32x4_t vb = ld16(S.vt + d * kVtStride + 16 * ((4 * ks + g) ^ ((d >> 3) & 7)));
+      for (int nt0 = 0; nt0 < 8; nt0 += VB) {
+        u32x4_t vb[VB];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          acc[mt][nt] = mfma16(pa[mt][ks][0], vb, acc[mt][nt]);
-          acc[mt][nt] = mfma16(pa[mt][ks][1], vb, acc[mt][nt]);
-        }
+        for (int u = 0; u < VB; ++u) vb[u] = vfrag(S.v, ks, 128 * wave + 16 * (nt0 + u));
+#pragma unroll
+        for (int u = 0; u < VB; ++u)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            acc[mt][nt0 + u] = mfma16(pa[mt][ks][0], vb[u], acc[mt][nt0 + u]);
+            acc[mt][nt0 + u] = mfma16(pa[mt][ks][1], vb[u], acc[mt][nt0 + u]);
+          }
       }
+  };
+
+  // sub-blocks in pairs, so that the two row buffers are named statically
+  u32x4_t k0[KS], k1[KS];
+  load_rows(0, k0);
+  for (int sb = 0; sb < n_sub; sb += 2) {
+    step(sb, k0, sb + 1, k1);
+    if (sb + 1 < n_sub) step(sb + 1, k1, sb + 2, k0);
   }
 
   const size_t slot = size_t(b) * a.n_chunks + chunk_id;
@@ -550,10 +603,10 @@ hipError_t launch_mla_qproj(const jssa_desc& d, const void* q, const float* P, c
   const bool mean = d.reduce == JSSA_REDUCE_MEAN;
   if (d.rank == 64) {
     if (mean) hipLaunchKernelGGL(mla_qproj_mean_kernel<64>, dim3(1, d.batch), dim3(256), 0, s, qa);
-    else hipLaunchKernelGGL(mla_qproj_kernel<64>, dim3(d.n_q_heads / 4, d.batch), dim3(256), 0, s, qa);
+    else hipLaunchKernelGGL(mla_qproj_kernel<64>, dim3(d.n_q_heads / 16, 4, d.batch), dim3(64), 0, s, qa);
   } else {
     if (mean) hipLaunchKernelGGL(mla_qproj_mean_kernel<32>, dim3(1, d.batch), dim3(256), 0, s, qa);
-    else hipLaunchKernelGGL(mla_qproj_kernel<32>, dim3(d.n_q_heads / 8, d.batch), dim3(256), 0, s, qa);
+    else hipLaunchKernelGGL(mla_qproj_kernel<32>, dim3(d.n_q_heads / 16, 2, d.batch), dim3(64), 0, s, qa);
   }
   return hipGetLastError();
 }
@@ -595,6 +648,7 @@ hipError_t launch_mla_attend(const jssa_desc& d, const void* q, const void* k_ca
   a.Hq = d.n_q_heads; a.t_max = d.t_max; a.idx_stride = d.topk + d.window;
   a.chunk = ws.chunk; a.n_chunks = ws.n_chunks; a.out_dtype = d.out_dtype;
   a.qscale = d.scale * kLog2e;
+  if (idx && ws.chunk > kMlaMaxChunk) return hipErrorInvalidValue;  // the chunk's indices are staged
   const dim3 grid(ws.n_chunks, d.n_q_heads / 32, d.batch), cgrid(d.n_q_heads, d.batch);
   if (idx) {
     hipLaunchKernelGGL(mla_attn_kernel<true>, grid, dim3(256), 0, s, a);

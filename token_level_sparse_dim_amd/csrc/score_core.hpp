@@ -158,26 +158,26 @@ __device__ __forceinline__ void load_qfrag(Ld ld, int G, QFrag<KPT, R, GE>& qf) 
     const float invG = 1.0f / float(G);
 #pragma unroll
     for (int s = 0; s < S::KS; ++s) {
-      uint16_t t[8][kQTerms];
+      float x[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int i = 32 * s + 8 * kg + j;
-        float x = 0.f;
+        x[j] = 0.f;
         if constexpr (GE == 1) {
           if (m == 0) {
             float sm = 0.f;
             for (int g = 0; g < G; ++g) sm += ld(g * R + i);
-            x = sm * invG;
+            x[j] = sm * invG;
           }
         } else {
-          if (m < G) x = ld(m * R + i);
+          if (m < G) x[j] = ld(m * R + i);
         }
-        split_bf16_terms<kQTerms>(x, t[j]);
       }
+      uint32_t w[4][kQTerms];
 #pragma unroll
-      for (int k = 0; k < kQTerms; ++k)
-        qf.a[s][k] = u32x4_t{uint32_t(t[0][k]) | (uint32_t(t[1][k]) << 16), uint32_t(t[2][k]) | (uint32_t(t[3][k]) << 16),
-                             uint32_t(t[4][k]) | (uint32_t(t[5][k]) << 16), uint32_t(t[6][k]) | (uint32_t(t[7][k]) << 16)};
+      for (int e = 0; e < 4; ++e) split_bf16x2_terms<kQTerms>(x[2 * e], x[2 * e + 1], w[e]);
+#pragma unroll
+      for (int k = 0; k < kQTerms; ++k) qf.a[s][k] = u32x4_t{w[0][k], w[1][k], w[2][k], w[3][k]};
     }
   } else {
     load_qreg<KPT, R, GE>(ld, G, qf.q);
