@@ -33,7 +33,7 @@ constexpr int kMaxPipeChunk = 1024;  // attention chunk limit of the fused decod
 // MLA layout: shared latent rows of kMlaDk elements, values = first kMlaDv
 constexpr int kMlaDk = 576;
 constexpr int kMlaDv = 512;
-constexpr int kMlaScoreTile = 2048;  // candidate tokens per MLA score workgroup
+constexpr int kMlaScoreTile = 1024;  // candidate tokens per MLA score workgroup
 constexpr int kMlaHeadGroup = 32;    // query heads per MLA attention workgroup
 
 // per-row state (u32 words).  The tickets and the ready flag are zero on

@@ -248,14 +248,14 @@ struct Pipe {
     uint32_t l_key;
   };
   struct ResolveSmem {
-    uint32_t keys[kPipeCandLds];  // token indices of the candidates by ordinal
+    uint64_t cand[kPipeCandLds];  // (token << 32 | key) of the candidates by ordinal
     uint32_t tab[kPipeMaxTiles];  // candidate prefix per tile
     uint32_t hist[2048];          // histograms of the cut
     uint32_t scan[8];
     uint32_t out[2];
   };
   static constexpr size_t kSmemScan = cmax(sizeof(SampleSmem), sizeof(ScoreSmem));
-  // the exact re-selection overlays ScoreSmem on ResolveSmem (its keys only on ResolveSmem::keys)
+  // the exact re-selection overlays ScoreSmem on ResolveSmem (only on ResolveSmem::cand)
   static constexpr size_t kSmemResolve = cmax(sizeof(ResolveSmem), sizeof(ScoreSmem));
 
   static __device__ const char* kp_row(const PipeArgs& a, int row) {
@@ -509,42 +509,49 @@ struct Pipe {
     };
     uint32_t kstar, istar;
     if (C <= uint32_t(kPipeCandLds)) {
+      // Gather every candidate into shared memory by ordinal.  Wave w copies
+      // tiles [UB w, UB w + UB) of each round: a tile's candidates are
+      // contiguous in its slot, so two wave loads move up to 128 of them; the
+      // tiles' boundaries come from one shared-memory read (lane u holds tile
+      // u's) and readlane, and every load of a round is issued before the
+      // first store.
+      {
+        constexpr int UB = 16;
+        const uint32_t lane = threadIdx.x & 63;
+        const int wave = threadIdx.x >> 6;
+        for (int r0 = wave * UB; r0 < n_tiles_row; r0 += 4 * UB) {
+          const int tl = r0 + int(lane);
+          const uint32_t tb = (lane <= uint32_t(UB) && tl < n_tiles_row) ? sm.tab[tl] : C;
+          uint64_t v0[UB], v1[UB];
+          uint32_t base[UB], cnt_t[UB];
+#pragma unroll
+          for (int u = 0; u < UB; ++u) {
+            base[u] = uint32_t(__builtin_amdgcn_readlane(int(tb), u));
+            cnt_t[u] = uint32_t(__builtin_amdgcn_readlane(int(tb), u + 1)) - base[u];  // 0 past the row's tiles
+            const uint64_t* src = slots + size_t(r0 + u) * TS;
+            v0[u] = lane < cnt_t[u] ? src[lane] : 0ull;
+            v1[u] = lane + 64u < cnt_t[u] ? src[lane + 64u] : 0ull;
+          }
+#pragma unroll
+          for (int u = 0; u < UB; ++u) {
+            if (lane < cnt_t[u]) sm.cand[base[u] + lane] = v0[u];
+            if (lane + 64u < cnt_t[u]) sm.cand[base[u] + lane + 64u] = v1[u];
+            for (uint32_t i = lane + 128u; i < cnt_t[u]; i += 64u)  // tiles with more than 128 candidates
+              sm.cand[base[u] + i] = slots[size_t(r0 + u) * TS + i];
+          }
+        }
+      }
+      __syncthreads();
       // Thread x owns the contiguous run of candidate ordinals [j0, j1): their
-      // keys stay in registers for every pass of the cut, their token indices
-      // go to shared memory.  Candidates are in token order, so ranking equal
-      // keys by ordinal ranks them by token index.
+      // keys stay in registers for every pass of the cut.  Candidates are in
+      // token order, so ranking equal keys by ordinal ranks them by token index.
       constexpr int MAXPER = kPipeCandLds / 256;
-      constexpr int BATCH = MAXPER;  // every load of the run in one round trip
       const uint32_t per = (C + 255) / 256;
       const uint32_t j0 = min(C, uint32_t(threadIdx.x) * per), j1 = min(C, j0 + per);
       const int cnt = int(j1 - j0);
       uint32_t kv[MAXPER];
-      {
-        uint32_t tile = cnt > 0 ? last_le(sm.tab, uint32_t(n_tiles_row), j0) : 0u;
-        uint32_t next = tile + 1 < uint32_t(n_tiles_row) ? sm.tab[tile + 1] : 0xffffffffu;
 #pragma unroll
-        for (int i0 = 0; i0 < MAXPER; i0 += BATCH) {
-          uint64_t v[BATCH];
-#pragma unroll
-          for (int u = 0; u < BATCH; ++u) {
-            const uint32_t j = j0 + uint32_t(i0 + u);
-            size_t off = 0;  // runs shorter than MAXPER re-read entry 0 (C >= 1) and ignore it
-            if (i0 + u < cnt) {
-              while (j >= next) {
-                ++tile;
-                next = tile + 1 < uint32_t(n_tiles_row) ? sm.tab[tile + 1] : 0xffffffffu;
-              }
-              off = size_t(tile) * TS + (j - sm.tab[tile]);
-            }
-            v[u] = slots[off];
-          }
-#pragma unroll
-          for (int u = 0; u < BATCH; ++u) {
-            kv[i0 + u] = uint32_t(v[u]);
-            if (i0 + u < cnt) sm.keys[j0 + i0 + u] = uint32_t(v[u] >> 32);  // token index of ordinal j
-          }
-        }
-      }
+      for (int i = 0; i < MAXPER; ++i) kv[i] = i < cnt ? uint32_t(sm.cand[j0 + i]) : 0u;
       // Radix digits of d = key - (smallest candidate key): the candidates sit
       // in a narrow band at the top, so digits of the key itself would pile
       // them into a few bins.  Passes of 11 bits from the top set bit of the
@@ -614,7 +621,7 @@ struct Pipe {
 #pragma unroll
       for (int i = 0; i < MAXPER; ++i) {
         if (i < cnt && (kv[i] > kstar || (kv[i] == kstar && j0 + uint32_t(i) <= istar))) {
-          if (pos < uint32_t(md.kk)) out[pos] = sm.keys[j0 + i];
+          if (pos < uint32_t(md.kk)) out[pos] = uint32_t(sm.cand[j0 + i] >> 32);
           ++pos;
         }
       }
