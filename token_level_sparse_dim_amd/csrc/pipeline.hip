@@ -46,6 +46,11 @@ constexpr int kPipeAttnNL = 8;         // K and V row loads per lane per attenti
 // per-row state word of the scan (zero on entry and exit): u64 at words 12-13,
 // (1 << 32) | L once the row's threshold is known
 constexpr int PW_L = 12;
+// per-row state word of the scan: claims of the row's shared tiles (reset by the resolve)
+constexpr int PW_STEAL = 14;
+#ifndef JSSA_PIPE_STATIC_PCT
+#define JSSA_PIPE_STATIC_PCT 70  // share of a row's tiles covered by the static score runs
+#endif
 // queue words: sticky diagnostics (a missing threshold; exact re-selections)
 enum PipeQueue : int { PQ_ERR = 2, PQ_FALLBACK = 3 };
 
@@ -246,6 +251,7 @@ struct Pipe {
       uint32_t keys[kPipeMaxItem];  // keys of the item's tokens, token order
     };
     uint32_t l_key;
+    int claim;
   };
   struct ResolveSmem {
     uint64_t cand[kPipeCandLds];  // (token << 32 | key) of the candidates by ordinal
@@ -422,6 +428,41 @@ struct Pipe {
     }
     __syncthreads();
     emit_keys(a, row, t_begin, t_end, sm.l_key, sm.keys);
+    // The row's shared tiles (those past the static runs): claimed one at a
+    // time from the row's counter by the row's runs as they finish, which
+    // evens out runs that stream at different rates.  The next claim is
+    // requested while the current tile is scanned.
+    const int pool0 = a.n_big * (a.item / TS);
+    // claims shared tiles of row rr (n_cand candidates, threshold l) until its pool is empty
+    auto drain = [&](int rr, int n_cand_rr, uint32_t l) {
+      const int n_tiles_rr = (n_cand_rr + TS - 1) / TS;
+      if (pool0 >= n_tiles_rr) return;
+      const char* krr = kp_row(a, rr);
+      uint32_t* ctr = state(a, rr) + PW_STEAL;
+      __syncthreads();  // every wave is done with keys[] and the previous claim
+      if (threadIdx.x == 0) sm.claim = int(__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      __syncthreads();
+      int c = sm.claim;
+      while (pool0 + c < n_tiles_rr) {
+        const int tb = (pool0 + c) * TS, te = min(tb + TS, n_cand_rr);
+        uint4 b1[S::U];
+        load_step(krr, tb, te, b1);
+        int nxt = 0;
+        if (threadIdx.x == 0) nxt = int(__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        __syncthreads();  // every wave has read the previous claim
+        scan_keys(krr, tb, te, qf, b1, sm.keys);
+        if (threadIdx.x == 0) sm.claim = nxt;
+        __syncthreads();
+        emit_keys(a, rr, tb, te, l, sm.keys);
+        c = sm.claim;
+        __syncthreads();  // keys[] is free again
+      }
+    };
+    // The row's shared tiles (those past the static runs), claimed one at a
+    // time by the row's runs as they finish, which evens out runs that stream
+    // at different rates.  (Also draining other rows' tiles, with their
+    // queries published by the samples, measured slower.)
+    drain(row, md.n_cand, sm.l_key);
   }
 
   // ---- RESOLVE (second launch) ------------------------------------------------------------
@@ -491,7 +532,10 @@ struct Pipe {
   static __device__ __forceinline__ void resolve_select(const PipeArgs& a, int row, const RowMode& md, char* smem) {
     ResolveSmem& sm = *reinterpret_cast<ResolveSmem*>(smem);
     uint32_t* out = reinterpret_cast<uint32_t*>(a.at.idx + size_t(row) * a.at.idx_stride);
-    if (threadIdx.x == 0) *l_word(a, row) = 0;  // read again only by the next call's scan
+    if (threadIdx.x == 0) {  // read again only by the next call's scan
+      *l_word(a, row) = 0;
+      state(a, row)[PW_STEAL] = 0;
+    }
     for (int j = threadIdx.x; j < md.nW; j += 256) out[md.kk + j] = uint32_t(md.Tb - md.nW + j);
     if (threadIdx.x == 0) const_cast<int32_t*>(a.at.n_sel)[row] = md.kk + md.nW;
     const int n_tiles_row = (md.n_cand + TS - 1) / TS;
@@ -789,9 +833,9 @@ static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
   using Pp = Pipe<KPT, R, GE, D, G, KVT>;
   if (Pp::TS != a.ts || Attn2Shape<KVT, D, G, kPipeAttnNL>::CH != a.at.chunk) return hipErrorInvalidValue;
   // score runs sized so that the samples and one run per resident workgroup
-  // cover every row: each run streams long enough that its row's threshold is
-  // known when it finishes, and the rows finish their scans together (per-run
-  // overhead makes short runs for balancing a loss)
+  // fit; a run streams long enough that its row's threshold is known when it
+  // finishes, and the row's remaining tiles are shared by its runs as they
+  // finish
   static int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
@@ -803,10 +847,13 @@ static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
   const int resident = per_cu * compute_units();
   const int n_tiles_max = (a.at.t_max + Pp::TS - 1) / Pp::TS;
   const int per_row = resident > 2 * a.n_rows ? (resident - a.n_rows) / a.n_rows : 1;
-  int big_tiles = (n_tiles_max + per_row - 1) / per_row;
+  // static runs cover JSSA_PIPE_STATIC_PCT% of a row's tiles; the rest are shared
+  int big_tiles = (JSSA_PIPE_STATIC_PCT * n_tiles_max) / (100 * per_row);
+  if (big_tiles < 1) big_tiles = 1;
   if (big_tiles > kPipeMaxItem / Pp::TS) big_tiles = kPipeMaxItem / Pp::TS;
   a.item = big_tiles * Pp::TS;
   a.n_big = (n_tiles_max + big_tiles - 1) / big_tiles;
+  if (a.n_big > per_row) a.n_big = per_row;
   a.n_small = 0;
   a.n_main = a.n_rows + a.n_rows * a.n_big;
   int grid = resident < a.n_main ? resident : a.n_main;
