@@ -1,0 +1,144 @@
+"""GPU parity at the full sizes of the two headline decode workloads, in the
+launch configuration the benchmark times: the 128K-context GQA step (batch 4,
+32 query / 8 KV heads, d = 128, r = 32, k = 2048) and the MLA step (batch 8, 128
+query heads sharing one 576-wide latent row, r = 64, k = 2048). As in the
+benchmark, the GPU projects the whole key cache, appends one new token at
+T_b - 1 and runs the fused decode on the decode workspace.
+
+The oracle checks sampled (sequence, KV head) rows one at a time: it projects
+that row's keys itself, and the row's projected keys in the GPU cache are
+replaced by the oracle's before the decode, so both sides score the same
+input (rows are independent in the decode). Every other row is checked by
+properties that hold at any size: selection counts, strictly ascending indices
+inside the sequence, finite outputs."""
+import numpy as np
+import pytest
+import torch
+
+import token_level_sparse_dim_amd as J
+from oracle import jssa_oracle as O
+from synth import WORKLOADS, generate, to_bf16_bits
+
+from _gpu_helpers import check_sets_within_tolerance, desc_for, rel_l2, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+ATT_TOL = 2e-3  # bf16 inputs, fp32 accumulation
+
+
+def _new_token(w, seed):
+    """One new key (and value) row per sequence, drawn as the benchmark draws it."""
+    rng = np.random.default_rng(seed)
+    kn = rng.standard_normal((w.batch, 1, w.n_kv_heads, w.d_k)).astype(np.float32)
+    vn = rng.standard_normal((w.batch, 1, w.n_kv_heads, w.d_v)).astype(np.float32)
+    return to_bf16_bits(kn), to_bf16_bits(vn)
+
+
+def _check_row_projection(got, k_rows, P_h, w):
+    """GPU projection of one row = round_bf16(fp32-accumulated K.P): within the
+    recursive summation bound plus half a bf16 step of the fp64 product, and
+    the oracle's correctly rounded value except next to a rounding boundary.
+    (The fraction is checked on whole rows; a single appended token only gets
+    the bound.) Returns the oracle's stored row."""
+    stored, exact = O.project_keys(k_rows[None, :, None, :], P_h[None], np.array([k_rows.shape[0]]), "bf16")
+    stored, exact = stored[0, 0], exact[0, 0]
+    g64 = O.to_f64(got)
+    bound = np.abs(O.to_f64(k_rows)) @ np.abs(P_h.astype(np.float64)) * (1.01 * w.d_k * 2.0 ** -24)
+    half_step = np.ldexp(1.0, np.frexp(np.maximum(np.abs(g64), np.abs(exact)))[1] - 9)
+    assert (np.abs(g64 - exact) <= bound + half_step).all()
+    if got.shape[0] >= 1024:
+        assert (got != stored).mean() < 1e-3
+    return stored
+
+
+def _check_structure(gi, gn, L, w):
+    """Properties of every row: the selection count, strictly ascending
+    indices inside the sequence, the window at the end."""
+    B, Hkv = gn.shape
+    for b in range(B):
+        n_cand = max(int(L[b]) - w.window, 0)
+        n_exp = min(w.window, int(L[b])) + min(w.topk, n_cand)
+        for h in range(Hkv):
+            assert int(gn[b, h]) == n_exp, (b, h, int(gn[b, h]), n_exp)
+            sel = gi[b, h, :n_exp]
+            assert (np.diff(sel) > 0).all() and sel[0] >= 0 and sel[-1] < L[b]
+            if w.window:
+                assert np.array_equal(sel[n_exp - w.window:], np.arange(L[b] - w.window, L[b]))
+
+
+def _run_full(w, samples, reduce=J.REDUCE_MAX):
+    inp = generate(w, seed=w.seed)  # the benchmark's first input set
+    desc = desc_for(w, reduce=reduce)
+    B, Hkv, T, r, G = w.batch, w.n_kv_heads, w.t_max, w.rank, w.group
+    L = inp["seq_lens"]
+    dev = "cuda"
+    q, P, K, seq = (to_dev(inp[k]) for k in ("q", "P", "k_cache", "seq_lens"))
+    V = None if w.mla else to_dev(inp["v_cache"])
+
+    # (1) the whole-cache projection the benchmark starts from; the sampled rows
+    # are checked and then replaced by the oracle's own projection
+    kp = torch.empty((B, Hkv, T, r), dtype=torch.bfloat16, device=dev)
+    J.append_projection(desc, T, torch.zeros(B, dtype=torch.int32, device=dev), P, K, kp)
+    torch.cuda.synchronize()
+    kp_ref = {}
+    for b, h in samples:
+        n = int(L[b])
+        got = to_host(kp[b, h, :n])
+        kp_ref[b, h] = _check_row_projection(got, inp["k_cache"][b, :n, h, :], inp["P"][h], w)
+        kp[b, h, :n] = to_dev(kp_ref[b, h])
+
+    # (2) one benchmark step: append the new token at T_b - 1, then the fused decode
+    kn, vn = _new_token(w, w.seed + 7)
+    pos = (seq - 1).contiguous()
+    J.append_kv(desc, to_dev(kn), None if w.mla else to_dev(vn), pos, P, K, V, kp)
+    ws = J.workspace(desc, J.OP_DECODE)
+    out = torch.empty((B, w.n_q_heads, w.d_v), device=dev)
+    lse = torch.empty((B, w.n_q_heads), device=dev)
+    J.decode(desc, q, P, kp, K, V, seq, out, lse, ws)
+    torch.cuda.synchronize()
+    o_bench, l_bench = to_host(out).copy(), to_host(lse).copy()
+    # the same call with the index lists exported: the same outputs
+    idx = torch.full((B, Hkv, w.topk + w.window), -1, dtype=torch.int32, device=dev)
+    n_sel = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+    J.decode(desc, q, P, kp, K, V, seq, out, lse, ws, idx_out=idx, n_sel_out=n_sel)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(out), o_bench) and np.array_equal(to_host(lse), l_bench)
+    gi, gn = to_host(idx), to_host(n_sel)
+    _check_structure(gi, gn, L, w)
+    assert np.isfinite(o_bench).all() and np.isfinite(l_bench).all()
+
+    # (3) the oracle on each sampled row, with the appended token in its cache
+    k_host = inp["k_cache"]
+    v_host = k_host[..., :w.d_v] if w.mla else inp["v_cache"]
+    for b in range(B):
+        k_host[b, L[b] - 1] = kn[b, 0]
+        if not w.mla:
+            v_host[b, L[b] - 1] = vn[b, 0]
+    for b, h in samples:
+        n = int(L[b])
+        assert np.array_equal(to_host(K[b, n - 1]), kn[b, 0])
+        kp_row = np.zeros((T, r), np.uint16)
+        kp_row[:n] = kp_ref[b, h]
+        kp_row[n - 1] = _check_row_projection(to_host(kp[b, h, n - 1:n]), k_host[b, n - 1:n, h, :],
+                                              inp["P"][h], w)
+        hs = slice(h * G, (h + 1) * G)
+        qs = inp["q"][b:b + 1, hs]
+        s64, n_cand = O.subspace_scores(qs, inp["P"][h:h + 1], kp_row[None, None], L[b:b + 1], w.window,
+                                        "max" if reduce == J.REDUCE_MAX else "mean")
+        check_sets_within_tolerance(gi[b:b + 1, h:h + 1], gn[b:b + 1, h:h + 1], s64, n_cand, L[b:b + 1],
+                                    w.topk, w.window)
+        ref, ref_lse = O.attention(qs, k_host[b:b + 1, :, h:h + 1], v_host[b:b + 1, :, h:h + 1],
+                                   np.where(gi[b:b + 1, h:h + 1] < 0, 0, gi[b:b + 1, h:h + 1]), gn[b:b + 1, h:h + 1], w.scale)
+        got_o, got_l = o_bench[b:b + 1, hs], l_bench[b:b + 1, hs]
+        assert rel_l2(got_o, ref) <= ATT_TOL, (b, h, rel_l2(got_o, ref))
+        assert np.abs(got_l - ref_lse).max() <= 1e-4 * max(1.0, np.abs(ref_lse).max()), (b, h)
+
+
+def test_full_ctx128k_step():
+    """All four sequences, first / middle / last KV heads."""
+    _run_full(WORKLOADS["ctx128k"], [(0, 0), (1, 3), (2, 7), (3, 4), (0, 7), (3, 0)])
+
+
+def test_full_mla_step():
+    """Three of the eight sequences (one latent row per sequence)."""
+    _run_full(WORKLOADS["mla"], [(0, 0), (4, 0), (7, 0)])
