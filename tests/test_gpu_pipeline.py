@@ -159,3 +159,39 @@ def test_fused_repeated_calls_share_workspace():
         check_sets_within_tolerance(gi, gn, s64, n_cand, seq, w.topk, w.window)
         ref, _ = O.attention(inp["q"], inp["k_cache"], inp["v_cache"], np.where(gi < 0, 0, gi), gn, w.scale)
         assert rel_l2(to_host(out), ref) <= 2e-3
+
+
+@pytest.mark.parametrize("n_groups,topk", [(5, 512), (5, 2500), (60, 512), (400, 700)],
+                         ids=["inside_top_group", "inside_second_group", "60_groups", "400_groups"])
+def test_decode_heavy_ties(n_groups, topk):
+    """Projected keys drawn from a few distinct rows, so the scores form large
+    groups of bitwise-equal values and the k-th lies inside one: the bin of
+    the cut is crowded, and ties go to the lower token index.  The decode must
+    equal the composed entry points, and the oracle's full-sort top-k on the
+    GPU's own fp32 scores (bit-exact selection on identical score arrays)."""
+    base = CASES["llama"]
+    w = scaled(base, topk=topk)
+    inp = inputs(base)
+    desc = desc_for(w)
+    kp = oracle_kp(inp, desc).copy()  # [B, Hkv, T, r] bf16 bits
+    B, Hkv, T, _ = kp.shape
+    rng = np.random.default_rng(11 + n_groups)
+    for b in range(B):
+        for h in range(Hkv):
+            rows = kp[b, h, rng.choice(T, n_groups, replace=False)].copy()
+            kp[b, h] = rows[rng.integers(0, n_groups, T)]
+    o1, _, i1, n1, ws = _run(desc, inp, kp, w, profiled=False)
+    o2, _, i2, n2 = _composed(desc, inp, kp, w)
+    assert np.array_equal(n1, n2) and np.array_equal(i1, i2)
+    assert rel_l2(o1, o2) <= 1e-5
+    scores = torch.empty((w.batch, w.n_kv_heads, w.t_max), device="cuda")
+    J.score(desc, to_dev(inp["q"]), to_dev(inp["P"]), to_dev(kp), to_dev(inp["seq_lens"]), scores)
+    s32 = to_host(scores).astype(np.float64)
+    ref_idx, ref_n = O.topk_select(s32, inp["seq_lens"], w.topk, w.window)
+    assert np.array_equal(ref_n, n1)
+    for b in range(B):
+        for h in range(Hkv):
+            n = int(ref_n[b, h])
+            assert np.array_equal(np.sort(ref_idx[b, h, :n]), i1[b, h, :n]), (b, h)
+    ref, _ = O.attention(inp["q"], inp["k_cache"], inp["v_cache"], np.where(i1 < 0, 0, i1), n1, w.scale)
+    assert rel_l2(o1, ref) <= 2e-3

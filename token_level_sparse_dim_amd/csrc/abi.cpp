@@ -111,13 +111,14 @@ bool workspace_layout(const jssa_desc& d, int op, Workspace* ws) {
   }
   const int cnt_tiles = ws->pipe_tiles > ws->n_sel_tiles ? ws->pipe_tiles : ws->n_sel_tiles;
   ws->row_state = take(rows * kRowStateWords * 4);
+  if (ws->pipe) ws->pipe_qp = take(rows * size_t(G) * d.rank * 4);
   ws->queue = take(kQueueWords * 4);
   if (op == JSSA_OP_TOPK || op == JSSA_OP_DECODE) {
     ws->hist1 = take(rows * kDigit1Bins * 4);
     ws->tile_cnt = take(rows * cnt_tiles * 4);
     ws->tile_off = take(rows * ws->n_sel_tiles * 4);
     ws->cand_base = take(rows * ws->n_sel_tiles * 4);
-    ws->cand = take(rows * size_t(d.t_max) * 8);
+    ws->cand = take((rows * size_t(d.t_max) + kCandPad) * 8);
   }
   if (op == JSSA_OP_ATTN || op == JSSA_OP_DECODE || op == JSSA_OP_DENSE) {
     const bool indexed = op != JSSA_OP_DENSE;

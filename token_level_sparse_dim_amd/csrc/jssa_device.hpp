@@ -181,10 +181,11 @@ __device__ __forceinline__ bool last_arrival(uint32_t* counter, uint32_t expecte
   return last;
 }
 
-// Block-wide exclusive prefix sum of one value per thread (blockDim.x == 256):
-// a shuffle scan inside each wave, then the four wave totals through `tmp`
-// (at least 4 words of shared memory).  Returns the exclusive prefix and the
+// Block-wide exclusive prefix sum of one value per thread (blockDim.x == 64 NW):
+// a shuffle scan inside each wave, then the NW wave totals through `tmp`
+// (at least NW words of shared memory).  Returns the exclusive prefix and the
 // block total through `total`.
+template <int NW = 4>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
@@ -197,7 +198,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* t
   __syncthreads();
   uint32_t before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const uint32_t c = tmp[w];
     before += (w < wave) ? c : 0u;
     all += c;

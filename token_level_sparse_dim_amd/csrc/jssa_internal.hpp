@@ -29,6 +29,7 @@ constexpr int kDigit1Bins = 1 << kDigit1Bits;
 constexpr int kMaxSelTiles = 4096;   // t_max <= kMaxSelTiles * kSelTile
 constexpr int kAttnBlock = 64;       // tokens per attention inner block (per workgroup pass)
 constexpr int kRowStateWords = 16;   // u32 words of per-row selection state
+constexpr int kCandPad = 128;        // candidate slots past the last row (read, never used)
 constexpr int kMaxPipeChunk = 1024;  // attention chunk limit of the fused decode
 // MLA layout: shared latent rows of kMlaDk elements, values = first kMlaDv
 constexpr int kMlaDk = 576;
@@ -71,6 +72,7 @@ struct Workspace {
   size_t idx = 0;        // i32 [rows][k+W]             (decode only)
   size_t n_sel = 0;      // i32 [rows]                  (decode only)
   size_t qfrag = 0;      // bf16 projected-query MFMA fragments (MLA score)
+  size_t pipe_qp = 0;    // f32 [rows][G][r] the rows' projected queries (fused decode)
   size_t total = 0;
   int n_chunks = 0;      // attention chunks per row
   int chunk = 0;         // tokens per attention chunk

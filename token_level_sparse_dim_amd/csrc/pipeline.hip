@@ -41,6 +41,9 @@ constexpr int kPipeNit = 4;            // workgroup steps per tile
 constexpr int kPipeMaxItem = 8192;     // tokens per score item at most (whole tiles)
 constexpr int kPipeCandLds = 8192;     // candidates resolved in shared memory
 constexpr int kPipeMaxTiles = 2048;    // tiles per row
+constexpr int kPipeCutList = 256;      // candidates of the cut's bin ranked directly (one per thread)
+constexpr int kPipeGatherTiles = 8;    // tiles per wave per gather round
+constexpr int kResolveThreads = 1024;  // threads of a resolve workgroup
 constexpr int kPipeAttnNL = 8;         // K and V row loads per lane per attention chunk
 
 // per-row state word of the scan (zero on entry and exit): u64 at words 12-13,
@@ -59,6 +62,7 @@ struct PipeArgs {
   const float* P;
   const void* kp;
   uint64_t* cand;      // [rows][t_max] candidate slots, ts entries per tile
+  float* qp_pub;       // [rows][G * r] projected queries, left by the sample for an exact re-selection
   uint32_t* tile_cnt;  // [rows][n_tiles]
   int G, d_k, topk, window, q_dtype, ts, n_tiles, n_rows, n_main, n_attn;
   int item, n_big, n_small;  // score runs: n_big runs of `item` tokens per row, then n_small single tiles
@@ -71,46 +75,107 @@ __device__ __forceinline__ void flag_error(const PipeArgs& a) { publish(a.at.que
 // flag set instead of hanging it).
 __device__ __forceinline__ bool past(uint64_t deadline) { return wall_clock64() > deadline; }
 
+// Inclusive prefix sum over the lanes of a wave.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  const uint32_t lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = uint32_t(__shfl_up(int(x), off));
+    if (lane >= uint32_t(off)) x += y;
+  }
+  return x;
+}
+
+// One wave: the bin of a 2048-bin histogram that holds the need-th largest
+// element, counting from the top; out[0] = the bin, out[1] = the number of
+// elements in higher bins (1 <= need <= total).  Lane l sums the 32 bins of
+// segment 63 - l (read from a per-lane rotation, so the lanes hit different
+// banks); a scan over the lanes finds the segment, whose 32 bins are then
+// spread over 32 lanes and scanned again.
+__device__ __forceinline__ void top_bin_wave(const uint32_t* hist, uint32_t need, uint32_t* out) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t seg = 63u - lane;
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) sum += hist[seg * 32u + ((uint32_t(j) + lane) & 31u)];
+  const uint32_t incl = wave_inclusive_scan(sum);
+  const uint64_t hit = __ballot(incl >= need);
+  const uint32_t l_star = hit ? uint32_t(__ffsll(static_cast<long long>(hit)) - 1) : 63u;  // first from the top
+  const uint32_t above = uint32_t(__builtin_amdgcn_readlane(int(incl - sum), int(l_star)));
+  const uint32_t seg_star = 63u - l_star;
+  // lane i < 32: bin seg_star * 32 + 31 - i (descending)
+  const uint32_t c = lane < 32u ? hist[seg_star * 32u + 31u - lane] : 0u;
+  const uint32_t incl2 = above + wave_inclusive_scan(c);
+  const uint64_t hit2 = __ballot(lane < 32u && incl2 >= need);
+  const uint32_t i_star = hit2 ? uint32_t(__ffsll(static_cast<long long>(hit2)) - 1) : 31u;
+  if (lane == i_star) {
+    out[0] = seg_star * 32u + 31u - i_star;
+    out[1] = incl2 - c;
+  }
+}
+
+// One wave: the bin of a 256-bin histogram that holds the need-th smallest
+// element, counting from the bottom; out[0] = the bin, out[1] = the number of
+// elements in lower bins (1 <= need <= total).  Lane l holds bins 4l .. 4l + 3.
+__device__ __forceinline__ void bottom_bin_wave(const uint32_t* hist, uint32_t need, uint32_t* out) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint4 c = reinterpret_cast<const uint4*>(hist)[lane];
+  const uint32_t sum = c.x + c.y + c.z + c.w;
+  const uint32_t incl = wave_inclusive_scan(sum);
+  const uint64_t hit = __ballot(incl >= need);
+  const uint32_t l_star = hit ? uint32_t(__ffsll(static_cast<long long>(hit)) - 1) : 63u;
+  if (lane == l_star) {
+    uint32_t cum = incl - sum, bin = 4u * lane + 3u;
+    if (cum + c.x >= need) bin = 4u * lane;
+    else if (cum + c.x + c.y >= need) { bin = 4u * lane + 1u; cum += c.x; }
+    else if (cum + c.x + c.y + c.z >= need) { bin = 4u * lane + 2u; cum += c.x + c.y; }
+    else cum += c.x + c.y + c.z;
+    out[0] = bin;
+    out[1] = cum;
+  }
+}
+
 // The need-th largest key among n candidates ((index << 32) | key, read via
 // `get`), with the tie cut: exactly `need` candidates satisfy
 // key > K* or (key == K* and index <= I*).  Radix digits of 11, 11 and 10 bits
-// over shared-memory histograms (`hist`: 2048 words); ties by the index bits
-// 23..16, 15..8, 7..0.  1 <= need <= n.
-template <typename Get>
-__device__ void kth_cut(Get get, uint32_t n, uint32_t need, bool want_ties, uint32_t* hist,
-                        uint32_t* scan, uint32_t* out, uint32_t* kstar_out, uint32_t* istar_out) {
+// over shared-memory histograms (`hist`: 2048 words, 16-byte aligned), each
+// digit's bin found by the first wave; ties by the index bits 23..16, 15..8,
+// 7..0.  1 <= need <= n; NT threads.
+template <int NT, typename Get>
+__device__ __forceinline__ void kth_cut(Get get, uint32_t n, uint32_t need, bool want_ties, uint32_t* hist,
+                                        uint32_t* out, uint32_t* kstar_out, uint32_t* istar_out) {
+  const uint32_t tid = threadIdx.x;
+  // one digit: `bin_of` maps a candidate to its bin, or to none (>= 2048)
+  auto digit = [&](auto bin_of) {
+    for (uint32_t i = tid; i < 2048u; i += NT) hist[i] = 0u;
+    __syncthreads();
+    for (uint32_t j = tid; j < n; j += NT) {
+      const uint32_t d = bin_of(get(j));
+      if (d < 2048u) atomicAdd(&hist[d], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) top_bin_wave(hist, need, out);
+    __syncthreads();
+    const uint32_t bin = out[0];
+    need -= out[1];
+    return bin;
+  };
   // digit A: bits 31..21
-  for (int i = threadIdx.x; i < 2048; i += 256) hist[i] = 0u;
-  __syncthreads();
-  for (uint32_t j = threadIdx.x; j < n; j += 256) atomicAdd(&hist[uint32_t(get(j)) >> 21], 1u);
-  __syncthreads();
-  find_bin_from_top<8>(hist, need, scan, out);
-  const uint32_t dA = out[0];
-  need -= out[1];
+  const uint32_t dA = digit([](uint64_t c) { return uint32_t(c) >> 21; });
   __syncthreads();
   // digit B: bits 20..10
-  for (int i = threadIdx.x; i < 2048; i += 256) hist[i] = 0u;
-  __syncthreads();
-  for (uint32_t j = threadIdx.x; j < n; j += 256) {
-    const uint32_t key = uint32_t(get(j));
-    if ((key >> 21) == dA) atomicAdd(&hist[(key >> 10) & 0x7ffu], 1u);
-  }
-  __syncthreads();
-  find_bin_from_top<8>(hist, need, scan, out);
-  const uint32_t hi22 = (dA << 11) | out[0];
-  need -= out[1];
+  const uint32_t dB = digit([&](uint64_t c) {
+    const uint32_t key = uint32_t(c);
+    return (key >> 21) == dA ? (key >> 10) & 0x7ffu : 2048u;
+  });
+  const uint32_t hi22 = (dA << 11) | dB;
   __syncthreads();
   // digit C: bits 9..0
-  for (int i = threadIdx.x; i < 1024; i += 256) hist[i] = 0u;
-  __syncthreads();
-  for (uint32_t j = threadIdx.x; j < n; j += 256) {
-    const uint32_t key = uint32_t(get(j));
-    if ((key >> 10) == hi22) atomicAdd(&hist[key & 0x3ffu], 1u);
-  }
-  __syncthreads();
-  find_bin_from_top<4>(hist, need, scan, out);
-  const uint32_t dC = out[0];
-  const uint32_t m_ties = need - out[1];
+  const uint32_t dC = digit([&](uint64_t c) {
+    const uint32_t key = uint32_t(c);
+    return (key >> 10) == hi22 ? key & 0x3ffu : 2048u;
+  });
+  const uint32_t m_ties = need;  // of the keys equal to K*, the m_ties lowest indices are taken
   const uint32_t n_eq = hist[dC];
   const uint32_t kstar = (hi22 << 10) | dC;
   __syncthreads();
@@ -118,16 +183,17 @@ __device__ void kth_cut(Get get, uint32_t n, uint32_t need, bool want_ties, uint
   if (want_ties && m_ties < n_eq) {
     uint32_t prefix = 0, m = m_ties;
     for (int shift = 16; shift >= 0; shift -= 8) {
-      hist[threadIdx.x] = 0u;
+      for (uint32_t i = tid; i < 256u; i += NT) hist[i] = 0u;
       __syncthreads();
-      for (uint32_t j = threadIdx.x; j < n; j += 256) {
+      for (uint32_t j = tid; j < n; j += NT) {
         const uint64_t c = get(j);
         const uint32_t t = uint32_t(c >> 32);
         if (uint32_t(c) == kstar && (t >> (shift + 8)) == (prefix >> (shift + 8)))
           atomicAdd(&hist[(t >> shift) & 0xffu], 1u);
       }
       __syncthreads();
-      find_bin_from_bottom<1>(hist, m, scan, out);
+      if (tid < 64) bottom_bin_wave(hist, m, out);
+      __syncthreads();
       prefix |= out[0] << shift;
       m -= out[1];
       __syncthreads();
@@ -152,6 +218,9 @@ __device__ __forceinline__ RowMode row_mode(const PipeArgs& a, int b) {
 }
 
 constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
+
+// 16 bytes at an 8-byte aligned address (two candidate slots)
+typedef uint32_t u32x4_a8 __attribute__((ext_vector_type(4), aligned(8)));
 
 // Projection of the group's queries: the G query rows and P[h] (in chunks of
 // at most 4096 floats, rows of d in order) are staged in shared memory with all
@@ -235,14 +304,14 @@ struct Pipe {
   static_assert(kPipeMaxItem % TS == 0, "score items are whole tiles");
   static constexpr int NW = kPipeNit * S::U;  // keys per lane per tile
   static constexpr int NSAMP = TS;            // sample size (one block of loads)
+  static constexpr int RT = kResolveThreads, RW = RT / 64;  // resolve workgroup: threads, waves
   using Qp = QpSmem<D, R, G>;
   using ASmem = Attn2Smem<KVT, D, G, kPipeAttnNL>;
 
   struct SampleSmem {
     Qp qp;
     uint32_t keys[NSAMP];
-    uint32_t hist[2048];
-    uint32_t scan[8];
+    alignas(16) uint32_t hist[2048];
     uint32_t out[2];
   };
   struct ScoreSmem {
@@ -254,11 +323,15 @@ struct Pipe {
     int claim;
   };
   struct ResolveSmem {
-    uint64_t cand[kPipeCandLds];  // (token << 32 | key) of the candidates by ordinal
-    uint32_t tab[kPipeMaxTiles];  // candidate prefix per tile
-    uint32_t hist[2048];          // histograms of the cut
-    uint32_t scan[8];
+    uint64_t cand[kPipeCandLds + 1];  // (token << 32 | key) of the candidates by ordinal; a dummy slot
+    uint32_t tab[kPipeMaxTiles];      // candidate prefix per tile
+    alignas(16) uint32_t hist[2048 + 1];  // histograms of the cut; a dummy bin
+    uint32_t bin_key[kPipeCutList], bin_ord[kPipeCutList];  // the candidates of the cut's bin
+    uint32_t wcnt[2][kPipeCandLds / 64];  // flagged candidates per 64 ordinals (two rounds)
+    uint32_t wsum[2][kResolveThreads / 64], wmin[kResolveThreads / 64], wmax[kResolveThreads / 64];
+    uint32_t scan[kResolveThreads / 64];
     uint32_t out[2];
+    uint32_t n_bin;
   };
   static constexpr size_t kSmemScan = cmax(sizeof(SampleSmem), sizeof(ScoreSmem));
   // the exact re-selection overlays ScoreSmem on ResolveSmem (only on ResolveSmem::cand)
@@ -312,6 +385,8 @@ struct Pipe {
         };
         uint4 v[HALF][S::U];
         project_query_staged<D, R, G>(a, b, h, sm.qp, [&] { load_half(0, v); });
+        // left for the resolve launch, in case the row has to be re-selected exactly
+        for (int j = threadIdx.x; j < G * R; j += 256) a.qp_pub[size_t(row) * G * R + j] = sm.qp.qp[j];
         QFrag<KPT, R, GE> qf;
         load_qfrag<KPT, R, GE>([&](int i) { return sm.qp.qp[i]; }, G, qf);
 #pragma unroll
@@ -332,8 +407,8 @@ struct Pipe {
         }
         __syncthreads();
         uint32_t kstar, istar;
-        kth_cut([&](uint32_t j) { return uint64_t(sm.keys[j]); }, uint32_t(n_samp), uint32_t(m), false,
-                sm.hist, sm.scan, sm.out, &kstar, &istar);
+        kth_cut<256>([&](uint32_t j) { return uint64_t(sm.keys[j]); }, uint32_t(n_samp), uint32_t(m), false,
+                     sm.hist, sm.out, &kstar, &istar);
         L = kstar;
       }
     }
@@ -371,6 +446,7 @@ struct Pipe {
   // workgroup that wrote them).  Each wave compacts whole tiles in rounds of 64
   // tokens (lane l takes token 64 k + l of round k, so the key reads are
   // conflict-free); a ballot per round gives the positions.
+  template <int NW = 4>
   static __device__ void emit_keys(const PipeArgs& a, int row, int t_begin, int t_end, uint32_t thr,
                                    const uint32_t* keys) {
     constexpr int PL = TS / 64;
@@ -378,7 +454,7 @@ struct Pipe {
     const int n_sub = (t_end - t_begin + TS - 1) / TS;
     const int tile0 = t_begin / TS;
     const unsigned long long below = (1ull << lane) - 1ull;
-    for (int s = wave; s < n_sub; s += 4) {
+    for (int s = wave; s < n_sub; s += NW) {
       const int t0 = t_begin + s * TS;
       const int n_tok = min(TS, t_end - t0);
       const uint32_t* kk = keys + s * TS;
@@ -466,67 +542,226 @@ struct Pipe {
   }
 
   // ---- RESOLVE (second launch) ------------------------------------------------------------
-  // Candidate counts of the row's tiles -> sm.tab (exclusive prefix); returns C.
-  static __device__ uint32_t count_candidates(const PipeArgs& a, int row, int n_tiles_row, ResolveSmem& sm) {
-    constexpr int PER = kPipeMaxTiles / 256;
-    const uint32_t* cnt = a.tile_cnt + size_t(row) * a.n_tiles;
-    uint32_t c[PER], local = 0;
+  // Gathers the row's candidates into shared memory by ordinal (token order).
+  // Each wave takes kPipeGatherTiles tiles a round and issues every load of the
+  // round at once: the tiles' counts (one per lane) and their first 128 slots
+  // (one 16-byte load per lane and tile: a tile's candidates are contiguous
+  // from the start of its slot; slots past the count are read but not used,
+  // and the candidate buffer has kCandPad slots past its last row, so no load
+  // needs a bound).  A shuffle scan of the counts and the four wave totals give
+  // the tiles' first ordinals, kept in sm.tab.  Stores of unused lanes go to a
+  // dummy slot.  Returns the number of candidates C; *kmin / *kmax: their
+  // smallest / largest key (C > 0).  FRESH: the slots and counts were
+  // rewritten by this workgroup after an earlier gather, so they are read
+  // with device-scope loads.
+  template <bool FRESH>
+  static __device__ __forceinline__ uint32_t gather(const PipeArgs& a, int row, int n_tiles_row, ResolveSmem& sm,
+                                                    uint32_t* kmin, uint32_t* kmax) {
+    constexpr int UB = kPipeGatherTiles;
+    const uint32_t lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const uint32_t* cnt_row = a.tile_cnt + size_t(row) * a.n_tiles;
+    const uint64_t* slots = a.cand + size_t(row) * a.at.t_max;
+    uint32_t run = 0, lo = 0xffffffffu, hi = 0u;
+    auto put = [&](bool ok, uint32_t pos, uint64_t c) {
+      const uint32_t key = uint32_t(c);
+      lo = min(lo, ok ? key : 0xffffffffu);
+      hi = max(hi, ok ? key : 0u);
+      sm.cand[(ok && pos < uint32_t(kPipeCandLds)) ? pos : uint32_t(kPipeCandLds)] = c;
+    };
+    int parity = 0;
+    for (int r0 = 0; r0 < n_tiles_row; r0 += RW * UB, parity ^= 1) {
+      const int t0 = r0 + wave * UB;
+      const int tl = min(t0 + int(lane & (UB - 1)), n_tiles_row - 1);
+      const bool own = lane < uint32_t(UB) && t0 + int(lane) < n_tiles_row;
+      uint32_t my_cnt = FRESH ? consume(cnt_row + tl) : cnt_row[tl];
+      my_cnt = own ? my_cnt : 0u;
+      uint64_t v0[UB], v1[UB];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int i = int(threadIdx.x) * PER + j;
-      c[j] = (i < n_tiles_row) ? consume(&cnt[i]) : 0u;
-      local += c[j];
-    }
-    uint32_t C;
-    uint32_t run = block_exclusive_scan(local, sm.scan, &C);
+      for (int u = 0; u < UB; ++u) {
+        const int t = min(t0 + u, n_tiles_row - 1);  // past the row's tiles: count 0
+        const uint64_t* src = slots + size_t(t) * TS + 2 * lane;
+        if (FRESH) {
+          v0[u] = consume(src);
+          v1[u] = consume(src + 1);
+        } else {
+          const u32x4_a8 w = *reinterpret_cast<const u32x4_a8*>(src);
+          v0[u] = uint64_t(w.x) | (uint64_t(w.y) << 32);
+          v1[u] = uint64_t(w.z) | (uint64_t(w.w) << 32);
+        }
+      }
+      uint32_t incl = my_cnt;  // inclusive scan over the lanes that own tiles
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      sm.tab[threadIdx.x * PER + j] = run;
-      run += c[j];
+      for (int off = 1; off < UB; off <<= 1) {
+        const uint32_t y = uint32_t(__shfl_up(int(incl), off));
+        incl += lane >= uint32_t(off) ? y : 0u;
+      }
+      sm.wsum[parity][wave] = uint32_t(__builtin_amdgcn_readlane(int(incl), UB - 1));
+      __syncthreads();
+      uint32_t wbase = run, rtot = 0;
+#pragma unroll
+      for (int w = 0; w < RW; ++w) {
+        const uint32_t c = sm.wsum[parity][w];
+        wbase += (w < wave) ? c : 0u;
+        rtot += c;
+      }
+      const uint32_t excl = incl - my_cnt;
+      if (own) sm.tab[t0 + lane] = wbase + excl;
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const uint32_t cnt_u = uint32_t(__builtin_amdgcn_readlane(int(my_cnt), u));
+        const uint32_t base_u = wbase + uint32_t(__builtin_amdgcn_readlane(int(excl), u));
+        put(2u * lane < cnt_u, base_u + 2u * lane, v0[u]);
+        put(2u * lane + 1u < cnt_u, base_u + 2u * lane + 1u, v1[u]);
+        if (cnt_u > 128u) {  // a crowded tile: the rest of its slot
+          const uint64_t* src = slots + size_t(t0 + u) * TS;
+          for (uint32_t i = lane + 128u; i < cnt_u; i += 64u) put(true, base_u + i, FRESH ? consume(src + i) : src[i]);
+        }
+      }
+      run += rtot;
     }
-    __syncthreads();
-    return C;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      lo = min(lo, uint32_t(__shfl_xor(int(lo), off)));
+      hi = max(hi, uint32_t(__shfl_xor(int(hi), off)));
+    }
+    sm.wmin[wave] = lo;
+    sm.wmax[wave] = hi;
+    __syncthreads();  // also: every gathered candidate is in shared memory
+    lo = 0xffffffffu;
+    hi = 0u;
+#pragma unroll
+    for (int w = 0; w < RW; ++w) {
+      lo = min(lo, sm.wmin[w]);
+      hi = max(hi, sm.wmax[w]);
+    }
+    *kmin = lo;
+    *kmax = hi;
+    return run;
   }
 
   // The sampled threshold let fewer than kk tokens through: rebuild the row's
   // candidate slots exactly (every key in or above the k-th key's top 11-bit
   // bin), scanning the row twice: once for the histogram of that digit, once
-  // to write the candidates.
+  // to write the candidates.  The scores are the scan's: the group's projected
+  // queries left by the sample, the same per-wave arithmetic, with the
+  // workgroup's four-wave groups taking the steps of an item in turn.
   static __device__ __forceinline__ void exact_candidates(const PipeArgs& a, int row, const RowMode& md, char* smem) {
-    const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
+    constexpr int NT = RT, NWG = RT / 256;
+    const uint32_t tid = threadIdx.x;
     ScoreSmem& ss = *reinterpret_cast<ScoreSmem*>(smem);
     ResolveSmem& rs = *reinterpret_cast<ResolveSmem*>(smem);
-    project_query_staged<D, R, G>(a, b, h, ss.qp, [] {});
+    const float* qp = a.qp_pub + size_t(row) * G * R;
     QFrag<KPT, R, GE> qf;
-    load_qfrag<KPT, R, GE>([&](int i) { return ss.qp.qp[i]; }, G, qf);
-    for (int i = threadIdx.x; i < 2048; i += 256) rs.hist[i] = 0u;
+    load_qfrag<KPT, R, GE>([&](int i) { return qp[i]; }, G, qf);
+    for (uint32_t i = tid; i < 2048u; i += NT) rs.hist[i] = 0u;
     __syncthreads();
     const char* kr = kp_row(a, row);
+    const int group = int(tid) >> 8;
     for (int pass = 0; pass < 2; ++pass) {
       uint32_t thr = 0;
       if (pass == 1) {
-        find_bin_from_top<8>(rs.hist, uint32_t(md.kk), rs.scan, rs.out);
+        if (tid < 64) top_bin_wave(rs.hist, uint32_t(md.kk), rs.out);
+        __syncthreads();
         thr = rs.out[0] << 21;
         __syncthreads();
       }
       for (int t_begin = 0; t_begin < md.n_cand; t_begin += kPipeMaxItem) {
         const int t_end = min(t_begin + kPipeMaxItem, md.n_cand);
-        uint4 b0[S::U];
-        load_step(kr, t_begin, t_end, b0);
-        scan_keys(kr, t_begin, t_end, qf, b0, ss.keys);
+        const int n_steps = (t_end - t_begin + S::PER_ITER - 1) / S::PER_ITER;
+        for (int st = group; st < n_steps; st += NWG) {
+          uint4 v[S::U];
+          load_step(kr, t_begin + st * S::PER_ITER, t_end, v);
+          uint32_t* kst = ss.keys + st * S::PER_ITER;
+          score_loads<KPT, R, GE>(v, qf, G, [&](int toff, float sc) { kst[toff] = score_key(sc); });
+        }
         __syncthreads();
         if (pass == 0) {
-          for (int i = threadIdx.x; i < t_end - t_begin; i += 256) atomicAdd(&rs.hist[ss.keys[i] >> 21], 1u);
+          for (int i = int(tid); i < t_end - t_begin; i += NT) atomicAdd(&rs.hist[ss.keys[i] >> 21], 1u);
         } else {
-          emit_keys(a, row, t_begin, t_end, thr, ss.keys);
+          emit_keys<NT / 64>(a, row, t_begin, t_end, thr, ss.keys);
         }
         __syncthreads();
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_add(a.at.queue + PQ_FALLBACK, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_fetch_add(a.at.queue + PQ_FALLBACK, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // Candidate ordinals in shared memory are spread over the RT threads in
+  // rounds: ordinal RT i + threadIdx.x belongs to round i, so every pass reads
+  // them contiguously.  word_offsets() gives, for a per-ordinal flag, the
+  // number of flagged ordinals before each wave's 64 ordinals of each round
+  // (one barrier; `buf` alternates between calls): the counts of the RW nper
+  // words of 64 ordinals, a scan of them in every wave, then a readlane per
+  // round.
+  template <int MAXPER, typename Flag>
+  static __device__ __forceinline__ void word_offsets(ResolveSmem& sm, int nper, int buf, Flag flag, uint32_t (&off)[MAXPER]) {
+    const uint32_t lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+      if (i >= nper) break;
+      sm.wcnt[buf][RW * i + wave] = uint32_t(__popcll(__ballot(flag(i))));  // every lane: the same word
+    }
+    __syncthreads();
+    const int nw = RW * nper;  // <= kPipeCandLds / 64: two words per lane at most
+    const uint32_t c0 = int(2 * lane) < nw ? sm.wcnt[buf][2 * lane] : 0u;
+    const uint32_t c1 = int(2 * lane + 1) < nw ? sm.wcnt[buf][2 * lane + 1] : 0u;
+    const uint32_t incl = wave_inclusive_scan(c0 + c1);
+    const uint32_t ex = (wave & 1) ? incl - c1 : incl - c0 - c1;  // this wave's words have its parity
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+      if (i >= nper) break;
+      off[i] = uint32_t(__builtin_amdgcn_readlane(int(ex), (RW * i + wave) >> 1));
+    }
+  }
+
+  // The cut (K*, I*) when the k-th key's bin of the first digit is too crowded
+  // to rank directly: radix passes of 11 bits over d = key - kmin from the top
+  // set bit of kmax - kmin down give K*; the `need` lowest ordinals among the
+  // keys equal to K* give I*.
+  template <int MAXPER>
+  static __device__ __forceinline__ void cut_by_passes(ResolveSmem& sm, const uint32_t (&kv)[MAXPER], int nper, uint32_t C,
+                                       uint32_t kmin, uint32_t kmax, uint32_t need, uint32_t* kstar_out,
+                                       uint32_t* istar_out) {
+    const uint32_t tid = threadIdx.x;
+    const int nbits = kmax > kmin ? 32 - __clz(kmax - kmin) : 1;
+    uint32_t prefix = 0;  // the digits of d* found so far
+    for (int hi = nbits; hi > 0; hi -= 11) {
+      const int sh = hi > 11 ? hi - 11 : 0;
+      for (int i = threadIdx.x; i < 2048; i += RT) sm.hist[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < MAXPER; ++i) {
+        if (i >= nper) break;
+        const uint32_t dv = kv[i] - kmin;
+        const bool in = uint32_t(i) * RT + tid < C && (hi >= 32 || (dv >> hi) == (prefix >> hi));
+        atomicAdd(&sm.hist[in ? (dv >> sh) & 0x7ffu : 2048u], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) top_bin_wave(sm.hist, need, sm.out);
+      __syncthreads();
+      prefix |= sm.out[0] << sh;
+      need -= sm.out[1];
+      __syncthreads();
+    }
+    const uint32_t kstar = prefix + kmin;
+    auto eq = [&](int i) { return uint32_t(i) * RT + tid < C && kv[i] == kstar; };
+    uint32_t off[MAXPER];
+    word_offsets<MAXPER>(sm, nper, 0, eq, off);
+    const uint64_t below = (1ull << (tid & 63)) - 1ull;
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+      if (i >= nper) break;
+      const bool e = eq(i);
+      const uint64_t mk = __ballot(e);
+      if (e && off[i] + uint32_t(__popcll(mk & below)) == need - 1u) sm.out[1] = uint32_t(i) * RT + tid;
+    }
+    __syncthreads();
+    *kstar_out = kstar;
+    *istar_out = sm.out[1];
   }
 
   static __device__ __forceinline__ void resolve_select(const PipeArgs& a, int row, const RowMode& md, char* smem) {
@@ -536,152 +771,143 @@ struct Pipe {
       *l_word(a, row) = 0;
       state(a, row)[PW_STEAL] = 0;
     }
-    for (int j = threadIdx.x; j < md.nW; j += 256) out[md.kk + j] = uint32_t(md.Tb - md.nW + j);
+    for (int j = threadIdx.x; j < md.nW; j += RT) out[md.kk + j] = uint32_t(md.Tb - md.nW + j);
     if (threadIdx.x == 0) const_cast<int32_t*>(a.at.n_sel)[row] = md.kk + md.nW;
     const int n_tiles_row = (md.n_cand + TS - 1) / TS;
-    uint32_t C = count_candidates(a, row, n_tiles_row, sm);
+    // the first digit's histogram is cleared while the gather's loads are in flight
+    for (int i = threadIdx.x; i < 2048; i += RT) sm.hist[i] = 0u;
+    if (threadIdx.x == 0) sm.n_bin = 0u;
+    uint32_t kmin, kmax;
+    uint32_t C = gather<false>(a, row, n_tiles_row, sm, &kmin, &kmax);
     if (C < uint32_t(md.kk)) {
       exact_candidates(a, row, md, smem);
-      C = count_candidates(a, row, n_tiles_row, sm);
+      for (int i = threadIdx.x; i < 2048; i += RT) sm.hist[i] = 0u;
+      if (threadIdx.x == 0) sm.n_bin = 0u;
+      C = gather<true>(a, row, n_tiles_row, sm, &kmin, &kmax);
     }
-    // the slots were written by the scan launch, or by this workgroup's exact
-    // re-selection: plain loads see them
-    const uint64_t* slots = a.cand + size_t(row) * a.at.t_max;
-    auto global_cand = [&](uint32_t j) {
-      const uint32_t tile = last_le(sm.tab, uint32_t(n_tiles_row), j);
-      return slots[size_t(tile) * TS + (j - sm.tab[tile])];
-    };
+    const uint32_t need = uint32_t(md.kk);  // 1 <= need <= C
     uint32_t kstar, istar;
     if (C <= uint32_t(kPipeCandLds)) {
-      // Gather every candidate into shared memory by ordinal.  Wave w copies
-      // tiles [UB w, UB w + UB) of each round: a tile's candidates are
-      // contiguous in its slot, so two wave loads move up to 128 of them; the
-      // tiles' boundaries come from one shared-memory read (lane u holds tile
-      // u's) and readlane, and every load of a round is issued before the
-      // first store.
-      {
-        constexpr int UB = 16;
-        const uint32_t lane = threadIdx.x & 63;
-        const int wave = threadIdx.x >> 6;
-        for (int r0 = wave * UB; r0 < n_tiles_row; r0 += 4 * UB) {
-          const int tl = r0 + int(lane);
-          const uint32_t tb = (lane <= uint32_t(UB) && tl < n_tiles_row) ? sm.tab[tl] : C;
-          uint64_t v0[UB], v1[UB];
-          uint32_t base[UB], cnt_t[UB];
-#pragma unroll
-          for (int u = 0; u < UB; ++u) {
-            base[u] = uint32_t(__builtin_amdgcn_readlane(int(tb), u));
-            cnt_t[u] = uint32_t(__builtin_amdgcn_readlane(int(tb), u + 1)) - base[u];  // 0 past the row's tiles
-            const uint64_t* src = slots + size_t(r0 + u) * TS;
-            v0[u] = lane < cnt_t[u] ? src[lane] : 0ull;
-            v1[u] = lane + 64u < cnt_t[u] ? src[lane + 64u] : 0ull;
-          }
-#pragma unroll
-          for (int u = 0; u < UB; ++u) {
-            if (lane < cnt_t[u]) sm.cand[base[u] + lane] = v0[u];
-            if (lane + 64u < cnt_t[u]) sm.cand[base[u] + lane + 64u] = v1[u];
-            for (uint32_t i = lane + 128u; i < cnt_t[u]; i += 64u)  // tiles with more than 128 candidates
-              sm.cand[base[u] + i] = slots[size_t(r0 + u) * TS + i];
-          }
-        }
-      }
-      __syncthreads();
-      // Thread x owns the contiguous run of candidate ordinals [j0, j1): their
-      // keys stay in registers for every pass of the cut.  Candidates are in
-      // token order, so ranking equal keys by ordinal ranks them by token index.
-      constexpr int MAXPER = kPipeCandLds / 256;
-      const uint32_t per = (C + 255) / 256;
-      const uint32_t j0 = min(C, uint32_t(threadIdx.x) * per), j1 = min(C, j0 + per);
-      const int cnt = int(j1 - j0);
+      // Ordinal RT i + threadIdx.x in round i; its key stays in kv[i].
+      // Candidates are in token order, so ranking equal keys by ordinal ranks
+      // them by token index.
+      constexpr int MAXPER = kPipeCandLds / RT;
+      const uint32_t tid = threadIdx.x, lane = tid & 63;
+      const int nper = int((C + RT - 1) / RT);
       uint32_t kv[MAXPER];
 #pragma unroll
-      for (int i = 0; i < MAXPER; ++i) kv[i] = i < cnt ? uint32_t(sm.cand[j0 + i]) : 0u;
-      // Radix digits of d = key - (smallest candidate key): the candidates sit
-      // in a narrow band at the top, so digits of the key itself would pile
-      // them into a few bins.  Passes of 11 bits from the top set bit of the
-      // largest d down.
-      uint32_t kmin = 0xffffffffu, kmax = 0u;
-#pragma unroll
-      for (int i = 0; i < MAXPER; ++i)
-        if (i < cnt) {
-          kmin = min(kmin, kv[i]);
-          kmax = max(kmax, kv[i]);
-        }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), off)));
-        kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), off)));
+      for (int i = 0; i < MAXPER; ++i) {
+        const uint32_t o = uint32_t(i) * RT + tid;
+        kv[i] = i < nper ? uint32_t(sm.cand[min(o, uint32_t(kPipeCandLds))]) : 0u;
       }
-      if ((threadIdx.x & 63) == 0) {
-        sm.scan[threadIdx.x >> 6] = kmin;
-        sm.scan[4 + (threadIdx.x >> 6)] = kmax;
-      }
-      __syncthreads();
-      kmin = min(min(sm.scan[0], sm.scan[1]), min(sm.scan[2], sm.scan[3]));
-      kmax = max(max(sm.scan[4], sm.scan[5]), max(sm.scan[6], sm.scan[7]));
-      __syncthreads();
+      auto live = [&](int i) { return uint32_t(i) * RT + tid < C; };
+      // One digit: the top 11 bits of d = key - kmin (the candidates sit in a
+      // narrow band at the top, so digits of the key itself would pile them
+      // into a few bins).  Everything above the k-th key's bin is taken; the
+      // bin's own candidates are ranked directly, by key and then ordinal.
       const int nbits = kmax > kmin ? 32 - __clz(kmax - kmin) : 1;
-      uint32_t need = uint32_t(md.kk), prefix = 0;  // prefix: the digits of d* found so far
-      for (int hi = nbits; hi > 0; hi -= 11) {
-        const int sh = hi > 11 ? hi - 11 : 0;
-        for (int i = threadIdx.x; i < 2048; i += 256) sm.hist[i] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < MAXPER; ++i) {
-          const uint32_t dv = kv[i] - kmin;
-          if (i < cnt && (hi >= 32 || (dv >> hi) == (prefix >> hi))) atomicAdd(&sm.hist[(dv >> sh) & 0x7ffu], 1u);
-        }
-        __syncthreads();
-        find_bin_from_top<8>(sm.hist, need, sm.scan, sm.out);
-        prefix |= sm.out[0] << sh;
-        need -= sm.out[1];
-        __syncthreads();
-      }
-      prefix += kmin;
-      kstar = prefix;
-      // ties: the `need` lowest ordinals among the keys equal to K* are taken
-      uint32_t eq = 0;
-#pragma unroll
-      for (int i = 0; i < MAXPER; ++i) eq += (i < cnt && kv[i] == kstar) ? 1u : 0u;
-      uint32_t n_eq;
-      const uint32_t eq_before = block_exclusive_scan(eq, sm.scan, &n_eq);
-      if (threadIdx.x == 0) sm.out[0] = 0xffffffffu;
-      __syncthreads();
-      if (need < n_eq && eq_before < need && need <= eq_before + eq) {
-        uint32_t seen = eq_before;
-#pragma unroll
-        for (int i = 0; i < MAXPER; ++i)
-          if (i < cnt && kv[i] == kstar && ++seen == need) sm.out[0] = j0 + uint32_t(i);
-      }
-      __syncthreads();
-      istar = sm.out[0];
-      // emission in token order
-      uint32_t mine = 0;
-#pragma unroll
-      for (int i = 0; i < MAXPER; ++i)
-        mine += (i < cnt && (kv[i] > kstar || (kv[i] == kstar && j0 + uint32_t(i) <= istar))) ? 1u : 0u;
-      uint32_t total;
-      uint32_t pos = block_exclusive_scan(mine, sm.scan, &total);
+      const int sh = nbits > 11 ? nbits - 11 : 0;
 #pragma unroll
       for (int i = 0; i < MAXPER; ++i) {
-        if (i < cnt && (kv[i] > kstar || (kv[i] == kstar && j0 + uint32_t(i) <= istar))) {
-          if (pos < uint32_t(md.kk)) out[pos] = uint32_t(sm.cand[j0 + i] >> 32);
-          ++pos;
+        if (i >= nper) break;
+        atomicAdd(&sm.hist[live(i) ? (kv[i] - kmin) >> sh : 2048u], 1u);  // dead lanes: the dummy bin
+      }
+      __syncthreads();
+      if (tid < 64) top_bin_wave(sm.hist, need, sm.out);
+      __syncthreads();
+      const uint32_t bin = sm.out[0];
+      const uint32_t need_bin = need - sm.out[1];  // 1 <= need_bin <= the bin's count
+      // the bin's candidates, listed a wave at a time
+      const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+      for (int i = 0; i < MAXPER; ++i) {
+        if (i >= nper) break;
+        const bool inb = live(i) && ((kv[i] - kmin) >> sh) == bin;
+        const uint64_t mk = __ballot(inb);
+        if (mk) {
+          uint32_t b0 = 0;
+          if (lane == 0) b0 = atomicAdd(&sm.n_bin, uint32_t(__popcll(mk)));
+          b0 = uint32_t(__builtin_amdgcn_readfirstlane(int(b0))) + uint32_t(__popcll(mk & below));
+          if (inb && b0 < uint32_t(kPipeCutList)) {
+            sm.bin_key[b0] = kv[i];
+            sm.bin_ord[b0] = uint32_t(i) * RT + tid;
+          }
         }
+      }
+      __syncthreads();
+      const uint32_t m = uint32_t(__builtin_amdgcn_readfirstlane(int(sm.n_bin)));
+      if (m <= 64u) {
+        // one wave: lane j holds the bin's j-th candidate; ranks by readlane
+        if (tid < 64) {
+          const uint32_t k = lane < m ? sm.bin_key[lane] : 0u;
+          const uint32_t o = lane < m ? sm.bin_ord[lane] : 0xffffffffu;
+          uint32_t rank = 0;
+          for (uint32_t j = 0; j < m; ++j) {
+            const uint32_t kj = uint32_t(__builtin_amdgcn_readlane(int(k), int(j)));
+            const uint32_t oj = uint32_t(__builtin_amdgcn_readlane(int(o), int(j)));
+            rank += (kj > k || (kj == k && oj < o)) ? 1u : 0u;
+          }
+          if (lane < m && rank == need_bin - 1u) {
+            sm.out[0] = k;
+            sm.out[1] = o;
+          }
+        }
+        __syncthreads();
+        kstar = sm.out[0];
+        istar = sm.out[1];
+      } else if (m <= uint32_t(kPipeCutList)) {
+        if (tid < m) {
+          const uint32_t k = sm.bin_key[tid], o = sm.bin_ord[tid];
+          uint32_t rank = 0;
+          for (uint32_t j = 0; j < m; ++j) {
+            const uint32_t kj = sm.bin_key[j], oj = sm.bin_ord[j];
+            rank += (kj > k || (kj == k && oj < o)) ? 1u : 0u;
+          }
+          if (rank == need_bin - 1u) {
+            sm.out[0] = k;
+            sm.out[1] = o;
+          }
+        }
+        __syncthreads();
+        kstar = sm.out[0];
+        istar = sm.out[1];
+      } else {
+        cut_by_passes<MAXPER>(sm, kv, nper, C, kmin, kmax, need, &kstar, &istar);
+      }
+      // emission in token order: a ballot per 64 ordinals places each taken
+      // candidate, so each wave store covers one run of consecutive positions
+      auto take = [&](int i) {
+        const uint32_t o = uint32_t(i) * RT + tid;
+        return o < C && (kv[i] > kstar || (kv[i] == kstar && o <= istar));
+      };
+      uint32_t off[MAXPER];
+      word_offsets<MAXPER>(sm, nper, 1, take, off);
+#pragma unroll
+      for (int i = 0; i < MAXPER; ++i) {
+        if (i >= nper) break;
+        const bool t = take(i);
+        const uint64_t mk = __ballot(t);
+        const uint32_t pos = off[i] + uint32_t(__popcll(mk & below));
+        if (t && pos < need) out[pos] = uint32_t(sm.cand[uint32_t(i) * RT + tid] >> 32);
       }
     } else {
       // more candidates than shared memory holds: every pass reads them in place
-      kth_cut(global_cand, C, uint32_t(md.kk), true, sm.hist, sm.scan, sm.out, &kstar, &istar);
-      const uint32_t per = (C + 255) / 256;
+      const uint64_t* slots = a.cand + size_t(row) * a.at.t_max;
+      auto global_cand = [&](uint32_t j) {
+        const uint32_t tile = last_le(sm.tab, uint32_t(n_tiles_row), j);
+        return slots[size_t(tile) * TS + (j - sm.tab[tile])];
+      };
+      kth_cut<RT>(global_cand, C, need, true, sm.hist, sm.out, &kstar, &istar);
+      const uint32_t per = (C + RT - 1) / RT;
       const uint32_t j0 = threadIdx.x * per, j1 = min(C, j0 + per);
       uint32_t mine = 0;
       for (uint32_t j = j0; j < j1; ++j) mine += passes(global_cand(j), kstar, istar);
       uint32_t total;
-      uint32_t pos = block_exclusive_scan(mine, sm.scan, &total);
+      uint32_t pos = block_exclusive_scan<RW>(mine, sm.scan, &total);
       for (uint32_t j = j0; j < j1; ++j) {
         const uint64_t c = global_cand(j);
         if (passes(c, kstar, istar)) {
-          if (pos < uint32_t(md.kk)) out[pos] = uint32_t(c >> 32);
+          if (pos < need) out[pos] = uint32_t(c >> 32);
           ++pos;
         }
       }
@@ -750,7 +976,7 @@ __global__ __launch_bounds__(256, 3) void scan_kernel(PipeArgs a) {
 
 // Resolve launch: one workgroup per (sequence, KV head) row.
 template <int KPT, int R, int GE, int D, int G, int KVT>
-__global__ __launch_bounds__(256, 1) void resolve_kernel(PipeArgs a) {
+__global__ __launch_bounds__(kResolveThreads, 1) void resolve_kernel(PipeArgs a) {
   using Pp = Pipe<KPT, R, GE, D, G, KVT>;
   __shared__ __align__(16) char smem[Pp::kSmemResolve];
   const int row = blockIdx.x;
@@ -863,7 +1089,7 @@ static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((scan_kernel<KPT, R, GE, D, G, KVT>), dim3(grid), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess) return e;
-  hipLaunchKernelGGL((resolve_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_rows), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((resolve_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_rows), dim3(kResolveThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess) return e;
   hipLaunchKernelGGL((attend_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_attn), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -897,6 +1123,7 @@ hipError_t launch_pipeline(const jssa_desc& d, const void* q, const float* P, co
   at.n_resolve = 0; at.attend = 1;
   a.P = P; a.kp = kp;
   a.cand = reinterpret_cast<uint64_t*>(ws_base + ws.cand);
+  a.qp_pub = reinterpret_cast<float*>(ws_base + ws.pipe_qp);
   a.tile_cnt = reinterpret_cast<uint32_t*>(ws_base + ws.tile_cnt);
   a.G = d.n_q_heads / d.n_kv_heads; a.d_k = d.d_k; a.topk = d.topk; a.window = d.window;
   a.q_dtype = d.kv_dtype; a.ts = ws.pipe_ts; a.n_tiles = ws.pipe_tiles;

@@ -42,10 +42,12 @@ constexpr int kQTerms = 3;  // bf16 terms per fp32 query coordinate (matrix-core
 
 // Token (offset within a workgroup step) and byte (within the token's row) of
 // this lane's u-th load.
+// (Waves 4 w' + j of a wider workgroup take the loads of wave j: the scores of
+// a token do not depend on which wave forms them.)
 template <int KPT, int R>
 __device__ __forceinline__ int slot_token(int u) {
   using S = ScanShape<KPT, R>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3;
   if constexpr (S::MF) return (wave * (S::U / S::KS) + u / S::KS) * 16 + (lane & 15);
   else return (wave * S::U + u) * S::TPW + lane / S::LPT;
 }
