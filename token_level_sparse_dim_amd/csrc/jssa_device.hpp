@@ -181,19 +181,43 @@ __device__ __forceinline__ bool last_arrival(uint32_t* counter, uint32_t expecte
   return last;
 }
 
+// ---- wave-wide scans and reductions through DPP ---------------------------------------
+// Row shifts by 1, 2, 4 and 8 give the inclusive scan inside each row of 16
+// lanes; the last lane of rows 0 and 2 is then broadcast into rows 1 and 3
+// (row_bcast:15), and lane 31 into rows 2 and 3 (row_bcast:31).  Lanes whose
+// source is outside the row take the operation's identity.
+template <typename Op>
+__device__ __forceinline__ uint32_t dpp_scan(uint32_t x, uint32_t id, Op op) {
+  x = op(x, uint32_t(__builtin_amdgcn_update_dpp(int(id), int(x), 0x111, 0xf, 0xf, false)));
+  x = op(x, uint32_t(__builtin_amdgcn_update_dpp(int(id), int(x), 0x112, 0xf, 0xf, false)));
+  x = op(x, uint32_t(__builtin_amdgcn_update_dpp(int(id), int(x), 0x114, 0xf, 0xf, false)));
+  x = op(x, uint32_t(__builtin_amdgcn_update_dpp(int(id), int(x), 0x118, 0xf, 0xf, false)));
+  x = op(x, uint32_t(__builtin_amdgcn_update_dpp(int(id), int(x), 0x142, 0xa, 0xf, false)));
+  x = op(x, uint32_t(__builtin_amdgcn_update_dpp(int(id), int(x), 0x143, 0xc, 0xf, false)));
+  return x;
+}
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x) {
+  return dpp_scan(x, 0u, [](uint32_t u, uint32_t v) { return u + v; });
+}
+// Minimum / maximum over the 64 lanes (the same value in every lane).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = dpp_scan(x, 0xffffffffu, [](uint32_t u, uint32_t v) { return u < v ? u : v; });
+  return uint32_t(__builtin_amdgcn_readlane(int(x), 63));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = dpp_scan(x, 0u, [](uint32_t u, uint32_t v) { return u > v ? u : v; });
+  return uint32_t(__builtin_amdgcn_readlane(int(x), 63));
+}
+
 // Block-wide exclusive prefix sum of one value per thread (blockDim.x == 64 NW):
-// a shuffle scan inside each wave, then the NW wave totals through `tmp`
+// a DPP scan inside each wave, then the NW wave totals through `tmp`
 // (at least NW words of shared memory).  Returns the exclusive prefix and the
 // block total through `total`.
 template <int NW = 4>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  const uint32_t x = wave_scan_incl(v);
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
   uint32_t before = 0, all = 0;

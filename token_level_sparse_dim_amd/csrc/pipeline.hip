@@ -75,17 +75,6 @@ __device__ __forceinline__ void flag_error(const PipeArgs& a) { publish(a.at.que
 // flag set instead of hanging it).
 __device__ __forceinline__ bool past(uint64_t deadline) { return wall_clock64() > deadline; }
 
-// Inclusive prefix sum over the lanes of a wave.
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
-  const uint32_t lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = uint32_t(__shfl_up(int(x), off));
-    if (lane >= uint32_t(off)) x += y;
-  }
-  return x;
-}
-
 // One wave: the bin of a 2048-bin histogram that holds the need-th largest
 // element, counting from the top; out[0] = the bin, out[1] = the number of
 // elements in higher bins (1 <= need <= total).  Lane l sums the 32 bins of
@@ -98,14 +87,14 @@ __device__ __forceinline__ void top_bin_wave(const uint32_t* hist, uint32_t need
   uint32_t sum = 0;
 #pragma unroll
   for (int j = 0; j < 32; ++j) sum += hist[seg * 32u + ((uint32_t(j) + lane) & 31u)];
-  const uint32_t incl = wave_inclusive_scan(sum);
+  const uint32_t incl = wave_scan_incl(sum);
   const uint64_t hit = __ballot(incl >= need);
   const uint32_t l_star = hit ? uint32_t(__ffsll(static_cast<long long>(hit)) - 1) : 63u;  // first from the top
   const uint32_t above = uint32_t(__builtin_amdgcn_readlane(int(incl - sum), int(l_star)));
   const uint32_t seg_star = 63u - l_star;
   // lane i < 32: bin seg_star * 32 + 31 - i (descending)
   const uint32_t c = lane < 32u ? hist[seg_star * 32u + 31u - lane] : 0u;
-  const uint32_t incl2 = above + wave_inclusive_scan(c);
+  const uint32_t incl2 = above + wave_scan_incl(c);
   const uint64_t hit2 = __ballot(lane < 32u && incl2 >= need);
   const uint32_t i_star = hit2 ? uint32_t(__ffsll(static_cast<long long>(hit2)) - 1) : 31u;
   if (lane == i_star) {
@@ -121,7 +110,7 @@ __device__ __forceinline__ void bottom_bin_wave(const uint32_t* hist, uint32_t n
   const uint32_t lane = threadIdx.x & 63;
   const uint4 c = reinterpret_cast<const uint4*>(hist)[lane];
   const uint32_t sum = c.x + c.y + c.z + c.w;
-  const uint32_t incl = wave_inclusive_scan(sum);
+  const uint32_t incl = wave_scan_incl(sum);
   const uint64_t hit = __ballot(incl >= need);
   const uint32_t l_star = hit ? uint32_t(__ffsll(static_cast<long long>(hit)) - 1) : 63u;
   if (lane == l_star) {
@@ -326,7 +315,8 @@ struct Pipe {
     uint64_t cand[kPipeCandLds + 1];  // (token << 32 | key) of the candidates by ordinal; a dummy slot
     uint32_t tab[kPipeMaxTiles];      // candidate prefix per tile
     alignas(16) uint32_t hist[2048 + 1];  // histograms of the cut; a dummy bin
-    uint32_t bin_key[kPipeCutList], bin_ord[kPipeCutList];  // the candidates of the cut's bin
+    alignas(16) uint32_t bin_key[kPipeCutList];  // the candidates of the cut's bin: keys
+    alignas(16) uint32_t bin_ord[kPipeCutList];  // and ordinals
     uint32_t wcnt[2][kPipeCandLds / 64];  // flagged candidates per 64 ordinals (two rounds)
     uint32_t wsum[2][kResolveThreads / 64], wmin[kResolveThreads / 64], wmax[kResolveThreads / 64];
     uint32_t scan[kResolveThreads / 64];
@@ -590,12 +580,7 @@ struct Pipe {
           v1[u] = uint64_t(w.z) | (uint64_t(w.w) << 32);
         }
       }
-      uint32_t incl = my_cnt;  // inclusive scan over the lanes that own tiles
-#pragma unroll
-      for (int off = 1; off < UB; off <<= 1) {
-        const uint32_t y = uint32_t(__shfl_up(int(incl), off));
-        incl += lane >= uint32_t(off) ? y : 0u;
-      }
+      const uint32_t incl = wave_scan_incl(my_cnt);  // over the lanes that own tiles
       sm.wsum[parity][wave] = uint32_t(__builtin_amdgcn_readlane(int(incl), UB - 1));
       __syncthreads();
       uint32_t wbase = run, rtot = 0;
@@ -620,11 +605,8 @@ struct Pipe {
       }
       run += rtot;
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      lo = min(lo, uint32_t(__shfl_xor(int(lo), off)));
-      hi = max(hi, uint32_t(__shfl_xor(int(hi), off)));
-    }
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
     sm.wmin[wave] = lo;
     sm.wmax[wave] = hi;
     __syncthreads();  // also: every gathered candidate is in shared memory
@@ -709,7 +691,7 @@ struct Pipe {
     const int nw = RW * nper;  // <= kPipeCandLds / 64: two words per lane at most
     const uint32_t c0 = int(2 * lane) < nw ? sm.wcnt[buf][2 * lane] : 0u;
     const uint32_t c1 = int(2 * lane + 1) < nw ? sm.wcnt[buf][2 * lane + 1] : 0u;
-    const uint32_t incl = wave_inclusive_scan(c0 + c1);
+    const uint32_t incl = wave_scan_incl(c0 + c1);
     const uint32_t ex = (wave & 1) ? incl - c1 : incl - c0 - c1;  // this wave's words have its parity
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
@@ -837,15 +819,19 @@ struct Pipe {
       __syncthreads();
       const uint32_t m = uint32_t(__builtin_amdgcn_readfirstlane(int(sm.n_bin)));
       if (m <= 64u) {
-        // one wave: lane j holds the bin's j-th candidate; ranks by readlane
+        // one wave: lane j holds the bin's j-th candidate and counts those
+        // ranked above it, four at a time (shared-memory broadcasts)
         if (tid < 64) {
           const uint32_t k = lane < m ? sm.bin_key[lane] : 0u;
           const uint32_t o = lane < m ? sm.bin_ord[lane] : 0xffffffffu;
           uint32_t rank = 0;
-          for (uint32_t j = 0; j < m; ++j) {
-            const uint32_t kj = uint32_t(__builtin_amdgcn_readlane(int(k), int(j)));
-            const uint32_t oj = uint32_t(__builtin_amdgcn_readlane(int(o), int(j)));
-            rank += (kj > k || (kj == k && oj < o)) ? 1u : 0u;
+          for (uint32_t j = 0; j < m; j += 4) {
+            const uint4 k4 = *reinterpret_cast<const uint4*>(&sm.bin_key[j]);
+            const uint4 o4 = *reinterpret_cast<const uint4*>(&sm.bin_ord[j]);
+            auto above = [&](uint32_t q, uint32_t kj, uint32_t oj) {
+              return (j + q < m && (kj > k || (kj == k && oj < o))) ? 1u : 0u;
+            };
+            rank += above(0, k4.x, o4.x) + above(1, k4.y, o4.y) + above(2, k4.z, o4.z) + above(3, k4.w, o4.w);
           }
           if (lane < m && rank == need_bin - 1u) {
             sm.out[0] = k;
