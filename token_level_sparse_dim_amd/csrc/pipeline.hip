@@ -38,6 +38,7 @@
 namespace jssa {
 
 constexpr int kPipeNit = 4;            // workgroup steps per tile
+constexpr int kPipePF = 3;             // score-scan steps in flight per workgroup
 constexpr int kPipeMaxItem = 8192;     // tokens per score item at most (whole tiles)
 constexpr int kPipeCandLds = 8192;     // candidates resolved in shared memory
 constexpr int kPipeMaxTiles = 2048;    // tiles per row
@@ -407,20 +408,38 @@ struct Pipe {
 
   // ---- SCORE ------------------------------------------------------------------------------
   // Scores tokens [t_begin, t_end) of the row into keys[t - t_begin] (token
-  // order).  b0 holds the first step's loads, already issued.  Loads carry no
-  // per-lane branch (tokens past the end re-read the last one), so the next
-  // step's loads stay in flight while the current step is scored.
+  // order).  pre[j] holds the loads of step j, already issued: kPipePF steps
+  // stay in flight, step st + kPipePF being requested as soon as step st is
+  // scored.  Loads carry no per-lane branch (tokens past the end re-read the
+  // last one).
   static __device__ void scan_keys(const char* kr, int t_begin, int t_end, const QFrag<KPT, R, GE>& qf,
-                                   uint4 (&b0)[S::U], uint32_t* keys) {
+                                   uint4 (&pre)[kPipePF][S::U], uint32_t* keys) {
     const int n_steps = (t_end - t_begin + S::PER_ITER - 1) / S::PER_ITER;
-    for (int st = 0; st < n_steps; ++st) {
-      uint4 b1[S::U];
-      load_step(kr, t_begin + (st + 1) * S::PER_ITER, t_end, b1);
-      uint32_t* kst = keys + st * S::PER_ITER;
-      score_loads<KPT, R, GE>(b0, qf, G, [&](int toff, float sc) { kst[toff] = score_key(sc); });
+    // whole groups of kPipePF steps with every reload unconditional (past the
+    // end they re-read the last token), so the wait before each step's use
+    // counts the same loads on every path; then the remaining steps
+    int st0 = 0;
+    for (; st0 + kPipePF <= n_steps; st0 += kPipePF) {
 #pragma unroll
-      for (int u = 0; u < S::U; ++u) b0[u] = b1[u];
+      for (int j = 0; j < kPipePF; ++j) {
+        uint32_t* kst = keys + (st0 + j) * S::PER_ITER;
+        score_loads<KPT, R, GE>(pre[j], qf, G, [&](int toff, float sc) { kst[toff] = score_key(sc); });
+        load_step(kr, t_begin + (st0 + j + kPipePF) * S::PER_ITER, t_end, pre[j]);
+      }
     }
+#pragma unroll
+    for (int j = 0; j < kPipePF; ++j) {
+      if (st0 + j < n_steps) {
+        uint32_t* kst = keys + (st0 + j) * S::PER_ITER;
+        score_loads<KPT, R, GE>(pre[j], qf, G, [&](int toff, float sc) { kst[toff] = score_key(sc); });
+      }
+    }
+  }
+  // the first kPipePF steps of [t_begin, t_end)
+  static __device__ __forceinline__ void load_first(const char* kr, int t_begin, int t_end,
+                                                    uint4 (&pre)[kPipePF][S::U]) {
+#pragma unroll
+    for (int j = 0; j < kPipePF; ++j) load_step(kr, t_begin + j * S::PER_ITER, t_end, pre[j]);
   }
   static __device__ void load_step(const char* kr, int base, int t_end, uint4 (&v)[S::U]) {
 #pragma unroll
@@ -473,16 +492,16 @@ struct Pipe {
     const int t_end = min(t_begin + len, md.n_cand);
     ScoreSmem& sm = *reinterpret_cast<ScoreSmem*>(smem);
     const char* kr = kp_row(a, row);
-    uint4 b0[S::U];
+    uint4 pre[kPipePF][S::U];
     uint64_t lw = 0;
     project_query_staged<D, R, G>(a, b, h, sm.qp, [&] {
-      load_step(kr, t_begin, t_end, b0);  // in flight during the query projection
+      load_first(kr, t_begin, t_end, pre);  // in flight during the query projection
       if (threadIdx.x == 0) lw = consume(l_word(a, row));
     });
     QFrag<KPT, R, GE> qf;
     load_qfrag<KPT, R, GE>([&](int i) { return sm.qp.qp[i]; }, G, qf);
     __syncthreads();  // the projection's shared memory becomes the key buffer
-    scan_keys(kr, t_begin, t_end, qf, b0, sm.keys);
+    scan_keys(kr, t_begin, t_end, qf, pre, sm.keys);
     // the row's threshold (its sample item was handed out before this item)
     if (threadIdx.x == 0) {
       while ((lw >> 32) == 0 && !past(deadline)) {
@@ -493,42 +512,36 @@ struct Pipe {
       sm.l_key = uint32_t(lw);
     }
     __syncthreads();
-    emit_keys(a, row, t_begin, t_end, sm.l_key, sm.keys);
     // The row's shared tiles (those past the static runs): claimed one at a
     // time from the row's counter by the row's runs as they finish, which
-    // evens out runs that stream at different rates.  The next claim is
-    // requested while the current tile is scanned.
+    // evens out runs that stream at different rates.  A claim is requested
+    // before it is needed (the first one before this run's emission, the next
+    // one while the current tile is scanned), and no barrier waits on it
+    // before its use.  (Also draining other rows' tiles measured slower.)
     const int pool0 = a.n_big * (a.item / TS);
-    // claims shared tiles of row rr (n_cand candidates, threshold l) until its pool is empty
-    auto drain = [&](int rr, int n_cand_rr, uint32_t l) {
-      const int n_tiles_rr = (n_cand_rr + TS - 1) / TS;
-      if (pool0 >= n_tiles_rr) return;
-      const char* krr = kp_row(a, rr);
-      uint32_t* ctr = state(a, rr) + PW_STEAL;
-      __syncthreads();  // every wave is done with keys[] and the previous claim
-      if (threadIdx.x == 0) sm.claim = int(__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const int n_tiles_row = (md.n_cand + TS - 1) / TS;
+    uint32_t* ctr = state(a, row) + PW_STEAL;
+    int first = 0;
+    if (threadIdx.x == 0 && pool0 < n_tiles_row)
+      first = int(__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    emit_keys(a, row, t_begin, t_end, sm.l_key, sm.keys);
+    if (pool0 >= n_tiles_row) return;
+    __syncthreads();  // every wave is done with keys[]
+    if (threadIdx.x == 0) sm.claim = first;
+    __syncthreads();
+    int c = sm.claim;
+    while (pool0 + c < n_tiles_row) {
+      const int tb = (pool0 + c) * TS, te = min(tb + TS, md.n_cand);
+      load_first(kr, tb, te, pre);
+      int nxt = 0;
+      if (threadIdx.x == 0) nxt = int(__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      scan_keys(kr, tb, te, qf, pre, sm.keys);
+      if (threadIdx.x == 0) sm.claim = nxt;
       __syncthreads();
-      int c = sm.claim;
-      while (pool0 + c < n_tiles_rr) {
-        const int tb = (pool0 + c) * TS, te = min(tb + TS, n_cand_rr);
-        uint4 b1[S::U];
-        load_step(krr, tb, te, b1);
-        int nxt = 0;
-        if (threadIdx.x == 0) nxt = int(__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        __syncthreads();  // every wave has read the previous claim
-        scan_keys(krr, tb, te, qf, b1, sm.keys);
-        if (threadIdx.x == 0) sm.claim = nxt;
-        __syncthreads();
-        emit_keys(a, rr, tb, te, l, sm.keys);
-        c = sm.claim;
-        __syncthreads();  // keys[] is free again
-      }
-    };
-    // The row's shared tiles (those past the static runs), claimed one at a
-    // time by the row's runs as they finish, which evens out runs that stream
-    // at different rates.  (Also draining other rows' tiles, with their
-    // queries published by the samples, measured slower.)
-    drain(row, md.n_cand, sm.l_key);
+      emit_keys(a, row, tb, te, sm.l_key, sm.keys);
+      c = sm.claim;
+      __syncthreads();  // keys[] and the claim are free again
+    }
   }
 
   // ---- RESOLVE (second launch) ------------------------------------------------------------
