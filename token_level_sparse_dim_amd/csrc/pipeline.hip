@@ -958,9 +958,14 @@ __global__ __launch_bounds__(256, 3) void scan_kernel(PipeArgs a) {
   for (; t < a.n_main; t += gridDim.x) {
     int r, t_begin, len;
     if (t < a.n_rows + n_big_all) {
+      // run `run` of row r at i = run * n_rows + (r - run mod n_rows): a row's
+      // runs are spread over the dispatch order and, rotating by one per
+      // round, over the XCDs (workgroup i goes to XCD i mod 8), so its shared
+      // tiles can even out slower XCDs
       const int i = t - a.n_rows;
-      r = i / a.n_big;
-      t_begin = (i - r * a.n_big) * a.item;
+      const int run = i / a.n_rows;
+      r = (i - run * a.n_rows + run) % a.n_rows;
+      t_begin = run * a.item;
       len = a.item;
     } else {
       const int i = t - a.n_rows - n_big_all;
