@@ -134,8 +134,85 @@ __global__ __launch_bounds__(256) void append_rows_kernel(AppendArgs a) {
   }
 }
 
+// The decode step's append (given new rows, d_k = DPER * 256 / R): thread
+// (o, part) needs key elements [part*DPER, (part+1)*DPER) and the same rows of
+// basis column o; those, the position and the rows to copy into the caches
+// are all requested at once, so the kernel waits for memory once.  The
+// projection adds in the same order as append_rows_kernel (an fma chain over
+// d, then the parts in order).
+template <int KVT, int KPT, int R, int DPER>
+__global__ __launch_bounds__(256) void append_new_kernel(AppendArgs a) {
+  constexpr int EB = Elem<KVT>::bytes;
+  constexpr int PARTS = 256 / R;
+  __shared__ float s_part[256];
+  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int o = threadIdx.x % R, part = threadIdx.x / R;
+  const int d0 = part * DPER;
+  const char* src = reinterpret_cast<const char*>(a.k_new) + ((size_t(b) * a.n_new + j) * a.Hkv + h) * a.d_k * EB;
+  const float* Pc = a.P + size_t(h) * a.d_k * R + o;
+  float kv[DPER], pv[DPER];
+#pragma unroll
+  for (int i = 0; i < DPER; ++i) {
+    if constexpr (KVT == 1) kv[i] = bf16_lo(uint32_t(reinterpret_cast<const uint16_t*>(src)[d0 + i]));
+    else kv[i] = reinterpret_cast<const float*>(src)[d0 + i];
+    pv[i] = Pc[size_t(d0 + i) * R];
+  }
+  const int n16k = a.d_k * EB / 16;
+  const bool copy_v = !a.mla && a.v_new;
+  const int n16v = copy_v ? a.d_v * EB / 16 : 0;
+  const char* vsrc = copy_v ? reinterpret_cast<const char*>(a.v_new) + ((size_t(b) * a.n_new + j) * a.Hkv + h) * a.d_v * EB
+                            : nullptr;
+  uint4 kc16 = make_uint4(0u, 0u, 0u, 0u), vc16 = make_uint4(0u, 0u, 0u, 0u);
+  if (int(threadIdx.x) < n16k) kc16 = load16(src + size_t(threadIdx.x) * 16);
+  if (int(threadIdx.x) < n16v) vc16 = load16(vsrc + size_t(threadIdx.x) * 16);
+  const int t = a.pos[b] + j;
+  const bool ok = t >= 0 && t < a.t_max;
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < DPER; ++i) acc = fmaf(kv[i], pv[i], acc);
+  s_part[threadIdx.x] = acc;
+  if (ok) {
+    if (int(threadIdx.x) < n16k)
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(a.k_cache) + ((size_t(b) * a.t_max + t) * a.Hkv + h) * a.d_k * EB +
+                                size_t(threadIdx.x) * 16) = kc16;
+    if (int(threadIdx.x) < n16v)
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(a.v_cache) + ((size_t(b) * a.t_max + t) * a.Hkv + h) * a.d_v * EB +
+                                size_t(threadIdx.x) * 16) = vc16;
+  }
+  __syncthreads();
+  if (ok && int(threadIdx.x) < R) {
+    float sum = 0.f;
+    for (int pp = 0; pp < PARTS; ++pp) sum += s_part[pp * R + threadIdx.x];
+    char* kprow = reinterpret_cast<char*>(a.kp) + ((size_t(b) * a.Hkv + h) * a.t_max + t) * R * Elem<KPT>::bytes;
+    if constexpr (KPT == 1) reinterpret_cast<uint16_t*>(kprow)[threadIdx.x] = f32_to_bf16_rne(sum);
+    else reinterpret_cast<float*>(kprow)[threadIdx.x] = sum;
+  }
+}
+
 template <int KVT, int KPT>
 static hipError_t dispatch_append_r(const AppendArgs& args, int r, dim3 grid, hipStream_t s) {
+  if (args.n_new <= kAppendRowsMax && args.k_new) {
+    dim3 g(args.n_new, grid.y, grid.z);
+    const int dper = args.d_k * r / 256;
+    if (args.d_k * r % 256 == 0) {
+      if (r == 32 && dper == 16) {
+        hipLaunchKernelGGL((append_new_kernel<KVT, KPT, 32, 16>), g, dim3(256), 0, s, args);
+        return hipGetLastError();
+      }
+      if (r == 64 && dper == 32) {
+        hipLaunchKernelGGL((append_new_kernel<KVT, KPT, 64, 32>), g, dim3(256), 0, s, args);
+        return hipGetLastError();
+      }
+      if (r == 16 && dper == 4) {
+        hipLaunchKernelGGL((append_new_kernel<KVT, KPT, 16, 4>), g, dim3(256), 0, s, args);
+        return hipGetLastError();
+      }
+      if (r == 32 && dper == 8) {
+        hipLaunchKernelGGL((append_new_kernel<KVT, KPT, 32, 8>), g, dim3(256), 0, s, args);
+        return hipGetLastError();
+      }
+    }
+  }
   if (args.n_new <= kAppendRowsMax) {
     dim3 g(args.n_new, grid.y, grid.z);
     switch (r) {
