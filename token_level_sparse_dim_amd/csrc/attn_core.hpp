@@ -395,8 +395,7 @@ __device__ __forceinline__ bool attend_chunk_2pass(const AttnArgs& a, Smem& S, i
     for (int g = wave; g < G; g += 4) {
       float mx = -INFINITY;
       for (int r = lane; r < CH; r += 64) mx = fmaxf(mx, S.w[r][g]);
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      mx = group_max<64>(mx);
       float sum = 0.f;
       for (int r = lane; r < CH; r += 64) {
         const float x = S.w[r][g];
@@ -404,8 +403,7 @@ __device__ __forceinline__ bool attend_chunk_2pass(const AttnArgs& a, Smem& S, i
         S.w[r][g] = wgt;
         sum += wgt;
       }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+      sum = group_sum<64>(sum);
       if (lane == 0) {
         S.ml[g][0] = mx;
         S.ml[g][1] = sum;
@@ -431,11 +429,9 @@ __device__ __forceinline__ bool attend_chunk_2pass(const AttnArgs& a, Smem& S, i
       }
     }
 #pragma unroll
-    for (int off = LR; off < 64; off <<= 1)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] += __shfl_xor(acc[g][e], off);
+      for (int e = 0; e < EPL; ++e) acc[g][e] = sum_across_groups<LR>(acc[g][e]);
     if (lane < LR) {
 #pragma unroll
       for (int g = 0; g < G; ++g)

@@ -105,6 +105,29 @@ constexpr int kDppXor2 = 0x4e;
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
 
+// Lanes l and l ^ 16 (l ^ 32) combined through the lane swaps of gfx950:
+// with both operands equal, v_permlane16_swap returns the lower and the upper
+// row of each 32-lane half (v_permlane32_swap: the lower and the upper half),
+// so their sum (max) is the pair's sum (max) in both lanes -- a VALU op, no
+// trip through the shared-memory crossbar.  The same value as v + shfl_xor(v,
+// 16) in either lane (addition and fmaxf are commutative).
+__device__ __forceinline__ float xor16_add(float v) {
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+__device__ __forceinline__ float xor32_add(float v) {
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
 // Sum over aligned groups of N lanes (N a power of two <= 64); every lane of
 // the group receives the group's sum.
 template <int N>
@@ -113,8 +136,8 @@ __device__ __forceinline__ float group_sum(float v) {
   if constexpr (N >= 4) v += dpp<kDppXor2>(v);
   if constexpr (N >= 8) v += dpp<kDppHalfMirror>(v);
   if constexpr (N >= 16) v += dpp<kDppMirror>(v);
-  if constexpr (N >= 32) v += __shfl_xor(v, 16);
-  if constexpr (N >= 64) v += __shfl_xor(v, 32);
+  if constexpr (N >= 32) v = xor16_add(v);
+  if constexpr (N >= 64) v = xor32_add(v);
   return v;
 }
 
@@ -124,8 +147,19 @@ __device__ __forceinline__ float group_max(float v) {
   if constexpr (N >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
   if constexpr (N >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
   if constexpr (N >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
-  if constexpr (N >= 32) v = fmaxf(v, __shfl_xor(v, 16));
-  if constexpr (N >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+  if constexpr (N >= 32) v = xor16_max(v);
+  if constexpr (N >= 64) v = xor32_max(v);
+  return v;
+}
+
+// Sum over lanes l ^ m for m = F, 2F, ..., 32 (F a power of two): the
+// lane groups of F lanes that hold the same positions of different rows.
+template <int F>
+__device__ __forceinline__ float sum_across_groups(float v) {
+#pragma unroll
+  for (int off = F; off < 16; off <<= 1) v += __shfl_xor(v, off);
+  if constexpr (F <= 16) v = xor16_add(v);
+  if constexpr (F <= 32) v = xor32_add(v);
   return v;
 }
 

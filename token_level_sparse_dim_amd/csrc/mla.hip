@@ -261,8 +261,7 @@ __global__ __launch_bounds__(256, 2) void mla_score_kernel(MlaScoreArgs a) {
             }
             best = fmaxf(best, fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3])));
           }
-          best = fmaxf(best, __shfl_xor(best, 16));
-          best = fmaxf(best, __shfl_xor(best, 32));
+          best = xor32_max(xor16_max(best));
           if (g == q) mine = best;
         }
         s_red[buf][wave][lane] = mine;
@@ -450,8 +449,7 @@ __global__ __launch_bounds__(256, 1) void mla_attn_kernel(MlaAttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[ht][i] = (pbase + i < cnt) ? st[ht][i] * a.qscale : -INFINITY;
       float mw = fmaxf(fmaxf(x[ht][0], x[ht][1]), fmaxf(x[ht][2], x[ht][3]));
-      mw = fmaxf(mw, __shfl_xor(mw, 16));
-      mw = fmaxf(mw, __shfl_xor(mw, 32));
+      mw = xor32_max(xor16_max(mw));
       if (g == 0) S.mx[wave][16 * ht + n16] = mw;
     }
     __syncthreads();
@@ -487,8 +485,7 @@ __global__ __launch_bounds__(256, 1) void mla_attn_kernel(MlaAttnArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) rs += bf16_lo(pa[mt][ks][sp][e]) + bf16_hi(pa[mt][ks][sp][e]);
         }
-      rs += __shfl_xor(rs, 16);
-      rs += __shfl_xor(rs, 32);
+      rs = xor32_add(xor16_add(rs));
       l_run[mt] = fmaf(alpha[mt], l_run[mt], rs);
       // accumulator rows are heads 16 mt + 4 g + i
       const float4 al = *reinterpret_cast<const float4*>(&S.alpha[16 * mt + 4 * g]);

@@ -210,7 +210,7 @@ __device__ __forceinline__ void score_loads(const uint4 (&v)[ScanShape<KPT, R>::
 #pragma unroll
         for (int i = 1; i < 4; ++i)
           if (4 * kg + i < G) best = fmaxf(best, c[i]);
-        if (G > 4) best = fmaxf(best, __shfl_xor(best, 16));
+        if (G > 4) best = xor16_max(best);
       }
       if (lane < 16) emit(slot_token<KPT, R>(q * S::KS), best);
     }
