@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define JSSA_ABI_VERSION 2
+#define JSSA_ABI_VERSION 3
 
 typedef enum {
   JSSA_OK = 0,
@@ -219,6 +219,27 @@ int32_t jssa_decode_profiled(const jssa_desc* desc, const void* q, const float* 
                              const int32_t* seq_lens, void* out, float* lse, int32_t* idx_out,
                              int32_t* n_sel_out, void* ws, size_t ws_bytes,
                              void* const* stage_events, void* stream);
+
+/* One whole decode step: jssa_append_kv of one new token per sequence
+ * (n_new = 1: k_new[b,0,h,:] / v_new[b,0,h,:] written at t = pos[b] and the
+ * key projected into kp_cache) followed by jssa_decode on the updated caches
+ * (JSSA summary section E.1: the new key is projected when it is generated,
+ * then the step scores, selects and attends).  Results are bit-identical to
+ * the two calls in sequence.  In the fused build the append runs inside the
+ * scan launch: each (sequence, KV head) row's sample appends its token before
+ * it publishes the row's threshold, and the scan re-scores the one step that
+ * holds pos[b] from the stored row after it has seen that threshold; no launch
+ * of its own.  Other shapes launch the append first (before
+ * stage_events[0]).  k_new / v_new: [B, 1, Hkv, d] (MLA: [B, 1, 1, d_k], v_new
+ * and v_cache unused, may be NULL); pos: int32 [B] device array; positions
+ * outside [0, t_max) are not written.  The caches are read and written in
+ * place.  stage_events may be NULL, else as for jssa_decode_profiled.
+ * Workspace op JSSA_OP_DECODE. */
+int32_t jssa_decode_step(const jssa_desc* desc, const void* k_new, const void* v_new,
+                         const int32_t* pos, const void* q, const float* P, void* kp_cache,
+                         void* k_cache, void* v_cache, const int32_t* seq_lens, void* out,
+                         float* lse, int32_t* idx_out, int32_t* n_sel_out, void* ws,
+                         size_t ws_bytes, void* const* stage_events, void* stream);
 
 /* Full-KV decode attention over all t < seq_lens[b] (the comparison path of
  * JSSA summary section 4.5), same outputs as jssa_indexed_attn.

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert J.abi_version() == 2
+    assert J.abi_version() == 3
     lib = J.lib()
     assert lib.jssa_status_str(0) == b"JSSA_OK"
     for code, name in _lib.STATUS.items():
@@ -106,10 +106,18 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.jssa_decode(d, *p[:6], null, null, null, null, null, 0, null) == -1
     assert lib.jssa_dense_decode(d, null, *p[:4], null, null, 0, null) == -1
     assert lib.jssa_append_kv(d, *p[:2], -1, *p[2:7], null) == -1
+    # decode step: the new token's rows and positions are required (GQA: v_new and v_cache too)
+    tail = (null, null, null, p[10], 1 << 40, null, null)  # lse, idx, n_sel, ws, ws_bytes, events, stream
+    assert lib.jssa_decode_step(d, null, *p[:9], *tail) == -1
+    assert lib.jssa_decode_step(d, p[0], p[1], null, *p[3:10], *tail) == -1
+    assert lib.jssa_decode_step(d, p[0], null, *p[2:10], *tail) == -1
+    assert lib.jssa_decode_step(d, *p[:10], null, null, null, null, 0, null, null) == -3  # workspace missing
     # misaligned data pointers
     odd = ctypes.c_void_p(4096 + 2)
     assert lib.jssa_score(d, odd, *p[:4], null, 0, null) == -4
     assert lib.jssa_decode(d, *p[:5], odd, p[6], null, null, null, p[7], 1 << 40, null) == -4
+    assert lib.jssa_decode_step(d, odd, *p[1:10], *tail) == -4
+    assert lib.jssa_decode_step(d, p[0], p[1], odd, *p[3:10], *tail) == -4
     # invalid descriptor wins over everything else
     bad = _desc(n_q_heads=30).c()
     assert lib.jssa_decode(bad, *p[:7], null, null, null, p[7], 1 << 40, null) == -1

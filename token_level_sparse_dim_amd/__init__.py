@@ -16,7 +16,7 @@ __all__ = [
     "Desc", "JssaError", "F32", "BF16", "REDUCE_MAX", "REDUCE_MEAN", "LAYOUT_GQA", "LAYOUT_MLA",
     "OP_TOPK", "OP_ATTN", "OP_DECODE", "OP_DENSE", "OP_SCORE", "lib", "abi_version", "check_desc",
     "workspace_bytes", "workspace", "append_kv", "append_projection", "score", "topk", "indexed_attn", "decode", "decode_profiled",
-    "dense_decode",
+    "decode_step", "dense_decode",
 ]
 
 _TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
@@ -123,21 +123,44 @@ def decode(desc: Desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, ws,
 
 def decode_profiled(desc: Desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, ws, events,
                     idx_out=None, n_sel_out=None, stream=None):
-    """``jssa_decode_profiled``: the staged decode (score scan, candidate pass,
-    resolve + attention launch) recording four stage events
-    (``torch.cuda.Event(enable_timing=True)``): before the score scan, after it,
-    after the candidate pass, after the resolve + attention launch.  torch
-    creates an event on its first record, so unrecorded events are recorded
-    once here first."""
+    """``jssa_decode_profiled``: :func:`decode` recording four stage events
+    (``torch.cuda.Event(enable_timing=True)``) around its launches; the fused
+    build records them before the scan, after it, after the resolve and after
+    the attention (the header lists the staged shapes' points)."""
+    arr = _event_array(events, stream)
+    kv = _TORCH_DTYPE[desc.kv_dtype]
+    call("jssa_decode_profiled", desc.c(), _ptr(q, kv, "q"), _ptr(P, torch.float32, "P"),
+         _ptr(kp_cache, _TORCH_DTYPE[desc.kp_dtype], "kp_cache"), _ptr(k_cache, kv, "k_cache"),
+         _ptr(v_cache, kv, "v_cache"), _ptr(seq_lens, torch.int32, "seq_lens"),
+         _ptr(out, _TORCH_DTYPE[desc.out_dtype], "out"), _ptr(lse, torch.float32, "lse"),
+         _ptr(idx_out, torch.int32, "idx_out"), _ptr(n_sel_out, torch.int32, "n_sel_out"),
+         _ptr(ws, torch.uint8, "ws"), ws.numel(), arr, _stream(stream))
+
+
+def _event_array(events, stream):
+    """A host array of the four events' HIP handles (torch creates an event on
+    its first record, so unrecorded events are recorded once here first)."""
     import ctypes
     if len(events) != 4:
         raise ValueError("four events are needed")
     for e in events:
         if not e.cuda_event:
             e.record(stream if stream is not None else torch.cuda.current_stream())
-    arr = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    return (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+
+
+def decode_step(desc: Desc, k_new, v_new, pos, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, ws,
+                idx_out=None, n_sel_out=None, events=None, stream=None):
+    """``jssa_decode_step``: append one new token per sequence (``k_new`` /
+    ``v_new`` ``[B, 1, Hkv, d]`` at ``pos``), then the decode on the updated
+    caches; the result of :func:`append_kv` followed by :func:`decode`.
+    ``events``: optional four stage events, as for :func:`decode_profiled`."""
     kv = _TORCH_DTYPE[desc.kv_dtype]
-    call("jssa_decode_profiled", desc.c(), _ptr(q, kv, "q"), _ptr(P, torch.float32, "P"),
+    if k_new.shape[1] != 1:
+        raise ValueError("decode_step appends exactly one token per sequence")
+    arr = None if events is None else _event_array(events, stream)
+    call("jssa_decode_step", desc.c(), _ptr(k_new, kv, "k_new"), _ptr(v_new, kv, "v_new"),
+         _ptr(pos, torch.int32, "pos"), _ptr(q, kv, "q"), _ptr(P, torch.float32, "P"),
          _ptr(kp_cache, _TORCH_DTYPE[desc.kp_dtype], "kp_cache"), _ptr(k_cache, kv, "k_cache"),
          _ptr(v_cache, kv, "v_cache"), _ptr(seq_lens, torch.int32, "seq_lens"),
          _ptr(out, _TORCH_DTYPE[desc.out_dtype], "out"), _ptr(lse, torch.float32, "lse"),

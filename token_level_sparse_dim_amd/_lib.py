@@ -52,6 +52,10 @@ SIGNATURES = {
     "jssa_decode_profiled": (_i32, [_PDESC, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                     _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                     _size_t, ctypes.POINTER(_c_void_p), _c_void_p]),
+    "jssa_decode_step": (_i32, [_PDESC, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                _c_void_p, _c_void_p, _c_void_p, _size_t, ctypes.POINTER(_c_void_p),
+                                _c_void_p]),
     "jssa_dense_decode": (_i32, [_PDESC, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                  _c_void_p, _c_void_p, _size_t, _c_void_p]),
 }

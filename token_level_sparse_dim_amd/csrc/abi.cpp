@@ -267,7 +267,7 @@ int32_t jssa_indexed_attn(const jssa_desc* desc, const void* q, const void* k_ca
 static int32_t decode_impl(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
                            const void* k_cache, const void* v_cache, const int32_t* seq_lens,
                            void* out, float* lse, int32_t* idx_out, int32_t* n_sel_out,
-                           void* ws, size_t ws_bytes, void* const* ev, void* stream) {
+                           void* ws, size_t ws_bytes, const NewToken* nt, void* const* ev, void* stream) {
   JSSA_TRY(check(desc, JSSA_OP_DECODE));
   const bool mla = desc->layout == JSSA_LAYOUT_MLA;
   if (!q || !P || !kp_cache || !k_cache || (!mla && !v_cache) || !seq_lens || !out) return JSSA_ERR_INVALID_ARG;
@@ -287,7 +287,12 @@ static int32_t decode_impl(const jssa_desc* desc, const void* q, const float* P,
   hipStream_t s = as_stream(stream);
   if (lay.pipe)
     return to_status(launch_pipeline(*desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, idx, n_sel,
-                                     base, lay, ev, s));
+                                     base, lay, nt, ev, s));
+  if (nt) {  // the staged launches: the append is a launch of its own, first
+    const hipError_t ea = launch_append(*desc, nt->k_new, nt->v_new, 1, nt->pos, P, nt->k_cache, nt->v_cache,
+                                        nt->kp_cache, s);
+    if (ea != hipSuccess) return to_status(ea);
+  }
   auto mark = [&](int i) { return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
   if (mla) {
     hipError_t e = launch_mla_qproj(*desc, q, P, base, lay, s);
@@ -320,7 +325,7 @@ int32_t jssa_decode(const jssa_desc* desc, const void* q, const float* P, const 
                     void* out, float* lse, int32_t* idx_out, int32_t* n_sel_out,
                     void* ws, size_t ws_bytes, void* stream) {
   return decode_impl(desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, idx_out, n_sel_out,
-                     ws, ws_bytes, nullptr, stream);
+                     ws, ws_bytes, nullptr, nullptr, stream);
 }
 
 int32_t jssa_decode_profiled(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
@@ -329,7 +334,21 @@ int32_t jssa_decode_profiled(const jssa_desc* desc, const void* q, const float* 
                              void* ws, size_t ws_bytes, void* const* stage_events, void* stream) {
   if (!stage_events) return JSSA_ERR_INVALID_ARG;
   return decode_impl(desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, idx_out, n_sel_out,
-                     ws, ws_bytes, stage_events, stream);
+                     ws, ws_bytes, nullptr, stage_events, stream);
+}
+
+int32_t jssa_decode_step(const jssa_desc* desc, const void* k_new, const void* v_new, const int32_t* pos,
+                         const void* q, const float* P, void* kp_cache, void* k_cache, void* v_cache,
+                         const int32_t* seq_lens, void* out, float* lse, int32_t* idx_out,
+                         int32_t* n_sel_out, void* ws, size_t ws_bytes, void* const* stage_events,
+                         void* stream) {
+  JSSA_TRY(check(desc, JSSA_OP_DECODE));
+  const bool mla = desc->layout == JSSA_LAYOUT_MLA;
+  if (!k_new || !pos || (!mla && (!v_new || !v_cache))) return JSSA_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(pos) || (!mla && !aligned16(v_new))) return JSSA_ERR_MISALIGNED;
+  const NewToken nt{k_new, mla ? nullptr : v_new, pos, k_cache, v_cache, kp_cache};
+  return decode_impl(desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, idx_out, n_sel_out,
+                     ws, ws_bytes, &nt, stage_events, stream);
 }
 
 int32_t jssa_dense_decode(const jssa_desc* desc, const void* q, const void* k_cache,

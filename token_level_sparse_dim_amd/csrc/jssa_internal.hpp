@@ -137,13 +137,25 @@ hipError_t launch_mla_attend(const jssa_desc& d, const void* q, const void* k_ca
 // size, tiles per row and attention chunk (tokens).
 bool pipeline_layout(const jssa_desc& d, int* ts, int* n_tiles, int* chunk);
 
+// The step's new token (one row per sequence and KV head, at t = pos[b]) and
+// the caches it is written to, for a decode that appends it itself.
+struct NewToken {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* pos;
+  void* k_cache;
+  void* v_cache;
+  void* kp_cache;
+};
+
 // The whole decode step in four launches (scan with sampled-threshold
 // candidate emission; resolve; attention chunks; chunk merge); requires
 // ws.pipe.  With `ev` (four events): recorded before the scan, after it, after
-// the resolve and after the merge.
+// the resolve and after the merge.  With `nt`, the scan launch also appends
+// the new token first (the caches in `nt` are the decode's caches).
 hipError_t launch_pipeline(const jssa_desc& d, const void* q, const float* P, const void* kp,
                            const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
                            float* lse, int32_t* idx, int32_t* n_sel, char* ws_base, const Workspace& ws,
-                           void* const* ev, hipStream_t s);
+                           const NewToken* nt, void* const* ev, hipStream_t s);
 
 }  // namespace jssa

@@ -48,8 +48,11 @@ constexpr int kResolveThreads = 1024;  // threads of a resolve workgroup
 constexpr int kPipeAttnNL = 8;         // K and V row loads per lane per attention chunk
 
 // per-row state word of the scan (zero on entry and exit): u64 at words 12-13,
-// (1 << 32) | L once the row's threshold is known
+// kLwSet | L once the row's threshold is known, plus kLwAppended once the
+// step's new token is in the row's caches (a decode that appends it)
 constexpr int PW_L = 12;
+constexpr uint64_t kLwSet = uint64_t(1) << 32;
+constexpr uint64_t kLwAppended = uint64_t(1) << 33;
 // per-row state word of the scan: claims of the row's shared tiles (reset by the resolve)
 constexpr int PW_STEAL = 14;
 #ifndef JSSA_PIPE_STATIC_PCT
@@ -64,6 +67,13 @@ struct PipeArgs {
   const void* kp;
   uint64_t* cand;      // [rows][t_max] candidate slots, ts entries per tile
   float* qp_pub;       // [rows][G * r] projected queries, left by the sample for an exact re-selection
+  // the step's new token, appended in this launch (k_new == nullptr: already appended)
+  const void* k_new;   // [B, 1, Hkv, d] (and v_new), written at t = pos[b]
+  const void* v_new;
+  const int32_t* pos;
+  void* k_w;           // the caches, writable
+  void* v_w;
+  void* kp_w;
   uint32_t* tile_cnt;  // [rows][n_tiles]
   int G, d_k, topk, window, q_dtype, ts, n_tiles, n_rows, n_main, n_attn;
   int item, n_big, n_small;  // score runs: n_big runs of `item` tokens per row, then n_small single tiles
@@ -303,6 +313,8 @@ struct Pipe {
     uint32_t keys[NSAMP];
     alignas(16) uint32_t hist[2048];
     uint32_t out[2];
+    float apart[256];  // the new key's projection: per-thread partial sums
+    uint32_t akp[R];   // and its rounded coordinates
   };
   struct ScoreSmem {
     union {
@@ -347,12 +359,111 @@ struct Pipe {
     if (threadIdx.x == 0) const_cast<int32_t*>(a.at.n_sel)[row] = md.kk + md.nW;
   }
 
+  // ---- APPEND (the step's new token, in the sample of its row) ---------------------------
+  // The new K and V rows of (b, h) go to the caches at t = pos[b] and the key
+  // is projected into the scoring cache with the arithmetic of the stand-alone
+  // append (thread (o, part): an fma chain over d in [part*DPER, +DPER), then
+  // the parts summed in order, rounded to the cache's type).  The sample does
+  // this after it has published the row's threshold (the threshold is on
+  // every score run's path, the new row only on one's).  The projected row is
+  // stored with device-scope stores and waited for before the row's word is
+  // marked (kLwAppended): the score run that holds the token waits for that
+  // mark, then re-scores the token's step from the stored row.
+  static constexpr int kAppendParts = 256 / R;
+  static_assert(D % kAppendParts == 0, "append slices");
+  static __device__ __forceinline__ void append_row(const PipeArgs& a, int b, int h, SampleSmem& sm) {
+    constexpr int EB = Elem<KVT>::bytes, DPER = D / kAppendParts;
+    const int o = threadIdx.x % R, part = threadIdx.x / R;
+    const int d0 = part * DPER;
+    const char* src = reinterpret_cast<const char*>(a.k_new) + (size_t(b) * a.at.Hkv + h) * D * EB;
+    const char* vsrc = reinterpret_cast<const char*>(a.v_new) + (size_t(b) * a.at.Hkv + h) * D * EB;
+    const float* Pc = a.P + size_t(h) * D * R + o;
+    float kv[DPER], pv[DPER];
+#pragma unroll
+    for (int i = 0; i < DPER; ++i) {
+      if constexpr (KVT == 1) kv[i] = bf16_lo(uint32_t(reinterpret_cast<const uint16_t*>(src)[d0 + i]));
+      else kv[i] = reinterpret_cast<const float*>(src)[d0 + i];
+      pv[i] = Pc[size_t(d0 + i) * R];
+    }
+    constexpr int N16 = D * EB / 16;
+    uint4 kc16 = make_uint4(0u, 0u, 0u, 0u), vc16 = make_uint4(0u, 0u, 0u, 0u);
+    if (threadIdx.x < N16) {
+      kc16 = load16(src + size_t(threadIdx.x) * 16);
+      vc16 = load16(vsrc + size_t(threadIdx.x) * 16);
+    }
+    const int t = a.pos[b];
+    const bool ok = t >= 0 && t < a.at.t_max;
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < DPER; ++i) acc = fmaf(kv[i], pv[i], acc);
+    sm.apart[threadIdx.x] = acc;
+    if (ok && threadIdx.x < N16) {
+      const size_t row_off = ((size_t(b) * a.at.t_max + t) * a.at.Hkv + h) * D * EB + size_t(threadIdx.x) * 16;
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(a.k_w) + row_off) = kc16;
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(a.v_w) + row_off) = vc16;
+    }
+    __syncthreads();
+    if (threadIdx.x < R) {
+      float sum = 0.f;
+      for (int pp = 0; pp < kAppendParts; ++pp) sum += sm.apart[pp * R + threadIdx.x];
+      sm.akp[threadIdx.x] = KPT == 1 ? uint32_t(f32_to_bf16_rne(sum)) : __float_as_uint(sum);
+    }
+    __syncthreads();
+    if (ok) {
+      char* kprow = reinterpret_cast<char*>(a.kp_w) + ((size_t(b) * a.at.Hkv + h) * a.at.t_max + t) * R * S::EB;
+      if constexpr (KPT == 1) {
+        if (threadIdx.x < R / 2)
+          publish(reinterpret_cast<uint32_t*>(kprow) + threadIdx.x,
+                  sm.akp[2 * threadIdx.x] | (sm.akp[2 * threadIdx.x + 1] << 16));
+      } else {
+        if (threadIdx.x < R) publish(reinterpret_cast<uint32_t*>(kprow) + threadIdx.x, sm.akp[threadIdx.x]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the projected row is stored before anything this row publishes
+    __syncthreads();
+  }
+  // One scan step's loads through device-scope loads (they see the row the
+  // sample appended in this launch).
+  static __device__ void load_step_fresh(const char* kr, int base, int t_end, uint4 (&v)[S::U]) {
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      const int t = min(base + slot_token<KPT, R>(u), t_end - 1);
+      const uint64_t* p = reinterpret_cast<const uint64_t*>(kr + size_t(t) * R * S::EB + slot_byte<KPT, R>(u));
+      const uint64_t lo = consume(p), hi = consume(p + 1);
+      v[u] = make_uint4(uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi), uint32_t(hi >> 32));
+    }
+  }
+  // Re-scores the step of [t_begin, t_end) that holds the appended token (if
+  // any), with the row as now stored; keys[] holds the range's keys.
+  static __device__ __forceinline__ void rescore_new(const PipeArgs& a, int row, int b, const char* kr,
+                                                     int t_begin, int t_end, const QFrag<KPT, R, GE>& qf,
+                                                     uint32_t* keys, uint64_t deadline) {
+    if (!a.k_new) return;
+    const int t = a.pos[b];
+    if (t < t_begin || t >= t_end) return;
+    if (threadIdx.x == 0) {  // the sample has stored the row
+      uint64_t lw = consume(l_word(a, row));
+      while (!(lw & kLwAppended) && !past(deadline)) {
+        __builtin_amdgcn_s_sleep(1);
+        lw = consume(l_word(a, row));
+      }
+      if (!(lw & kLwAppended)) flag_error(a);
+    }
+    __syncthreads();
+    const int st = (t - t_begin) / S::PER_ITER;
+    uint4 v[S::U];
+    load_step_fresh(kr, t_begin + st * S::PER_ITER, t_end, v);
+    uint32_t* kst = keys + st * S::PER_ITER;
+    score_loads<KPT, R, GE>(v, qf, G, [&](int toff, float sc) { kst[toff] = score_key(sc); });
+  }
+
   // ---- SAMPLE -----------------------------------------------------------------------------
   static __device__ __forceinline__ void sample(const PipeArgs& a, int row, SampleSmem& sm) {
     const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
     const RowMode md = row_mode(a, b);
     if (!md.select()) {
       resolve_trivial(a, row, md);
+      if (a.k_new) append_row(a, b, h, sm);  // no score run reads this row
       return;
     }
     uint32_t L = 0;  // every token is a candidate unless a sample allows a higher threshold
@@ -403,7 +514,11 @@ struct Pipe {
         L = kstar;
       }
     }
-    if (threadIdx.x == 0) publish(l_word(a, row), (uint64_t(1) << 32) | L);
+    if (threadIdx.x == 0) publish(l_word(a, row), kLwSet | L);
+    if (a.k_new) {
+      append_row(a, b, h, sm);
+      if (threadIdx.x == 0) publish(l_word(a, row), kLwSet | kLwAppended | L);
+    }
   }
 
   // ---- SCORE ------------------------------------------------------------------------------
@@ -512,6 +627,8 @@ struct Pipe {
       sm.l_key = uint32_t(lw);
     }
     __syncthreads();
+    rescore_new(a, row, b, kr, t_begin, t_end, qf, sm.keys, deadline);
+    __syncthreads();
     // The row's shared tiles (those past the static runs): claimed one at a
     // time from the row's counter by the row's runs as they finish, which
     // evens out runs that stream at different rates.  A claim is requested
@@ -536,6 +653,7 @@ struct Pipe {
       int nxt = 0;
       if (threadIdx.x == 0) nxt = int(__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       scan_keys(kr, tb, te, qf, pre, sm.keys);
+      rescore_new(a, row, b, kr, tb, te, qf, sm.keys, deadline);
       if (threadIdx.x == 0) sm.claim = nxt;
       __syncthreads();
       emit_keys(a, row, tb, te, sm.l_key, sm.keys);
@@ -1111,9 +1229,13 @@ static hipError_t launch_pipe_reduce(const PipeArgs& a, bool mean, void* const* 
 hipError_t launch_pipeline(const jssa_desc& d, const void* q, const float* P, const void* kp,
                            const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
                            float* lse, int32_t* idx, int32_t* n_sel, char* ws_base, const Workspace& ws,
-                           void* const* ev, hipStream_t s) {
+                           const NewToken* nt, void* const* ev, hipStream_t s) {
   if (!ws.pipe) return hipErrorInvalidValue;
   PipeArgs a{};
+  if (nt) {
+    a.k_new = nt->k_new; a.v_new = nt->v_new; a.pos = nt->pos;
+    a.k_w = nt->k_cache; a.v_w = nt->v_cache; a.kp_w = nt->kp_cache;
+  }
   AttnArgs& at = a.at;
   at.q = q; at.k = k_cache; at.v = v_cache; at.idx = idx; at.n_sel = n_sel; at.seq_lens = seq_lens;
   at.out = out; at.lse = lse;
