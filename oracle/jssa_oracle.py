@@ -13,8 +13,9 @@ step open, the plainest reading is taken and named in the docstring
 
 Conventions
 -----------
-* All arithmetic is float64.  Inputs are either float32 arrays or bf16 bit
-  patterns stored as ``uint16``; ``to_f64`` decodes both exactly.
+* All arithmetic is float64.  Inputs are float32 arrays, bf16 bit patterns
+  stored as ``uint16`` or (projected keys only) FP8 E4M3 codes stored as
+  ``uint8``; ``to_f64`` decodes all three exactly.
 * Shapes: q ``[B, Hq, d_k]``; key/value cache ``[B, T_max, Hkv, d]``;
   basis ``P`` ``[Hkv, d_k, r]``; projected-key cache ``[B, Hkv, T_max, r]``;
   ``G = Hq // Hkv`` query heads per KV head, query head ``hq`` belongs to KV
@@ -32,7 +33,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "to_f64", "round_to_bf16_bits", "project_keys", "project_query",
+    "to_f64", "round_to_bf16_bits", "e4m3_to_f64", "round_to_e4m3_bits", "project_keys", "project_query",
     "subspace_scores", "topk_select", "attention", "dense_attention", "decode",
     "n_selected", "kth_score",
 ]
@@ -42,11 +43,71 @@ __all__ = [
 # number formats
 # ---------------------------------------------------------------------------
 def to_f64(x: np.ndarray) -> np.ndarray:
-    """Exact float64 value of a float32 array or of bf16 bit patterns (uint16)."""
+    """Exact float64 value of a float32 array, of bf16 bit patterns (uint16)
+    or of FP8 E4M3 codes (uint8)."""
     x = np.asarray(x)
     if x.dtype == np.uint16:
         return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if x.dtype == np.uint8:
+        return e4m3_to_f64(x)
     return x.astype(np.float64)
+
+
+def e4m3_to_f64(code: np.ndarray) -> np.ndarray:
+    """Value of FP8 E4M3 codes (the OCP 8-bit floating point format "E4M3",
+    the FP8 of the projected scoring cache, JSSA summary Appendix A.3).
+
+    Bit 7 is the sign, bits 6..3 the exponent field e (bias 7), bits 2..0 the
+    mantissa m: e > 0 encodes (1 + m/8) * 2**(e-7), e == 0 encodes the
+    subnormal m * 2**-9.  The all-ones pattern S.1111.111 is NaN; there are
+    no infinities, so the largest magnitude is 1.75 * 2**8 = 448.
+    """
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
+    out = sign * mag
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def round_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round exact values to FP8 E4M3, round-to-nearest, ties to even,
+    saturating; return the codes (uint8).
+
+    Reading: the pages store the scoring cache in FP8 without saying how
+    values are rounded or whether a scale is applied; this takes the plainest
+    scale-free encoding.  The spacing of representable values around |x| is
+    2**(e-3) with e = floor(log2 |x|) clamped at the smallest normal exponent
+    -6 (which covers the subnormals, spaced 2**-9); ``np.rint`` on x / spacing
+    rounds half to even.  A result above the largest finite value saturates to
+    +-448 (the format has no infinity); NaN becomes 0x7F.  -0.0 keeps its sign.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    fin = np.isfinite(x)
+    ax = np.abs(np.where(fin, x, 0.0))
+    nz = fin & (ax > 0)
+    e = np.full(x.shape, -6, np.int64)
+    e[nz] = np.maximum(np.floor(np.log2(ax[nz])).astype(np.int64), -6)
+    lo = nz & (np.ldexp(1.0, e) > ax) & (e > -6)
+    e[lo] -= 1
+    hi = nz & (np.ldexp(1.0, e + 1) <= ax)
+    e[hi] += 1
+    spacing = np.ldexp(1.0, e - 3)
+    mag = np.where(fin, np.rint(ax / spacing) * spacing, np.inf)
+    mag = np.minimum(mag, 448.0)  # saturate (infinities included)
+    # encode the magnitude: normal (1 + m/8) 2**k for mag >= 2**-6, else m 2**-9
+    code = np.zeros(x.shape, np.int64)
+    norm = mag >= 2.0 ** -6
+    k = np.zeros(x.shape, np.int64)
+    k[norm] = np.floor(np.log2(mag[norm])).astype(np.int64)
+    k[norm & (np.ldexp(1.0, k) > mag)] -= 1
+    k[norm & (np.ldexp(1.0, k + 1) <= mag)] += 1
+    mant = np.where(norm, mag / np.ldexp(1.0, k) * 8.0 - 8.0, mag / 2.0 ** -9)
+    code = np.where(norm, ((k + 7) << 3) | np.rint(mant).astype(np.int64), np.rint(mant).astype(np.int64))
+    code = code | np.where(np.signbit(x), 0x80, 0)
+    code = np.where(np.isnan(x), 0x7F, code)
+    return code.astype(np.uint8)
 
 
 def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -89,13 +150,15 @@ def project_keys(k_cache: np.ndarray, P: np.ndarray, seq_lens: np.ndarray, out_d
 
     JSSA summary §3.1 and §3.4: a scoring-only cache of keys projected onto
     the shared basis is kept per layer and KV head; §E.1: each newly generated
-    key is projected into it at every step.  Appendix A.3 stores it in FP8;
-    here it is stored in the cache dtype ``out_dtype`` ('bf16' -> round to
-    nearest even from the exact float64 product, 'f32' -> float32 rounding).
-    Rows t >= T_b are zero.
+    key is projected into it at every step.  Appendix A.3 stores it in FP8
+    (§E.2: FP8 halves the cache against BF16).  It is stored in the cache
+    dtype ``out_dtype``, rounded once from the exact float64 product: 'bf16'
+    (nearest even, uint16 bits), 'fp8' (E4M3 nearest even, saturating, uint8
+    codes; ``round_to_e4m3_bits``) or 'f32' (float32 rounding).  Rows
+    t >= T_b are zero.
 
-    Returns ``(stored, exact)``: the stored cache (uint16 bits or float32) and
-    the float64 products, both ``[B, Hkv, T_max, r]``.
+    Returns ``(stored, exact)``: the stored cache and the float64 products,
+    both ``[B, Hkv, T_max, r]``.
     """
     B, T, Hkv, _ = k_cache.shape
     r = P.shape[2]
@@ -107,6 +170,8 @@ def project_keys(k_cache: np.ndarray, P: np.ndarray, seq_lens: np.ndarray, out_d
             exact[b, h, :n] = to_f64(k_cache[b, :n, h, :]) @ P64[h]
     if out_dtype == "bf16":
         stored = round_to_bf16_bits(exact)
+    elif out_dtype == "fp8":
+        stored = round_to_e4m3_bits(exact)
     elif out_dtype == "f32":
         stored = exact.astype(np.float32)
     else:

@@ -71,6 +71,73 @@ def test_to_f64_decodes_bits():
     assert O.to_f64(bits).tolist() == want
 
 
+# ----------------------------------------------------------------------------- FP8 E4M3
+def test_e4m3_rounding_golden():
+    """Hand-derived E4M3 round-to-nearest-even cases: ties, subnormals, the
+    largest value and saturation."""
+    rows = []
+    with open(os.path.join(GOLDEN, "e4m3_rne.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            val, code = line.split()[:2]
+            rows.append((float.fromhex(val), int(code, 16)))
+    x = np.array([r[0] for r in rows])
+    want = np.array([r[1] for r in rows], np.uint8)
+    got = O.round_to_e4m3_bits(x)
+    assert (got == want).all(), list(zip(x, got, want))
+    assert len(rows) >= 20
+
+
+def test_e4m3_decoding_matches_format_definition_and_library():
+    """All 256 codes: the OFP8 E4M3 definition written out with exact
+    rationals, and torch's float8_e4m3fn reading of the same bytes."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = O.e4m3_to_f64(codes)
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            assert math.isnan(got[c])
+            continue
+        mag = Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+        assert got[c] == float(-mag if s else mag) and math.copysign(1.0, got[c]) == (-1.0 if s else 1.0)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    assert np.array_equal(np.isnan(got), np.isnan(lib))
+    assert np.array_equal(got[~np.isnan(got)], lib[~np.isnan(lib)])
+    assert np.nanmax(got) == 448.0 and np.nanmin(got) == -448.0
+    assert O.to_f64(np.array([0x38, 0xC0], np.uint8)).tolist() == [1.0, -2.0]
+
+
+def test_e4m3_rounding_brute_force_and_library():
+    """Every code rounds back to itself; every midpoint between neighbouring
+    values goes to the even code and points just beside it to the nearer one;
+    inside the range the rounding equals torch's float32 -> float8_e4m3fn
+    conversion; beyond it, it saturates."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = O.e4m3_to_f64(codes)
+    finite = ~np.isnan(vals)
+    assert (O.round_to_e4m3_bits(vals[finite]) == codes[finite]).all()
+    pos = np.unique(vals[finite & (vals >= 0)])
+    for a, b in zip(pos[:-1], pos[1:]):
+        ca, cb = O.round_to_e4m3_bits(np.array([a, b]))
+        mid = (a + b) / 2
+        even = ca if ca % 2 == 0 else cb
+        assert O.round_to_e4m3_bits(np.array([mid]))[0] == even
+        assert O.round_to_e4m3_bits(np.array([-mid]))[0] == even | 0x80
+        eps = (b - a) * 2.0 ** -20
+        assert O.round_to_e4m3_bits(np.array([mid - eps, mid + eps])).tolist() == [ca, cb]
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.standard_normal(50000) * 3.0, rng.standard_normal(20000) * 0.01,
+                        rng.uniform(-448.0, 448.0, 20000)]).astype(np.float32)
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (O.round_to_e4m3_bits(x.astype(np.float64)) == lib).all()
+    big = np.array([464.0, 470.0, 1e6, np.inf, -500.0, -np.inf])
+    assert O.round_to_e4m3_bits(big).tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE]
+    assert O.round_to_e4m3_bits(np.array([np.nan]))[0] == 0x7F
+    assert O.round_to_e4m3_bits(np.array([0.0, -0.0])).tolist() == [0x00, 0x80]
+
+
 # ----------------------------------------------------------------------------- key projection
 def test_project_keys_identity_basis_is_exact():
     """r = d and P = I: the projected cache holds the keys bit for bit."""
@@ -111,6 +178,31 @@ def test_project_keys_bf16_is_single_rounding_of_exact_product():
     dn = O.to_f64(kp - np.uint16(1))
     assert (np.abs(v - exact) <= np.abs(up - exact)).all()
     assert (np.abs(v - exact) <= np.abs(dn - exact)).all()
+
+
+def test_project_keys_fp8_is_single_rounding_of_exact_product():
+    """FP8 store: the nearest E4M3 value to the exact product (no code lies
+    strictly closer), saturating; the identity basis reproduces keys that are
+    E4M3 values."""
+    rng = np.random.default_rng(4)
+    K = (rng.standard_normal((1, 64, 2, 32)) * 4.0).astype(np.float32)
+    P = np.stack([scipy.stats.ortho_group.rvs(32, random_state=20 + h)[:, :8] for h in range(2)]).astype(np.float32)
+    kp, exact = O.project_keys(K, P, np.array([64], np.int32), "fp8")
+    assert kp.dtype == np.uint8
+    v = O.to_f64(kp)
+    allv = O.e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    allv = allv[~np.isnan(allv)]
+    nearest = np.abs(exact[..., None] - allv).min(axis=-1)
+    assert (np.abs(v - exact) == nearest).all()
+    # identity basis on keys that are E4M3 values: stored bit for bit
+    codes = rng.integers(0, 256, size=(1, 9, 2, 8)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38
+    Kv = O.e4m3_to_f64(codes).astype(np.float32)
+    Pi = np.broadcast_to(np.eye(8, dtype=np.float32), (2, 8, 8)).copy()
+    kpi, _ = O.project_keys(Kv, Pi, np.array([9], np.int32), "fp8")
+    want = codes[0].transpose(1, 0, 2)
+    want = np.where(want == 0x80, 0x00, want)  # -0.0 * 1 + 0.0 * ... sums to +0.0
+    assert (kpi[0] == want).all()
 
 
 # ----------------------------------------------------------------------------- scores
