@@ -17,6 +17,10 @@ per-stage breakdown from HIP events, the roofline of the dominant kernel
 (the projected-key scan), the dense full-KV decode on the same inputs, and the
 CPU oracle timed on a bounded sample on the host cores.
 
+``--kp fp8`` keeps the projected-key cache in FP8 E4M3 (the pages' own
+scoring-cache format) instead of the workload's bf16: the scan reads half the
+bytes.  The default line is the bf16 configuration.
+
 ``--calibrate-copy MB`` instead runs a plain device-to-device copy of MB
 mebibytes a few times and exits: the known-size kernel whose hardware byte
 counters scale those of the scan kernel.
@@ -49,6 +53,8 @@ def parse():
                     choices=["tiny", "llama8b_32k", "ctx128k", "hybrid_ragged", "mla"])
     ap.add_argument("--topk", type=int, default=None, help="override the budget k")
     ap.add_argument("--reduce", default="max", choices=["max", "mean"])
+    ap.add_argument("--kp", default="native", choices=["native", "fp8"],
+                    help="projected-key cache dtype: the workload's own (bf16 / f32) or FP8 E4M3")
     ap.add_argument("--sets", type=int, default=2, help="independent input sets rotated per step")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense full-KV comparison")
@@ -99,8 +105,9 @@ def main():
     dev = torch.device("cuda:0")
     dt = J.BF16 if w.dtype == "bf16" else J.F32
     reduce = J.REDUCE_MAX if args.reduce == "max" else J.REDUCE_MEAN
+    kpt = J.FP8_E4M3 if args.kp == "fp8" else dt
     desc = J.Desc(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, d_k=w.d_k, d_v=w.d_v,
-                  rank=w.rank, t_max=w.t_max, topk=w.topk, window=w.window, kv_dtype=dt, kp_dtype=dt,
+                  rank=w.rank, t_max=w.t_max, topk=w.topk, window=w.window, kv_dtype=dt, kp_dtype=kpt,
                   out_dtype=J.F32, reduce=reduce, layout=J.LAYOUT_MLA if w.mla else J.LAYOUT_GQA,
                   scale=w.scale)
 
@@ -112,12 +119,13 @@ def main():
     # ---- inputs: independent seeded sets, resident in HBM ---------------------------------
     sets, host0 = [], None
     tdt = torch.bfloat16 if dt == J.BF16 else torch.float32
+    kpdt = torch.uint8 if kpt == J.FP8_E4M3 else tdt
     for si in range(args.sets):
         t0 = time.time()
         inp = generate(w, seed=w.seed + 100 * si)
         s = {k: up(inp[k]) for k in ("q", "P", "k_cache", "seq_lens")}
         s["v_cache"] = None if w.mla else up(inp["v_cache"])  # MLA: the value is a prefix of K
-        s["kp"] = torch.empty((w.batch, w.n_kv_heads, w.t_max, w.rank), dtype=tdt, device=dev)
+        s["kp"] = torch.empty((w.batch, w.n_kv_heads, w.t_max, w.rank), dtype=kpdt, device=dev)
         J.append_projection(desc, w.t_max, torch.zeros(w.batch, dtype=torch.int32, device=dev),
                             s["P"], s["k_cache"], s["kp"])
         # the new token of each step: written at position T_b - 1
@@ -183,7 +191,8 @@ def main():
     n_cand = np.maximum(L - w.window, 0)
     n_sel = np.minimum(w.window, L) + np.minimum(w.topk, n_cand)
     eb = 2 if dt == J.BF16 else 4
-    kp_bytes = int(n_cand.sum()) * w.n_kv_heads * w.rank * eb
+    kp_eb = 1 if kpt == J.FP8_E4M3 else eb
+    kp_bytes = int(n_cand.sum()) * w.n_kv_heads * w.rank * kp_eb
     row_bytes = w.d_k * eb if w.mla else (w.d_k + w.d_v) * eb  # MLA: a latent row is read once
     sel_bytes = int(n_sel.sum()) * w.n_kv_heads * row_bytes
     eff_bytes = kp_bytes + sel_bytes
@@ -193,7 +202,8 @@ def main():
 
     traffic = None
     kname = "mla_score_kernel" if w.mla else "scan_kernel"
-    tpath = os.path.join(ROOT, "profiles", f"{kname}_{args.workload}_traffic.json")
+    wl = args.workload + ("_kpfp8" if kpt == J.FP8_E4M3 else "")
+    tpath = os.path.join(ROOT, "profiles", f"{kname}_{wl}_traffic.json")
     if os.path.exists(tpath):
         try:
             with open(tpath) as f:
@@ -210,10 +220,12 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if dt == J.BF16 else "f32", "data": "synthetic (seeded, resident in HBM)",
-        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.n_q_heads,
+        "config": {"workload": w.name + ("-kp-fp8" if kpt == J.FP8_E4M3 else ""), "batch": w.batch,
+                   "q_heads": w.n_q_heads,
                    "kv_heads": w.n_kv_heads, "head_dim": w.d_k, "value_dim": w.d_v,
                    "layout": "mla" if w.mla else "gqa", "rank": w.rank, "context": w.t_max,
                    "topk": w.topk, "window": w.window, "reduce": args.reduce,
+                   "kp_dtype": {J.BF16: "bf16", J.F32: "f32", J.FP8_E4M3: "fp8_e4m3"}[kpt],
                    "step": "append new token + fused sparse decode", "input_sets": args.sets},
         "eff_bytes_per_step": eff_bytes, "eff_GBps": round(eff_gbps, 1),
         "pct_peak": round(100.0 * eff_gbps / HBM_PEAK_GBPS, 2),
@@ -249,11 +261,12 @@ def main():
 
     # ---- CPU oracle on a bounded sample ------------------------------------------------------------
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(w, host0, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, host0, args.cpu_seconds,
+                                              "fp8" if kpt == J.FP8_E4M3 else w.dtype)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(w, host0, budget_s):
+def cpu_baseline(w, host0, budget_s, kp_dtype):
     """The fp64 oracle (scores on the stored projected keys, full-sort top-k,
     exact softmax attention) on sequence 0 of input set 0, all KV heads; repeated
     within the time budget, best run scaled to the whole batch."""
@@ -265,7 +278,7 @@ def cpu_baseline(w, host0, budget_s):
     except Exception:
         threads = 1
     seq = host0["seq_lens"][:1]
-    kp, _ = O.project_keys(host0["k_cache"], host0["P"], seq, "bf16" if w.dtype == "bf16" else "f32")
+    kp, _ = O.project_keys(host0["k_cache"], host0["P"], seq, kp_dtype)
     best, runs, t_all = float("inf"), 0, time.perf_counter()
     while runs < 3 or (time.perf_counter() - t_all < budget_s and runs < 50):
         t0 = time.perf_counter()

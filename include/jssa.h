@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define JSSA_ABI_VERSION 3
+#define JSSA_ABI_VERSION 4
 
 typedef enum {
   JSSA_OK = 0,
@@ -70,7 +70,13 @@ typedef enum {
   JSSA_ERR_HIP = -5           /* a HIP launch failed */
 } jssa_status;
 
-typedef enum { JSSA_F32 = 0, JSSA_BF16 = 1 } jssa_dtype;
+/* JSSA_FP8_E4M3 (the OCP 8-bit format E4M3: bias 7, largest value 448, no
+ * infinity) is a projected-key cache dtype only (JSSA summary appendix A.3:
+ * the scoring cache is FP8; section E.2: it halves that cache against bf16).
+ * Codes are stored one byte per element, scale-free; the projection rounds to
+ * nearest even and saturates at +-448.  Built for GQA with bf16 q/K/V and
+ * rank 32 or 64. */
+typedef enum { JSSA_F32 = 0, JSSA_BF16 = 1, JSSA_FP8_E4M3 = 2 } jssa_dtype;
 
 /* How a KV head reduces the subspace scores of its G query heads.
  * MAX: s_t = max_g (q_g P).Kp_t.  MEAN: s_t = mean_g (q_g P).Kp_t, which is

@@ -37,7 +37,7 @@ def to_host(t: torch.Tensor) -> np.ndarray:
 
 
 def kp_dtype_str(desc: J.Desc) -> str:
-    return "bf16" if desc.kp_dtype == J.BF16 else "f32"
+    return {J.BF16: "bf16", J.F32: "f32", J.FP8_E4M3: "fp8"}[desc.kp_dtype]
 
 
 def oracle_kp(inp: dict, desc: J.Desc) -> np.ndarray:

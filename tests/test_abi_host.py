@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert J.abi_version() == 3
+    assert J.abi_version() == 4
     lib = J.lib()
     assert lib.jssa_status_str(0) == b"JSSA_OK"
     for code, name in _lib.STATUS.items():
@@ -66,6 +66,13 @@ def test_struct_layout_matches_header():
     (dict(d_v=64), -2),
     (dict(n_q_heads=48, n_kv_heads=3), -2),  # G = 16
     (dict(rank=256, d_k=128), -1),     # rank > d_k
+    (dict(kp_dtype=J.FP8_E4M3), 0),     # FP8 projected keys, rank 32
+    (dict(kp_dtype=J.FP8_E4M3, rank=64), 0),
+    (dict(kp_dtype=J.FP8_E4M3, rank=16), -2),  # FP8 keys are scored on the matrix cores only
+    (dict(kp_dtype=J.FP8_E4M3, kv_dtype=J.F32), -2),
+    (dict(kv_dtype=J.FP8_E4M3), -1),    # q, K and V are never FP8
+    (dict(out_dtype=J.FP8_E4M3), -1),
+    (dict(kp_dtype=3), -1),
 ])
 def test_descriptor_validation(kw, status):
     assert J.check_desc(_desc(**kw), J.OP_DECODE) == status
@@ -147,6 +154,7 @@ def _mla(**kw):
     (dict(d_k=512, d_v=448), -2),
     (dict(kv_dtype=J.F32, kp_dtype=J.F32), -2),
     (dict(kp_dtype=J.F32), -2),
+    (dict(kp_dtype=J.FP8_E4M3), -2),          # MLA keeps bf16 projected keys
 ])
 def test_mla_descriptor_validation(kw, status):
     for op in (J.OP_DECODE, J.OP_SCORE, J.OP_ATTN, J.OP_DENSE, 0):

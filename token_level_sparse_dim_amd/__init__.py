@@ -9,17 +9,19 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import (BF16, F32, LAYOUT_GQA, LAYOUT_MLA, OP_ATTN, OP_DECODE, OP_DENSE, OP_SCORE, OP_TOPK,
+from ._lib import (BF16, F32, FP8_E4M3, LAYOUT_GQA, LAYOUT_MLA, OP_ATTN, OP_DECODE, OP_DENSE, OP_SCORE,
+                   OP_TOPK,
                    REDUCE_MAX, REDUCE_MEAN, Desc, JssaError, call, lib)
 
 __all__ = [
-    "Desc", "JssaError", "F32", "BF16", "REDUCE_MAX", "REDUCE_MEAN", "LAYOUT_GQA", "LAYOUT_MLA",
+    "Desc", "JssaError", "F32", "BF16", "FP8_E4M3", "REDUCE_MAX", "REDUCE_MEAN", "LAYOUT_GQA", "LAYOUT_MLA",
     "OP_TOPK", "OP_ATTN", "OP_DECODE", "OP_DENSE", "OP_SCORE", "lib", "abi_version", "check_desc",
     "workspace_bytes", "workspace", "append_kv", "append_projection", "score", "topk", "indexed_attn", "decode", "decode_profiled",
     "decode_step", "dense_decode",
 ]
 
-_TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
+# FP8 E4M3 projected keys travel as their byte codes
+_TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, FP8_E4M3: torch.uint8}
 
 
 def _ptr(t, dtype=None, name="tensor"):

@@ -13,7 +13,7 @@ from dataclasses import dataclass
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjssa.so")
 
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2  # FP8_E4M3: projected-key caches only (uint8 codes)
 REDUCE_MAX, REDUCE_MEAN = 0, 1
 LAYOUT_GQA, LAYOUT_MLA = 0, 1
 OP_TOPK, OP_ATTN, OP_DECODE, OP_DENSE, OP_SCORE = 1, 2, 3, 4, 5

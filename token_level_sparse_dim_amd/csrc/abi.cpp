@@ -66,7 +66,8 @@ static int32_t check(const jssa_desc* d, int op) {
   if (selects && int64_t(d->topk) + d->window < 1) return JSSA_ERR_INVALID_ARG;
   if (int64_t(d->topk) + d->window > (int64_t(1) << 30)) return JSSA_ERR_INVALID_ARG;
   if (d->kv_dtype != JSSA_F32 && d->kv_dtype != JSSA_BF16) return JSSA_ERR_INVALID_ARG;
-  if (d->kp_dtype != JSSA_F32 && d->kp_dtype != JSSA_BF16) return JSSA_ERR_INVALID_ARG;
+  if (d->kp_dtype != JSSA_F32 && d->kp_dtype != JSSA_BF16 && d->kp_dtype != JSSA_FP8_E4M3)
+    return JSSA_ERR_INVALID_ARG;
   if (d->out_dtype != JSSA_F32 && d->out_dtype != JSSA_BF16) return JSSA_ERR_INVALID_ARG;
   if (d->reduce != JSSA_REDUCE_MAX && d->reduce != JSSA_REDUCE_MEAN) return JSSA_ERR_INVALID_ARG;
   if (d->layout != JSSA_LAYOUT_GQA && d->layout != JSSA_LAYOUT_MLA) return JSSA_ERR_INVALID_ARG;
@@ -86,6 +87,9 @@ static int32_t check(const jssa_desc* d, int op) {
   if (d->d_k != d->d_v) return JSSA_ERR_UNSUPPORTED;
   if (d->d_k != 64 && d->d_k != 128) return JSSA_ERR_UNSUPPORTED;
   if (G != 1 && G != 2 && G != 4 && G != 8) return JSSA_ERR_UNSUPPORTED;
+  // FP8 projected keys: scored on the matrix cores (bf16 q/K/V, rank 32 or 64)
+  if (d->kp_dtype == JSSA_FP8_E4M3 && (d->kv_dtype != JSSA_BF16 || (d->rank != 32 && d->rank != 64)))
+    return JSSA_ERR_UNSUPPORTED;
   return JSSA_OK;
 }
 

@@ -76,6 +76,16 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       w.w = uint32_t(f32_to_bf16_rne(acc[i + 6])) | (uint32_t(f32_to_bf16_rne(acc[i + 7])) << 16);
       *reinterpret_cast<uint4*>(kprow + i * 2) = w;
     }
+  } else if constexpr (KPT == 2) {
+#pragma unroll
+    for (int i = 0; i < R; i += 16) {
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[k] = f32_to_e4m3_sat(acc[i + 4 * k]) | (f32_to_e4m3_sat(acc[i + 4 * k + 1]) << 8) |
+               (f32_to_e4m3_sat(acc[i + 4 * k + 2]) << 16) | (f32_to_e4m3_sat(acc[i + 4 * k + 3]) << 24);
+      *reinterpret_cast<uint4*>(kprow + i) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < R; i += 4)
@@ -130,6 +140,7 @@ __global__ __launch_bounds__(256) void append_rows_kernel(AppendArgs a) {
     for (int pp = 0; pp < PARTS; ++pp) sum += s_part[pp * R + threadIdx.x];
     char* kprow = reinterpret_cast<char*>(a.kp) + ((size_t(b) * a.Hkv + h) * a.t_max + t) * R * Elem<KPT>::bytes;
     if constexpr (KPT == 1) reinterpret_cast<uint16_t*>(kprow)[threadIdx.x] = f32_to_bf16_rne(sum);
+    else if constexpr (KPT == 2) reinterpret_cast<uint8_t*>(kprow)[threadIdx.x] = uint8_t(f32_to_e4m3_sat(sum));
     else reinterpret_cast<float*>(kprow)[threadIdx.x] = sum;
   }
 }
@@ -185,6 +196,7 @@ __global__ __launch_bounds__(256) void append_new_kernel(AppendArgs a) {
     for (int pp = 0; pp < PARTS; ++pp) sum += s_part[pp * R + threadIdx.x];
     char* kprow = reinterpret_cast<char*>(a.kp) + ((size_t(b) * a.Hkv + h) * a.t_max + t) * R * Elem<KPT>::bytes;
     if constexpr (KPT == 1) reinterpret_cast<uint16_t*>(kprow)[threadIdx.x] = f32_to_bf16_rne(sum);
+    else if constexpr (KPT == 2) reinterpret_cast<uint8_t*>(kprow)[threadIdx.x] = uint8_t(f32_to_e4m3_sat(sum));
     else reinterpret_cast<float*>(kprow)[threadIdx.x] = sum;
   }
 }
@@ -242,6 +254,10 @@ hipError_t launch_append(const jssa_desc& d, const void* k_new, const void* v_ne
   a.mla = d.layout == JSSA_LAYOUT_MLA;
   dim3 grid((n_new + 255) / 256, d.n_kv_heads, d.batch);
   const bool kvb = d.kv_dtype == JSSA_BF16, kpb = d.kp_dtype == JSSA_BF16;
+  if (d.kp_dtype == JSSA_FP8_E4M3) {
+    if (!kvb) return hipErrorInvalidValue;
+    return dispatch_append_r<1, 2>(a, d.rank, grid, s);
+  }
   if (kvb && kpb) return dispatch_append_r<1, 1>(a, d.rank, grid, s);
   if (kvb && !kpb) return dispatch_append_r<1, 0>(a, d.rank, grid, s);
   if (!kvb && kpb) return dispatch_append_r<0, 1>(a, d.rank, grid, s);

@@ -12,13 +12,47 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ---- elements ------------------------------------------------------------------
-// DT = 0: float32, DT = 1: bfloat16 (stored as uint16 bit patterns).
+// DT = 0: float32, DT = 1: bfloat16 (stored as uint16 bit patterns), DT = 2:
+// FP8 E4M3 (OCP E4M3: bias 7, largest value 448, no infinity; the projected
+// scoring cache only).
 template <int DT> struct Elem;
 template <> struct Elem<0> { static constexpr int bytes = 4; static constexpr int per16 = 4; };
 template <> struct Elem<1> { static constexpr int bytes = 2; static constexpr int per16 = 8; };
+template <> struct Elem<2> { static constexpr int bytes = 1; static constexpr int per16 = 16; };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+// Two E4M3 codes (byte 2*HI and 2*HI+1 of w) -> their values; every E4M3
+// value is a float (gfx950 reads the OCP encoding).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+template <bool HI>
+__device__ __forceinline__ f32x2_t e4m3x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+}
+// Four E4M3 codes (a word) -> four bfloat16 values in two words (exact: an
+// E4M3 value has 4 significant bits and an exponent inside bfloat16's range).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+struct u32pair {
+  uint32_t lo, hi;  // codes 0-1 and 2-3
+};
+__device__ __forceinline__ u32pair e4m3x4_to_bf16(uint32_t w) {
+  return {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
+}
+// Eight E4M3 codes (two words) -> the 8-element bf16 operand of one K-step.
+__device__ __forceinline__ u32x4_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const u32pair a = e4m3x4_to_bf16(w0), b = e4m3x4_to_bf16(w1);
+  return u32x4_t{a.lo, a.hi, b.lo, b.hi};
+}
+// float -> E4M3 code, round to nearest, ties to even, saturating at +-448 (the
+// conversion instruction rounds to nearest even; the clamp makes magnitudes
+// past 448 saturate instead of becoming NaN).  NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float f) {
+  const float c = (f != f) ? f : fminf(fmaxf(f, -448.f), 448.f);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0u, false) & 0xffu;
+}
 
 // Unpack one 16-byte vector into Elem<DT>::per16 floats (exact).
 template <int DT>
@@ -26,6 +60,13 @@ __device__ __forceinline__ void unpack16(const uint4& v, float* out) {
   if constexpr (DT == 0) {
     out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
     out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
+  } else if constexpr (DT == 2) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2_t a = e4m3x2_to_f32<false>(w[i]), b = e4m3x2_to_f32<true>(w[i]);
+      out[4 * i + 0] = a.x; out[4 * i + 1] = a.y; out[4 * i + 2] = b.x; out[4 * i + 3] = b.y;
+    }
   } else {
     out[0] = bf16_lo(v.x); out[1] = bf16_hi(v.x); out[2] = bf16_lo(v.y); out[3] = bf16_hi(v.y);
     out[4] = bf16_lo(v.z); out[5] = bf16_hi(v.z); out[6] = bf16_lo(v.w); out[7] = bf16_hi(v.w);
@@ -38,7 +79,6 @@ __device__ __forceinline__ uint4 load16(const void* p) {
 
 // 16-byte load with the nontemporal hint: for data streamed once (the
 // projected-key scan, K/V rows), so it does not displace reusable lines.
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load16_nt(const void* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);

@@ -37,7 +37,7 @@
 
 namespace jssa {
 
-constexpr int kPipeNit = 4;            // workgroup steps per tile
+constexpr int kPipeTileTokens = 1024;  // tokens per tile (at least two workgroup steps)
 constexpr int kPipePF = 3;             // score-scan steps in flight per workgroup
 constexpr int kPipeMaxItem = 8192;     // tokens per score item at most (whole tiles)
 constexpr int kPipeCandLds = 8192;     // candidates resolved in shared memory
@@ -55,6 +55,9 @@ constexpr uint64_t kLwSet = uint64_t(1) << 32;
 constexpr uint64_t kLwAppended = uint64_t(1) << 33;
 // per-row state word of the scan: claims of the row's shared tiles (reset by the resolve)
 constexpr int PW_STEAL = 14;
+#ifndef JSSA_PIPE_PER_CU
+#define JSSA_PIPE_PER_CU 3  // scan workgroups per compute unit at most (0: as many as fit)
+#endif
 #ifndef JSSA_PIPE_STATIC_PCT
 #define JSSA_PIPE_STATIC_PCT 70  // share of a row's tiles covered by the static score runs
 #endif
@@ -300,9 +303,9 @@ __device__ __forceinline__ void project_query_staged(const PipeArgs& a, int b, i
 template <int KPT, int R, int GE, int D, int G, int KVT>
 struct Pipe {
   using S = ScanShape<KPT, R>;
-  static constexpr int TS = kPipeNit * S::PER_ITER;  // tokens per tile
-  static_assert(kPipeMaxItem % TS == 0, "score items are whole tiles");
-  static constexpr int NW = kPipeNit * S::U;  // keys per lane per tile
+  static constexpr int TS = kPipeTileTokens > 2 * S::PER_ITER ? kPipeTileTokens : 2 * S::PER_ITER;  // tokens per tile
+  static constexpr int NIT = TS / S::PER_ITER;  // workgroup steps per tile
+  static_assert(kPipeMaxItem % TS == 0 && NIT % 2 == 0, "score items are whole tiles of whole step pairs");
   static constexpr int NSAMP = TS;            // sample size (one block of loads)
   static constexpr int RT = kResolveThreads, RW = RT / 64;  // resolve workgroup: threads, waves
   using Qp = QpSmem<D, R, G>;
@@ -406,7 +409,9 @@ struct Pipe {
     if (threadIdx.x < R) {
       float sum = 0.f;
       for (int pp = 0; pp < kAppendParts; ++pp) sum += sm.apart[pp * R + threadIdx.x];
-      sm.akp[threadIdx.x] = KPT == 1 ? uint32_t(f32_to_bf16_rne(sum)) : __float_as_uint(sum);
+      sm.akp[threadIdx.x] = KPT == 1   ? uint32_t(f32_to_bf16_rne(sum))
+                            : KPT == 2 ? f32_to_e4m3_sat(sum)
+                                       : __float_as_uint(sum);
     }
     __syncthreads();
     if (ok) {
@@ -415,6 +420,11 @@ struct Pipe {
         if (threadIdx.x < R / 2)
           publish(reinterpret_cast<uint32_t*>(kprow) + threadIdx.x,
                   sm.akp[2 * threadIdx.x] | (sm.akp[2 * threadIdx.x + 1] << 16));
+      } else if constexpr (KPT == 2) {
+        if (threadIdx.x < R / 4) {
+          const uint32_t* c = sm.akp + 4 * threadIdx.x;
+          publish(reinterpret_cast<uint32_t*>(kprow) + threadIdx.x, c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24));
+        }
       } else {
         if (threadIdx.x < R) publish(reinterpret_cast<uint32_t*>(kprow) + threadIdx.x, sm.akp[threadIdx.x]);
       }
@@ -475,7 +485,7 @@ struct Pipe {
       if (m < n_samp) {
         // the sampled projected keys are requested before the query projection
         const char* kr = kp_row(a, row);
-        constexpr int HALF = kPipeNit / 2;  // steps per batch of loads
+        constexpr int HALF = NIT / 2;  // steps per batch of loads
         auto load_half = [&](int it0, uint4 (&v)[HALF][S::U]) {
 #pragma unroll
           for (int it = 0; it < HALF; ++it)
@@ -1123,25 +1133,28 @@ __global__ __launch_bounds__(D) void merge_kernel(PipeArgs a) {
 }
 
 // ---- host side ------------------------------------------------------------------------------
-// Shapes with a fused build: (kv/kp dtype, d, rank, G).  Others run the staged launches.
+// Shapes with a fused build: (kv dtype, kp dtype, d, rank, G).  Others run the staged launches.
 struct PipeShape {
-  int dt, d, r, g;
+  int kv, kp, d, r, g;
 };
 static const PipeShape kPipeShapes[] = {
-    {JSSA_BF16, 128, 32, 4}, {JSSA_BF16, 128, 64, 1}, {JSSA_BF16, 64, 16, 4},
-    {JSSA_F32, 64, 16, 4},   {JSSA_F32, 128, 32, 2},
+    {JSSA_BF16, JSSA_BF16, 128, 32, 4},     {JSSA_BF16, JSSA_BF16, 128, 64, 1},
+    {JSSA_BF16, JSSA_BF16, 64, 16, 4},      {JSSA_F32, JSSA_F32, 64, 16, 4},
+    {JSSA_F32, JSSA_F32, 128, 32, 2},       {JSSA_BF16, JSSA_FP8_E4M3, 128, 32, 4},
+    {JSSA_BF16, JSSA_FP8_E4M3, 128, 64, 1},
 };
 
 static int scan_tile_tokens(int dt, int r) {
-  const int per16 = dt == JSSA_BF16 ? 8 : 4;
-  return kPipeNit * 4 * (64 / (r / per16)) * JSSA_SCORE_UNROLL;
+  const int per16 = dt == JSSA_FP8_E4M3 ? 16 : dt == JSSA_BF16 ? 8 : 4;
+  const int per_iter = 4 * (64 / (r / per16)) * JSSA_SCORE_UNROLL;
+  return kPipeTileTokens > 2 * per_iter ? kPipeTileTokens : 2 * per_iter;
 }
 
 bool pipeline_layout(const jssa_desc& d, int* ts, int* n_tiles, int* chunk) {
   const int G = d.n_q_heads / d.n_kv_heads;
   bool ok = false;
   for (const PipeShape& s : kPipeShapes)
-    ok |= (d.kv_dtype == s.dt && d.kp_dtype == s.dt && d.d_k == s.d && d.rank == s.r && G == s.g);
+    ok |= (d.kv_dtype == s.kv && d.kp_dtype == s.kp && d.d_k == s.d && d.rank == s.r && G == s.g);
   if (!ok || d.layout != JSSA_LAYOUT_GQA) return false;
   *ts = scan_tile_tokens(d.kp_dtype, d.rank);
   *n_tiles = (d.t_max + *ts - 1) / *ts;
@@ -1190,6 +1203,9 @@ static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_kernel<KPT, R, GE, D, G, KVT>, 256, 0) != hipSuccess ||
         n < 1)
       n = 1;
+#if JSSA_PIPE_PER_CU > 0
+    if (n > JSSA_PIPE_PER_CU) n = JSSA_PIPE_PER_CU;
+#endif
     per_cu = n;
   }
   const int resident = per_cu * compute_units();
@@ -1220,10 +1236,10 @@ static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
   return mark(3);
 }
 
-template <int DT, int D, int R, int G>
+template <int KVT, int KPT, int D, int R, int G>
 static hipError_t launch_pipe_reduce(const PipeArgs& a, bool mean, void* const* ev, hipStream_t s) {
-  if (mean) return launch_pipe_t<DT, R, 1, D, G, DT>(a, ev, s);
-  return launch_pipe_t<DT, R, G, D, G, DT>(a, ev, s);
+  if (mean) return launch_pipe_t<KPT, R, 1, D, G, KVT>(a, ev, s);
+  return launch_pipe_t<KPT, R, G, D, G, KVT>(a, ev, s);
 }
 
 hipError_t launch_pipeline(const jssa_desc& d, const void* q, const float* P, const void* kp,
@@ -1258,13 +1274,16 @@ hipError_t launch_pipeline(const jssa_desc& d, const void* q, const float* P, co
   a.spin_ticks = wait_ticks();
   const int G = a.G;
   const bool mean = d.reduce == JSSA_REDUCE_MEAN;
-  if (d.kv_dtype == JSSA_BF16) {
-    if (d.d_k == 128 && d.rank == 32 && G == 4) return launch_pipe_reduce<1, 128, 32, 4>(a, mean, ev, s);
-    if (d.d_k == 128 && d.rank == 64 && G == 1) return launch_pipe_reduce<1, 128, 64, 1>(a, mean, ev, s);
-    if (d.d_k == 64 && d.rank == 16 && G == 4) return launch_pipe_reduce<1, 64, 16, 4>(a, mean, ev, s);
+  if (d.kv_dtype == JSSA_BF16 && d.kp_dtype == JSSA_FP8_E4M3) {
+    if (d.d_k == 128 && d.rank == 32 && G == 4) return launch_pipe_reduce<1, 2, 128, 32, 4>(a, mean, ev, s);
+    if (d.d_k == 128 && d.rank == 64 && G == 1) return launch_pipe_reduce<1, 2, 128, 64, 1>(a, mean, ev, s);
+  } else if (d.kv_dtype == JSSA_BF16) {
+    if (d.d_k == 128 && d.rank == 32 && G == 4) return launch_pipe_reduce<1, 1, 128, 32, 4>(a, mean, ev, s);
+    if (d.d_k == 128 && d.rank == 64 && G == 1) return launch_pipe_reduce<1, 1, 128, 64, 1>(a, mean, ev, s);
+    if (d.d_k == 64 && d.rank == 16 && G == 4) return launch_pipe_reduce<1, 1, 64, 16, 4>(a, mean, ev, s);
   } else {
-    if (d.d_k == 64 && d.rank == 16 && G == 4) return launch_pipe_reduce<0, 64, 16, 4>(a, mean, ev, s);
-    if (d.d_k == 128 && d.rank == 32 && G == 2) return launch_pipe_reduce<0, 128, 32, 2>(a, mean, ev, s);
+    if (d.d_k == 64 && d.rank == 16 && G == 4) return launch_pipe_reduce<0, 0, 64, 16, 4>(a, mean, ev, s);
+    if (d.d_k == 128 && d.rank == 32 && G == 2) return launch_pipe_reduce<0, 0, 128, 32, 2>(a, mean, ev, s);
   }
   return hipErrorInvalidValue;
 }

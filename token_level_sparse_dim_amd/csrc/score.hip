@@ -180,6 +180,11 @@ hipError_t launch_score(const jssa_desc& d, const void* q, const float* P, const
   a.d_k = d.d_k; a.t_max = d.t_max; a.topk = d.topk; a.window = d.window; a.q_dtype = d.kv_dtype;
   const int ge = (d.reduce == JSSA_REDUCE_MEAN) ? 1 : a.G;
   dim3 grid((d.t_max + kScoreTile - 1) / kScoreTile, d.n_kv_heads, d.batch);
+  if (d.kp_dtype == JSSA_FP8_E4M3) {  // matrix-core shapes only
+    if (d.rank == 32) return dispatch_ge<2, 32>(a, ge, grid, s);
+    if (d.rank == 64) return dispatch_ge<2, 64>(a, ge, grid, s);
+    return hipErrorInvalidValue;
+  }
   if (d.kp_dtype == JSSA_BF16) return dispatch_r<1>(a, d.rank, ge, grid, s);
   return dispatch_r<0>(a, d.rank, ge, grid, s);
 }
