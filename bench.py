@@ -28,6 +28,7 @@ counters scale those of the scan kernel.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -58,6 +59,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=2, help="independent input sets rotated per step")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense full-KV comparison")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the gather-free vs gather-then-attend attention-stage comparison")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="only run a device copy of MB MiB (counter calibration) and exit")
@@ -259,11 +262,60 @@ def main():
         log(f"dense: {dense_ms * 1e3:.1f} us/step, speedup {dense_ms / ms_step:.2f}x")
         del wsd
 
+    # ---- attention stage: gather-free vs gather-then-attend on the same selection -------------------
+    if not args.no_ablation:
+        result["attention_stage"] = attention_ablation(J, w, desc, sets[0], stream, max(20, args.steps // 4))
+
     # ---- CPU oracle on a bounded sample ------------------------------------------------------------
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, host0, args.cpu_seconds,
                                               "fp8" if kpt == J.FP8_E4M3 else w.dtype)
     print(json.dumps(result), flush=True)
+
+
+def attention_ablation(J, w, desc, s, stream, reps):
+    """The pages' attention-stage comparison (JSSA summary section 4.7: the same
+    selected tokens attended gather-free vs gathered first): one decode's index
+    lists, then (a) the stand-alone gather-free indexed attention, (b) the
+    gather of the selected K/V rows into packed buffers followed by the dense
+    decode over them.  Averages over `reps` launches of each."""
+    import torch
+    S = w.topk + w.window
+    dev = s["q"].device
+    idx = torch.full((w.batch, w.n_kv_heads, S), -1, dtype=torch.int32, device=dev)
+    n_sel = torch.zeros((w.batch, w.n_kv_heads), dtype=torch.int32, device=dev)
+    out = torch.empty((w.batch, w.n_q_heads, w.d_v), device=dev)
+    lse = torch.empty((w.batch, w.n_q_heads), device=dev)
+    J.decode(desc, s["q"], s["P"], s["kp"], s["k_cache"], s["v_cache"], s["seq_lens"], out, lse,
+             J.workspace(desc, J.OP_DECODE, device=dev), idx_out=idx, n_sel_out=n_sel)
+    kv = s["k_cache"].dtype
+    Kg = torch.empty((w.batch, S, w.n_kv_heads, w.d_k), dtype=kv, device=dev)
+    Vg = None if w.mla else torch.empty((w.batch, S, w.n_kv_heads, w.d_v), dtype=kv, device=dev)
+    lens = torch.empty((w.batch,), dtype=torch.int32, device=dev)
+    pdesc = dataclasses.replace(desc, t_max=S, topk=S, window=0)  # the packed rows as a cache
+    ws_a, ws_d = J.workspace(desc, J.OP_ATTN, device=dev), J.workspace(pdesc, J.OP_DENSE, device=dev)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    t_free = timed(lambda: J.indexed_attn(desc, s["q"], s["k_cache"], s["v_cache"], idx, n_sel, out, lse, ws_a))
+    t_gather = timed(lambda: J.gather_kv(desc, s["k_cache"], s["v_cache"], idx, n_sel, Kg, Vg, lens))
+    t_dense = timed(lambda: J.dense_decode(pdesc, s["q"], Kg, Vg, lens, out, lse, ws_d))
+    res = {"gather_free_us": round(t_free, 2), "gather_us": round(t_gather, 2),
+           "dense_on_packed_us": round(t_dense, 2), "gather_then_attend_us": round(t_gather + t_dense, 2),
+           "gather_free_speedup": round((t_gather + t_dense) / t_free, 3), "reps": reps}
+    log(f"attention stage: gather-free {t_free:.2f} us, gather {t_gather:.2f} + dense on packed "
+        f"{t_dense:.2f} us ({res['gather_free_speedup']:.2f}x)")
+    return res
 
 
 def cpu_baseline(w, host0, budget_s, kp_dtype):

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define JSSA_ABI_VERSION 4
+#define JSSA_ABI_VERSION 5
 
 typedef enum {
   JSSA_OK = 0,
@@ -246,6 +246,23 @@ int32_t jssa_decode_step(const jssa_desc* desc, const void* k_new, const void* v
                          void* k_cache, void* v_cache, const int32_t* seq_lens, void* out,
                          float* lse, int32_t* idx_out, int32_t* n_sel_out, void* ws,
                          size_t ws_bytes, void* const* stage_events, void* stream);
+
+/* Gather of the selected rows into packed buffers: the first half of the
+ * gather-then-attend baseline that gather-free execution is compared against
+ * (JSSA summary section 2.2 and Figure 2(b); section 4.7: with the same
+ * selected tokens, gather-free execution roughly doubles the attention-stage
+ * speedup).  For i < n_sel[b,h] (S = topk + window):
+ *   k_packed[b,i,h,:] = k_cache[b, idx[b,h,i], h, :]   (v likewise)
+ * with indices clamped into [0, t_max) as the attention clamps them; entries
+ * i >= n_sel are not written.  The packed buffers [B, S, Hkv, d] keep the
+ * cache layout, so jssa_dense_decode with t_max = S and seq_lens =
+ * packed_lens attends over exactly the selected rows.  packed_lens (int32
+ * [B], may be NULL) receives n_sel[b, 0].  MLA: one index list per sequence
+ * (Hkv = 1), whole latent rows packed, v_cache / v_packed unused (may be
+ * NULL).  No workspace. */
+int32_t jssa_gather_kv(const jssa_desc* desc, const void* k_cache, const void* v_cache,
+                       const int32_t* idx, const int32_t* n_sel, void* k_packed, void* v_packed,
+                       int32_t* packed_lens, void* stream);
 
 /* Full-KV decode attention over all t < seq_lens[b] (the comparison path of
  * JSSA summary section 4.5), same outputs as jssa_indexed_attn.

@@ -35,7 +35,7 @@ import numpy as np
 __all__ = [
     "to_f64", "round_to_bf16_bits", "e4m3_to_f64", "round_to_e4m3_bits", "project_keys", "project_query",
     "subspace_scores", "topk_select", "attention", "dense_attention", "decode",
-    "n_selected", "kth_score",
+    "n_selected", "kth_score", "gather_rows",
 ]
 
 
@@ -337,6 +337,28 @@ def dense_attention(q, k_cache, v_cache, seq_lens, scale: float):
         idx[b, :, :Tb] = np.arange(Tb, dtype=np.int32)
         n_sel[b, :] = Tb
     return attention(q, k_cache, v_cache, idx, n_sel, scale)
+
+
+def gather_rows(cache: np.ndarray, idx: np.ndarray, n_sel: np.ndarray) -> np.ndarray:
+    """The gather of the gather-then-attend baseline: the selected rows copied,
+    in list order, into a packed buffer ``[B, S, Hkv, d]`` (S = idx.shape[2]):
+    ``packed[b, i, h] = cache[b, idx[b, h, i], h]`` for i < n_sel[b, h], zero
+    past it.
+
+    JSSA summary §2.2 and Figure 2(b): gathering the selected KV entries into
+    a contiguous buffer before attention is the cost gather-free execution
+    (§3.3) avoids; §4.7 compares the two on the same selected tokens.
+    Attending densely over the first n_sel packed rows is the same attention
+    as ``attention`` over the index list.
+    """
+    B, _, Hkv, d = cache.shape
+    S = idx.shape[2]
+    out = np.zeros((B, S, Hkv, d), dtype=cache.dtype)
+    for b in range(B):
+        for h in range(Hkv):
+            n = int(n_sel[b, h])
+            out[b, :n, h] = cache[b, idx[b, h, :n], h]
+    return out
 
 
 def decode(q, P, kp_cache, k_cache, v_cache, seq_lens, topk: int, window: int,

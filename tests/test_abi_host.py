@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert J.abi_version() == 4
+    assert J.abi_version() == 5
     lib = J.lib()
     assert lib.jssa_status_str(0) == b"JSSA_OK"
     for code, name in _lib.STATUS.items():
@@ -113,6 +113,9 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.jssa_decode(d, *p[:6], null, null, null, null, null, 0, null) == -1
     assert lib.jssa_dense_decode(d, null, *p[:4], null, null, 0, null) == -1
     assert lib.jssa_append_kv(d, *p[:2], -1, *p[2:7], null) == -1
+    assert lib.jssa_gather_kv(d, p[0], null, *p[2:6], null, null) == -1  # GQA needs V
+    assert lib.jssa_gather_kv(d, *p[:3], null, *p[4:6], null, null) == -1
+    assert lib.jssa_gather_kv(d, *p[:5], ctypes.c_void_p(4096 + 4), null, null) == -4
     # decode step: the new token's rows and positions are required (GQA: v_new and v_cache too)
     tail = (null, null, null, p[10], 1 << 40, null, null)  # lse, idx, n_sel, ws, ws_bytes, events, stream
     assert lib.jssa_decode_step(d, null, *p[:9], *tail) == -1

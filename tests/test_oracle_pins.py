@@ -485,6 +485,38 @@ def test_mla_shared_latent_row_values():
     assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
 
 
+def test_gather_then_dense_attention_equals_indexed_attention():
+    """Dense attention over the packed rows equals the indexed attention over
+    the same lists (ragged counts, repeated and unsorted indices, MLA's one
+    list per sequence), and the packed rows are the indexed rows."""
+    rng = np.random.default_rng(17)
+    B, T, Hkv, G, d = 3, 40, 2, 3, 8
+    K = rng.standard_normal((B, T, Hkv, d)).astype(np.float32)
+    V = rng.standard_normal((B, T, Hkv, d)).astype(np.float32)
+    q = rng.standard_normal((B, Hkv * G, d)).astype(np.float32)
+    S = 12
+    idx = rng.integers(0, T, size=(B, Hkv, S)).astype(np.int32)
+    n_sel = np.array([[12, 12], [5, 5], [0, 0]], np.int32)
+    Kg, Vg = O.gather_rows(K, idx, n_sel), O.gather_rows(V, idx, n_sel)
+    for b in range(B):
+        for h in range(Hkv):
+            for i in range(S):
+                want = K[b, idx[b, h, i], h] if i < n_sel[b, h] else np.zeros(d, np.float32)
+                assert np.array_equal(Kg[b, i, h], want)
+    ref, ref_lse = O.attention(q, K, V, idx, n_sel, 0.3)
+    got, got_lse = O.dense_attention(q, Kg, Vg, n_sel[:, 0], 0.3)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(fin, np.isfinite(got_lse)) and np.allclose(got_lse[fin], ref_lse[fin], rtol=1e-12)
+    # MLA: one latent row per token, the value a prefix of it
+    L = rng.standard_normal((B, T, 1, d)).astype(np.float32)
+    qm = rng.standard_normal((B, 4, d)).astype(np.float32)
+    Lg = O.gather_rows(L, idx[:, :1], n_sel[:, :1])
+    ref, _ = O.attention(qm, L, L[..., :5], idx[:, :1], n_sel[:, :1], 0.5)
+    got, _ = O.dense_attention(qm, Lg, Lg[..., :5], n_sel[:, 0], 0.5)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
 def test_kth_score():
     s = np.array([5.0, 1.0, 5.0, 3.0, np.nan])
     assert O.kth_score(s, 5, 1) == 5.0

@@ -17,7 +17,7 @@ __all__ = [
     "Desc", "JssaError", "F32", "BF16", "FP8_E4M3", "REDUCE_MAX", "REDUCE_MEAN", "LAYOUT_GQA", "LAYOUT_MLA",
     "OP_TOPK", "OP_ATTN", "OP_DECODE", "OP_DENSE", "OP_SCORE", "lib", "abi_version", "check_desc",
     "workspace_bytes", "workspace", "append_kv", "append_projection", "score", "topk", "indexed_attn", "decode", "decode_profiled",
-    "decode_step", "dense_decode",
+    "decode_step", "gather_kv", "dense_decode",
 ]
 
 # FP8 E4M3 projected keys travel as their byte codes
@@ -168,6 +168,16 @@ def decode_step(desc: Desc, k_new, v_new, pos, q, P, kp_cache, k_cache, v_cache,
          _ptr(out, _TORCH_DTYPE[desc.out_dtype], "out"), _ptr(lse, torch.float32, "lse"),
          _ptr(idx_out, torch.int32, "idx_out"), _ptr(n_sel_out, torch.int32, "n_sel_out"),
          _ptr(ws, torch.uint8, "ws"), ws.numel(), arr, _stream(stream))
+
+
+def gather_kv(desc: Desc, k_cache, v_cache, idx, n_sel, k_packed, v_packed, packed_lens=None, stream=None):
+    """``jssa_gather_kv``: pack the selected K/V rows into ``[B, topk + window,
+    Hkv, d]`` buffers (the gather-then-attend baseline); ``packed_lens``
+    receives the per-sequence counts for :func:`dense_decode` on them."""
+    kv = _TORCH_DTYPE[desc.kv_dtype]
+    call("jssa_gather_kv", desc.c(), _ptr(k_cache, kv, "k_cache"), _ptr(v_cache, kv, "v_cache"),
+         _ptr(idx, torch.int32, "idx"), _ptr(n_sel, torch.int32, "n_sel"), _ptr(k_packed, kv, "k_packed"),
+         _ptr(v_packed, kv, "v_packed"), _ptr(packed_lens, torch.int32, "packed_lens"), _stream(stream))
 
 
 def dense_decode(desc: Desc, q, k_cache, v_cache, seq_lens, out, lse, ws, stream=None):

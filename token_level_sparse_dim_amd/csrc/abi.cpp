@@ -355,6 +355,19 @@ int32_t jssa_decode_step(const jssa_desc* desc, const void* k_new, const void* v
                      ws, ws_bytes, &nt, stage_events, stream);
 }
 
+int32_t jssa_gather_kv(const jssa_desc* desc, const void* k_cache, const void* v_cache, const int32_t* idx,
+                       const int32_t* n_sel, void* k_packed, void* v_packed, int32_t* packed_lens,
+                       void* stream) {
+  JSSA_TRY(check(desc, JSSA_OP_ATTN));
+  const bool mla = desc->layout == JSSA_LAYOUT_MLA;
+  if (!k_cache || !idx || !n_sel || !k_packed || (!mla && (!v_cache || !v_packed))) return JSSA_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(idx) || !aligned16(n_sel) ||
+      !aligned16(k_packed) || !aligned16(v_packed) || (packed_lens && !aligned16(packed_lens)))
+    return JSSA_ERR_MISALIGNED;
+  return to_status(launch_gather_kv(*desc, k_cache, v_cache, idx, n_sel, k_packed, v_packed, packed_lens,
+                                    as_stream(stream)));
+}
+
 int32_t jssa_dense_decode(const jssa_desc* desc, const void* q, const void* k_cache,
                           const void* v_cache, const int32_t* seq_lens, void* out, float* lse,
                           void* ws, size_t ws_bytes, void* stream) {

@@ -118,6 +118,10 @@ hipError_t launch_resolve_attend(const jssa_desc& d, bool resolve, bool attend, 
                                  char* ws_base, const Workspace& ws, hipStream_t s);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+// Packs the selected K (and V) rows into [B, topk + window, Hkv, d] buffers
+// (gather.hip); lens_out[b] = n_sel[b, 0] if given.
+hipError_t launch_gather_kv(const jssa_desc& d, const void* k_cache, const void* v_cache, const int32_t* idx,
+                            const int32_t* n_sel, void* k_out, void* v_out, int32_t* lens_out, hipStream_t s);
 
 // MLA scoring on the matrix cores: the query projection into ws.qfrag, then
 // the score scan that reads it; with `hist` the scan also builds the
