@@ -204,3 +204,39 @@ def test_mla_empty_and_short_sequences():
     got, got_lse = to_host(out), to_host(lse)
     _check_attention(got, got_lse, ref_out, ref_lse)
     assert (got[0] == 0).all() and np.isneginf(got_lse[0]).all()
+
+
+@pytest.mark.parametrize("n_new", [1, 3])
+@pytest.mark.parametrize("w", [W_A, W_H64], ids=["r64", "r32"])
+def test_mla_append_new_rows(w, n_new):
+    """A step's new latent rows (the wide-row append: 1024 threads per row):
+    the rows are copied into the cache, their keys projected within the fp32
+    summation bound plus half a bf16 step of the exact product and equal to
+    the oracle's rounding except next to a rounding boundary; nothing else is
+    written."""
+    from synth import to_bf16_bits
+    inp = inputs(w)
+    desc = desc_for(w)
+    rng = np.random.default_rng(31 + n_new)
+    k = to_dev(inp["k_cache"])
+    kp = torch.zeros((w.batch, 1, w.t_max, w.rank), dtype=torch.bfloat16, device="cuda")
+    pos = np.array([w.t_max - 4 - 5 * b for b in range(w.batch)], np.int32)
+    kn = to_bf16_bits(rng.standard_normal((w.batch, n_new, 1, w.d_k)).astype(np.float32))
+    J.append_kv(desc, to_dev(kn), None, to_dev(pos), to_dev(inp["P"]), k, None, kp)
+    ref_k = inp["k_cache"].copy()
+    for b in range(w.batch):
+        ref_k[b, pos[b]:pos[b] + n_new] = kn[b]
+    assert np.array_equal(to_host(k), ref_k)
+    stored, exact = O.project_keys(ref_k, inp["P"], np.full(w.batch, w.t_max), "bf16")
+    got = to_host(kp)
+    absK = np.abs(O.to_f64(ref_k))
+    for b in range(w.batch):
+        rows = slice(pos[b], pos[b] + n_new)
+        bound = (absK[b, rows, 0] @ np.abs(inp["P"][0].astype(np.float64))) * (1.01 * w.d_k * 2.0 ** -24)
+        g64, ex = O.to_f64(got[b, 0, rows]), exact[b, 0, rows]
+        half = np.ldexp(1.0, np.frexp(np.maximum(np.abs(g64), np.abs(ex)))[1] - 9)
+        assert (np.abs(g64 - ex) <= bound + half).all()
+        assert (got[b, 0, rows] != stored[b, 0, rows]).mean() <= 0.05
+        mask = np.ones(w.t_max, bool)
+        mask[rows] = False
+        assert (got[b, 0, mask] == 0).all()
