@@ -37,7 +37,11 @@
 
 namespace jssa {
 
-constexpr int kPipeTileTokens = 1024;  // tokens per tile (at least two workgroup steps)
+#ifndef JSSA_PIPE_TILE_TOKENS
+#define JSSA_PIPE_TILE_TOKENS 1024
+#endif
+constexpr int kPipeTileTokens = JSSA_PIPE_TILE_TOKENS;  // tokens per tile (at least two workgroup steps)
+constexpr int kPipeSampleTokens = 1024;                 // tokens of the threshold sample
 constexpr int kPipePF = 3;             // score-scan steps in flight per workgroup
 constexpr int kPipeMaxItem = 8192;     // tokens per score item at most (whole tiles)
 constexpr int kPipeCandLds = 8192;     // candidates resolved in shared memory
@@ -306,7 +310,9 @@ struct Pipe {
   static constexpr int TS = kPipeTileTokens > 2 * S::PER_ITER ? kPipeTileTokens : 2 * S::PER_ITER;  // tokens per tile
   static constexpr int NIT = TS / S::PER_ITER;  // workgroup steps per tile
   static_assert(kPipeMaxItem % TS == 0 && NIT % 2 == 0, "score items are whole tiles of whole step pairs");
-  static constexpr int NSAMP = TS;            // sample size (one block of loads)
+  // sample size: two batches of whole steps
+  static constexpr int NSAMP = kPipeSampleTokens > 2 * S::PER_ITER ? kPipeSampleTokens : 2 * S::PER_ITER;
+  static constexpr int NIT_S = NSAMP / S::PER_ITER;
   static constexpr int RT = kResolveThreads, RW = RT / 64;  // resolve workgroup: threads, waves
   using Qp = QpSmem<D, R, G>;
   using ASmem = Attn2Smem<KVT, D, G, kPipeAttnNL>;
@@ -485,7 +491,7 @@ struct Pipe {
       if (m < n_samp) {
         // the sampled projected keys are requested before the query projection
         const char* kr = kp_row(a, row);
-        constexpr int HALF = NIT / 2;  // steps per batch of loads
+        constexpr int HALF = NIT_S / 2;  // steps per batch of loads
         auto load_half = [&](int it0, uint4 (&v)[HALF][S::U]) {
 #pragma unroll
           for (int it = 0; it < HALF; ++it)
@@ -1147,7 +1153,7 @@ static const PipeShape kPipeShapes[] = {
 static int scan_tile_tokens(int dt, int r) {
   const int per16 = dt == JSSA_FP8_E4M3 ? 16 : dt == JSSA_BF16 ? 8 : 4;
   const int per_iter = 4 * (64 / (r / per16)) * JSSA_SCORE_UNROLL;
-  return kPipeTileTokens > 2 * per_iter ? kPipeTileTokens : 2 * per_iter;
+  return kPipeTileTokens > 2 * per_iter ? kPipeTileTokens : 2 * per_iter;  // Pipe::TS
 }
 
 bool pipeline_layout(const jssa_desc& d, int* ts, int* n_tiles, int* chunk) {
