@@ -1,9 +1,11 @@
 """GPU parity at the full sizes of the two headline decode workloads, in the
-launch configuration the benchmark times: the 128K-context GQA step (batch 4,
-32 query / 8 KV heads, d = 128, r = 32, k = 2048) and the MLA step (batch 8, 128
+launch configuration the benchmark times (one ``jssa_decode_step``): the
+128K-context GQA step (batch 4, 32 query / 8 KV heads, d = 128, r = 32,
+k = 2048) and the MLA step (batch 8, 128
 query heads sharing one 576-wide latent row, r = 64, k = 2048). As in the
-benchmark, the GPU projects the whole key cache, appends one new token at
-T_b - 1 and runs the fused decode on the decode workspace.
+benchmark, the GPU projects the whole key cache, then appends one new token at
+T_b - 1 and decodes in one call on the decode workspace (also with FP8
+projected keys).
 
 The oracle checks sampled (sequence, KV head) rows one at a time: it projects
 that row's keys itself, and the row's projected keys in the GPU cache are
@@ -34,17 +36,23 @@ def _new_token(w, seed):
     return to_bf16_bits(kn), to_bf16_bits(vn)
 
 
-def _check_row_projection(got, k_rows, P_h, w):
-    """GPU projection of one row = round_bf16(fp32-accumulated K.P): within the
-    recursive summation bound plus half a bf16 step of the fp64 product, and
-    the oracle's correctly rounded value except next to a rounding boundary.
-    (The fraction is checked on whole rows; a single appended token only gets
-    the bound.) Returns the oracle's stored row."""
-    stored, exact = O.project_keys(k_rows[None, :, None, :], P_h[None], np.array([k_rows.shape[0]]), "bf16")
+def _check_row_projection(got, k_rows, P_h, w, kp="bf16"):
+    """GPU projection of one row = the fp32-accumulated K.P rounded to the
+    cache type (bf16, or FP8 E4M3 saturating at 448): within the recursive
+    summation bound plus half a step of the fp64 product, and the oracle's
+    correctly rounded value except next to a rounding boundary. (The fraction
+    is checked on whole rows; a single appended token only gets the bound.)
+    Returns the oracle's stored row."""
+    stored, exact = O.project_keys(k_rows[None, :, None, :], P_h[None], np.array([k_rows.shape[0]]), kp)
     stored, exact = stored[0, 0], exact[0, 0]
     g64 = O.to_f64(got)
     bound = np.abs(O.to_f64(k_rows)) @ np.abs(P_h.astype(np.float64)) * (1.01 * w.d_k * 2.0 ** -24)
-    half_step = np.ldexp(1.0, np.frexp(np.maximum(np.abs(g64), np.abs(exact)))[1] - 9)
+    if kp == "fp8":
+        exact = np.clip(exact, -448.0, 448.0)
+        e = np.maximum(np.frexp(np.maximum(np.abs(g64), np.abs(exact)))[1] - 1, -6)
+        half_step = np.ldexp(1.0, e - 4)
+    else:
+        half_step = np.ldexp(1.0, np.frexp(np.maximum(np.abs(g64), np.abs(exact)))[1] - 9)
     assert (np.abs(g64 - exact) <= bound + half_step).all()
     if got.shape[0] >= 1024:
         assert (got != stored).mean() < 1e-3
@@ -66,9 +74,10 @@ def _check_structure(gi, gn, L, w):
                 assert np.array_equal(sel[n_exp - w.window:], np.arange(L[b] - w.window, L[b]))
 
 
-def _run_full(w, samples, reduce=J.REDUCE_MAX):
+def _run_full(w, samples, reduce=J.REDUCE_MAX, kp_dtype=J.BF16):
     inp = generate(w, seed=w.seed)  # the benchmark's first input set
-    desc = desc_for(w, reduce=reduce)
+    desc = desc_for(w, reduce=reduce, kp_dtype=kp_dtype)
+    kps = "fp8" if kp_dtype == J.FP8_E4M3 else "bf16"
     B, Hkv, T, r, G = w.batch, w.n_kv_heads, w.t_max, w.rank, w.group
     L = inp["seq_lens"]
     dev = "cuda"
@@ -77,30 +86,35 @@ def _run_full(w, samples, reduce=J.REDUCE_MAX):
 
     # (1) the whole-cache projection the benchmark starts from; the sampled rows
     # are checked and then replaced by the oracle's own projection
-    kp = torch.empty((B, Hkv, T, r), dtype=torch.bfloat16, device=dev)
+    kp = torch.empty((B, Hkv, T, r), dtype=torch.uint8 if kps == "fp8" else torch.bfloat16, device=dev)
     J.append_projection(desc, T, torch.zeros(B, dtype=torch.int32, device=dev), P, K, kp)
     torch.cuda.synchronize()
     kp_ref = {}
     for b, h in samples:
         n = int(L[b])
         got = to_host(kp[b, h, :n])
-        kp_ref[b, h] = _check_row_projection(got, inp["k_cache"][b, :n, h, :], inp["P"][h], w)
+        kp_ref[b, h] = _check_row_projection(got, inp["k_cache"][b, :n, h, :], inp["P"][h], w, kps)
         kp[b, h, :n] = to_dev(kp_ref[b, h])
 
-    # (2) one benchmark step: append the new token at T_b - 1, then the fused decode
+    # (2) one benchmark step (jssa_decode_step): append the new token at
+    # T_b - 1 and decode, in the decode's launches
     kn, vn = _new_token(w, w.seed + 7)
     pos = (seq - 1).contiguous()
-    J.append_kv(desc, to_dev(kn), None if w.mla else to_dev(vn), pos, P, K, V, kp)
+    kn_d, vn_d = to_dev(kn), None if w.mla else to_dev(vn)
     ws = J.workspace(desc, J.OP_DECODE)
     out = torch.empty((B, w.n_q_heads, w.d_v), device=dev)
     lse = torch.empty((B, w.n_q_heads), device=dev)
-    J.decode(desc, q, P, kp, K, V, seq, out, lse, ws)
+    J.decode_step(desc, kn_d, vn_d, pos, q, P, kp, K, V, seq, out, lse, ws)
     torch.cuda.synchronize()
     o_bench, l_bench = to_host(out).copy(), to_host(lse).copy()
-    # the same call with the index lists exported: the same outputs
+    # the same step again (the same row re-appended) with the index lists
+    # exported, and the plain decode: the same outputs
     idx = torch.full((B, Hkv, w.topk + w.window), -1, dtype=torch.int32, device=dev)
     n_sel = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
-    J.decode(desc, q, P, kp, K, V, seq, out, lse, ws, idx_out=idx, n_sel_out=n_sel)
+    J.decode_step(desc, kn_d, vn_d, pos, q, P, kp, K, V, seq, out, lse, ws, idx_out=idx, n_sel_out=n_sel)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(out), o_bench) and np.array_equal(to_host(lse), l_bench)
+    J.decode(desc, q, P, kp, K, V, seq, out, lse, ws)
     torch.cuda.synchronize()
     assert np.array_equal(to_host(out), o_bench) and np.array_equal(to_host(lse), l_bench)
     gi, gn = to_host(idx), to_host(n_sel)
@@ -117,10 +131,10 @@ def _run_full(w, samples, reduce=J.REDUCE_MAX):
     for b, h in samples:
         n = int(L[b])
         assert np.array_equal(to_host(K[b, n - 1]), kn[b, 0])
-        kp_row = np.zeros((T, r), np.uint16)
+        kp_row = np.zeros((T, r), np.uint8 if kps == "fp8" else np.uint16)
         kp_row[:n] = kp_ref[b, h]
         kp_row[n - 1] = _check_row_projection(to_host(kp[b, h, n - 1:n]), k_host[b, n - 1:n, h, :],
-                                              inp["P"][h], w)
+                                              inp["P"][h], w, kps)
         hs = slice(h * G, (h + 1) * G)
         qs = inp["q"][b:b + 1, hs]
         s64, n_cand = O.subspace_scores(qs, inp["P"][h:h + 1], kp_row[None, None], L[b:b + 1], w.window,
@@ -137,6 +151,11 @@ def _run_full(w, samples, reduce=J.REDUCE_MAX):
 def test_full_ctx128k_step():
     """All four sequences, first / middle / last KV heads."""
     _run_full(WORKLOADS["ctx128k"], [(0, 0), (1, 3), (2, 7), (3, 4), (0, 7), (3, 0)])
+
+
+def test_full_ctx128k_step_fp8_keys():
+    """The same step with the FP8 E4M3 projected-key cache (the bench's --kp fp8)."""
+    _run_full(WORKLOADS["ctx128k"], [(0, 0), (1, 5), (3, 7)], kp_dtype=J.FP8_E4M3)
 
 
 def test_full_mla_step():
