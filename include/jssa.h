@@ -211,15 +211,16 @@ int32_t jssa_decode(const jssa_desc* desc, const void* q, const float* P, const 
                     void* ws, size_t ws_bytes, void* stream);
 
 /* jssa_decode that also records four caller-created HIP events
- * (stage_events[i] is a hipEvent_t; the array is a host array) on `stream`,
- * around its launches -- the per-component latency breakdown of JSSA summary
- * section E.1 (scan, selection, attention).  Fused build: [0] before the scan
- * (which also writes the candidates), [1] after it, [2] after the resolve,
- * [3] after the attention.  Other GQA shapes: [0] before the score scan, [1]
- * after it, [2] after the candidate pass, [3] after the resolve + attention.
- * MLA: [0] after the query projection (before the score scan), [1] after the
- * scan, [2] after the candidate pass, [3] after the resolve, the attention
- * and the chunk merge. */
+ * (stage_events[i] is a hipEvent_t created with timing; the array is a host
+ * array) on `stream`, around its launches -- the per-component latency
+ * breakdown of JSSA summary section E.1 (scan, selection, attention).  Fused
+ * build: [0] and [1] are the scan kernel's own start and end (the kernel's
+ * execution, as a profiler reports it; the scan also writes the candidates),
+ * [2] is recorded after the resolve, [3] after the attention.  Other GQA
+ * shapes: [0] before the score scan, [1] after it, [2] after the candidate
+ * pass, [3] after the resolve + attention.  MLA: [0] and [1] the score scan
+ * kernel's start and end, [2] after the candidate pass, [3] after the
+ * resolve, the attention and the chunk merge. */
 int32_t jssa_decode_profiled(const jssa_desc* desc, const void* q, const float* P,
                              const void* kp_cache, const void* k_cache, const void* v_cache,
                              const int32_t* seq_lens, void* out, float* lse, int32_t* idx_out,

@@ -300,9 +300,8 @@ static int32_t decode_impl(const jssa_desc* desc, const void* q, const float* P,
   auto mark = [&](int i) { return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
   if (mla) {
     hipError_t e = launch_mla_qproj(*desc, q, P, base, lay, s);
-    if (e == hipSuccess) e = mark(0);
-    if (e == hipSuccess) e = launch_mla_scan(*desc, kp_cache, seq_lens, scores, true, base, lay, s);
-    if (e == hipSuccess) e = mark(1);
+    // events [0] and [1] take the score scan kernel's own start and end
+    if (e == hipSuccess) e = launch_mla_scan(*desc, kp_cache, seq_lens, scores, true, base, lay, s, ev);
     if (e == hipSuccess) e = launch_candidates(*desc, scores, seq_lens, base, lay, s);
     if (e == hipSuccess) e = mark(2);
     if (e == hipSuccess)

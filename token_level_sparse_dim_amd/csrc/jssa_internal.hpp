@@ -129,7 +129,8 @@ hipError_t launch_gather_kv(const jssa_desc& d, const void* k_cache, const void*
 hipError_t launch_mla_qproj(const jssa_desc& d, const void* q, const float* P, char* ws_base, const Workspace& ws,
                             hipStream_t s);
 hipError_t launch_mla_scan(const jssa_desc& d, const void* kp, const int32_t* seq_lens, float* scores, bool hist,
-                           char* ws_base, const Workspace& ws, hipStream_t s);
+                           char* ws_base, const Workspace& ws, hipStream_t s,
+                           void* const* ev = nullptr);
 
 // MLA attention over idx / n_sel (idx == nullptr: every t < seq_lens[b]) in
 // chunks of ws.chunk rows, then the log-sum-exp merge of the chunks.

@@ -17,6 +17,8 @@
 //    way (V is exact in bf16).
 //
 // (Operand layout of v_mfma_f32_16x16x32_bf16: see mfma16 in jssa_device.hpp.)
+#include <hip/hip_ext.h>
+
 #include "jssa_device.hpp"
 #include "jssa_internal.hpp"
 #include "select_common.hpp"
@@ -609,7 +611,7 @@ hipError_t launch_mla_qproj(const jssa_desc& d, const void* q, const float* P, c
 }
 
 hipError_t launch_mla_scan(const jssa_desc& d, const void* kp, const int32_t* seq_lens, float* scores, bool hist,
-                           char* ws_base, const Workspace& ws, hipStream_t s) {
+                           char* ws_base, const Workspace& ws, hipStream_t s, void* const* ev) {
   const bool mean = d.reduce == JSSA_REDUCE_MEAN;
   MlaScoreArgs sa;
   sa.qf = reinterpret_cast<const uint16_t*>(ws_base + ws.qfrag);
@@ -620,14 +622,22 @@ hipError_t launch_mla_scan(const jssa_desc& d, const void* kp, const int32_t* se
   sa.MT = mean ? 1 : d.n_q_heads / 16;
   const dim3 grid((d.t_max + kMlaScoreTile - 1) / kMlaScoreTile, d.batch);
   const bool two = d.n_q_heads / 64 == 2;
+  // with `ev`, events ev[0] / ev[1] take the kernel's own start and end
+  auto go = [&](auto kernel) {
+    if (ev)
+      hipExtLaunchKernelGGL(kernel, grid, dim3(256), 0, s, static_cast<hipEvent_t>(ev[0]),
+                            static_cast<hipEvent_t>(ev[1]), 0u, sa);
+    else
+      hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, sa);
+  };
   if (d.rank == 64) {
-    if (mean) hipLaunchKernelGGL((mla_score_kernel<64, 1, true>), grid, dim3(256), 0, s, sa);
-    else if (two) hipLaunchKernelGGL((mla_score_kernel<64, 2, false>), grid, dim3(256), 0, s, sa);
-    else hipLaunchKernelGGL((mla_score_kernel<64, 1, false>), grid, dim3(256), 0, s, sa);
+    if (mean) go(mla_score_kernel<64, 1, true>);
+    else if (two) go(mla_score_kernel<64, 2, false>);
+    else go(mla_score_kernel<64, 1, false>);
   } else {
-    if (mean) hipLaunchKernelGGL((mla_score_kernel<32, 1, true>), grid, dim3(256), 0, s, sa);
-    else if (two) hipLaunchKernelGGL((mla_score_kernel<32, 2, false>), grid, dim3(256), 0, s, sa);
-    else hipLaunchKernelGGL((mla_score_kernel<32, 1, false>), grid, dim3(256), 0, s, sa);
+    if (mean) go(mla_score_kernel<32, 1, true>);
+    else if (two) go(mla_score_kernel<32, 2, false>);
+    else go(mla_score_kernel<32, 1, false>);
   }
   return hipGetLastError();
 }

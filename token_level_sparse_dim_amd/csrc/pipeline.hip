@@ -29,6 +29,8 @@
 
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "attn_core.hpp"
 #include "jssa_device.hpp"
 #include "jssa_internal.hpp"
@@ -1229,10 +1231,14 @@ static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
   int grid = resident < a.n_main ? resident : a.n_main;
   if (grid < a.n_rows) grid = a.n_rows;  // one sample per workgroup at most
   auto mark = [&](int i) { return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
-  hipError_t e = mark(0);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((scan_kernel<KPT, R, GE, D, G, KVT>), dim3(grid), dim3(256), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (ev) {  // events [0] and [1] take the scan kernel's own start and end
+    hipExtLaunchKernelGGL((scan_kernel<KPT, R, GE, D, G, KVT>), dim3(grid), dim3(256), 0, s,
+                          static_cast<hipEvent_t>(ev[0]), static_cast<hipEvent_t>(ev[1]), 0u, a);
+  } else {
+    hipLaunchKernelGGL((scan_kernel<KPT, R, GE, D, G, KVT>), dim3(grid), dim3(256), 0, s, a);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((resolve_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_rows), dim3(kResolveThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess) return e;
   hipLaunchKernelGGL((attend_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_attn), dim3(256), 0, s, a);
