@@ -35,7 +35,7 @@ import numpy as np
 __all__ = [
     "to_f64", "round_to_bf16_bits", "e4m3_to_f64", "round_to_e4m3_bits", "project_keys", "project_query",
     "subspace_scores", "topk_select", "attention", "dense_attention", "decode",
-    "n_selected", "kth_score", "gather_rows",
+    "n_selected", "kth_score", "gather_rows", "soft_vote",
 ]
 
 
@@ -274,6 +274,41 @@ def topk_select(scores: np.ndarray, seq_lens, topk: int, window: int):
             idx[b, h, :sel.size] = sel
             n_sel[b, h] = sel.size
     return idx, n_sel
+
+
+def soft_vote(scores: np.ndarray, seq_lens, window: int, scale: float) -> np.ndarray:
+    """Head-shared soft voting: one score per token of a sequence from all of
+    its KV heads' scores.
+
+    JSSA summary §E.3 compares per-KV-head selection (the method's default)
+    with head-shared soft voting, which gives one token set per sequence; the
+    pages do not spell the vote out.  Reading: each KV head votes with the
+    softmax of its scaled scores over the sequence's candidates (t < T_b - W),
+    and the votes are summed over the KV heads:
+
+        vote[b, t] = sum_h exp(scale * s[b,h,t]) / sum_u exp(scale * s[b,h,u])
+
+    (each head's votes sum to one).  NaN scores get no vote.  The shared set
+    is ``topk_select`` of the vote (ties to the lower index), used by every
+    KV head.  Returns ``vote`` float64 ``[B, 1, T_max]``, NaN past the
+    candidates.
+    """
+    B, Hkv, T = scores.shape
+    vote = np.full((B, 1, T), np.nan)
+    for b in range(B):
+        n = max(int(seq_lens[b]) - window, 0)
+        if n == 0:
+            continue
+        acc = np.zeros(n)
+        for h in range(Hkv):
+            x = scale * np.asarray(scores[b, h, :n], dtype=np.float64)
+            ok = ~np.isnan(x)
+            if not ok.any():
+                continue
+            e = np.where(ok, np.exp(x - np.max(x[ok])), 0.0)
+            acc += e / e.sum()
+        vote[b, 0, :n] = acc
+    return vote
 
 
 def kth_score(scores: np.ndarray, n_cand: int, topk: int) -> float:

@@ -517,6 +517,36 @@ def test_gather_then_dense_attention_equals_indexed_attention():
     assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
 
 
+def test_soft_vote_pins():
+    """Head-shared soft voting against its definition's consequences: each
+    head's votes sum to one (the total is Hkv); one head's vote ranks tokens
+    as its scores do (so the shared set is that head's top-k); adding a
+    constant to a head's scores changes nothing; a hand-computed two-head
+    case; candidates only (window and padding excluded); NaN scores vote 0."""
+    rng = np.random.default_rng(23)
+    B, Hkv, T = 2, 3, 50
+    s = rng.standard_normal((B, Hkv, T))
+    seq = np.array([50, 31])
+    v = O.soft_vote(s, seq, 5, 0.7)
+    assert np.allclose(np.nansum(v[:, 0], axis=1), [Hkv, Hkv], rtol=1e-12)
+    assert np.isnan(v[0, 0, 45:]).all() and np.isnan(v[1, 0, 26:]).all() and not np.isnan(v[1, 0, :26]).any()
+    one = O.soft_vote(s[:, :1], seq, 5, 0.7)
+    i1, n1 = O.topk_select(one, seq, 7, 5)
+    i0, n0 = O.topk_select(s[:, :1], seq, 7, 5)
+    assert np.array_equal(i1, i0) and np.array_equal(n1, n0)
+    shifted = s.copy()
+    shifted[:, 1] += 3.25
+    assert np.allclose(O.soft_vote(shifted, seq, 5, 0.7), v, rtol=1e-12, equal_nan=True)
+    # two heads, three tokens, scale 1: vote = softmax(h0) + softmax(h1)
+    hand = np.array([[[0.0, np.log(3.0), 0.0], [np.log(2.0), 0.0, np.log(2.0)]]])
+    got = O.soft_vote(hand, np.array([3]), 0, 1.0)[0, 0]
+    assert np.allclose(got, [1 / 5 + 2 / 5, 3 / 5 + 1 / 5, 1 / 5 + 2 / 5], rtol=1e-12)
+    nan = s.copy()
+    nan[0, :, 3] = np.nan
+    vn = O.soft_vote(nan, seq, 5, 0.7)
+    assert vn[0, 0, 3] == 0.0 and np.isclose(np.nansum(vn[0, 0]), Hkv)
+
+
 def test_kth_score():
     s = np.array([5.0, 1.0, 5.0, 3.0, np.nan])
     assert O.kth_score(s, 5, 1) == 5.0
