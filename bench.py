@@ -265,6 +265,8 @@ def main():
     # ---- attention stage: gather-free vs gather-then-attend on the same selection -------------------
     if not args.no_ablation:
         result["attention_stage"] = attention_ablation(J, w, desc, sets[0], stream, max(20, args.steps // 4))
+        if not w.mla:
+            result["selection_variant"] = selection_variant(J, w, desc, sets[0], stream, max(20, args.steps // 4))
 
     # ---- CPU oracle on a bounded sample ------------------------------------------------------------
     if not args.no_cpu:
@@ -315,6 +317,49 @@ def attention_ablation(J, w, desc, s, stream, reps):
            "gather_free_speedup": round((t_gather + t_dense) / t_free, 3), "reps": reps}
     log(f"attention stage: gather-free {t_free:.2f} us, gather {t_gather:.2f} + dense on packed "
         f"{t_dense:.2f} us ({res['gather_free_speedup']:.2f}x)")
+    return res
+
+
+def selection_variant(J, w, desc, s, stream, reps):
+    """Per-KV-head sets (the method's) against head-shared soft voting (one
+    set per sequence; JSSA summary section E.3) on the same fp32 scores: the
+    stand-alone selection of each, then the indexed attention over each
+    selection (same k, the same bytes per KV head).  Averages over `reps`."""
+    import torch
+    dev = s["q"].device
+    S = w.topk + w.window
+    scores = torch.empty((w.batch, w.n_kv_heads, w.t_max), device=dev)
+    J.score(desc, s["q"], s["P"], s["kp"], s["seq_lens"], scores)
+    idx_ph = torch.full((w.batch, w.n_kv_heads, S), -1, dtype=torch.int32, device=dev)
+    n_ph = torch.zeros((w.batch, w.n_kv_heads), dtype=torch.int32, device=dev)
+    idx_sh, n_sh = torch.full_like(idx_ph, -1), torch.zeros_like(n_ph)
+    out = torch.empty((w.batch, w.n_q_heads, w.d_v), device=dev)
+    lse = torch.empty((w.batch, w.n_q_heads), device=dev)
+    ws_t, ws_v = J.workspace(desc, J.OP_TOPK, device=dev), J.workspace(desc, J.OP_VOTE, device=dev)
+    ws_a = J.workspace(desc, J.OP_ATTN, device=dev)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    t_sel_ph = timed(lambda: J.topk(desc, scores, s["seq_lens"], idx_ph, n_ph, ws_t))
+    t_sel_sh = timed(lambda: J.vote_select(desc, scores, s["seq_lens"], idx_sh, n_sh, ws_v))
+    t_att_ph = timed(lambda: J.indexed_attn(desc, s["q"], s["k_cache"], s["v_cache"], idx_ph, n_ph, out, lse, ws_a))
+    t_att_sh = timed(lambda: J.indexed_attn(desc, s["q"], s["k_cache"], s["v_cache"], idx_sh, n_sh, out, lse, ws_a))
+    distinct = int(torch.unique(idx_ph[0, :, :int(n_ph[0, 0])]).numel())
+    res = {"per_kv_head": {"select_us": round(t_sel_ph, 2), "attention_us": round(t_att_ph, 2)},
+           "head_shared_vote": {"select_us": round(t_sel_sh, 2), "attention_us": round(t_att_sh, 2)},
+           "distinct_tokens_seq0_per_kv_head_sets": distinct, "reps": reps}
+    log(f"selection: per-KV-head top-k {t_sel_ph:.2f} us + attention {t_att_ph:.2f} us; head-shared vote "
+        f"{t_sel_sh:.2f} us + attention {t_att_sh:.2f} us")
     return res
 
 

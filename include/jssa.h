@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define JSSA_ABI_VERSION 5
+#define JSSA_ABI_VERSION 6
 
 typedef enum {
   JSSA_OK = 0,
@@ -96,7 +96,8 @@ typedef enum {
   JSSA_OP_ATTN = 2,    /* jssa_indexed_attn */
   JSSA_OP_DECODE = 3,  /* jssa_decode */
   JSSA_OP_DENSE = 4,   /* jssa_dense_decode */
-  JSSA_OP_SCORE = 5    /* jssa_score */
+  JSSA_OP_SCORE = 5,   /* jssa_score */
+  JSSA_OP_VOTE = 6     /* jssa_vote_select */
 } jssa_op;
 
 typedef struct {
@@ -247,6 +248,22 @@ int32_t jssa_decode_step(const jssa_desc* desc, const void* k_new, const void* v
                          void* k_cache, void* v_cache, const int32_t* seq_lens, void* out,
                          float* lse, int32_t* idx_out, int32_t* n_sel_out, void* ws,
                          size_t ws_bytes, void* const* stage_events, void* stream);
+
+/* Head-shared soft-voting selection, the alternative the pages compare the
+ * per-KV-head sets with (JSSA summary section E.3: one token set per
+ * sequence).  The pages do not define the vote; here each KV head votes with
+ * the softmax of its scaled scores over the sequence's candidates
+ * t < T_b - W (scale = desc->scale; NaN scores get no vote), the votes are
+ * summed over the KV heads,
+ *   vote[b,t] = sum_h exp(scale s[b,h,t]) / sum_u exp(scale s[b,h,u]),
+ * the top-k of the vote (as jssa_topk: ties to the lower index, then the
+ * window) is taken once per sequence and written to every KV head's list:
+ * idx[b,h,:] and n_sel[b,h] are the same for all h, in jssa_topk's format, so
+ * jssa_indexed_attn attends over them unchanged.  scores: [B, Hkv, t_max]
+ * fp32 (e.g. from jssa_score).  GQA layout, Hkv <= 64.  Workspace op
+ * JSSA_OP_VOTE. */
+int32_t jssa_vote_select(const jssa_desc* desc, const float* scores, const int32_t* seq_lens,
+                         int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream);
 
 /* Gather of the selected rows into packed buffers: the first half of the
  * gather-then-attend baseline that gather-free execution is compared against

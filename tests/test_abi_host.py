@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert J.abi_version() == 5
+    assert J.abi_version() == 6
     lib = J.lib()
     assert lib.jssa_status_str(0) == b"JSSA_OK"
     for code, name in _lib.STATUS.items():
@@ -87,7 +87,7 @@ def test_selection_needs_a_budget_or_window():
 
 def test_workspace_sizes():
     d = _desc()
-    for op in (J.OP_TOPK, J.OP_ATTN, J.OP_DECODE, J.OP_DENSE, J.OP_SCORE):
+    for op in (J.OP_TOPK, J.OP_ATTN, J.OP_DECODE, J.OP_DENSE, J.OP_SCORE, J.OP_VOTE):
         n = J.workspace_bytes(d, op)
         assert n > 0 and n % 256 == 0
     assert J.workspace_bytes(d, J.OP_DECODE) > J.workspace_bytes(d, J.OP_TOPK)
@@ -113,6 +113,9 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.jssa_decode(d, *p[:6], null, null, null, null, null, 0, null) == -1
     assert lib.jssa_dense_decode(d, null, *p[:4], null, null, 0, null) == -1
     assert lib.jssa_append_kv(d, *p[:2], -1, *p[2:7], null) == -1
+    assert lib.jssa_vote_select(d, *p[:3], null, p[10], 1 << 40, null) == -1
+    assert lib.jssa_vote_select(d, *p[:4], null, 0, null) == -3  # workspace missing
+    assert lib.jssa_vote_select(_mla().c(), *p[:4], p[10], 1 << 40, null) == -2  # MLA: one set already
     assert lib.jssa_gather_kv(d, p[0], null, *p[2:6], null, null) == -1  # GQA needs V
     assert lib.jssa_gather_kv(d, *p[:3], null, *p[4:6], null, null) == -1
     assert lib.jssa_gather_kv(d, *p[:5], ctypes.c_void_p(4096 + 4), null, null) == -4

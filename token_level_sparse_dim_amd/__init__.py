@@ -10,14 +10,14 @@ from __future__ import annotations
 import torch
 
 from ._lib import (BF16, F32, FP8_E4M3, LAYOUT_GQA, LAYOUT_MLA, OP_ATTN, OP_DECODE, OP_DENSE, OP_SCORE,
-                   OP_TOPK,
+                   OP_TOPK, OP_VOTE,
                    REDUCE_MAX, REDUCE_MEAN, Desc, JssaError, call, lib)
 
 __all__ = [
     "Desc", "JssaError", "F32", "BF16", "FP8_E4M3", "REDUCE_MAX", "REDUCE_MEAN", "LAYOUT_GQA", "LAYOUT_MLA",
-    "OP_TOPK", "OP_ATTN", "OP_DECODE", "OP_DENSE", "OP_SCORE", "lib", "abi_version", "check_desc",
+    "OP_TOPK", "OP_ATTN", "OP_DECODE", "OP_DENSE", "OP_SCORE", "OP_VOTE", "lib", "abi_version", "check_desc",
     "workspace_bytes", "workspace", "append_kv", "append_projection", "score", "topk", "indexed_attn", "decode", "decode_profiled",
-    "decode_step", "gather_kv", "dense_decode",
+    "decode_step", "vote_select", "gather_kv", "dense_decode",
 ]
 
 # FP8 E4M3 projected keys travel as their byte codes
@@ -168,6 +168,15 @@ def decode_step(desc: Desc, k_new, v_new, pos, q, P, kp_cache, k_cache, v_cache,
          _ptr(out, _TORCH_DTYPE[desc.out_dtype], "out"), _ptr(lse, torch.float32, "lse"),
          _ptr(idx_out, torch.int32, "idx_out"), _ptr(n_sel_out, torch.int32, "n_sel_out"),
          _ptr(ws, torch.uint8, "ws"), ws.numel(), arr, _stream(stream))
+
+
+def vote_select(desc: Desc, scores, seq_lens, idx, n_sel, ws, stream=None):
+    """``jssa_vote_select``: head-shared soft-voting selection: one top-k of
+    the KV heads' summed softmax votes per sequence, written to every KV
+    head's list (``idx`` ``[B, Hkv, k + W]``, ``n_sel`` ``[B, Hkv]``)."""
+    call("jssa_vote_select", desc.c(), _ptr(scores, torch.float32, "scores"),
+         _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(idx, torch.int32, "idx"),
+         _ptr(n_sel, torch.int32, "n_sel"), _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream))
 
 
 def gather_kv(desc: Desc, k_cache, v_cache, idx, n_sel, k_packed, v_packed, packed_lens=None, stream=None):

@@ -16,7 +16,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjssa.so
 F32, BF16, FP8_E4M3 = 0, 1, 2  # FP8_E4M3: projected-key caches only (uint8 codes)
 REDUCE_MAX, REDUCE_MEAN = 0, 1
 LAYOUT_GQA, LAYOUT_MLA = 0, 1
-OP_TOPK, OP_ATTN, OP_DECODE, OP_DENSE, OP_SCORE = 1, 2, 3, 4, 5
+OP_TOPK, OP_ATTN, OP_DECODE, OP_DENSE, OP_SCORE, OP_VOTE = 1, 2, 3, 4, 5, 6
 
 STATUS = {0: "JSSA_OK", -1: "JSSA_ERR_INVALID_ARG", -2: "JSSA_ERR_UNSUPPORTED",
           -3: "JSSA_ERR_WORKSPACE", -4: "JSSA_ERR_MISALIGNED", -5: "JSSA_ERR_HIP"}
@@ -55,6 +55,8 @@ SIGNATURES = {
     "jssa_decode_step": (_i32, [_PDESC, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                 _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                 _c_void_p, _c_void_p, _c_void_p, _size_t, ctypes.POINTER(_c_void_p),
+                                _c_void_p]),
+    "jssa_vote_select": (_i32, [_PDESC, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t,
                                 _c_void_p]),
     "jssa_gather_kv": (_i32, [_PDESC, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                               _c_void_p, _c_void_p]),

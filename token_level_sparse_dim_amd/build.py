@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libjssa.so")
-SOURCES = ["abi.cpp", "append.hip", "score.hip", "select.hip", "attn.hip", "pipeline.hip", "mla.hip", "gather.hip"]
+SOURCES = ["abi.cpp", "append.hip", "score.hip", "select.hip", "attn.hip", "pipeline.hip", "mla.hip", "gather.hip", "vote.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 CFLAGS = [

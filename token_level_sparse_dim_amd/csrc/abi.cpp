@@ -62,7 +62,7 @@ static int32_t check(const jssa_desc* d, int op) {
   if (d->n_q_heads % d->n_kv_heads != 0) return JSSA_ERR_INVALID_ARG;
   if (d->t_max < 1 || d->t_max > kMaxSelTiles * kSelTile) return JSSA_ERR_INVALID_ARG;
   if (d->topk < 0 || d->window < 0) return JSSA_ERR_INVALID_ARG;
-  const bool selects = op == JSSA_OP_TOPK || op == JSSA_OP_ATTN || op == JSSA_OP_DECODE;
+  const bool selects = op == JSSA_OP_TOPK || op == JSSA_OP_ATTN || op == JSSA_OP_DECODE || op == JSSA_OP_VOTE;
   if (selects && int64_t(d->topk) + d->window < 1) return JSSA_ERR_INVALID_ARG;
   if (int64_t(d->topk) + d->window > (int64_t(1) << 30)) return JSSA_ERR_INVALID_ARG;
   if (d->kv_dtype != JSSA_F32 && d->kv_dtype != JSSA_BF16) return JSSA_ERR_INVALID_ARG;
@@ -75,6 +75,8 @@ static int32_t check(const jssa_desc* d, int op) {
   if (d->d_k < 1 || d->d_v < 1 || d->rank < 1 || d->rank > d->d_k) return JSSA_ERR_INVALID_ARG;
   if (d->rank != 16 && d->rank != 32 && d->rank != 64) return JSSA_ERR_UNSUPPORTED;
   const int G = d->n_q_heads / d->n_kv_heads;
+  if (op == JSSA_OP_VOTE && (d->layout != JSSA_LAYOUT_GQA || d->n_kv_heads > kVoteMaxHeads))
+    return JSSA_ERR_UNSUPPORTED;  // (MLA has one index set per sequence already)
   if (d->layout == JSSA_LAYOUT_MLA) {
     // one latent row per token, the value is a prefix of it
     if (d->n_kv_heads != 1 || d->d_v > d->d_k) return JSSA_ERR_INVALID_ARG;
@@ -142,6 +144,17 @@ bool workspace_layout(const jssa_desc& d, int op, Workspace* ws) {
     const size_t mt = d.reduce == JSSA_REDUCE_MEAN ? 1 : size_t(d.n_q_heads) / 16;
     ws->qfrag = take(size_t(d.batch) * mt * (d.rank / 32) * 2 * 64 * 16);
   }
+  if (op == JSSA_OP_VOTE) {
+    const size_t n_vchunks = (size_t(d.t_max) + kVoteChunk - 1) / kVoteChunk;
+    ws->vote_part = take(rows * n_vchunks * 2 * 4);
+    ws->vote = take(size_t(d.batch) * d.t_max * 4);
+    ws->vote_idx = take(size_t(d.batch) * (size_t(d.topk) + d.window) * 4);
+    ws->vote_nsel = take(size_t(d.batch) * 4);
+    ws->vote_range = take(size_t(d.batch) * 2 * 4);
+    Workspace lt;
+    if (!workspace_layout(vote_desc(d), JSSA_OP_TOPK, &lt)) return false;
+    ws->vote_topk = take(lt.total);
+  }
   ws->total = off;
   return true;
 }
@@ -180,12 +193,12 @@ const char* jssa_status_str(int32_t s) {
 }
 
 int32_t jssa_check_desc(const jssa_desc* desc, int32_t op) {
-  if (op < 0 || op > JSSA_OP_SCORE) return JSSA_ERR_INVALID_ARG;
+  if (op < 0 || op > JSSA_OP_VOTE) return JSSA_ERR_INVALID_ARG;
   return check(desc, op);
 }
 
 size_t jssa_workspace_bytes(const jssa_desc* desc, int32_t op) {
-  if (!desc || op < JSSA_OP_TOPK || op > JSSA_OP_SCORE) return 0;
+  if (!desc || op < JSSA_OP_TOPK || op > JSSA_OP_VOTE) return 0;
   Workspace w;
   if (!workspace_layout(*desc, op, &w)) return 0;
   return w.total;
@@ -352,6 +365,18 @@ int32_t jssa_decode_step(const jssa_desc* desc, const void* k_new, const void* v
   const NewToken nt{k_new, mla ? nullptr : v_new, pos, k_cache, v_cache, kp_cache};
   return decode_impl(desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, idx_out, n_sel_out,
                      ws, ws_bytes, &nt, stage_events, stream);
+}
+
+int32_t jssa_vote_select(const jssa_desc* desc, const float* scores, const int32_t* seq_lens, int32_t* idx,
+                         int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {
+  JSSA_TRY(check(desc, JSSA_OP_VOTE));
+  if (!scores || !seq_lens || !idx || !n_sel) return JSSA_ERR_INVALID_ARG;
+  if (!aligned16(scores) || !aligned16(seq_lens) || !aligned16(idx) || !aligned16(n_sel))
+    return JSSA_ERR_MISALIGNED;
+  Workspace lay;
+  JSSA_TRY(check_ws(*desc, JSSA_OP_VOTE, ws, ws_bytes, &lay));
+  return to_status(launch_vote_select(*desc, scores, seq_lens, idx, n_sel, static_cast<char*>(ws), lay,
+                                      as_stream(stream)));
 }
 
 int32_t jssa_gather_kv(const jssa_desc* desc, const void* k_cache, const void* v_cache, const int32_t* idx,

@@ -33,6 +33,8 @@ constexpr int kCandPad = 128;        // candidate slots past the last row (read,
 constexpr int kMaxPipeChunk = 1024;  // attention chunk limit of the fused decode
 // MLA layout: shared latent rows of kMlaDk elements, values = first kMlaDv
 constexpr int kMlaDk = 576;
+constexpr int kVoteChunk = 2048;    // candidates per partial of the head-shared vote
+constexpr int kVoteMaxHeads = 64;   // KV heads the vote merges in shared memory
 constexpr int kMlaDv = 512;
 constexpr int kMlaScoreTile = 1024;  // candidate tokens per MLA score workgroup
 constexpr int kMlaHeadGroup = 32;    // query heads per MLA attention workgroup
@@ -73,6 +75,12 @@ struct Workspace {
   size_t n_sel = 0;      // i32 [rows]                  (decode only)
   size_t qfrag = 0;      // bf16 projected-query MFMA fragments (MLA score)
   size_t pipe_qp = 0;    // f32 [rows][G][r] the rows' projected queries (fused decode)
+  size_t vote_part = 0;  // f32 [rows][vote chunks][2]  (head-shared voting)
+  size_t vote = 0;       // f32 [B][t_max]              the sequences' votes
+  size_t vote_idx = 0;   // i32 [B][k+W]                the shared lists
+  size_t vote_nsel = 0;  // i32 [B]
+  size_t vote_range = 0; // u32 [B][2]                  (zero on entry and exit)
+  size_t vote_topk = 0;  // the top-k workspace of the one-head vote descriptor
   size_t total = 0;
   int n_chunks = 0;      // attention chunks per row
   int chunk = 0;         // tokens per attention chunk
@@ -118,6 +126,12 @@ hipError_t launch_resolve_attend(const jssa_desc& d, bool resolve, bool attend, 
                                  char* ws_base, const Workspace& ws, hipStream_t s);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+// Head-shared soft voting (vote.hip): the vote of every KV head's scores, its
+// top-k (with the one-head descriptor vote_desc(d)) and the list copied to
+// every KV head.
+jssa_desc vote_desc(const jssa_desc& d);
+hipError_t launch_vote_select(const jssa_desc& d, const float* scores, const int32_t* seq_lens, int32_t* idx,
+                              int32_t* n_sel, char* ws_base, const Workspace& ws, hipStream_t s);
 // Packs the selected K (and V) rows into [B, topk + window, Hkv, d] buffers
 // (gather.hip); lens_out[b] = n_sel[b, 0] if given.
 hipError_t launch_gather_kv(const jssa_desc& d, const void* k_cache, const void* v_cache, const int32_t* idx,
