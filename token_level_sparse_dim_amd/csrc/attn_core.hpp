@@ -465,20 +465,61 @@ __device__ __forceinline__ bool attend_chunk_2pass(const AttnArgs& a, Smem& S, i
 // Merge of one (row, head) in a launch after the chunks' (plain-stored)
 // partials: thread dd owns output element dd; every chunk's max, sum and
 // partial are read in batches of kMergeBatch loads issued together, folded
-// into a running log-sum-exp in chunk order.  blockDim.x == D.
+// into a running log-sum-exp in chunk order.  The first batch is requested
+// together with the row's n_sel (the partial buffers hold n_chunks chunks per
+// row, so the loads stay in bounds; chunks past the row's live count are
+// discarded once n_sel arrives): one memory round trip for rows of at most
+// kMergeBatch chunks.  blockDim.x == D.
 constexpr int kMergeBatch = 16;
 
 template <int D, int G>
-__device__ __forceinline__ void merge_rows(const AttnArgs& a, int row, int g, int n) {
+__device__ __forceinline__ void merge_fold(float& M, float& L, float& A, const float (&m)[kMergeBatch],
+                                           const float (&l)[kMergeBatch], const float (&v)[kMergeBatch]) {
+  float Mb = M;
+#pragma unroll
+  for (int i = 0; i < kMergeBatch; ++i) Mb = fmaxf(Mb, m[i]);
+  const float sc = (M == -INFINITY) ? 0.f : fast_exp2(M - Mb);
+  L *= sc;
+  A *= sc;
+#pragma unroll
+  for (int i = 0; i < kMergeBatch; ++i) {
+    const float w = (m[i] == -INFINITY) ? 0.f : fast_exp2(m[i] - Mb);
+    L = fmaf(w, l[i], L);
+    A = fmaf(w, v[i], A);
+  }
+  M = Mb;
+}
+
+template <int D, int G>
+__device__ __forceinline__ void merge_rows(const AttnArgs& a, int row, int g) {
   const int b = row / a.Hkv, h = row - b * a.Hkv;
   const int dd = threadIdx.x;
-  const int n_live = (n + a.chunk - 1) / a.chunk;
   const size_t oi = (size_t(b) * a.Hq + size_t(h) * G + g) * D + dd;
-  float M = -INFINITY, L = 0.f, A = 0.f;
   const float* racc = a.part_acc + size_t(row) * a.n_chunks * G * D + size_t(g) * D + dd;
   const float* rml = a.part_ml + size_t(row) * a.n_chunks * G * 2 + size_t(g) * 2;
-  for (int c0 = 0; c0 < n_live; c0 += kMergeBatch) {
-    float m[kMergeBatch], l[kMergeBatch], v[kMergeBatch];
+  const int pre = min(kMergeBatch, a.n_chunks);
+  float m[kMergeBatch], l[kMergeBatch], v[kMergeBatch];
+#pragma unroll
+  for (int i = 0; i < kMergeBatch; ++i) {  // issued before n_sel is known
+    const bool ok = i < pre;
+    m[i] = ok ? rml[size_t(i) * G * 2] : -INFINITY;
+    l[i] = ok ? rml[size_t(i) * G * 2 + 1] : 0.f;
+    v[i] = ok ? racc[size_t(i) * G * D] : 0.f;
+  }
+  int n = a.n_sel[row];
+  n = n < 0 ? 0 : (n > a.idx_stride ? a.idx_stride : n);
+  const int n_live = (n + a.chunk - 1) / a.chunk;
+#pragma unroll
+  for (int i = 0; i < kMergeBatch; ++i) {
+    if (i >= n_live) {
+      m[i] = -INFINITY;
+      l[i] = 0.f;
+      v[i] = 0.f;
+    }
+  }
+  float M = -INFINITY, L = 0.f, A = 0.f;
+  merge_fold<D, G>(M, L, A, m, l, v);
+  for (int c0 = kMergeBatch; c0 < n_live; c0 += kMergeBatch) {
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
       const bool ok = c0 + i < n_live;
@@ -486,19 +527,7 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, int row, int g, in
       l[i] = ok ? rml[size_t(c0 + i) * G * 2 + 1] : 0.f;
       v[i] = ok ? racc[size_t(c0 + i) * G * D] : 0.f;
     }
-    float Mb = M;
-#pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i) Mb = fmaxf(Mb, m[i]);
-    const float sc = (M == -INFINITY) ? 0.f : fast_exp2(M - Mb);
-    L *= sc;
-    A *= sc;
-#pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i) {
-      const float w = (m[i] == -INFINITY) ? 0.f : fast_exp2(m[i] - Mb);
-      L = fmaf(w, l[i], L);
-      A = fmaf(w, v[i], A);
-    }
-    M = Mb;
+    merge_fold<D, G>(M, L, A, m, l, v);
   }
   const float o = n_live > 0 ? A / L : 0.f;
   if (a.out_dtype == JSSA_BF16) reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_rne(o);

@@ -1062,9 +1062,7 @@ struct Pipe {
     attend_chunk_2pass<KVT, D, G, kPipeAttnNL, false>(a.at, S_, row, b, h, chunk, n);
   }
   static __device__ __forceinline__ void merge(const PipeArgs& a, int row, int g) {
-    int n = a.at.n_sel[row];
-    n = n < 0 ? 0 : (n > a.at.idx_stride ? a.at.idx_stride : n);
-    merge_rows<D, G>(a.at, row, g, n);
+    merge_rows<D, G>(a.at, row, g);
   }
 };
 
