@@ -65,7 +65,7 @@ constexpr int PW_STEAL = 14;
 #define JSSA_PIPE_PER_CU 3  // scan workgroups per compute unit at most (0: as many as fit)
 #endif
 #ifndef JSSA_PIPE_STATIC_PCT
-#define JSSA_PIPE_STATIC_PCT 70  // share of a row's tiles covered by the static score runs
+#define JSSA_PIPE_STATIC_PCT 100  // share of a row's tiles covered by the static score runs
 #endif
 // queue words: sticky diagnostics (a missing threshold; exact re-selections)
 enum PipeQueue : int { PQ_ERR = 2, PQ_FALLBACK = 3 };
@@ -1217,8 +1217,9 @@ static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
   const int resident = per_cu * compute_units();
   const int n_tiles_max = (a.at.t_max + Pp::TS - 1) / Pp::TS;
   const int per_row = resident > 2 * a.n_rows ? (resident - a.n_rows) / a.n_rows : 1;
-  // static runs cover JSSA_PIPE_STATIC_PCT% of a row's tiles; the rest are shared
-  int big_tiles = (JSSA_PIPE_STATIC_PCT * n_tiles_max) / (100 * per_row);
+  // static runs cover JSSA_PIPE_STATIC_PCT% of a row's tiles (whole tiles per run, rounded
+  // up); the rest, and whatever the longest run (kPipeMaxItem tokens) leaves, are shared
+  int big_tiles = (JSSA_PIPE_STATIC_PCT * n_tiles_max + 100 * per_row - 1) / (100 * per_row);
   if (big_tiles < 1) big_tiles = 1;
   if (big_tiles > kPipeMaxItem / Pp::TS) big_tiles = kPipeMaxItem / Pp::TS;
   a.item = big_tiles * Pp::TS;
