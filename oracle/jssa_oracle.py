@@ -408,3 +408,49 @@ def decode(q, P, kp_cache, k_cache, v_cache, seq_lens, topk: int, window: int,
     idx, n_sel = topk_select(s, seq_lens, topk, window)
     out, lse = attention(q, k_cache, v_cache, idx, n_sel, scale)
     return {"scores": s, "n_cand": n_cand, "idx": idx, "n_sel": n_sel, "out": out, "lse": lse}
+
+
+def write_new_rows(cache: np.ndarray, new_rows: np.ndarray, pos) -> np.ndarray:
+    """The step's new token rows written into a copy of a cache.
+
+    JSSA summary §E.1 (each newly generated key and value is appended every
+    step).  ``cache`` ``[B, T_max, H, d]``, ``new_rows`` ``[B, 1, H, d]``;
+    ``cache[b, pos[b]] = new_rows[b, 0]`` for ``0 <= pos[b] < T_max``, other
+    positions are left as they are.
+    """
+    out = np.array(cache, copy=True)
+    for b in range(out.shape[0]):
+        t = int(pos[b])
+        if 0 <= t < out.shape[1]:
+            out[b, t] = new_rows[b, 0]
+    return out
+
+
+def layer_stack_decode(layers, seq_lens, topk: int, window: int, scale: float,
+                       indexer_every: int, reduce: str = "max"):
+    """One decode step through a stack of layers that select only at indexer
+    layers and reuse those lists in the layers after them.
+
+    JSSA summary appendix C (with a model's own sparse-attention schedule,
+    selection runs only at indexer layers and adjacent layers reuse the
+    indices).  Reading: layer ``l`` is an indexer layer when
+    ``l % indexer_every == 0``; it scores, selects and attends as
+    :func:`decode`; every other layer attends over the most recent indexer
+    layer's ``idx`` / ``n_sel`` with its own query and caches.  Every layer
+    caches the same token positions.  ``layers``: dicts with ``q``,
+    ``k_cache``, ``v_cache`` and, for indexer layers, ``P`` and
+    ``kp_cache``.  Returns one dict per layer with ``out``, ``lse``, ``idx``,
+    ``n_sel`` and ``indexer``.
+    """
+    res = []
+    idx = n_sel = None
+    for li, L in enumerate(layers):
+        if li % indexer_every == 0:
+            r = decode(L["q"], L["P"], L["kp_cache"], L["k_cache"], L["v_cache"], seq_lens,
+                       topk, window, scale, reduce)
+            idx, n_sel = r["idx"], r["n_sel"]
+            res.append({"out": r["out"], "lse": r["lse"], "idx": idx, "n_sel": n_sel, "indexer": True})
+        else:
+            out, lse = attention(L["q"], L["k_cache"], L["v_cache"], idx, n_sel, scale)
+            res.append({"out": out, "lse": lse, "idx": idx, "n_sel": n_sel, "indexer": False})
+    return res

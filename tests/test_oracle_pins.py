@@ -547,6 +547,68 @@ def test_soft_vote_pins():
     assert vn[0, 0, 3] == 0.0 and np.isclose(np.nansum(vn[0, 0]), Hkv)
 
 
+def _stack_layers(rng, n_layers, B, T, Hkv, G, d, r):
+    layers = []
+    for _ in range(n_layers):
+        P = np.stack([scipy.stats.ortho_group.rvs(d, random_state=int(rng.integers(1 << 30)))[:, :r]
+                      for _ in range(Hkv)]).astype(np.float32)
+        layers.append({"q": rng.standard_normal((B, Hkv * G, d)).astype(np.float32),
+                       "k_cache": rng.standard_normal((B, T, Hkv, d)).astype(np.float32),
+                       "v_cache": rng.standard_normal((B, T, Hkv, d)).astype(np.float32), "P": P})
+    return layers
+
+
+def test_layer_stack_reuse_pins():
+    """Layers that reuse an indexer layer's lists (JSSA summary appendix C)."""
+    rng = np.random.default_rng(31)
+    B, T, Hkv, G, d, r = 2, 48, 2, 2, 8, 4
+    seq = np.array([48, 30], np.int32)
+    topk, W, scale = 10, 4, 0.4
+    layers = _stack_layers(rng, 4, B, T, Hkv, G, d, r)
+    for L in layers:
+        L["kp_cache"], _ = O.project_keys(L["k_cache"], L["P"], seq, "f32")
+    res = O.layer_stack_decode(layers, seq, topk, W, scale, indexer_every=2)
+    assert [x["indexer"] for x in res] == [True, False, True, False]
+    for li in (1, 3):
+        idx, n_sel = res[li - 1]["idx"], res[li - 1]["n_sel"]
+        assert np.array_equal(res[li]["idx"], idx)
+        # the reuse layer's own selection differs, so the pin below tells the lists apart
+        own = O.decode(layers[li]["q"], layers[li]["P"], layers[li]["kp_cache"], layers[li]["k_cache"],
+                       layers[li]["v_cache"], seq, topk, W, scale)
+        assert not np.array_equal(own["idx"], idx)
+        # softmax (scipy) over its own rows at the indexer's positions
+        L = layers[li]
+        for b in range(B):
+            for hq in range(Hkv * G):
+                h = hq // G
+                sel = idx[b, h, :n_sel[b, h]]
+                logits = scale * (L["k_cache"][b, sel, h].astype(np.float64) @ L["q"][b, hq].astype(np.float64))
+                ref = scipy.special.softmax(logits) @ L["v_cache"][b, sel, h].astype(np.float64)
+                assert np.allclose(res[li]["out"][b, hq], ref, rtol=1e-12, atol=1e-12)
+                assert abs(res[li]["lse"][b, hq] - scipy.special.logsumexp(logits)) < 1e-12
+    # a reuse layer with the indexer layer's own query and caches gives its result exactly
+    twin = [layers[0], {k: layers[0][k] for k in ("q", "k_cache", "v_cache")}]
+    r2 = O.layer_stack_decode(twin, seq, topk, W, scale, indexer_every=2)
+    assert np.array_equal(r2[1]["out"], r2[0]["out"]) and np.array_equal(r2[1]["lse"], r2[0]["lse"])
+    # a budget covering every token: every layer, reused or not, is dense attention (torch SDPA)
+    full = O.layer_stack_decode(layers, np.array([T, T], np.int32), T, 0, scale, indexer_every=3)
+    for li, L in enumerate(layers):
+        ref = _sdpa_reference(L["q"].astype(np.float64), L["k_cache"].astype(np.float64),
+                              L["v_cache"].astype(np.float64), scale)
+        assert np.allclose(full[li]["out"], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_write_new_rows():
+    cache = np.arange(2 * 5 * 2 * 3, dtype=np.float32).reshape(2, 5, 2, 3)
+    new = -np.ones((2, 1, 2, 3), np.float32)
+    out = O.write_new_rows(cache, new, np.array([3, 5]))  # sequence 1: past t_max, not written
+    assert (out[0, 3] == -1).all()
+    keep = np.ones(cache.shape, bool)
+    keep[0, 3] = False
+    assert np.array_equal(out[keep], cache[keep])
+    assert np.array_equal(O.write_new_rows(cache, new, np.array([-1, 5])), cache)
+
+
 def test_kth_score():
     s = np.array([5.0, 1.0, 5.0, 3.0, np.nan])
     assert O.kth_score(s, 5, 1) == 5.0
