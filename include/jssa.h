@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define JSSA_ABI_VERSION 6
+#define JSSA_ABI_VERSION 7
 
 typedef enum {
   JSSA_OK = 0,
@@ -248,6 +248,24 @@ int32_t jssa_decode_step(const jssa_desc* desc, const void* k_new, const void* v
                          void* k_cache, void* v_cache, const int32_t* seq_lens, void* out,
                          float* lse, int32_t* idx_out, int32_t* n_sel_out, void* ws,
                          size_t ws_bytes, void* const* stage_events, void* stream);
+
+/* One decode step of a layer that reuses another layer's selection (JSSA
+ * summary appendix C: with a model's own sparse-attention schedule, tokens
+ * are selected only at indexer layers and the adjacent layers reuse those
+ * indices).  Such a layer keeps no scoring cache: the step writes the new
+ * token's K and V rows (k_new[b,0,h,:] / v_new[b,0,h,:] at t = pos[b], no
+ * projection; positions outside [0, t_max) are not written; k_new == NULL:
+ * nothing is appended), then attends over idx / n_sel exactly as
+ * jssa_indexed_attn does.  idx / n_sel are an indexer layer's lists of the
+ * same step ([B, Hkv, topk + window] and [B, Hkv], e.g. idx_out / n_sel_out of
+ * its jssa_decode_step); both layers index the same token positions.  The
+ * fused build runs the decode's own attention and chunk-merge launches; other
+ * shapes the stand-alone attention.  MLA: k_new [B, 1, 1, d_k], v_new and
+ * v_cache unused (may be NULL).  Workspace op JSSA_OP_DECODE. */
+int32_t jssa_reuse_step(const jssa_desc* desc, const void* k_new, const void* v_new,
+                        const int32_t* pos, const void* q, void* k_cache, void* v_cache,
+                        const int32_t* idx, const int32_t* n_sel, void* out, float* lse, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /* Head-shared soft-voting selection, the alternative the pages compare the
  * per-KV-head sets with (JSSA summary section E.3: one token set per

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert J.abi_version() == 6
+    assert J.abi_version() == 7
     lib = J.lib()
     assert lib.jssa_status_str(0) == b"JSSA_OK"
     for code, name in _lib.STATUS.items():
@@ -125,6 +125,18 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.jssa_decode_step(d, p[0], p[1], null, *p[3:10], *tail) == -1
     assert lib.jssa_decode_step(d, p[0], null, *p[2:10], *tail) == -1
     assert lib.jssa_decode_step(d, *p[:10], null, null, null, null, 0, null, null) == -3  # workspace missing
+    # reuse step: q, the caches, the lists and out are required; the new rows
+    # need their positions (GQA: and v_new); k_new NULL appends nothing
+    rs = (p[10], 1 << 40, null)  # ws, ws_bytes, stream
+    assert lib.jssa_reuse_step(d, *p[:3], null, *p[4:9], null, *rs) == -1
+    assert lib.jssa_reuse_step(d, p[0], p[1], null, *p[3:9], null, *rs) == -1
+    assert lib.jssa_reuse_step(d, p[0], null, *p[2:9], null, *rs) == -1
+    assert lib.jssa_reuse_step(d, *p[:7], null, p[8], null, *rs) == -1
+    assert lib.jssa_reuse_step(d, *p[:9], null, null, 0, null) == -3  # workspace missing
+    assert lib.jssa_reuse_step(d, null, null, null, *p[3:9], null, null, 0, null) == -3
+    assert lib.jssa_reuse_step(d, *p[:8], ctypes.c_void_p(4096 + 2), null, *rs) == -4
+    assert lib.jssa_reuse_step(_mla().c(), p[0], null, p[2], p[3], p[4], null, *p[6:9], null, null, 0,
+                               null) == -3  # MLA: no V
     # misaligned data pointers
     odd = ctypes.c_void_p(4096 + 2)
     assert lib.jssa_score(d, odd, *p[:4], null, 0, null) == -4

@@ -170,6 +170,21 @@ def decode_step(desc: Desc, k_new, v_new, pos, q, P, kp_cache, k_cache, v_cache,
          _ptr(ws, torch.uint8, "ws"), ws.numel(), arr, _stream(stream))
 
 
+def reuse_step(desc: Desc, k_new, v_new, pos, q, k_cache, v_cache, idx, n_sel, out, lse, ws, stream=None):
+    """``jssa_reuse_step``: one decode step of a layer that reuses an indexer
+    layer's selection: the new token's K/V rows (``[B, 1, Hkv, d]`` at
+    ``pos``; ``k_new=None``: none) are written without projection, then the
+    indexed attention over ``idx`` / ``n_sel``. Workspace op ``OP_DECODE``."""
+    kv = _TORCH_DTYPE[desc.kv_dtype]
+    if k_new is not None and k_new.shape[1] != 1:
+        raise ValueError("reuse_step appends exactly one token per sequence")
+    call("jssa_reuse_step", desc.c(), _ptr(k_new, kv, "k_new"), _ptr(v_new, kv, "v_new"),
+         _ptr(pos, torch.int32, "pos"), _ptr(q, kv, "q"), _ptr(k_cache, kv, "k_cache"),
+         _ptr(v_cache, kv, "v_cache"), _ptr(idx, torch.int32, "idx"), _ptr(n_sel, torch.int32, "n_sel"),
+         _ptr(out, _TORCH_DTYPE[desc.out_dtype], "out"), _ptr(lse, torch.float32, "lse"),
+         _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream))
+
+
 def vote_select(desc: Desc, scores, seq_lens, idx, n_sel, ws, stream=None):
     """``jssa_vote_select``: head-shared soft-voting selection: one top-k of
     the KV heads' summed softmax votes per sequence, written to every KV

@@ -281,6 +281,33 @@ int32_t jssa_indexed_attn(const jssa_desc* desc, const void* q, const void* k_ca
                                          static_cast<char*>(ws), lay, as_stream(stream)));
 }
 
+int32_t jssa_reuse_step(const jssa_desc* desc, const void* k_new, const void* v_new,
+                        const int32_t* pos, const void* q, void* k_cache, void* v_cache,
+                        const int32_t* idx, const int32_t* n_sel, void* out, float* lse, void* ws,
+                        size_t ws_bytes, void* stream) {
+  JSSA_TRY(check(desc, JSSA_OP_DECODE));
+  const bool mla = desc->layout == JSSA_LAYOUT_MLA;
+  if (!q || !k_cache || (!mla && !v_cache) || !idx || !n_sel || !out) return JSSA_ERR_INVALID_ARG;
+  if (k_new && (!pos || (!mla && !v_new))) return JSSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(idx) || !aligned16(n_sel) ||
+      !aligned16(out) || (lse && !aligned16(lse)) || (k_new && (!aligned16(k_new) || !aligned16(pos))) ||
+      (k_new && !mla && !aligned16(v_new)))
+    return JSSA_ERR_MISALIGNED;
+  Workspace lay;
+  JSSA_TRY(check_ws(*desc, JSSA_OP_DECODE, ws, ws_bytes, &lay));
+  char* base = static_cast<char*>(ws);
+  hipStream_t s = as_stream(stream);
+  if (k_new) {
+    const hipError_t e = launch_copy_new(*desc, k_new, mla ? nullptr : v_new, pos, k_cache, v_cache, s);
+    if (e != hipSuccess) return to_status(e);
+  }
+  if (mla)
+    return to_status(launch_mla_attend(*desc, q, k_cache, idx, n_sel, nullptr, out, lse, base, lay, s));
+  if (lay.pipe) return to_status(launch_pipe_attend(*desc, q, k_cache, v_cache, idx, n_sel, out, lse, base, lay, s));
+  return to_status(launch_resolve_attend(*desc, false, true, q, k_cache, v_cache, const_cast<int32_t*>(idx),
+                                         const_cast<int32_t*>(n_sel), nullptr, out, lse, base, lay, s));
+}
+
 static int32_t decode_impl(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
                            const void* k_cache, const void* v_cache, const int32_t* seq_lens,
                            void* out, float* lse, int32_t* idx_out, int32_t* n_sel_out,

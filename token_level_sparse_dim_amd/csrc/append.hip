@@ -339,4 +339,36 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The step's new K and V rows of a layer that keeps no scoring cache (its
+// index lists come from another layer): one workgroup per sequence copies the
+// token's Hkv rows of K, then of V, in 16-byte pieces (all of a sequence's
+// rows of one token are contiguous in both layouts).
+__global__ __launch_bounds__(256) void copy_new_kernel(const char* k_new, const char* v_new, const int32_t* pos,
+                                                       char* k_cache, char* v_cache, int kb, int vb, int t_max) {
+  const int b = blockIdx.x;
+  const int t = pos[b];
+  if (t < 0 || t >= t_max) return;
+  const int nk = kb / 16, n = nk + vb / 16;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    if (i < nk)
+      *reinterpret_cast<uint4*>(k_cache + (size_t(b) * t_max + t) * kb + size_t(i) * 16) =
+          load16(k_new + size_t(b) * kb + size_t(i) * 16);
+    else
+      *reinterpret_cast<uint4*>(v_cache + (size_t(b) * t_max + t) * vb + size_t(i - nk) * 16) =
+          load16(v_new + size_t(b) * vb + size_t(i - nk) * 16);
+  }
+}
+
+hipError_t launch_copy_new(const jssa_desc& d, const void* k_new, const void* v_new, const int32_t* pos,
+                           void* k_cache, void* v_cache, hipStream_t s) {
+  const int eb = d.kv_dtype == JSSA_BF16 ? 2 : 4;
+  const bool mla = d.layout == JSSA_LAYOUT_MLA;
+  const int kb = d.n_kv_heads * d.d_k * eb, vb = mla ? 0 : d.n_kv_heads * d.d_v * eb;
+  if ((kb & 15) || (vb & 15) || d.batch <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy_new_kernel, dim3(unsigned(d.batch)), dim3(256), 0, s, static_cast<const char*>(k_new),
+                     static_cast<const char*>(v_new), pos, static_cast<char*>(k_cache), static_cast<char*>(v_cache),
+                     kb, vb, d.t_max);
+  return hipGetLastError();
+}
+
 }  // namespace jssa

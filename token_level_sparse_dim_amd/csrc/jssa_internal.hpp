@@ -176,5 +176,15 @@ hipError_t launch_pipeline(const jssa_desc& d, const void* q, const float* P, co
                            const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
                            float* lse, int32_t* idx, int32_t* n_sel, char* ws_base, const Workspace& ws,
                            const NewToken* nt, void* const* ev, hipStream_t s);
+// The fused decode's attention and chunk-merge launches on caller-provided
+// index lists (stride topk + window), with the decode workspace (pipeline
+// shapes only).
+hipError_t launch_pipe_attend(const jssa_desc& d, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* idx, const int32_t* n_sel, void* out, float* lse, char* ws_base,
+                              const Workspace& ws, hipStream_t s);
+// Copies the step's new K (and V) rows, [B, 1, Hkv, d], to t = pos[b] of the
+// caches (no projection); rows with t outside [0, t_max) are skipped.
+hipError_t launch_copy_new(const jssa_desc& d, const void* k_new, const void* v_new, const int32_t* pos,
+                           void* k_cache, void* v_cache, hipStream_t s);
 
 }  // namespace jssa

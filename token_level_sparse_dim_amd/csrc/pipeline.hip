@@ -83,6 +83,7 @@ struct PipeArgs {
   void* k_w;           // the caches, writable
   void* v_w;
   void* kp_w;
+  int attend_only;     // host side: launch the attention and merge only, on caller lists
   uint32_t* tile_cnt;  // [rows][n_tiles]
   int G, d_k, topk, window, q_dtype, ts, n_tiles, n_rows, n_main, n_attn;
   int item, n_big, n_small;  // score runs: n_big runs of `item` tokens per row, then n_small single tiles
@@ -1199,6 +1200,13 @@ template <int KPT, int R, int GE, int D, int G, int KVT>
 static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
   using Pp = Pipe<KPT, R, GE, D, G, KVT>;
   if (Pp::TS != a.ts || Attn2Shape<KVT, D, G, kPipeAttnNL>::CH != a.at.chunk) return hipErrorInvalidValue;
+  if (a.attend_only) {  // caller-provided index lists: the attention and merge launches only
+    hipLaunchKernelGGL((attend_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_attn), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((merge_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_rows * G), dim3(D), 0, s, a);
+    return hipGetLastError();
+  }
   // score runs sized so that the samples and one run per resident workgroup
   // fit; a run streams long enough that its row's threshold is known when it
   // finishes, and the row's remaining tiles are shared by its runs as they
@@ -1253,12 +1261,13 @@ static hipError_t launch_pipe_reduce(const PipeArgs& a, bool mean, void* const* 
   return launch_pipe_t<KPT, R, G, D, G, KVT>(a, ev, s);
 }
 
-hipError_t launch_pipeline(const jssa_desc& d, const void* q, const float* P, const void* kp,
-                           const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
-                           float* lse, int32_t* idx, int32_t* n_sel, char* ws_base, const Workspace& ws,
-                           const NewToken* nt, void* const* ev, hipStream_t s) {
+static hipError_t pipeline_impl(const jssa_desc& d, const void* q, const float* P, const void* kp,
+                                const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
+                                float* lse, int32_t* idx, int32_t* n_sel, char* ws_base, const Workspace& ws,
+                                const NewToken* nt, void* const* ev, bool attend_only, hipStream_t s) {
   if (!ws.pipe) return hipErrorInvalidValue;
   PipeArgs a{};
+  a.attend_only = attend_only;
   if (nt) {
     a.k_new = nt->k_new; a.v_new = nt->v_new; a.pos = nt->pos;
     a.k_w = nt->k_cache; a.v_w = nt->v_cache; a.kp_w = nt->kp_cache;
@@ -1297,6 +1306,20 @@ hipError_t launch_pipeline(const jssa_desc& d, const void* q, const float* P, co
     if (d.d_k == 128 && d.rank == 32 && G == 2) return launch_pipe_reduce<0, 0, 128, 32, 2>(a, mean, ev, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_pipeline(const jssa_desc& d, const void* q, const float* P, const void* kp,
+                           const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
+                           float* lse, int32_t* idx, int32_t* n_sel, char* ws_base, const Workspace& ws,
+                           const NewToken* nt, void* const* ev, hipStream_t s) {
+  return pipeline_impl(d, q, P, kp, k_cache, v_cache, seq_lens, out, lse, idx, n_sel, ws_base, ws, nt, ev, false, s);
+}
+
+hipError_t launch_pipe_attend(const jssa_desc& d, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* idx, const int32_t* n_sel, void* out, float* lse, char* ws_base,
+                              const Workspace& ws, hipStream_t s) {
+  return pipeline_impl(d, q, nullptr, nullptr, k_cache, v_cache, nullptr, out, lse, const_cast<int32_t*>(idx),
+                       const_cast<int32_t*>(n_sel), ws_base, ws, nullptr, nullptr, true, s);
 }
 
 }  // namespace jssa
