@@ -267,6 +267,7 @@ def main():
         result["attention_stage"] = attention_ablation(J, w, desc, sets[0], stream, max(20, args.steps // 4))
         if not w.mla:
             result["selection_variant"] = selection_variant(J, w, desc, sets[0], stream, max(20, args.steps // 4))
+        result["layer_reuse"] = layer_reuse(J, w, desc, sets[0], stream, max(20, args.steps // 4), ms_step)
 
     # ---- CPU oracle on a bounded sample ------------------------------------------------------------
     if not args.no_cpu:
@@ -317,6 +318,43 @@ def attention_ablation(J, w, desc, s, stream, reps):
            "gather_free_speedup": round((t_gather + t_dense) / t_free, 3), "reps": reps}
     log(f"attention stage: gather-free {t_free:.2f} us, gather {t_gather:.2f} + dense on packed "
         f"{t_dense:.2f} us ({res['gather_free_speedup']:.2f}x)")
+    return res
+
+
+def layer_reuse(J, w, desc, s, stream, reps, ms_step):
+    """A layer that reuses an indexer layer's selection (JSSA summary appendix C:
+    selection only at indexer layers, the adjacent layers reuse the indices):
+    its step writes the new token's K/V rows (no scoring cache) and attends
+    over the indexer's lists.  Averages over `reps` steps on one decode's lists;
+    `per_layer_us` is the mean step of a group of one indexer layer and m - 1
+    reusing layers."""
+    import torch
+    dev = s["q"].device
+    idx = torch.full((w.batch, w.n_kv_heads, w.topk + w.window), -1, dtype=torch.int32, device=dev)
+    n_sel = torch.zeros((w.batch, w.n_kv_heads), dtype=torch.int32, device=dev)
+    out = torch.empty((w.batch, w.n_q_heads, w.d_v), device=dev)
+    lse = torch.empty((w.batch, w.n_q_heads), device=dev)
+    ws = J.workspace(desc, J.OP_DECODE, device=dev)
+    J.decode(desc, s["q"], s["P"], s["kp"], s["k_cache"], s["v_cache"], s["seq_lens"], out, lse, ws,
+             idx_out=idx, n_sel_out=n_sel)
+    for _ in range(3):
+        J.reuse_step(desc, s["k_new"], s["v_new"], s["pos"], s["q"], s["k_cache"], s["v_cache"], idx, n_sel,
+                     out, lse, ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        J.reuse_step(desc, s["k_new"], s["v_new"], s["pos"], s["q"], s["k_cache"], s["v_cache"], idx, n_sel,
+                     out, lse, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_reuse = e0.elapsed_time(e1) / reps * 1e3
+    t_index = ms_step * 1e3
+    res = {"reuse_step_us": round(t_reuse, 2), "indexer_step_us": round(t_index, 2),
+           "per_layer_us": {str(m): round((t_index + (m - 1) * t_reuse) / m, 2) for m in (1, 2, 4)},
+           "reps": reps}
+    log(f"layer reuse: reuse step {t_reuse:.2f} us vs indexer step {t_index:.2f} us; one indexer per 2 / 4 "
+        f"layers: {res['per_layer_us']['2']:.2f} / {res['per_layer_us']['4']:.2f} us per layer")
     return res
 
 
