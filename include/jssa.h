@@ -185,7 +185,9 @@ int32_t jssa_topk(const jssa_desc* desc, const float* scores, const int32_t* seq
  * clamped into that range.  MLA: all Hq heads share the one index set per
  * sequence; the value is the first d_v columns of the selected row; q.K and
  * P V run on the matrix cores with fp32 accumulation and the probabilities
- * entered as bf16 hi + lo terms (about 16 significant bits).
+ * entered as bf16 hi + lo terms (about 16 significant bits).  Shapes with a
+ * fused decode build run the decode's own attention and chunk-merge launches
+ * (the same results as the attention inside jssa_decode).
  * Workspace op JSSA_OP_ATTN. */
 int32_t jssa_indexed_attn(const jssa_desc* desc, const void* q, const void* k_cache,
                           const void* v_cache, const int32_t* idx, const int32_t* n_sel,

@@ -109,7 +109,9 @@ bool workspace_layout(const jssa_desc& d, int op, Workspace* ws) {
   const bool mla = d.layout == JSSA_LAYOUT_MLA;
   ws->n_sel_tiles = (d.t_max + kSelTile - 1) / kSelTile;
   int pipe_chunk = 0;
-  if (op == JSSA_OP_DECODE && pipeline_layout(d, &ws->pipe_ts, &ws->pipe_tiles, &pipe_chunk)) {
+  // fused-build shapes: the decode, and the stand-alone indexed attention (which
+  // runs the decode's attention and merge launches), use the pipeline's chunking
+  if ((op == JSSA_OP_DECODE || op == JSSA_OP_ATTN) && pipeline_layout(d, &ws->pipe_ts, &ws->pipe_tiles, &pipe_chunk)) {
     const int64_t n_max = int64_t(d.topk) + d.window;
     ws->pipe = true;
     ws->pipe_chunk = pipe_chunk;
@@ -276,6 +278,9 @@ int32_t jssa_indexed_attn(const jssa_desc* desc, const void* q, const void* k_ca
   if (mla)
     return to_status(launch_mla_attend(*desc, q, k_cache, idx, n_sel, nullptr, out, lse, static_cast<char*>(ws),
                                        lay, as_stream(stream)));
+  if (lay.pipe)
+    return to_status(launch_pipe_attend(*desc, q, k_cache, v_cache, idx, n_sel, out, lse, static_cast<char*>(ws),
+                                        lay, as_stream(stream)));
   return to_status(launch_resolve_attend(*desc, false, true, q, k_cache, v_cache, const_cast<int32_t*>(idx),
                                          const_cast<int32_t*>(n_sel), nullptr, out, lse,
                                          static_cast<char*>(ws), lay, as_stream(stream)));
