@@ -172,6 +172,12 @@ def main():
     wall = time.perf_counter() - wall0
     ms_step = e0.elapsed_time(e1) / args.steps
     log(f"sparse step: {ms_step * 1e3:.2f} us (events), {wall / args.steps * 1e6:.2f} us (wall)")
+    # the library's sticky device diagnostics over the warm-up and timed steps:
+    # a bounded in-kernel wait that gave up would make the timed results wrong
+    dstat = [int(x) for x in J.workspace_status(ws).cpu()]
+    if dstat[J.STATUS_WAIT_TIMEOUT]:
+        print(f"bench.py: a bounded device wait gave up during the timed steps ({dstat})", file=sys.stderr)
+        sys.exit(3)
 
     # ---- per-stage breakdown from HIP events on the launch stream -------------------------------
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -233,6 +239,11 @@ def main():
         "eff_bytes_per_step": eff_bytes, "eff_GBps": round(eff_gbps, 1),
         "pct_peak": round(100.0 * eff_gbps / HBM_PEAK_GBPS, 2),
         "stages_us": {n: round(float(v), 2) for n, v in zip(names, stage_us)},
+        "device_status": {"wait_timeouts": dstat[J.STATUS_WAIT_TIMEOUT],
+                          "exact_reselections": dstat[J.STATUS_EXACT_REDO],
+                          "shared_tile_claims": dstat[J.STATUS_SHARED_CLAIMS],
+                          "global_cut_rows": dstat[J.STATUS_GLOBAL_CUT],
+                          "steps": args.warmup + args.steps},
         "roofline": {"kernel": "mla_score_kernel (MFMA projected-key scan + histogram)" if w.mla
                      else "scan_kernel (projected-key scan + candidate emission)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

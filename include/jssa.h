@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define JSSA_ABI_VERSION 7
+#define JSSA_ABI_VERSION 8
 
 typedef enum {
   JSSA_OK = 0,
@@ -134,6 +134,36 @@ size_t jssa_workspace_bytes(const jssa_desc* desc, int32_t op);
 /* Zero-fills a workspace (a fill kernel on `stream`, safe inside graph
  * capture).  Needed once before a workspace's first use. */
 int32_t jssa_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Device-side diagnostics of a workspace.  Entry points that take `ws`
+ * record, in its first 256 bytes, sticky words that accumulate over calls
+ * until cleared.  This enqueues on `stream` a copy of JSSA_STATUS_WORDS
+ * uint32 words into status_out (a DEVICE array, 16-byte aligned) and, if
+ * `clear` is nonzero, resets them to zero; it does not synchronise (read
+ * status_out after the stream has reached this point).
+ *   status_out[JSSA_STATUS_WAIT_TIMEOUT]  nonzero if a bounded in-kernel wait
+ *       gave up (a workgroup waited seconds for a value another workgroup of
+ *       the same launch publishes).  It means a broken invariant, never a
+ *       normal outcome: the selections and outputs of the calls since the last
+ *       clear must be treated as wrong.
+ *   status_out[JSSA_STATUS_EXACT_REDO]    rows re-selected exactly because the
+ *       sampled threshold of the fused decode admitted fewer than k tokens
+ *       (results stay exact; a count only).
+ *   status_out[JSSA_STATUS_SHARED_CLAIMS] claims of shared score tiles made by
+ *       the fused decode's scan when a row's static runs do not cover it (a
+ *       count only).
+ *   status_out[JSSA_STATUS_GLOBAL_CUT]    rows of the fused decode whose
+ *       candidates exceeded shared memory, so that the exact cut ran over
+ *       global memory (a count only).
+ * ws: a workspace of any op (at least 256 bytes, 256-byte aligned).
+ * Calls that use the workspace concurrently race with the copy and clear. */
+#define JSSA_STATUS_WORDS 4
+#define JSSA_STATUS_WAIT_TIMEOUT 0
+#define JSSA_STATUS_EXACT_REDO 1
+#define JSSA_STATUS_SHARED_CLAIMS 2
+#define JSSA_STATUS_GLOBAL_CUT 3
+int32_t jssa_workspace_status(void* ws, size_t ws_bytes, uint32_t* status_out, int32_t clear,
+                              void* stream);
 
 /* Append and project (JSSA summary section E.1: each newly generated key is
  * projected into the scoring cache; sections 3.1 and 3.4: the cache holds
@@ -236,10 +266,11 @@ int32_t jssa_decode_profiled(const jssa_desc* desc, const void* q, const float* 
  * (JSSA summary section E.1: the new key is projected when it is generated,
  * then the step scores, selects and attends).  Results are bit-identical to
  * the two calls in sequence.  In the fused build the append runs inside the
- * scan launch: each (sequence, KV head) row's sample appends its token before
- * it publishes the row's threshold, and the scan re-scores the one step that
- * holds pos[b] from the stored row after it has seen that threshold; no launch
- * of its own.  Other shapes launch the append first (before
+ * scan launch: each (sequence, KV head) row's sample first publishes the
+ * row's threshold, then writes the new K/V rows and the projected key and
+ * marks the row as appended; the score run whose range holds pos[b] waits for
+ * that mark and re-scores the one step that holds pos[b] from the stored row;
+ * no launch of its own.  Other shapes launch the append first (before
  * stage_events[0]).  k_new / v_new: [B, 1, Hkv, d] (MLA: [B, 1, 1, d_k], v_new
  * and v_cache unused, may be NULL); pos: int32 [B] device array; positions
  * outside [0, t_max) are not written.  The caches are read and written in

@@ -26,3 +26,35 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _no_device_wait_timeouts(request):
+    """Every workspace a GPU test creates is checked after the test: no bounded
+    in-kernel wait may have given up (the library's sticky device error word,
+    read through jssa_workspace_status)."""
+    if "gpu" not in request.keywords:
+        yield
+        return
+    import torch
+    if not torch.cuda.is_available():
+        yield
+        return
+    import token_level_sparse_dim_amd as J
+    made = []
+    orig = J.workspace
+
+    def tracking(*args, **kwargs):
+        ws = orig(*args, **kwargs)
+        made.append(ws)
+        return ws
+
+    J.workspace = tracking
+    try:
+        yield
+    finally:
+        J.workspace = orig
+    torch.cuda.synchronize()
+    timeouts = [int(J.workspace_status(ws).cpu()[J.STATUS_WAIT_TIMEOUT]) for ws in made]
+    made.clear()
+    assert not any(timeouts), f"a bounded device wait gave up in {request.node.nodeid}: {timeouts}"

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert J.abi_version() == 7
+    assert J.abi_version() == 8
     lib = J.lib()
     assert lib.jssa_status_str(0) == b"JSSA_OK"
     for code, name in _lib.STATUS.items():
@@ -151,6 +151,22 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.jssa_workspace_init(None, 64, None) == -1
     assert lib.jssa_workspace_init(ctypes.c_void_p(4096 + 8), 64, None) == -3
     assert lib.jssa_workspace_init(None, 0, None) == 0  # nothing to do
+    # workspace status: the workspace and the output are required; the
+    # workspace holds at least its 256-byte queue region, 256-byte aligned
+    assert lib.jssa_workspace_status(None, 256, p[0], 1, None) == -1
+    assert lib.jssa_workspace_status(p[0], 256, None, 1, None) == -1
+    assert lib.jssa_workspace_status(ctypes.c_void_p(4096 + 16), 256, p[1], 1, None) == -3
+    assert lib.jssa_workspace_status(p[0], 128, p[1], 1, None) == -3
+    assert lib.jssa_workspace_status(p[0], 256, ctypes.c_void_p(4096 + 4), 1, None) == -4
+
+
+def test_status_words_match_header():
+    src = open(HEADER).read()
+    for name, val in (("JSSA_STATUS_WORDS", 4), ("JSSA_STATUS_WAIT_TIMEOUT", J.STATUS_WAIT_TIMEOUT),
+                      ("JSSA_STATUS_EXACT_REDO", J.STATUS_EXACT_REDO),
+                      ("JSSA_STATUS_SHARED_CLAIMS", J.STATUS_SHARED_CLAIMS),
+                      ("JSSA_STATUS_GLOBAL_CUT", J.STATUS_GLOBAL_CUT)):
+        assert re.search(rf"#define {name} {val}\b", src), name
 
 
 def _mla(**kw):

@@ -254,8 +254,7 @@ def test_fp8_sample_threshold_fallback_is_exact():
             rows = (6.0 / np.linalg.norm(v)) * v[None, :] * (1.0 + 0.05 * rng.random((grid.size, 1)))
             kp[b, h, grid] = O.round_to_e4m3_bits(rows)
     o1, _, i1, n1, ws = _decode(desc, w, inp, kp)
-    q0 = (w.batch * w.n_kv_heads * 16 * 4 + 255) // 256 * 256
-    assert int(ws[q0 + 12:q0 + 16].cpu().numpy().view(np.uint32)[0]) >= 1  # rows re-selected
+    assert int(J.workspace_status(ws, clear=False).cpu()[J.STATUS_EXACT_REDO]) >= 1  # rows re-selected
     _, _, i2, n2, _ = _composed(desc, w, inp, kp)
     assert np.array_equal(i1, i2) and np.array_equal(n1, n2)
     s64, n_cand = O.subspace_scores(inp["q"], inp["P"], kp, inp["seq_lens"], w.window)

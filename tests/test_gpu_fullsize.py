@@ -19,7 +19,7 @@ import torch
 
 import token_level_sparse_dim_amd as J
 from oracle import jssa_oracle as O
-from synth import WORKLOADS, generate, to_bf16_bits
+from synth import WORKLOADS, generate, scaled, to_bf16_bits
 
 from _gpu_helpers import check_sets_within_tolerance, desc_for, rel_l2, to_dev, to_host
 
@@ -74,12 +74,20 @@ def _check_structure(gi, gn, L, w):
                 assert np.array_equal(sel[n_exp - w.window:], np.arange(L[b] - w.window, L[b]))
 
 
-def _run_full(w, samples, reduce=J.REDUCE_MAX, kp_dtype=J.BF16):
+def _run_full(w, samples, reduce=J.REDUCE_MAX, kp_dtype=J.BF16, pos_of=None):
+    """samples: (sequence, KV head) pairs, or a function of the sequence
+    lengths that returns them; pos_of: the new token's position per sequence
+    from the lengths (default T_b - 1, as the benchmark appends it).  Returns
+    the decode workspace's diagnostic words."""
     inp = generate(w, seed=w.seed)  # the benchmark's first input set
     desc = desc_for(w, reduce=reduce, kp_dtype=kp_dtype)
     kps = "fp8" if kp_dtype == J.FP8_E4M3 else "bf16"
     B, Hkv, T, r, G = w.batch, w.n_kv_heads, w.t_max, w.rank, w.group
     L = inp["seq_lens"]
+    if callable(samples):
+        samples = samples(L)
+    pos_h = (L - 1 if pos_of is None else pos_of(L)).astype(np.int32)
+    assert ((pos_h >= 0) & (pos_h < L)).all()
     dev = "cuda"
     q, P, K, seq = (to_dev(inp[k]) for k in ("q", "P", "k_cache", "seq_lens"))
     V = None if w.mla else to_dev(inp["v_cache"])
@@ -99,7 +107,7 @@ def _run_full(w, samples, reduce=J.REDUCE_MAX, kp_dtype=J.BF16):
     # (2) one benchmark step (jssa_decode_step): append the new token at
     # T_b - 1 and decode, in the decode's launches
     kn, vn = _new_token(w, w.seed + 7)
-    pos = (seq - 1).contiguous()
+    pos = to_dev(pos_h)
     kn_d, vn_d = to_dev(kn), None if w.mla else to_dev(vn)
     ws = J.workspace(desc, J.OP_DECODE)
     out = torch.empty((B, w.n_q_heads, w.d_v), device=dev)
@@ -117,6 +125,7 @@ def _run_full(w, samples, reduce=J.REDUCE_MAX, kp_dtype=J.BF16):
     J.decode(desc, q, P, kp, K, V, seq, out, lse, ws)
     torch.cuda.synchronize()
     assert np.array_equal(to_host(out), o_bench) and np.array_equal(to_host(lse), l_bench)
+    status = to_host(J.workspace_status(ws, clear=False))
     gi, gn = to_host(idx), to_host(n_sel)
     _check_structure(gi, gn, L, w)
     assert np.isfinite(o_bench).all() and np.isfinite(l_bench).all()
@@ -125,16 +134,16 @@ def _run_full(w, samples, reduce=J.REDUCE_MAX, kp_dtype=J.BF16):
     k_host = inp["k_cache"]
     v_host = k_host[..., :w.d_v] if w.mla else inp["v_cache"]
     for b in range(B):
-        k_host[b, L[b] - 1] = kn[b, 0]
+        k_host[b, pos_h[b]] = kn[b, 0]
         if not w.mla:
-            v_host[b, L[b] - 1] = vn[b, 0]
+            v_host[b, pos_h[b]] = vn[b, 0]
     for b, h in samples:
-        n = int(L[b])
-        assert np.array_equal(to_host(K[b, n - 1]), kn[b, 0])
+        n, t = int(L[b]), int(pos_h[b])
+        assert np.array_equal(to_host(K[b, t]), kn[b, 0])
         kp_row = np.zeros((T, r), np.uint8 if kps == "fp8" else np.uint16)
         kp_row[:n] = kp_ref[b, h]
-        kp_row[n - 1] = _check_row_projection(to_host(kp[b, h, n - 1:n]), k_host[b, n - 1:n, h, :],
-                                              inp["P"][h], w, kps)
+        kp_row[t] = _check_row_projection(to_host(kp[b, h, t:t + 1]), k_host[b, t:t + 1, h, :],
+                                          inp["P"][h], w, kps)
         hs = slice(h * G, (h + 1) * G)
         qs = inp["q"][b:b + 1, hs]
         s64, n_cand = O.subspace_scores(qs, inp["P"][h:h + 1], kp_row[None, None], L[b:b + 1], w.window,
@@ -146,11 +155,13 @@ def _run_full(w, samples, reduce=J.REDUCE_MAX, kp_dtype=J.BF16):
         got_o, got_l = o_bench[b:b + 1, hs], l_bench[b:b + 1, hs]
         assert rel_l2(got_o, ref) <= ATT_TOL, (b, h, rel_l2(got_o, ref))
         assert np.abs(got_l - ref_lse).max() <= 1e-4 * max(1.0, np.abs(ref_lse).max()), (b, h)
+    return status
 
 
 def test_full_ctx128k_step():
     """All four sequences, first / middle / last KV heads."""
-    _run_full(WORKLOADS["ctx128k"], [(0, 0), (1, 3), (2, 7), (3, 4), (0, 7), (3, 0)])
+    st = _run_full(WORKLOADS["ctx128k"], [(0, 0), (1, 3), (2, 7), (3, 4), (0, 7), (3, 0)])
+    assert st[J.STATUS_GLOBAL_CUT] == 0
 
 
 def test_full_ctx128k_step_fp8_keys():
@@ -161,3 +172,34 @@ def test_full_ctx128k_step_fp8_keys():
 def test_full_mla_step():
     """Three of the eight sequences (one latent row per sequence)."""
     _run_full(WORKLOADS["mla"], [(0, 0), (4, 0), (7, 0)])
+
+
+def test_full_ctx128k_step_k8192():
+    """The budget swept up to k = 8192: about 13,000 tokens pass the sampled
+    threshold, more than the selection holds in shared memory, so every row's
+    exact cut runs over global memory."""
+    w = scaled(WORKLOADS["ctx128k"], topk=8192)
+    st = _run_full(w, [(0, 0), (1, 6), (3, 3)])
+    assert st[J.STATUS_GLOBAL_CUT] == 3 * w.batch * w.n_kv_heads, st  # the helper decodes three times
+
+
+def test_full_ctx128k_step_k512():
+    """The budget swept down to k = 512."""
+    _run_full(scaled(WORKLOADS["ctx128k"], topk=512), [(0, 2), (2, 0), (3, 7)])
+
+
+def test_full_hybrid_ragged_step():
+    """The hybrid workload at full size: 16 sequences of 8K..128K tokens, the
+    last 512 always attended, k = 2048 of the rest.  With 128 rows each row has
+    a few static score runs, so the long rows' last tiles are shared and
+    claimed; the new token is the last candidate of each sequence (W + 1 from
+    the end), in a shared tile of every long row.  Sampled: the two longest
+    and the shortest sequence."""
+    w = WORKLOADS["hybrid_ragged"]
+
+    def pick(L):
+        o = np.argsort(L)
+        return [(int(o[-1]), 0), (int(o[-2]), 5), (int(o[0]), 7)]
+
+    st = _run_full(w, pick, pos_of=lambda L: L - w.window - 1)
+    assert st[J.STATUS_SHARED_CLAIMS] > 0, st

@@ -16,7 +16,8 @@ from ._lib import (BF16, F32, FP8_E4M3, LAYOUT_GQA, LAYOUT_MLA, OP_ATTN, OP_DECO
 __all__ = [
     "Desc", "JssaError", "F32", "BF16", "FP8_E4M3", "REDUCE_MAX", "REDUCE_MEAN", "LAYOUT_GQA", "LAYOUT_MLA",
     "OP_TOPK", "OP_ATTN", "OP_DECODE", "OP_DENSE", "OP_SCORE", "OP_VOTE", "lib", "abi_version", "check_desc",
-    "workspace_bytes", "workspace", "append_kv", "append_projection", "score", "topk", "indexed_attn", "decode", "decode_profiled",
+    "workspace_bytes", "workspace", "workspace_status", "STATUS_WAIT_TIMEOUT", "STATUS_EXACT_REDO",
+    "STATUS_SHARED_CLAIMS", "STATUS_GLOBAL_CUT", "append_kv", "append_projection", "score", "topk", "indexed_attn", "decode", "decode_profiled",
     "decode_step", "vote_select", "gather_kv", "dense_decode",
 ]
 
@@ -66,6 +67,22 @@ def workspace(desc: Desc, op: int, device="cuda", stream=None) -> torch.Tensor:
     ws = torch.empty(n, dtype=torch.uint8, device=device)
     call("jssa_workspace_init", _ptr(ws, torch.uint8, "ws"), n, _stream(stream))
     return ws
+
+
+STATUS_WAIT_TIMEOUT, STATUS_EXACT_REDO, STATUS_SHARED_CLAIMS, STATUS_GLOBAL_CUT = 0, 1, 2, 3
+
+
+def workspace_status(ws, clear: bool = True, out=None, stream=None) -> torch.Tensor:
+    """``jssa_workspace_status``: the workspace's diagnostic words, copied into a
+    4-element int32 device tensor (``out`` or a new one) on the stream and, with
+    ``clear``, reset.  Index with ``STATUS_WAIT_TIMEOUT`` (nonzero: a bounded
+    in-kernel wait gave up, results since the last clear are wrong),
+    ``STATUS_EXACT_REDO``, ``STATUS_SHARED_CLAIMS`` and ``STATUS_GLOBAL_CUT`` (counts)."""
+    if out is None:
+        out = torch.zeros(4, dtype=torch.int32, device=ws.device)
+    call("jssa_workspace_status", _ptr(ws, torch.uint8, "ws"), ws.numel(), _ptr(out, torch.int32, "out"),
+         1 if clear else 0, _stream(stream))
+    return out
 
 
 def append_kv(desc: Desc, k_new, v_new, pos, P, k_cache, v_cache, kp_cache, stream=None):

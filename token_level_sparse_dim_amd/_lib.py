@@ -38,6 +38,7 @@ SIGNATURES = {
     "jssa_check_desc": (_i32, [_PDESC, _i32]),
     "jssa_workspace_bytes": (_size_t, [_PDESC, _i32]),
     "jssa_workspace_init": (_i32, [_c_void_p, _size_t, _c_void_p]),
+    "jssa_workspace_status": (_i32, [_c_void_p, _size_t, _c_void_p, _i32, _c_void_p]),
     "jssa_append_kv": (_i32, [_PDESC, _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p,
                               _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "jssa_score": (_i32, [_PDESC, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,

@@ -118,9 +118,9 @@ bool workspace_layout(const jssa_desc& d, int op, Workspace* ws) {
     ws->pipe_n_chunks = int((n_max + pipe_chunk - 1) / pipe_chunk);
   }
   const int cnt_tiles = ws->pipe_tiles > ws->n_sel_tiles ? ws->pipe_tiles : ws->n_sel_tiles;
+  ws->queue = take(kQueueWords * 4);  // first: jssa_workspace_status finds it at offset 0
   ws->row_state = take(rows * kRowStateWords * 4);
   if (ws->pipe) ws->pipe_qp = take(rows * size_t(G) * d.rank * 4);
-  ws->queue = take(kQueueWords * 4);
   if (op == JSSA_OP_TOPK || op == JSSA_OP_DECODE) {
     ws->hist1 = take(rows * kDigit1Bins * 4);
     ws->tile_cnt = take(rows * cnt_tiles * 4);
@@ -159,6 +159,17 @@ bool workspace_layout(const jssa_desc& d, int op, Workspace* ws) {
   }
   ws->total = off;
   return true;
+}
+
+Workspace rebase_workspace(const Workspace& w, size_t delta, size_t queue) {
+  Workspace r = w;
+  for (size_t* f : {&r.hist1, &r.row_state, &r.tile_cnt, &r.tile_off, &r.cand_base, &r.cand, &r.part_acc,
+                    &r.part_ml, &r.scores, &r.idx, &r.n_sel, &r.qfrag, &r.pipe_qp, &r.vote_part, &r.vote,
+                    &r.vote_idx, &r.vote_nsel, &r.vote_range, &r.vote_topk})
+    *f += delta;
+  r.queue = queue;
+  r.total = w.total + delta;
+  return r;
 }
 
 static int32_t check_ws(const jssa_desc& d, int op, void* ws, size_t ws_bytes, Workspace* lay) {
@@ -210,6 +221,14 @@ int32_t jssa_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   if (!ws && ws_bytes) return JSSA_ERR_INVALID_ARG;
   if (ws && (reinterpret_cast<uintptr_t>(ws) % 256) != 0) return JSSA_ERR_WORKSPACE;
   return to_status(launch_zero(ws, ws_bytes, as_stream(stream)));
+}
+
+int32_t jssa_workspace_status(void* ws, size_t ws_bytes, uint32_t* status_out, int32_t clear, void* stream) {
+  if (!ws || !status_out) return JSSA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) % 256) != 0 || ws_bytes < kQueueWords * sizeof(uint32_t))
+    return JSSA_ERR_WORKSPACE;
+  if (!aligned16(status_out)) return JSSA_ERR_MISALIGNED;
+  return to_status(launch_status(static_cast<uint32_t*>(ws), status_out, clear != 0, as_stream(stream)));
 }
 
 int32_t jssa_append_kv(const jssa_desc* desc, const void* k_new, const void* v_new, int32_t n_new,

@@ -339,6 +339,21 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Diagnostic words of a workspace: copied out (plain loads: the calls that
+// wrote them are earlier launches on the stream) and optionally cleared.
+__global__ __launch_bounds__(64) void status_kernel(uint32_t* queue, uint32_t* out, int clear) {
+  const int i = threadIdx.x;
+  if (i < kStatusWords) {
+    out[i] = queue[QW_ERR + i];
+    if (clear) queue[QW_ERR + i] = 0u;
+  }
+}
+
+hipError_t launch_status(uint32_t* queue, uint32_t* out, bool clear, hipStream_t s) {
+  hipLaunchKernelGGL(status_kernel, dim3(1), dim3(64), 0, s, queue, out, clear ? 1 : 0);
+  return hipGetLastError();
+}
+
 // The step's new K and V rows of a layer that keeps no scoring cache (its
 // index lists come from another layer): one workgroup per sequence copies the
 // token's Hkv rows of K, then of V, in 16-byte pieces (all of a sequence's

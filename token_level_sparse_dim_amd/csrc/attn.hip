@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   __shared__ __align__(16) char smem_raw[kSmem];
   __shared__ uint32_t s_item;
 
-  if (threadIdx.x == 0) s_item = __hip_atomic_fetch_add(&a.queue[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) s_item = __hip_atomic_fetch_add(&a.queue[QW_NEXT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const int item = int(s_item);
   if (RESOLVE && item < a.n_resolve) {
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     if (threadIdx.x == 0) {
       uint32_t spins = 0;
       while (consume(&rstate[RS_READY]) == 0u && ++spins < kSpinLimit) __builtin_amdgcn_s_sleep(2);
-      if (spins >= kSpinLimit) publish(&a.queue[2], 1u);  // broken invariant: flagged, not hung
+      if (spins >= kSpinLimit) publish(&a.queue[QW_ERR], 1u);  // broken invariant: flagged, not hung
     }
     __syncthreads();
   }

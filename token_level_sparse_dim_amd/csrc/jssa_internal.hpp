@@ -52,9 +52,20 @@ enum RowState : int {
   RS_TICKET_ATTN = 9,   // arrivals of attention chunks
 };
 
-// Work queue of the resolve + attention launch: [0] next item, [1] finished
-// items (both zero on entry and exit).
+// Queue words of a workspace (the first region of every layout).  QW_NEXT and
+// QW_DONE are the work queue of the resolve + attention launch (zero on entry
+// and exit); the others are sticky diagnostics that accumulate over calls
+// until jssa_workspace_status clears them.
+enum QueueWord : int {
+  QW_NEXT = 0,    // next item of the resolve + attention launch
+  QW_DONE = 1,    // finished items of that launch
+  QW_ERR = 2,     // nonzero: a bounded wait gave up (that call's results are unreliable)
+  QW_REDO = 3,    // rows re-selected exactly (the sampled threshold admitted fewer than k tokens)
+  QW_CLAIMS = 4,  // claims of shared score tiles made by the fused scan
+  QW_BIG = 5,     // rows whose candidates exceeded shared memory (cut in global memory)
+};
 constexpr int kQueueWords = 64;
+constexpr int kStatusWords = 4;  // words jssa_workspace_status reports: QW_ERR .. QW_ERR + 3
 
 // ---- workspace layout ---------------------------------------------------------
 // Every region starts 256-byte aligned.  The zero-on-entry regions are
@@ -126,6 +137,13 @@ hipError_t launch_resolve_attend(const jssa_desc& d, bool resolve, bool attend, 
                                  char* ws_base, const Workspace& ws, hipStream_t s);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+// Copies the workspace's diagnostic words (QW_ERR ..) to `out` and, with
+// `clear`, zeroes them (a kernel: safe inside graph capture).
+hipError_t launch_status(uint32_t* queue, uint32_t* out, bool clear, hipStream_t s);
+// A layout whose regions are shifted by `delta` bytes except the queue, which
+// is placed at `queue`: a nested workspace that reports its diagnostics in
+// its parent's queue.
+Workspace rebase_workspace(const Workspace& w, size_t delta, size_t queue);
 // Head-shared soft voting (vote.hip): the vote of every KV head's scores, its
 // top-k (with the one-head descriptor vote_desc(d)) and the list copied to
 // every KV head.

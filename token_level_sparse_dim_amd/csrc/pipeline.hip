@@ -67,8 +67,6 @@ constexpr int PW_STEAL = 14;
 #ifndef JSSA_PIPE_STATIC_PCT
 #define JSSA_PIPE_STATIC_PCT 100  // share of a row's tiles covered by the static score runs
 #endif
-// queue words: sticky diagnostics (a missing threshold; exact re-selections)
-enum PipeQueue : int { PQ_ERR = 2, PQ_FALLBACK = 3 };
 
 struct PipeArgs {
   AttnArgs at;  // q, k, v, idx and n_sel (outputs), seq_lens, out, lse, partials, row_state, queue
@@ -90,7 +88,7 @@ struct PipeArgs {
   uint64_t spin_ticks;  // wall-clock ticks after the launch's start when every wait gives up
 };
 
-__device__ __forceinline__ void flag_error(const PipeArgs& a) { publish(a.at.queue + PQ_ERR, 1u); }
+__device__ __forceinline__ void flag_error(const PipeArgs& a) { publish(a.at.queue + QW_ERR, 1u); }
 
 // Waits are bounded in time (a broken invariant ends the launch with the error
 // flag set instead of hanging it).
@@ -818,7 +816,7 @@ struct Pipe {
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) __hip_atomic_fetch_add(a.at.queue + PQ_FALLBACK, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_fetch_add(a.at.queue + QW_REDO, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // Candidate ordinals in shared memory are spread over the RT threads in
@@ -901,7 +899,11 @@ struct Pipe {
     uint32_t* out = reinterpret_cast<uint32_t*>(a.at.idx + size_t(row) * a.at.idx_stride);
     if (threadIdx.x == 0) {  // read again only by the next call's scan
       *l_word(a, row) = 0;
-      state(a, row)[PW_STEAL] = 0;
+      const uint32_t claims = state(a, row)[PW_STEAL];
+      if (claims) {
+        __hip_atomic_fetch_add(a.at.queue + QW_CLAIMS, claims, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        state(a, row)[PW_STEAL] = 0;
+      }
     }
     for (int j = threadIdx.x; j < md.nW; j += RT) out[md.kk + j] = uint32_t(md.Tb - md.nW + j);
     if (threadIdx.x == 0) const_cast<int32_t*>(a.at.n_sel)[row] = md.kk + md.nW;
@@ -911,7 +913,8 @@ struct Pipe {
     if (threadIdx.x == 0) sm.n_bin = 0u;
     uint32_t kmin, kmax;
     uint32_t C = gather<false>(a, row, n_tiles_row, sm, &kmin, &kmax);
-    if (C < uint32_t(md.kk)) {
+    const bool fresh = C < uint32_t(md.kk);  // the slots are rewritten below (read back device-scope)
+    if (fresh) {
       exact_candidates(a, row, md, smem);
       for (int i = threadIdx.x; i < 2048; i += RT) sm.hist[i] = 0u;
       if (threadIdx.x == 0) sm.n_bin = 0u;
@@ -1028,10 +1031,12 @@ struct Pipe {
       }
     } else {
       // more candidates than shared memory holds: every pass reads them in place
+      if (threadIdx.x == 0) __hip_atomic_fetch_add(a.at.queue + QW_BIG, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const uint64_t* slots = a.cand + size_t(row) * a.at.t_max;
       auto global_cand = [&](uint32_t j) {
         const uint32_t tile = last_le(sm.tab, uint32_t(n_tiles_row), j);
-        return slots[size_t(tile) * TS + (j - sm.tab[tile])];
+        const uint64_t* p = slots + size_t(tile) * TS + (j - sm.tab[tile]);
+        return fresh ? consume(p) : *p;
       };
       kth_cut<RT>(global_cand, C, need, true, sm.hist, sm.out, &kstar, &istar);
       const uint32_t per = (C + RT - 1) / RT;
@@ -1196,6 +1201,25 @@ static int compute_units() {
   return cus[dev];
 }
 
+// Scan workgroups resident per compute unit (cached per device and kernel).
+template <int KPT, int R, int GE, int D, int G, int KVT>
+static int scan_per_cu() {
+  static int per_cu[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (per_cu[dev] == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_kernel<KPT, R, GE, D, G, KVT>, 256, 0) != hipSuccess ||
+        n < 1)
+      n = 1;
+#if JSSA_PIPE_PER_CU > 0
+    if (n > JSSA_PIPE_PER_CU) n = JSSA_PIPE_PER_CU;
+#endif
+    per_cu[dev] = n;
+  }
+  return per_cu[dev];
+}
+
 template <int KPT, int R, int GE, int D, int G, int KVT>
 static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
   using Pp = Pipe<KPT, R, GE, D, G, KVT>;
@@ -1211,18 +1235,7 @@ static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
   // fit; a run streams long enough that its row's threshold is known when it
   // finishes, and the row's remaining tiles are shared by its runs as they
   // finish
-  static int per_cu = 0;
-  if (per_cu == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_kernel<KPT, R, GE, D, G, KVT>, 256, 0) != hipSuccess ||
-        n < 1)
-      n = 1;
-#if JSSA_PIPE_PER_CU > 0
-    if (n > JSSA_PIPE_PER_CU) n = JSSA_PIPE_PER_CU;
-#endif
-    per_cu = n;
-  }
-  const int resident = per_cu * compute_units();
+  const int resident = scan_per_cu<KPT, R, GE, D, G, KVT>() * compute_units();
   const int n_tiles_max = (a.at.t_max + Pp::TS - 1) / Pp::TS;
   const int per_row = resident > 2 * a.n_rows ? (resident - a.n_rows) / a.n_rows : 1;
   // static runs cover JSSA_PIPE_STATIC_PCT% of a row's tiles (whole tiles per run, rounded

@@ -190,9 +190,12 @@ hipError_t launch_vote_select(const jssa_desc& d, const float* scores, const int
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // the shared selection: the stand-alone top-k of the vote (one "KV head")
   const jssa_desc vd = vote_desc(d);
-  Workspace lt;
-  if (!workspace_layout(vd, JSSA_OP_TOPK, &lt)) return hipErrorInvalidValue;
-  char* tbase = ws_base + ws.vote_topk;
+  Workspace nested;
+  if (!workspace_layout(vd, JSSA_OP_TOPK, &nested)) return hipErrorInvalidValue;
+  // the nested top-k workspace, addressed from this one's base, with this one's
+  // queue (its diagnostics are reported with the vote's)
+  const Workspace lt = rebase_workspace(nested, ws.vote_topk, ws.queue);
+  char* tbase = ws_base;
   int32_t* sidx = reinterpret_cast<int32_t*>(ws_base + ws.vote_idx);
   int32_t* sn = reinterpret_cast<int32_t*>(ws_base + ws.vote_nsel);
   e = launch_hist(vd, a.vote, seq_lens, tbase, lt, s);
