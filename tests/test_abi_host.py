@@ -90,7 +90,11 @@ def test_workspace_sizes():
     for op in (J.OP_TOPK, J.OP_ATTN, J.OP_DECODE, J.OP_DENSE, J.OP_SCORE, J.OP_VOTE):
         n = J.workspace_bytes(d, op)
         assert n > 0 and n % 256 == 0
-    assert J.workspace_bytes(d, J.OP_DECODE) > J.workspace_bytes(d, J.OP_TOPK)
+    slots = d.batch * d.n_kv_heads * d.t_max * 8  # candidate slots: 8 bytes per token and row
+    assert J.workspace_bytes(d, J.OP_DECODE) > slots and J.workspace_bytes(d, J.OP_TOPK) > slots
+    # the fused decode keeps no per-token score array; the staged decode (G = 2 in bf16) does
+    staged = _desc(n_q_heads=16)
+    assert J.workspace_bytes(staged, J.OP_DECODE) > J.workspace_bytes(staged, J.OP_TOPK) + slots // 2
     assert J.workspace_bytes(_desc(n_q_heads=30), J.OP_DECODE) == 0
     assert J.workspace_bytes(d, 99) == 0
 
@@ -222,3 +226,4 @@ def test_mla_entry_points_accept_null_v_cache_and_need_a_score_workspace():
     # GQA still requires v_cache
     g = _desc().c()
     assert lib.jssa_dense_decode(g, p[0], p[1], null, p[2], p[3], null, null, 0, null) == -1
+

@@ -117,15 +117,20 @@ bool workspace_layout(const jssa_desc& d, int op, Workspace* ws) {
     ws->pipe_chunk = pipe_chunk;
     ws->pipe_n_chunks = int((n_max + pipe_chunk - 1) / pipe_chunk);
   }
-  const int cnt_tiles = ws->pipe_tiles > ws->n_sel_tiles ? ws->pipe_tiles : ws->n_sel_tiles;
+  // the fused decode uses its own tile counts and candidate slots only; the
+  // staged selection also needs the first-digit histogram and tile tables
+  const bool staged = op == JSSA_OP_TOPK || (op == JSSA_OP_DECODE && !ws->pipe);
+  const int cnt_tiles = staged ? ws->n_sel_tiles : ws->pipe_tiles;
   ws->queue = take(kQueueWords * 4);  // first: jssa_workspace_status finds it at offset 0
   ws->row_state = take(rows * kRowStateWords * 4);
   if (ws->pipe) ws->pipe_qp = take(rows * size_t(G) * d.rank * 4);
   if (op == JSSA_OP_TOPK || op == JSSA_OP_DECODE) {
-    ws->hist1 = take(rows * kDigit1Bins * 4);
+    if (staged) ws->hist1 = take(rows * kDigit1Bins * 4);
     ws->tile_cnt = take(rows * cnt_tiles * 4);
-    ws->tile_off = take(rows * ws->n_sel_tiles * 4);
-    ws->cand_base = take(rows * ws->n_sel_tiles * 4);
+    if (staged) {
+      ws->tile_off = take(rows * ws->n_sel_tiles * 4);
+      ws->cand_base = take(rows * ws->n_sel_tiles * 4);
+    }
     ws->cand = take((rows * size_t(d.t_max) + kCandPad) * 8);
   }
   if (op == JSSA_OP_ATTN || op == JSSA_OP_DECODE || op == JSSA_OP_DENSE) {
@@ -138,7 +143,7 @@ bool workspace_layout(const jssa_desc& d, int op, Workspace* ws) {
     ws->part_ml = take(rows * part_chunks * size_t(G) * 2 * 4);
   }
   if (op == JSSA_OP_DECODE) {
-    ws->scores = take(rows * size_t(d.t_max) * 4);
+    if (staged) ws->scores = take(rows * size_t(d.t_max) * 4);
     ws->idx = take(rows * (size_t(d.topk) + d.window) * 4);
     ws->n_sel = take(rows * 4);
   }
