@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define JSSA_ABI_VERSION 8
+#define JSSA_ABI_VERSION 9
 
 typedef enum {
   JSSA_OK = 0,
@@ -67,7 +67,9 @@ typedef enum {
   JSSA_ERR_UNSUPPORTED = -2,  /* valid but not built: shape/dtype combination */
   JSSA_ERR_WORKSPACE = -3,    /* workspace missing, too small or misaligned */
   JSSA_ERR_MISALIGNED = -4,   /* a data pointer is not 16-byte aligned */
-  JSSA_ERR_HIP = -5           /* a HIP launch failed */
+  JSSA_ERR_HIP = -5,          /* a HIP launch failed */
+  JSSA_ERR_TOO_LARGE = -6     /* the call needs more than the static scratch of
+                                 jssa_decode_step_static */
 } jssa_status;
 
 /* JSSA_FP8_E4M3 (the OCP 8-bit format E4M3: bias 7, largest value 448, no
@@ -281,6 +283,30 @@ int32_t jssa_decode_step(const jssa_desc* desc, const void* k_new, const void* v
                          void* k_cache, void* v_cache, const int32_t* seq_lens, void* out,
                          float* lse, int32_t* idx_out, int32_t* n_sel_out, void* ws,
                          size_t ws_bytes, void* const* stage_events, void* stream);
+
+/* jssa_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The intermediates live in one static
+ * device array of JSSA_STATIC_SCRATCH_BYTES bytes that the library holds on
+ * each GPU it runs on until the process ends; nothing is allocated or freed
+ * by the call.  Same arguments (stage events excepted) and results, bit for
+ * bit, as jssa_decode_step with a zeroed workspace.
+ * Limits: the shapes with a fused decode build (GQA; see jssa_decode) only,
+ * else JSSA_ERR_UNSUPPORTED; at most JSSA_STATIC_SCRATCH_ROWS (sequence, KV
+ * head) rows, and jssa_workspace_bytes(desc, JSSA_OP_DECODE) plus the rows'
+ * reserved state must fit the array, else JSSA_ERR_TOO_LARGE (for example
+ * batch 16, 8 KV heads and t_max 131072 fit; the candidate slots take
+ * 8 bytes per cached token and KV head).  The first call on a GPU enqueues
+ * a zero fill of the array's counters on `stream`.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other host threads) race and give wrong results;
+ * serialise them.  No workspace diagnostics are reported. */
+#define JSSA_STATIC_SCRATCH_BYTES (160u << 20)
+#define JSSA_STATIC_SCRATCH_ROWS 8192
+int32_t jssa_decode_step_static(const jssa_desc* desc, const void* k_new, const void* v_new,
+                                const int32_t* pos, const void* q, const float* P, void* kp_cache,
+                                void* k_cache, void* v_cache, const int32_t* seq_lens, void* out,
+                                float* lse, int32_t* idx_out, int32_t* n_sel_out, void* stream);
 
 /* One decode step of a layer that reuses another layer's selection (JSSA
  * summary appendix C: with a model's own sparse-attention schedule, tokens

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert J.abi_version() == 8
+    assert J.abi_version() == 9
     lib = J.lib()
     assert lib.jssa_status_str(0) == b"JSSA_OK"
     for code, name in _lib.STATUS.items():
@@ -227,3 +227,21 @@ def test_mla_entry_points_accept_null_v_cache_and_need_a_score_workspace():
     g = _desc().c()
     assert lib.jssa_dense_decode(g, p[0], p[1], null, p[2], p[3], null, null, 0, null) == -1
 
+
+def test_static_decode_step_rejects_before_touching_the_gpu():
+    """jssa_decode_step_static validates like jssa_decode_step, then rejects
+    descriptors without a fused build and calls whose intermediates exceed its
+    static scratch, all on the host."""
+    lib = J.lib()
+    p = _fake(13)
+    null = None
+    d = _desc().c()
+    assert lib.jssa_decode_step_static(None, *p, null) == -1
+    assert lib.jssa_decode_step_static(d, null, *p[1:], null) == -1          # k_new missing
+    assert lib.jssa_decode_step_static(d, p[0], null, *p[2:], null) == -1    # GQA: v_new missing
+    assert lib.jssa_decode_step_static(d, ctypes.c_void_p(4096 + 2), *p[1:], null) == -4
+    assert lib.jssa_decode_step_static(_desc(n_q_heads=16).c(), *p, null) == -2  # G = 2 in bf16: staged shape
+    assert lib.jssa_decode_step_static(_mla().c(), *p, null) == -2
+    assert lib.jssa_decode_step_static(_desc(batch=64, t_max=1 << 20).c(), *p, null) == -6  # 4 GiB of slots
+    assert lib.jssa_decode_step_static(_desc(batch=2048, n_kv_heads=8).c(), *p, null) == -6  # > 8192 rows
+    assert lib.jssa_status_str(-6) == b"JSSA_ERR_TOO_LARGE"

@@ -18,7 +18,7 @@ __all__ = [
     "OP_TOPK", "OP_ATTN", "OP_DECODE", "OP_DENSE", "OP_SCORE", "OP_VOTE", "lib", "abi_version", "check_desc",
     "workspace_bytes", "workspace", "workspace_status", "STATUS_WAIT_TIMEOUT", "STATUS_EXACT_REDO",
     "STATUS_SHARED_CLAIMS", "STATUS_GLOBAL_CUT", "append_kv", "append_projection", "score", "topk", "indexed_attn", "decode", "decode_profiled",
-    "decode_step", "vote_select", "gather_kv", "dense_decode",
+    "decode_step", "decode_step_static", "vote_select", "gather_kv", "dense_decode",
 ]
 
 # FP8 E4M3 projected keys travel as their byte codes
@@ -185,6 +185,22 @@ def decode_step(desc: Desc, k_new, v_new, pos, q, P, kp_cache, k_cache, v_cache,
          _ptr(out, _TORCH_DTYPE[desc.out_dtype], "out"), _ptr(lse, torch.float32, "lse"),
          _ptr(idx_out, torch.int32, "idx_out"), _ptr(n_sel_out, torch.int32, "n_sel_out"),
          _ptr(ws, torch.uint8, "ws"), ws.numel(), arr, _stream(stream))
+
+
+def decode_step_static(desc: Desc, k_new, v_new, pos, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse,
+                       idx_out=None, n_sel_out=None, stream=None):
+    """``jssa_decode_step_static``: :func:`decode_step` without a workspace (the
+    library's static device scratch holds the intermediates; nothing is
+    allocated).  Calls that overlap on one GPU race."""
+    kv = _TORCH_DTYPE[desc.kv_dtype]
+    if k_new.shape[1] != 1:
+        raise ValueError("decode_step_static appends exactly one token per sequence")
+    call("jssa_decode_step_static", desc.c(), _ptr(k_new, kv, "k_new"), _ptr(v_new, kv, "v_new"),
+         _ptr(pos, torch.int32, "pos"), _ptr(q, kv, "q"), _ptr(P, torch.float32, "P"),
+         _ptr(kp_cache, _TORCH_DTYPE[desc.kp_dtype], "kp_cache"), _ptr(k_cache, kv, "k_cache"),
+         _ptr(v_cache, kv, "v_cache"), _ptr(seq_lens, torch.int32, "seq_lens"),
+         _ptr(out, _TORCH_DTYPE[desc.out_dtype], "out"), _ptr(lse, torch.float32, "lse"),
+         _ptr(idx_out, torch.int32, "idx_out"), _ptr(n_sel_out, torch.int32, "n_sel_out"), _stream(stream))
 
 
 def reuse_step(desc: Desc, k_new, v_new, pos, q, k_cache, v_cache, idx, n_sel, out, lse, ws, stream=None):

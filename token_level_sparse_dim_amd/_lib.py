@@ -19,7 +19,7 @@ LAYOUT_GQA, LAYOUT_MLA = 0, 1
 OP_TOPK, OP_ATTN, OP_DECODE, OP_DENSE, OP_SCORE, OP_VOTE = 1, 2, 3, 4, 5, 6
 
 STATUS = {0: "JSSA_OK", -1: "JSSA_ERR_INVALID_ARG", -2: "JSSA_ERR_UNSUPPORTED",
-          -3: "JSSA_ERR_WORKSPACE", -4: "JSSA_ERR_MISALIGNED", -5: "JSSA_ERR_HIP"}
+          -3: "JSSA_ERR_WORKSPACE", -4: "JSSA_ERR_MISALIGNED", -5: "JSSA_ERR_HIP", -6: "JSSA_ERR_TOO_LARGE"}
 
 # every function include/jssa.h declares, with its ctypes signature
 _c_void_p, _i32, _size_t = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
@@ -57,6 +57,9 @@ SIGNATURES = {
                                 _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                 _c_void_p, _c_void_p, _c_void_p, _size_t, ctypes.POINTER(_c_void_p),
                                 _c_void_p]),
+    "jssa_decode_step_static": (_i32, [_PDESC, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                       _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                       _c_void_p, _c_void_p, _c_void_p]),
     "jssa_reuse_step": (_i32, [_PDESC, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t, _c_void_p]),
     "jssa_vote_select": (_i32, [_PDESC, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t,

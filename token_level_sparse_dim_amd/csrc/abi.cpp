@@ -206,6 +206,7 @@ const char* jssa_status_str(int32_t s) {
     case JSSA_ERR_WORKSPACE: return "JSSA_ERR_WORKSPACE";
     case JSSA_ERR_MISALIGNED: return "JSSA_ERR_MISALIGNED";
     case JSSA_ERR_HIP: return "JSSA_ERR_HIP";
+    case JSSA_ERR_TOO_LARGE: return "JSSA_ERR_TOO_LARGE";
   }
   return "JSSA_ERR_UNKNOWN";
 }
@@ -337,10 +338,14 @@ int32_t jssa_reuse_step(const jssa_desc* desc, const void* k_new, const void* v_
                                          const_cast<int32_t*>(n_sel), nullptr, out, lse, base, lay, s));
 }
 
-static int32_t decode_impl(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
-                           const void* k_cache, const void* v_cache, const int32_t* seq_lens,
-                           void* out, float* lse, int32_t* idx_out, int32_t* n_sel_out,
-                           void* ws, size_t ws_bytes, const NewToken* nt, void* const* ev, void* stream) {
+}  // extern "C"
+
+namespace jssa {
+
+// Host-side checks of a decode's arguments (everything but the workspace).
+int32_t check_decode_args(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
+                          const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
+                          float* lse, int32_t* idx_out, int32_t* n_sel_out, const NewToken* nt, void* const* ev) {
   JSSA_TRY(check(desc, JSSA_OP_DECODE));
   const bool mla = desc->layout == JSSA_LAYOUT_MLA;
   if (!q || !P || !kp_cache || !k_cache || (!mla && !v_cache) || !seq_lens || !out) return JSSA_ERR_INVALID_ARG;
@@ -351,9 +356,19 @@ static int32_t decode_impl(const jssa_desc* desc, const void* q, const float* P,
   if (ev)
     for (int i = 0; i < 4; ++i)
       if (!ev[i]) return JSSA_ERR_INVALID_ARG;
-  Workspace lay;
-  JSSA_TRY(check_ws(*desc, JSSA_OP_DECODE, ws, ws_bytes, &lay));
-  char* base = static_cast<char*>(ws);
+  if (nt) {  // the step's new token: rows and positions (GQA: the value row and cache too)
+    if (!nt->k_new || !nt->pos || (!mla && (!nt->v_new || !nt->v_cache))) return JSSA_ERR_INVALID_ARG;
+    if (!aligned16(nt->k_new) || !aligned16(nt->pos) || (!mla && !aligned16(nt->v_new))) return JSSA_ERR_MISALIGNED;
+  }
+  return JSSA_OK;
+}
+
+// The decode's launches on a workspace whose layout is `lay` (checked by the caller).
+int32_t decode_launch(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
+                      const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out, float* lse,
+                      int32_t* idx_out, int32_t* n_sel_out, char* base, const Workspace& lay, const NewToken* nt,
+                      void* const* ev, void* stream) {
+  const bool mla = desc->layout == JSSA_LAYOUT_MLA;
   float* scores = reinterpret_cast<float*>(base + lay.scores);
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + lay.idx);
   int32_t* n_sel = n_sel_out ? n_sel_out : reinterpret_cast<int32_t*>(base + lay.n_sel);
@@ -392,6 +407,22 @@ static int32_t decode_impl(const jssa_desc* desc, const void* q, const float* P,
   return to_status(e);
 }
 
+}  // namespace jssa
+
+extern "C" {
+
+static int32_t decode_impl(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
+                           const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                           void* out, float* lse, int32_t* idx_out, int32_t* n_sel_out,
+                           void* ws, size_t ws_bytes, const NewToken* nt, void* const* ev, void* stream) {
+  JSSA_TRY(check_decode_args(desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, idx_out, n_sel_out, nt,
+                             ev));
+  Workspace lay;
+  JSSA_TRY(check_ws(*desc, JSSA_OP_DECODE, ws, ws_bytes, &lay));
+  return decode_launch(desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, idx_out, n_sel_out,
+                       static_cast<char*>(ws), lay, nt, ev, stream);
+}
+
 int32_t jssa_decode(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
                     const void* k_cache, const void* v_cache, const int32_t* seq_lens,
                     void* out, float* lse, int32_t* idx_out, int32_t* n_sel_out,
@@ -416,8 +447,6 @@ int32_t jssa_decode_step(const jssa_desc* desc, const void* k_new, const void* v
                          void* stream) {
   JSSA_TRY(check(desc, JSSA_OP_DECODE));
   const bool mla = desc->layout == JSSA_LAYOUT_MLA;
-  if (!k_new || !pos || (!mla && (!v_new || !v_cache))) return JSSA_ERR_INVALID_ARG;
-  if (!aligned16(k_new) || !aligned16(pos) || (!mla && !aligned16(v_new))) return JSSA_ERR_MISALIGNED;
   const NewToken nt{k_new, mla ? nullptr : v_new, pos, k_cache, v_cache, kp_cache};
   return decode_impl(desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, idx_out, n_sel_out,
                      ws, ws_bytes, &nt, stage_events, stream);

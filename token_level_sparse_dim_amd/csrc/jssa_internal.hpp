@@ -200,6 +200,16 @@ hipError_t launch_pipeline(const jssa_desc& d, const void* q, const float* P, co
 hipError_t launch_pipe_attend(const jssa_desc& d, const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* idx, const int32_t* n_sel, void* out, float* lse, char* ws_base,
                               const Workspace& ws, hipStream_t s);
+// Host-side checks of a decode's arguments except the workspace (abi.cpp),
+// and the decode's launches on a workspace of layout `lay` (nt: the step's new
+// token, appended first; ev: four stage events or null).
+int32_t check_decode_args(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
+                          const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
+                          float* lse, int32_t* idx_out, int32_t* n_sel_out, const NewToken* nt, void* const* ev);
+int32_t decode_launch(const jssa_desc* desc, const void* q, const float* P, const void* kp_cache,
+                      const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out, float* lse,
+                      int32_t* idx_out, int32_t* n_sel_out, char* base, const Workspace& lay, const NewToken* nt,
+                      void* const* ev, void* stream);
 // Copies the step's new K (and V) rows, [B, 1, Hkv, d], to t = pos[b] of the
 // caches (no projection); rows with t outside [0, t_max) are skipped.
 hipError_t launch_copy_new(const jssa_desc& d, const void* k_new, const void* v_new, const int32_t* pos,
