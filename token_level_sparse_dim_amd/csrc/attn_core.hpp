@@ -535,4 +535,171 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, int row, int g) {
   if (dd == 0 && a.lse) a.lse[size_t(b) * a.Hq + h * G + g] = n_live > 0 ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
 
+// ---- one row's portion of its index list, by NW waves --------------------------------
+// The fused decode's attention: the workgroup that selected a row's tokens (or
+// read them from a caller's list) attends over its portion of the list, `cnt`
+// token indices in S.idx[].  Sub-chunks of CH = NW * RPW * NL tokens: every K
+// and V row of a sub-chunk is requested at once (NL 16-byte loads of each per
+// lane), then
+//   pass 1: base-2 logits of the G query heads -> shared memory;
+//   one wave per head: the sub-chunk's max against the running max M, the
+//           weights exp2(logit - M'), their sum added to the running sum L
+//           after scaling it by exp2(M - M');
+//   pass 2: every lane scales its running V sums by the same factor and adds
+//           its rows' weighted V.
+// At the end the row groups of each wave are summed through lane swaps and
+// the NW waves through shared memory, and the portion's partial (M, L, acc)
+// is written with plain stores for the merge launch (merge_rows).
+template <int KVT, int D, int NW, int NL>
+struct PortionShape {
+  static constexpr int EB = Elem<KVT>::bytes;
+  static constexpr int EPL = Elem<KVT>::per16;
+  static constexpr int LR = D / EPL;   // lanes per K/V row
+  static constexpr int RPW = 64 / LR;  // rows per wave per load
+  static constexpr int CH = NW * RPW * NL;
+};
+
+template <int KVT, int D, int G, int NW, int NL>
+struct PortionSmem {
+  static constexpr int CH = PortionShape<KVT, D, NW, NL>::CH;
+  float q[G][D];        // the group's queries, scaled to base-2 logits
+  float w[CH][G];       // logits, then weights
+  float ml[G][4];       // running max M, running sum L, this sub-chunk's rescale factor
+  float acc[NW][G][D];  // per-wave partial outputs
+};
+
+// Stages the G query rows of (b, h), scaled by qscale, in S.q (every thread
+// of the NW waves; read after a barrier).
+template <int KVT, int D, int G, int NW, int NL>
+__device__ __forceinline__ void stage_group_query(const AttnArgs& a, int b, int h, PortionSmem<KVT, D, G, NW, NL>& S) {
+  constexpr int EB = Elem<KVT>::bytes;
+  for (int j = threadIdx.x; j < G * D; j += NW * 64) {
+    const size_t e = (size_t(b) * a.Hq + size_t(h) * G) * D + j;
+    const float x = EB == 2 ? bf16_lo(uint32_t(reinterpret_cast<const uint16_t*>(a.q)[e]))
+                            : reinterpret_cast<const float*>(a.q)[e];
+    S.q[j / D][j % D] = x * a.qscale;
+  }
+}
+
+template <int KVT, int D, int G, int NW, int NL>
+__device__ __forceinline__ void attend_portion(const AttnArgs& a, PortionSmem<KVT, D, G, NW, NL>& S,
+                                               const int* sidx, int row, int b, int h, int part, int cnt) {
+  using SH = PortionShape<KVT, D, NW, NL>;
+  constexpr int EB = SH::EB, EPL = SH::EPL, LR = SH::LR, RPW = SH::RPW, CH = SH::CH;
+  static_assert(LR >= 4 && LR <= 32 && G <= NW, "row split");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p = lane % LR, rsub = lane / LR;
+  float* pacc = a.part_acc + (size_t(row) * a.n_chunks + part) * G * D;
+  float* pml = a.part_ml + (size_t(row) * a.n_chunks + part) * G * 2;
+  if (cnt <= 0) return;  // an empty portion past the row's list: the merge ignores it
+  const char* kbase = reinterpret_cast<const char*>(a.k);
+  const char* vbase = reinterpret_cast<const char*>(a.v);
+  const size_t row_stride = size_t(a.Hkv) * D * EB;
+  const size_t head_off = (size_t(b) * a.t_max * a.Hkv + h) * D * EB + size_t(p) * EPL * EB;
+  if (threadIdx.x < G) {
+    S.ml[threadIdx.x][0] = -INFINITY;
+    S.ml[threadIdx.x][1] = 0.f;
+  }
+  float acc[G][EPL];
+  __syncthreads();  // S.q staged, S.ml set
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+  for (int c0 = 0; c0 < cnt; c0 += CH) {
+    const int n = min(CH, cnt - c0);
+    uint4 kr[NL], vr[NL];
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {  // rows past n re-read a valid row and get weight 0
+      const int r = (k * NW + wave) * RPW + rsub;
+      const int t = min(max(sidx[c0 + min(r, n - 1)], 0), a.t_max - 1);  // indices are clamped
+      const size_t off = head_off + size_t(t) * row_stride;
+      kr[k] = load16_nt(kbase + off);
+      vr[k] = load16_nt(vbase + off);
+    }
+    // pass 1: logits
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int r = (k * NW + wave) * RPW + rsub;
+      float kf[EPL];
+      unpack16<KVT>(kr[k], kf);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float* qg = &S.q[g][p * EPL];  // shared-memory reads: the queries stay out of registers
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s = fmaf(qg[e], kf[e], s);
+        s = group_sum<LR>(s);
+        if (p == 0) S.w[r][g] = (r < n) ? s : -INFINITY;
+      }
+    }
+    __syncthreads();
+    if (wave < G) {
+      const int g = wave;
+      float mx = -INFINITY;
+      for (int r = lane; r < CH; r += 64) mx = fmaxf(mx, S.w[r][g]);
+      mx = group_max<64>(mx);
+      const float m_old = S.ml[g][0];
+      const float m_new = fmaxf(m_old, mx);  // finite: the sub-chunk has a valid row
+      float sum = 0.f;
+      for (int r = lane; r < CH; r += 64) {
+        const float x = S.w[r][g];
+        const float wgt = (x == -INFINITY) ? 0.f : fast_exp2(x - m_new);
+        S.w[r][g] = wgt;
+        sum += wgt;
+      }
+      sum = group_sum<64>(sum);
+      if (lane == 0) {
+        const float alpha = (m_old == -INFINITY) ? 0.f : fast_exp2(m_old - m_new);
+        S.ml[g][0] = m_new;
+        S.ml[g][1] = S.ml[g][1] * alpha + sum;
+        S.ml[g][2] = alpha;
+      }
+    }
+    __syncthreads();
+    // pass 2: weighted V rows
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float alpha = S.ml[g][2];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+    }
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int r = (k * NW + wave) * RPW + rsub;
+      float vf[EPL];
+      unpack16<KVT>(vr[k], vf);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float wgt = S.w[r][g];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(wgt, vf[e], acc[g][e]);
+      }
+    }
+    __syncthreads();  // S.w and the factors are rewritten by the next sub-chunk
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = sum_across_groups<LR>(acc[g][e]);
+  if (lane < LR) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) S.acc[wave][g][p * EPL + e] = acc[g][e];
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < G * D; j += NW * 64) {
+    const int g = j / D, dd = j - g * D;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; w += 2) v += S.acc[w][g][dd] + S.acc[w + 1][g][dd];
+    pacc[j] = v;
+    if (dd == 0) {
+      pml[2 * g] = S.ml[g][0];
+      pml[2 * g + 1] = S.ml[g][1];
+    }
+  }
+}
+
 }  // namespace jssa

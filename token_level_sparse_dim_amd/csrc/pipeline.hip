@@ -1,4 +1,4 @@
-// Sparse decode step in four launches (JSSA summary Figure 1 and section
+// Sparse decode step in three launches (JSSA summary Figure 1 and section
 // E.1: subspace score scan, per-KV-head top-k selection, gather-free indexed
 // attention).
 //
@@ -14,14 +14,16 @@
 //                   are sized so that one run per resident workgroup covers
 //                   the rows: a run streams long enough that its row's
 //                   threshold is known by the time it is needed.
-// Resolve launch, one workgroup per row: the exact k-th key and tie cut among
-//   the row's candidates, the ascending index list plus the window, n_sel.  If
-//   fewer than k tokens reached L (the sample misled), the row is redone
-//   exactly: its scores are recomputed, first for the exact top radix digit of
-//   the k-th key, then to rewrite the candidate slots from that digit.
-// Attention launch, one workgroup per chunk of a row's index list, then a
-//   merge launch (one workgroup per row and query head) that combines the
-//   chunks' partials.
+// Select + attend launch, a few workgroups per row (the parts of its list):
+//   each part finds the exact k-th key and tie cut among the row's candidates
+//   (the same selection in every part of the row), keeps its own positions of
+//   the ascending index list plus window (writing them to the output list),
+//   and attends over them.  If fewer than k tokens reached L (the sample
+//   misled), the row is redone exactly: its scores are recomputed, first for
+//   the exact top radix digit of the k-th key, then to rewrite the candidate
+//   slots from that digit (every part writes the same values).
+// Merge launch, one workgroup per row and query head: the log-sum-exp
+//   combine of the parts' partials.
 // Data passes between launches through plain stores and loads; the only wait
 // inside a launch is a score run's on its row's sample (an item of a lower
 // workgroup index), bounded in time.
@@ -51,7 +53,10 @@ constexpr int kPipeMaxTiles = 2048;    // tiles per row
 constexpr int kPipeCutList = 256;      // candidates of the cut's bin ranked directly (one per thread)
 constexpr int kPipeGatherTiles = 8;    // tiles per wave per gather round
 constexpr int kResolveThreads = 1024;  // threads of a resolve workgroup
-constexpr int kPipeAttnNL = 8;         // K and V row loads per lane per attention chunk
+constexpr int kPortionNL = 4;          // K and V row loads per lane per attention sub-chunk
+constexpr int kPipeMaxPortion = 2048;  // list positions per select/attend workgroup at most
+constexpr int kPipeMaxParts = 16;      // select/attend workgroups per row at most
+constexpr int kPipePartTarget = 256;   // select/attend workgroups a launch aims for (one per CU)
 
 // per-row state word of the scan (zero on entry and exit): u64 at words 12-13,
 // kLwSet | L once the row's threshold is known, plus kLwAppended once the
@@ -316,7 +321,6 @@ struct Pipe {
   static constexpr int NIT_S = NSAMP / S::PER_ITER;
   static constexpr int RT = kResolveThreads, RW = RT / 64;  // resolve workgroup: threads, waves
   using Qp = QpSmem<D, R, G>;
-  using ASmem = Attn2Smem<KVT, D, G, kPipeAttnNL>;
 
   struct SampleSmem {
     Qp qp;
@@ -347,8 +351,6 @@ struct Pipe {
     uint32_t n_bin;
   };
   static constexpr size_t kSmemScan = cmax(sizeof(SampleSmem), sizeof(ScoreSmem));
-  // the exact re-selection overlays ScoreSmem on ResolveSmem (only on ResolveSmem::cand)
-  static constexpr size_t kSmemResolve = cmax(sizeof(ResolveSmem), sizeof(ScoreSmem));
 
   static __device__ const char* kp_row(const PipeArgs& a, int row) {
     return reinterpret_cast<const char*>(a.kp) + size_t(row) * a.at.t_max * R * S::EB;
@@ -776,7 +778,8 @@ struct Pipe {
   // to write the candidates.  The scores are the scan's: the group's projected
   // queries left by the sample, the same per-wave arithmetic, with the
   // workgroup's four-wave groups taking the steps of an item in turn.
-  static __device__ __forceinline__ void exact_candidates(const PipeArgs& a, int row, const RowMode& md, char* smem) {
+  static __device__ __forceinline__ void exact_candidates(const PipeArgs& a, int row, const RowMode& md, char* smem,
+                                                          bool leader) {
     constexpr int NT = RT, NWG = RT / 256;
     const uint32_t tid = threadIdx.x;
     ScoreSmem& ss = *reinterpret_cast<ScoreSmem*>(smem);
@@ -816,7 +819,7 @@ struct Pipe {
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) __hip_atomic_fetch_add(a.at.queue + QW_REDO, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (leader && tid == 0) __hip_atomic_fetch_add(a.at.queue + QW_REDO, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // Candidate ordinals in shared memory are spread over the RT threads in
@@ -894,19 +897,24 @@ struct Pipe {
     *istar_out = sm.out[1];
   }
 
-  static __device__ __forceinline__ void resolve_select(const PipeArgs& a, int row, const RowMode& md, char* smem) {
+  // The row's exact selection among its candidates: the k-th key K* and the
+  // tie cut I*, then emit(pos, token) for each selected candidate, pos its
+  // place in the ascending list (0 <= pos < kk).  Several workgroups may
+  // select the same row (each emits its own part); only the `leader` resets
+  // the row's state for the next call, writes n_sel and counts diagnostics.
+  template <typename Emit>
+  static __device__ __forceinline__ void select_row(const PipeArgs& a, int row, const RowMode& md, char* smem,
+                                                    bool leader, Emit emit) {
     ResolveSmem& sm = *reinterpret_cast<ResolveSmem*>(smem);
-    uint32_t* out = reinterpret_cast<uint32_t*>(a.at.idx + size_t(row) * a.at.idx_stride);
-    if (threadIdx.x == 0) {  // read again only by the next call's scan
+    if (leader && threadIdx.x == 0) {  // read again only by the next call's scan
       *l_word(a, row) = 0;
       const uint32_t claims = state(a, row)[PW_STEAL];
       if (claims) {
         __hip_atomic_fetch_add(a.at.queue + QW_CLAIMS, claims, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         state(a, row)[PW_STEAL] = 0;
       }
+      const_cast<int32_t*>(a.at.n_sel)[row] = md.kk + md.nW;
     }
-    for (int j = threadIdx.x; j < md.nW; j += RT) out[md.kk + j] = uint32_t(md.Tb - md.nW + j);
-    if (threadIdx.x == 0) const_cast<int32_t*>(a.at.n_sel)[row] = md.kk + md.nW;
     const int n_tiles_row = (md.n_cand + TS - 1) / TS;
     // the first digit's histogram is cleared while the gather's loads are in flight
     for (int i = threadIdx.x; i < 2048; i += RT) sm.hist[i] = 0u;
@@ -915,7 +923,7 @@ struct Pipe {
     uint32_t C = gather<false>(a, row, n_tiles_row, sm, &kmin, &kmax);
     const bool fresh = C < uint32_t(md.kk);  // the slots are rewritten below (read back device-scope)
     if (fresh) {
-      exact_candidates(a, row, md, smem);
+      exact_candidates(a, row, md, smem, leader);
       for (int i = threadIdx.x; i < 2048; i += RT) sm.hist[i] = 0u;
       if (threadIdx.x == 0) sm.n_bin = 0u;
       C = gather<true>(a, row, n_tiles_row, sm, &kmin, &kmax);
@@ -1027,11 +1035,12 @@ struct Pipe {
         const bool t = take(i);
         const uint64_t mk = __ballot(t);
         const uint32_t pos = off[i] + uint32_t(__popcll(mk & below));
-        if (t && pos < need) out[pos] = uint32_t(sm.cand[uint32_t(i) * RT + tid] >> 32);
+        if (t && pos < need) emit(pos, uint32_t(sm.cand[uint32_t(i) * RT + tid] >> 32));
       }
     } else {
       // more candidates than shared memory holds: every pass reads them in place
-      if (threadIdx.x == 0) __hip_atomic_fetch_add(a.at.queue + QW_BIG, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (leader && threadIdx.x == 0)
+        __hip_atomic_fetch_add(a.at.queue + QW_BIG, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const uint64_t* slots = a.cand + size_t(row) * a.at.t_max;
       auto global_cand = [&](uint32_t j) {
         const uint32_t tile = last_le(sm.tab, uint32_t(n_tiles_row), j);
@@ -1048,24 +1057,85 @@ struct Pipe {
       for (uint32_t j = j0; j < j1; ++j) {
         const uint64_t c = global_cand(j);
         if (passes(c, kstar, istar)) {
-          if (pos < need) out[pos] = uint32_t(c >> 32);
+          if (pos < need) emit(pos, uint32_t(c >> 32));
           ++pos;
         }
       }
     }
   }
 
-  // ---- ATTN -------------------------------------------------------------------------------
-  static __device__ __forceinline__ void attend(const PipeArgs& a, int row, int chunk, ASmem& S_) {
+  // ---- SELECT + ATTEND (second launch) ---------------------------------------------------
+  // Workgroup (row, part) selects the row exactly (every part of a row does
+  // the same selection; part 0 also writes n_sel and resets the row's state),
+  // keeps the positions [part * chunk, (part + 1) * chunk) of the ascending
+  // list plus window (and writes them to the output list), then attends over
+  // them and leaves the part's partial for the merge launch.  Rows with
+  // nothing to choose got their list from the scan launch; their parts derive
+  // their tokens from the positions.
+  static constexpr int kAttnNW = kResolveThreads / 64;
+  using PSmem = PortionSmem<KVT, D, G, kAttnNW, kPortionNL>;
+  struct SelSmem {
+    union {
+      ResolveSmem rs;  // the selection (the exact re-selection overlays ScoreSmem on it)
+      ScoreSmem ss;
+      PSmem at;        // the attention, once the selection is done
+    };
+    int sidx[kPipeMaxPortion];  // the part's token indices
+  };
+  // the group's query element of this thread (requested before the selection)
+  static __device__ __forceinline__ float query_elem(const PipeArgs& a, int b, int h) {
+    return threadIdx.x < G * D ? load_elem(a.at.q, (size_t(b) * a.at.Hq + size_t(h) * G) * D + threadIdx.x, a.q_dtype)
+                               : 0.f;
+  }
+  static __device__ __forceinline__ void attend_part(const PipeArgs& a, SelSmem& sm, int row, int b, int h, int part,
+                                                     int cnt, float qv) {
+    if (cnt <= 0) return;  // uniform over the workgroup
+    if (threadIdx.x < G * D) sm.at.q[threadIdx.x / D][threadIdx.x % D] = qv * a.at.qscale;
+    attend_portion<KVT, D, G, kAttnNW, kPortionNL>(a.at, sm.at, sm.sidx, row, b, h, part, cnt);
+  }
+  static __device__ __forceinline__ void select_attend(const PipeArgs& a, int row, int part, SelSmem& sm) {
     const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
-    // the chunk's index entries and n_sel (written by the previous launch) in one round trip
-    const int c0 = chunk * a.at.chunk;
-    const int32_t* src = a.at.idx + size_t(row) * a.at.idx_stride;
-    for (int i = threadIdx.x; i < a.at.chunk; i += 256) S_.idx[i] = src[min(c0 + i, a.at.idx_stride - 1)];
+    const RowMode md = row_mode(a, b);
+    const float qv = query_elem(a, b, h);
+    const int p0 = part * a.at.chunk;
+    const int p1 = min(p0 + a.at.chunk, md.kk + md.nW);
+    const int cnt = p1 > p0 ? p1 - p0 : 0;
+    int32_t* out = a.at.idx + size_t(row) * a.at.idx_stride;
+    if (md.select()) {
+      select_row(a, row, md, reinterpret_cast<char*>(&sm), part == 0, [&](uint32_t pos, uint32_t tok) {
+        if (int(pos) >= p0 && int(pos) < p1) {
+          sm.sidx[int(pos) - p0] = int(tok);
+          out[pos] = int(tok);
+        }
+      });
+    }
+    // positions past the selection (the window) and every position of a row
+    // with nothing to choose
+    for (int i = threadIdx.x; i < cnt; i += RT) {
+      const int pos = p0 + i;
+      if (pos >= md.kk) {
+        const int tok = md.Tb - md.nW + (pos - md.kk);
+        sm.sidx[i] = tok;
+        if (md.select()) out[pos] = tok;
+      } else if (!md.select()) {
+        sm.sidx[i] = pos;
+      }
+    }
+    __syncthreads();  // the part's list is complete; the selection's shared memory is free
+    attend_part(a, sm, row, b, h, part, cnt, qv);
+  }
+  // The same parts over a caller's index lists (n_sel[row] entries of idx).
+  static __device__ __forceinline__ void list_attend(const PipeArgs& a, int row, int part, SelSmem& sm) {
+    const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
+    const float qv = query_elem(a, b, h);
     int n = a.at.n_sel[row];
     n = n < 0 ? 0 : (n > a.at.idx_stride ? a.at.idx_stride : n);
+    const int p0 = part * a.at.chunk;
+    const int cnt = p0 < n ? min(a.at.chunk, n - p0) : 0;
+    const int32_t* src = a.at.idx + size_t(row) * a.at.idx_stride + p0;
+    for (int i = threadIdx.x; i < cnt; i += RT) sm.sidx[i] = src[i];
     __syncthreads();
-    attend_chunk_2pass<KVT, D, G, kPipeAttnNL, false>(a.at, S_, row, b, h, chunk, n);
+    attend_part(a, sm, row, b, h, part, cnt, qv);
   }
   static __device__ __forceinline__ void merge(const PipeArgs& a, int row, int g) {
     merge_rows<D, G>(a.at, row, g);
@@ -1118,23 +1188,35 @@ __global__ __launch_bounds__(256, 3) void scan_kernel(PipeArgs a) {
   }
 }
 
-// Resolve launch: one workgroup per (sequence, KV head) row.
-template <int KPT, int R, int GE, int D, int G, int KVT>
-__global__ __launch_bounds__(kResolveThreads, 1) void resolve_kernel(PipeArgs a) {
-  using Pp = Pipe<KPT, R, GE, D, G, KVT>;
-  __shared__ __align__(16) char smem[Pp::kSmemResolve];
-  const int row = blockIdx.x;
-  const RowMode md = row_mode(a, row / a.at.Hkv);
-  if (md.select()) Pp::resolve_select(a, row, md, smem);
+// Workgroup i of the select/attend launches runs on XCD i mod 8: the parts of
+// a row are placed on one XCD, so the row's candidates, read by every part,
+// come from that XCD's L2 after the first read.  False for the padding
+// workgroups of the last rows.
+__device__ __forceinline__ bool part_of(const PipeArgs& a, int i, int* row, int* part) {
+  const int x = i & 7, j = i >> 3;
+  *row = x + 8 * (j / a.at.n_chunks);
+  *part = j % a.at.n_chunks;
+  return *row < a.n_rows;
 }
 
-// Attention launch: one workgroup per chunk of a row's index list, each
-// leaving its partial for the merge launch.
+// Select + attend launch: one workgroup per (row, part of its list).
 template <int KPT, int R, int GE, int D, int G, int KVT>
-__global__ __launch_bounds__(256, 3) void attend_kernel(PipeArgs a) {
+__global__ __launch_bounds__(kResolveThreads, 1) void select_attend_kernel(PipeArgs a) {
   using Pp = Pipe<KPT, R, GE, D, G, KVT>;
-  __shared__ __align__(16) char smem[sizeof(typename Pp::ASmem)];
-  Pp::attend(a, blockIdx.x / a.at.n_chunks, blockIdx.x % a.at.n_chunks, *reinterpret_cast<typename Pp::ASmem*>(smem));
+  __shared__ __align__(16) char smem[sizeof(typename Pp::SelSmem)];
+  int row, part;
+  if (!part_of(a, blockIdx.x, &row, &part)) return;
+  Pp::select_attend(a, row, part, *reinterpret_cast<typename Pp::SelSmem*>(smem));
+}
+
+// Attention over caller lists: the same parts and arithmetic.
+template <int KPT, int R, int GE, int D, int G, int KVT>
+__global__ __launch_bounds__(kResolveThreads, 1) void list_attend_kernel(PipeArgs a) {
+  using Pp = Pipe<KPT, R, GE, D, G, KVT>;
+  __shared__ __align__(16) char smem[sizeof(typename Pp::SelSmem)];
+  int row, part;
+  if (!part_of(a, blockIdx.x, &row, &part)) return;
+  Pp::list_attend(a, row, part, *reinterpret_cast<typename Pp::SelSmem*>(smem));
 }
 
 // Merge launch: one workgroup of D threads per (row, query head).
@@ -1170,8 +1252,19 @@ bool pipeline_layout(const jssa_desc& d, int* ts, int* n_tiles, int* chunk) {
   if (!ok || d.layout != JSSA_LAYOUT_GQA) return false;
   *ts = scan_tile_tokens(d.kp_dtype, d.rank);
   *n_tiles = (d.t_max + *ts - 1) / *ts;
-  const int per16 = d.kv_dtype == JSSA_BF16 ? 8 : 4;
-  *chunk = kPipeAttnNL * 4 * (64 / (d.d_k / per16));  // the two-pass attention chunk
+  // the select/attend parts of a row: about kPipePartTarget workgroups in all,
+  // at most kPipeMaxPortion list positions each (a function of the descriptor
+  // only, so results do not depend on the device)
+  const int64_t n_max = int64_t(d.topk) + d.window;
+  const int64_t rows = int64_t(d.batch) * d.n_kv_heads;
+  int64_t parts = (kPipePartTarget + rows - 1) / rows;
+  if (parts > kPipeMaxParts) parts = kPipeMaxParts;
+  const int64_t need = (n_max + kPipeMaxPortion - 1) / kPipeMaxPortion;
+  if (parts < need) parts = need;
+  if (parts > kPipeMaxParts || n_max < 1) return false;
+  int64_t c = (n_max + parts - 1) / parts;
+  c = (c + 63) / 64 * 64;
+  *chunk = int(c);  // list positions per part; ceil(n_max / chunk) <= kPipeMaxParts parts
   return *n_tiles <= kPipeMaxTiles;
 }
 
@@ -1223,9 +1316,10 @@ static int scan_per_cu() {
 template <int KPT, int R, int GE, int D, int G, int KVT>
 static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
   using Pp = Pipe<KPT, R, GE, D, G, KVT>;
-  if (Pp::TS != a.ts || Attn2Shape<KVT, D, G, kPipeAttnNL>::CH != a.at.chunk) return hipErrorInvalidValue;
+  if (Pp::TS != a.ts || a.at.chunk % 64 != 0 || a.at.chunk > kPipeMaxPortion || a.at.n_chunks > kPipeMaxParts)
+    return hipErrorInvalidValue;
   if (a.attend_only) {  // caller-provided index lists: the attention and merge launches only
-    hipLaunchKernelGGL((attend_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_attn), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((list_attend_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_attn), dim3(kResolveThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((merge_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_rows * G), dim3(D), 0, s, a);
@@ -1259,10 +1353,8 @@ static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
     hipLaunchKernelGGL((scan_kernel<KPT, R, GE, D, G, KVT>), dim3(grid), dim3(256), 0, s, a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((resolve_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_rows), dim3(kResolveThreads), 0, s, a);
+  hipLaunchKernelGGL((select_attend_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_attn), dim3(kResolveThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess) return e;
-  hipLaunchKernelGGL((attend_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_attn), dim3(256), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((merge_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_rows * G), dim3(D), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return mark(3);
@@ -1303,7 +1395,7 @@ static hipError_t pipeline_impl(const jssa_desc& d, const void* q, const float* 
   a.G = d.n_q_heads / d.n_kv_heads; a.d_k = d.d_k; a.topk = d.topk; a.window = d.window;
   a.q_dtype = d.kv_dtype; a.ts = ws.pipe_ts; a.n_tiles = ws.pipe_tiles;
   a.n_rows = d.batch * d.n_kv_heads;
-  a.n_attn = a.n_rows * ws.pipe_n_chunks;
+  a.n_attn = 8 * ((a.n_rows + 7) / 8) * ws.pipe_n_chunks;  // (row, part) workgroups, rows padded to the 8 XCDs
   a.spin_ticks = wait_ticks();
   const int G = a.G;
   const bool mean = d.reduce == JSSA_REDUCE_MEAN;
