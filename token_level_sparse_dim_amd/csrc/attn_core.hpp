@@ -538,10 +538,16 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, int row, int g) {
 // ---- one row's portion of its index list, by NW waves --------------------------------
 // The fused decode's attention: the workgroup that selected a row's tokens (or
 // read them from a caller's list) attends over its portion of the list, `cnt`
-// token indices in S.idx[].  Sub-chunks of CH = NW * RPW * NL tokens: every K
+// token indices in sidx[].  Sub-chunks of CH = NW * RPW * NL tokens: every K
 // and V row of a sub-chunk is requested at once (NL 16-byte loads of each per
-// lane), then
-//   pass 1: base-2 logits of the G query heads -> shared memory;
+// lane, lane (p, rsub) taking elements EPL p .. EPL p + EPL - 1 of rows rsub,
+// rsub + RPW, ...), the next sub-chunk's as soon as this one is done (two
+// sub-chunks in flight measured slower: more barriers for the same transfer).
+// Per sub-chunk:
+//   pass 1: the G heads' logits -> shared memory (bf16: v_dot2c_f32_bf16 on
+//           the packed bf16 pairs of K and of the unscaled query, products
+//           exact and summed in fp32, then scaled; fp32: fma chains with the
+//           scaled query);
 //   one wave per head: the sub-chunk's max against the running max M, the
 //           weights exp2(logit - M'), their sum added to the running sum L
 //           after scaling it by exp2(M - M');
@@ -562,23 +568,16 @@ struct PortionShape {
 template <int KVT, int D, int G, int NW, int NL>
 struct PortionSmem {
   static constexpr int CH = PortionShape<KVT, D, NW, NL>::CH;
-  float q[G][D];        // the group's queries, scaled to base-2 logits
-  float w[CH][G];       // logits, then weights
-  float ml[G][4];       // running max M, running sum L, this sub-chunk's rescale factor
-  float acc[NW][G][D];  // per-wave partial outputs
+  // the group's queries: bf16 as stored (packed pairs), fp32 scaled to base-2 logits
+  alignas(16) uint32_t q[KVT == 1 ? G * D / 2 : G * D];
+  alignas(16) float w[CH][G];  // logits, then weights
+  float ml[G][4];              // running max M, running sum L, this sub-chunk's rescale factor
+  float acc[NW][G][D];         // per-wave partial outputs
 };
 
-// Stages the G query rows of (b, h), scaled by qscale, in S.q (every thread
-// of the NW waves; read after a barrier).
-template <int KVT, int D, int G, int NW, int NL>
-__device__ __forceinline__ void stage_group_query(const AttnArgs& a, int b, int h, PortionSmem<KVT, D, G, NW, NL>& S) {
-  constexpr int EB = Elem<KVT>::bytes;
-  for (int j = threadIdx.x; j < G * D; j += NW * 64) {
-    const size_t e = (size_t(b) * a.Hq + size_t(h) * G) * D + j;
-    const float x = EB == 2 ? bf16_lo(uint32_t(reinterpret_cast<const uint16_t*>(a.q)[e]))
-                            : reinterpret_cast<const float*>(a.q)[e];
-    S.q[j / D][j % D] = x * a.qscale;
-  }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
 template <int KVT, int D, int G, int NW, int NL>
@@ -586,6 +585,7 @@ __device__ __forceinline__ void attend_portion(const AttnArgs& a, PortionSmem<KV
                                                const int* sidx, int row, int b, int h, int part, int cnt) {
   using SH = PortionShape<KVT, D, NW, NL>;
   constexpr int EB = SH::EB, EPL = SH::EPL, LR = SH::LR, RPW = SH::RPW, CH = SH::CH;
+  constexpr int QW = KVT == 1 ? EPL / 2 : EPL;  // query words per lane and head
   static_assert(LR >= 4 && LR <= 32 && G <= NW, "row split");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int p = lane % LR, rsub = lane / LR;
@@ -596,40 +596,54 @@ __device__ __forceinline__ void attend_portion(const AttnArgs& a, PortionSmem<KV
   const char* vbase = reinterpret_cast<const char*>(a.v);
   const size_t row_stride = size_t(a.Hkv) * D * EB;
   const size_t head_off = (size_t(b) * a.t_max * a.Hkv + h) * D * EB + size_t(p) * EPL * EB;
-  if (threadIdx.x < G) {
-    S.ml[threadIdx.x][0] = -INFINITY;
-    S.ml[threadIdx.x][1] = 0.f;
-  }
-  float acc[G][EPL];
-  __syncthreads();  // S.q staged, S.ml set
+  const int n_sub = (cnt + CH - 1) / CH;
+  // K and V rows of sub-chunk c (rows past cnt re-read a valid row and get weight 0)
+  auto load_sub = [&](int c, uint4 (&kr)[NL], uint4 (&vr)[NL]) {
+    const int c0 = min(c, n_sub - 1) * CH;
 #pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
-  for (int c0 = 0; c0 < cnt; c0 += CH) {
-    const int n = min(CH, cnt - c0);
-    uint4 kr[NL], vr[NL];
-#pragma unroll
-    for (int k = 0; k < NL; ++k) {  // rows past n re-read a valid row and get weight 0
+    for (int k = 0; k < NL; ++k) {
       const int r = (k * NW + wave) * RPW + rsub;
-      const int t = min(max(sidx[c0 + min(r, n - 1)], 0), a.t_max - 1);  // indices are clamped
+      const int t = min(max(sidx[min(c0 + r, cnt - 1)], 0), a.t_max - 1);  // indices are clamped
       const size_t off = head_off + size_t(t) * row_stride;
       kr[k] = load16_nt(kbase + off);
       vr[k] = load16_nt(vbase + off);
     }
+  };
+  uint4 kA[NL], vA[NL];
+  load_sub(0, kA, vA);
+  if (threadIdx.x < G) {
+    S.ml[threadIdx.x][0] = -INFINITY;
+    S.ml[threadIdx.x][1] = 0.f;
+  }
+  __syncthreads();  // S.q staged, S.ml set
+  uint32_t qreg[G][QW];
+  float acc[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int e = 0; e < QW; ++e) qreg[g][e] = S.q[(g * D + p * EPL) / (EPL / QW) + e];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+  }
+  auto sub_chunk = [&](int c, const uint4 (&kr)[NL], const uint4 (&vr)[NL]) {
+    const int n = min(CH, cnt - c * CH);
     // pass 1: logits
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
       const int r = (k * NW + wave) * RPW + rsub;
-      float kf[EPL];
-      unpack16<KVT>(kr[k], kf);
+      const uint32_t kw[4] = {kr[k].x, kr[k].y, kr[k].z, kr[k].w};
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float* qg = &S.q[g][p * EPL];  // shared-memory reads: the queries stay out of registers
         float s = 0.f;
+        if constexpr (KVT == 1) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) s = fmaf(qg[e], kf[e], s);
+          for (int e = 0; e < 4; ++e) s = dot2_bf16(kw[e], qreg[g][e], s);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s = fmaf(__uint_as_float(qreg[g][e]), __uint_as_float(kw[e]), s);
+        }
         s = group_sum<LR>(s);
+        if (KVT == 1) s *= a.qscale;
         if (p == 0) S.w[r][g] = (r < n) ? s : -INFINITY;
       }
     }
@@ -657,26 +671,38 @@ __device__ __forceinline__ void attend_portion(const AttnArgs& a, PortionSmem<KV
       }
     }
     __syncthreads();
-    // pass 2: weighted V rows
+    // pass 2: weighted V rows (the running sums rescaled first, after the first sub-chunk)
+    if (c > 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float alpha = S.ml[g][2];
+      for (int g = 0; g < G; ++g) {
+        const float alpha = S.ml[g][2];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+        for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+      }
     }
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
       const int r = (k * NW + wave) * RPW + rsub;
       float vf[EPL];
       unpack16<KVT>(vr[k], vf);
+      float wr[G];
+      if constexpr (G == 4) {  // one 16-byte shared-memory read
+        const float4 w4 = *reinterpret_cast<const float4*>(&S.w[r][0]);
+        wr[0] = w4.x; wr[1] = w4.y; wr[2] = w4.z; wr[3] = w4.w;
+      } else {
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float wgt = S.w[r][g];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(wgt, vf[e], acc[g][e]);
+        for (int g = 0; g < G; ++g) wr[g] = S.w[r][g];
       }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(wr[g], vf[e], acc[g][e]);
     }
     __syncthreads();  // S.w and the factors are rewritten by the next sub-chunk
+  };
+  for (int c = 0; c < n_sub; ++c) {
+    sub_chunk(c, kA, vA);
+    if (c + 1 < n_sub) load_sub(c + 1, kA, vA);
   }
 #pragma unroll
   for (int g = 0; g < G; ++g)

@@ -53,7 +53,10 @@ constexpr int kPipeMaxTiles = 2048;    // tiles per row
 constexpr int kPipeCutList = 256;      // candidates of the cut's bin ranked directly (one per thread)
 constexpr int kPipeGatherTiles = 8;    // tiles per wave per gather round
 constexpr int kResolveThreads = 1024;  // threads of a resolve workgroup
-constexpr int kPortionNL = 4;          // K and V row loads per lane per attention sub-chunk
+#ifndef JSSA_PORTION_NL
+#define JSSA_PORTION_NL 2
+#endif
+constexpr int kPortionNL = JSSA_PORTION_NL;  // K and V row loads per lane per attention sub-chunk
 constexpr int kPipeMaxPortion = 2048;  // list positions per select/attend workgroup at most
 constexpr int kPipeMaxParts = 16;      // select/attend workgroups per row at most
 constexpr int kPipePartTarget = 256;   // select/attend workgroups a launch aims for (one per CU)
@@ -681,15 +684,16 @@ struct Pipe {
     }
   }
 
-  // ---- RESOLVE (second launch) ------------------------------------------------------------
+  // ---- SELECTION (second launch) ----------------------------------------------------------
   // Gathers the row's candidates into shared memory by ordinal (token order).
   // Each wave takes kPipeGatherTiles tiles a round and issues every load of the
-  // round at once: the tiles' counts (one per lane) and their first 128 slots
-  // (one 16-byte load per lane and tile: a tile's candidates are contiguous
-  // from the start of its slot; slots past the count are read but not used,
-  // and the candidate buffer has kCandPad slots past its last row, so no load
-  // needs a bound).  A shuffle scan of the counts and the four wave totals give
-  // the tiles' first ordinals, kept in sm.tab.  Stores of unused lanes go to a
+  // round at once: the tiles' counts (one per lane) and their first 64 slots
+  // (one 8-byte load per lane and tile: a tile's candidates are contiguous
+  // from the start of its slot, about 40 at 128K context and k = 2048; slots
+  // past the count are read but not used, and the candidate buffer has
+  // kCandPad slots past its last row, so no load needs a bound; a tile with
+  // more than 64 takes a second round trip).  A shuffle scan of the counts and
+  // the wave totals give the tiles' first ordinals, kept in sm.tab.  Stores of unused lanes go to a
   // dummy slot.  Returns the number of candidates C; *kmin / *kmax: their
   // smallest / largest key (C > 0).  FRESH: the slots and counts were
   // rewritten by this workgroup after an earlier gather, so they are read
@@ -716,19 +720,12 @@ struct Pipe {
       const bool own = lane < uint32_t(UB) && t0 + int(lane) < n_tiles_row;
       uint32_t my_cnt = FRESH ? consume(cnt_row + tl) : cnt_row[tl];
       my_cnt = own ? my_cnt : 0u;
-      uint64_t v0[UB], v1[UB];
+      uint64_t v0[UB];
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         const int t = min(t0 + u, n_tiles_row - 1);  // past the row's tiles: count 0
-        const uint64_t* src = slots + size_t(t) * TS + 2 * lane;
-        if (FRESH) {
-          v0[u] = consume(src);
-          v1[u] = consume(src + 1);
-        } else {
-          const u32x4_a8 w = *reinterpret_cast<const u32x4_a8*>(src);
-          v0[u] = uint64_t(w.x) | (uint64_t(w.y) << 32);
-          v1[u] = uint64_t(w.z) | (uint64_t(w.w) << 32);
-        }
+        const uint64_t* src = slots + size_t(t) * TS + lane;
+        v0[u] = FRESH ? consume(src) : *src;
       }
       const uint32_t incl = wave_scan_incl(my_cnt);  // over the lanes that own tiles
       sm.wsum[parity][wave] = uint32_t(__builtin_amdgcn_readlane(int(incl), UB - 1));
@@ -746,11 +743,10 @@ struct Pipe {
       for (int u = 0; u < UB; ++u) {
         const uint32_t cnt_u = uint32_t(__builtin_amdgcn_readlane(int(my_cnt), u));
         const uint32_t base_u = wbase + uint32_t(__builtin_amdgcn_readlane(int(excl), u));
-        put(2u * lane < cnt_u, base_u + 2u * lane, v0[u]);
-        put(2u * lane + 1u < cnt_u, base_u + 2u * lane + 1u, v1[u]);
-        if (cnt_u > 128u) {  // a crowded tile: the rest of its slot
+        put(lane < cnt_u, base_u + lane, v0[u]);
+        if (cnt_u > 64u) {  // a crowded tile: the rest of its slot
           const uint64_t* src = slots + size_t(t0 + u) * TS;
-          for (uint32_t i = lane + 128u; i < cnt_u; i += 64u) put(true, base_u + i, FRESH ? consume(src + i) : src[i]);
+          for (uint32_t i = lane + 64u; i < cnt_u; i += 64u) put(true, base_u + i, FRESH ? consume(src + i) : src[i]);
         }
       }
       run += rtot;
@@ -1082,32 +1078,46 @@ struct Pipe {
     };
     int sidx[kPipeMaxPortion];  // the part's token indices
   };
-  // the group's query element of this thread (requested before the selection)
-  static __device__ __forceinline__ float query_elem(const PipeArgs& a, int b, int h) {
-    return threadIdx.x < G * D ? load_elem(a.at.q, (size_t(b) * a.at.Hq + size_t(h) * G) * D + threadIdx.x, a.q_dtype)
-                               : 0.f;
+  // The group's queries, requested before the selection and staged in shared
+  // memory after it: bf16 as stored, in 16-byte pieces (thread i holds piece
+  // i of the G rows); fp32 one element per thread, scaled to base-2 logits.
+  static constexpr int kQPieces = KVT == 1 ? G * D / 8 : G * D;
+  static_assert(kQPieces <= kResolveThreads, "query staging");
+  static __device__ __forceinline__ uint4 query_piece(const PipeArgs& a, int b, int h) {
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    const size_t q0 = (size_t(b) * a.at.Hq + size_t(h) * G) * D;
+    if (threadIdx.x < kQPieces) {
+      if constexpr (KVT == 1) v = load16(reinterpret_cast<const uint16_t*>(a.at.q) + q0 + threadIdx.x * 8);
+      else v.x = __float_as_uint(reinterpret_cast<const float*>(a.at.q)[q0 + threadIdx.x] * a.at.qscale);
+    }
+    return v;
   }
   static __device__ __forceinline__ void attend_part(const PipeArgs& a, SelSmem& sm, int row, int b, int h, int part,
-                                                     int cnt, float qv) {
+                                                     int cnt, const uint4& qp) {
     if (cnt <= 0) return;  // uniform over the workgroup
-    if (threadIdx.x < G * D) sm.at.q[threadIdx.x / D][threadIdx.x % D] = qv * a.at.qscale;
+    if (threadIdx.x < kQPieces) {
+      if constexpr (KVT == 1) reinterpret_cast<uint4*>(sm.at.q)[threadIdx.x] = qp;
+      else sm.at.q[threadIdx.x] = qp.x;
+    }
     attend_portion<KVT, D, G, kAttnNW, kPortionNL>(a.at, sm.at, sm.sidx, row, b, h, part, cnt);
   }
   static __device__ __forceinline__ void select_attend(const PipeArgs& a, int row, int part, SelSmem& sm) {
     const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
     const RowMode md = row_mode(a, b);
-    const float qv = query_elem(a, b, h);
+    const uint4 qp = query_piece(a, b, h);
     const int p0 = part * a.at.chunk;
     const int p1 = min(p0 + a.at.chunk, md.kk + md.nW);
     const int cnt = p1 > p0 ? p1 - p0 : 0;
     int32_t* out = a.at.idx + size_t(row) * a.at.idx_stride;
     if (md.select()) {
-      select_row(a, row, md, reinterpret_cast<char*>(&sm), part == 0, [&](uint32_t pos, uint32_t tok) {
-        if (int(pos) >= p0 && int(pos) < p1) {
-          sm.sidx[int(pos) - p0] = int(tok);
-          out[pos] = int(tok);
-        }
-      });
+      select_row(
+          a, row, md, reinterpret_cast<char*>(&sm), part == 0,
+          [&](uint32_t pos, uint32_t tok) {
+            if (int(pos) >= p0 && int(pos) < p1) {
+              sm.sidx[int(pos) - p0] = int(tok);
+              out[pos] = int(tok);
+            }
+          });
     }
     // positions past the selection (the window) and every position of a row
     // with nothing to choose
@@ -1122,12 +1132,12 @@ struct Pipe {
       }
     }
     __syncthreads();  // the part's list is complete; the selection's shared memory is free
-    attend_part(a, sm, row, b, h, part, cnt, qv);
+    attend_part(a, sm, row, b, h, part, cnt, qp);
   }
   // The same parts over a caller's index lists (n_sel[row] entries of idx).
   static __device__ __forceinline__ void list_attend(const PipeArgs& a, int row, int part, SelSmem& sm) {
     const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
-    const float qv = query_elem(a, b, h);
+    const uint4 qp = query_piece(a, b, h);
     int n = a.at.n_sel[row];
     n = n < 0 ? 0 : (n > a.at.idx_stride ? a.at.idx_stride : n);
     const int p0 = part * a.at.chunk;
@@ -1135,7 +1145,7 @@ struct Pipe {
     const int32_t* src = a.at.idx + size_t(row) * a.at.idx_stride + p0;
     for (int i = threadIdx.x; i < cnt; i += RT) sm.sidx[i] = src[i];
     __syncthreads();
-    attend_part(a, sm, row, b, h, part, cnt, qv);
+    attend_part(a, sm, row, b, h, part, cnt, qp);
   }
   static __device__ __forceinline__ void merge(const PipeArgs& a, int row, int g) {
     merge_rows<D, G>(a.at, row, g);
