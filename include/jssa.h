@@ -218,8 +218,9 @@ int32_t jssa_topk(const jssa_desc* desc, const float* scores, const int32_t* seq
  * sequence; the value is the first d_v columns of the selected row; q.K and
  * P V run on the matrix cores with fp32 accumulation and the probabilities
  * entered as bf16 hi + lo terms (about 16 significant bits).  Shapes with a
- * fused decode build run the decode's own attention and chunk-merge launches
- * (the same results as the attention inside jssa_decode).
+ * fused decode build run the decode's own attention over parts of each list
+ * and its in-launch merge of the parts (the same results as the attention
+ * inside jssa_decode).
  * Workspace op JSSA_OP_ATTN. */
 int32_t jssa_indexed_attn(const jssa_desc* desc, const void* q, const void* k_cache,
                           const void* v_cache, const int32_t* idx, const int32_t* n_sel,
@@ -229,14 +230,18 @@ int32_t jssa_indexed_attn(const jssa_desc* desc, const void* q, const void* k_ca
  * jssa_indexed_attn (JSSA summary Figure 1 and section E.1), bit-identical in
  * idx / n_sel, with intermediates in the workspace.  For the shapes with a
  * fused build (bf16: d 128 rank 32 G 4, d 128 rank 64 G 1, d 64 rank 16 G 4;
- * f32: d 64 rank 16 G 4, d 128 rank 32 G 2; GQA layout) it runs in four
- * launches: a scan that scores every candidate and keeps, per tile, the
- * tokens at or above a threshold taken from a strided sample of the row's
- * scores; a resolve that selects exactly among them (re-selecting a row
- * exactly in the rare case fewer than k tokens passed the threshold); the
- * attention over chunks of the selection; the merge of the chunks.  Other shapes run the stand-alone kernels in sequence (MLA:
- * query projection, score scan with the first-digit histogram, candidate
- * pass, resolve, attention, chunk merge).
+ * bf16 K/V with FP8 projected keys: d 128 rank 32 G 4, d 128 rank 64 G 1;
+ * f32: d 64 rank 16 G 4, d 128 rank 32 G 2; GQA layout; topk + window at most
+ * 32768) it runs in two launches: a scan that scores every candidate and
+ * keeps, per tile, the tokens at or above a threshold taken from a strided
+ * sample of the row's scores; then a few workgroups per (sequence, KV head)
+ * that each select the row exactly among those tokens (re-selecting it exactly
+ * in the rare case fewer than k passed the threshold), keep their part of the
+ * list, attend over it, and merge the parts (the row's last part).  The
+ * attention over a part is the one jssa_indexed_attn runs on these shapes, so
+ * both give the same outputs for the same lists.  Other shapes run the
+ * stand-alone kernels in sequence (MLA: query projection, score scan with the
+ * first-digit histogram, candidate pass, resolve, attention, chunk merge).
  * idx_out / n_sel_out may be NULL; when given they receive the selection.
  * The new token is expected to be appended (jssa_append_kv) before this
  * call.  Workspace op JSSA_OP_DECODE. */
@@ -251,11 +256,12 @@ int32_t jssa_decode(const jssa_desc* desc, const void* q, const float* P, const 
  * breakdown of JSSA summary section E.1 (scan, selection, attention).  Fused
  * build: [0] and [1] are the scan kernel's own start and end (the kernel's
  * execution, as a profiler reports it; the scan also writes the candidates),
- * [2] is recorded after the resolve, [3] after the attention.  Other GQA
- * shapes: [0] before the score scan, [1] after it, [2] after the candidate
- * pass, [3] after the resolve + attention.  MLA: [0] and [1] the score scan
- * kernel's start and end, [2] after the candidate pass, [3] after the
- * resolve, the attention and the chunk merge. */
+ * [2] is recorded after the select/attend launch (selection, attention and
+ * merge), [3] right after [2].  Other GQA shapes: [0] before the score scan,
+ * [1] after it, [2] after the candidate pass, [3] after the resolve +
+ * attention.  MLA: [0] and [1] the score scan kernel's start and end, [2]
+ * after the candidate pass, [3] after the resolve, the attention and the
+ * chunk merge. */
 int32_t jssa_decode_profiled(const jssa_desc* desc, const void* q, const float* P,
                              const void* kp_cache, const void* k_cache, const void* v_cache,
                              const int32_t* seq_lens, void* out, float* lse, int32_t* idx_out,
@@ -318,7 +324,7 @@ int32_t jssa_decode_step_static(const jssa_desc* desc, const void* k_new, const 
  * jssa_indexed_attn does.  idx / n_sel are an indexer layer's lists of the
  * same step ([B, Hkv, topk + window] and [B, Hkv], e.g. idx_out / n_sel_out of
  * its jssa_decode_step); both layers index the same token positions.  The
- * fused build runs the decode's own attention and chunk-merge launches; other
+ * fused build runs the decode's own attention and merge of its parts; other
  * shapes the stand-alone attention.  MLA: k_new [B, 1, 1, d_k], v_new and
  * v_cache unused (may be NULL).  Workspace op JSSA_OP_DECODE. */
 int32_t jssa_reuse_step(const jssa_desc* desc, const void* k_new, const void* v_new,

@@ -308,168 +308,8 @@ __device__ bool attend_chunk(const AttnArgs& a, Smem& S, int row, int b, int h, 
   return true;
 }
 
-// Two-pass variant for short chunks (the fused decode): every K and V row of
-// the chunk is requested at once (NL 16-byte loads of each per lane), then
-//   pass 1: base-2 logits of the G query heads -> shared memory; one wave per
-//           head finds the chunk's max m_g and sum l_g of exp2(logit - m_g)
-//           and turns the logits into those weights;
-//   pass 2: acc[g] = sum_t w[t][g] * V[t], summed over the row groups of a wave
-//           with shuffles and over the 4 waves through shared memory.
-// The chunk partial (m_g, l_g, acc[g]) is the one attend_chunk publishes, so
-// the same log-sum-exp combine finishes the row.  One chunk covers
-// CH = NL * 4 * RPW tokens (a.chunk must equal it).
-template <int KVT, int D, int G, int NL>
-struct Attn2Shape {
-  static constexpr int EB = Elem<KVT>::bytes;
-  static constexpr int EPL = Elem<KVT>::per16;
-  static constexpr int LR = D / EPL;   // lanes per K/V row
-  static constexpr int RPW = 64 / LR;  // rows per wave per load
-  static constexpr int CH = NL * 4 * RPW;
-};
-
-template <int KVT, int D, int G, int NL>
-struct Attn2Smem {
-  static_assert(4 * G * D >= kCombineBatch * G + 2 * G, "combine scratch fits in acc");
-  static constexpr int CH = Attn2Shape<KVT, D, G, NL>::CH;
-  int idx[CH];
-  float w[CH][G];      // logits, then weights
-  float ml[G][2];      // chunk max and sum of each head
-  float acc[4][G][D];  // per-wave partial outputs
-};
-
-// MERGE: the row's last chunk merges the partials here (device-scope hand-off
-// through a ticket); otherwise the partials are written with plain stores for
-// a later launch (merge_rows) to merge.
-template <int KVT, int D, int G, int NL, bool MERGE = true, typename Smem>
-__device__ __forceinline__ bool attend_chunk_2pass(const AttnArgs& a, Smem& S, int row, int b, int h, int chunk_id, int n) {
-  using SH = Attn2Shape<KVT, D, G, NL>;
-  constexpr int EB = SH::EB, EPL = SH::EPL, LR = SH::LR, RPW = SH::RPW, CH = SH::CH;
-  static_assert(LR >= 4 && LR <= 32, "row split");
-  const int c0 = chunk_id * CH;
-  const int cnt = c0 < n ? min(c0 + CH, n) - c0 : 0;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float* pacc = a.part_acc + (size_t(row) * a.n_chunks + chunk_id) * G * D;
-  float* pml = a.part_ml + (size_t(row) * a.n_chunks + chunk_id) * G * 2;
-
-  if (cnt > 0) {
-    const int p = lane % LR, rsub = lane / LR;
-    const char* kbase = reinterpret_cast<const char*>(a.k);
-    const char* vbase = reinterpret_cast<const char*>(a.v);
-    const size_t row_stride = size_t(a.Hkv) * D * EB;
-    const size_t head_off = (size_t(b) * a.t_max * a.Hkv + h) * D * EB + size_t(p) * EPL * EB;
-    uint4 kr[NL], vr[NL];
-#pragma unroll
-    for (int k = 0; k < NL; ++k) {  // rows past cnt re-read a valid row and get weight 0
-      const int r = (k * 4 + wave) * RPW + rsub;
-      const int t = min(max(S.idx[min(r, cnt - 1)], 0), a.t_max - 1);  // indices are clamped
-      const size_t off = head_off + size_t(t) * row_stride;
-      kr[k] = load16_nt(kbase + off);
-      vr[k] = load16_nt(vbase + off);
-    }
-    float qreg[G][EPL];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const uint4 raw = load16(reinterpret_cast<const char*>(a.q) +
-                               ((size_t(b) * a.Hq + size_t(h) * G + g) * D + p * EPL) * EB);
-      float tmp[EPL];
-      unpack16<KVT>(raw, tmp);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) qreg[g][e] = tmp[e] * a.qscale;
-    }
-    // pass 1: logits
-#pragma unroll
-    for (int k = 0; k < NL; ++k) {
-      const int r = (k * 4 + wave) * RPW + rsub;
-      float kf[EPL];
-      unpack16<KVT>(kr[k], kf);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) s = fmaf(qreg[g][e], kf[e], s);
-        s = group_sum<LR>(s);
-        if (p == 0) S.w[r][g] = (r < cnt) ? s : -INFINITY;
-      }
-    }
-    __syncthreads();
-    for (int g = wave; g < G; g += 4) {
-      float mx = -INFINITY;
-      for (int r = lane; r < CH; r += 64) mx = fmaxf(mx, S.w[r][g]);
-      mx = group_max<64>(mx);
-      float sum = 0.f;
-      for (int r = lane; r < CH; r += 64) {
-        const float x = S.w[r][g];
-        const float wgt = (x == -INFINITY) ? 0.f : fast_exp2(x - mx);
-        S.w[r][g] = wgt;
-        sum += wgt;
-      }
-      sum = group_sum<64>(sum);
-      if (lane == 0) {
-        S.ml[g][0] = mx;
-        S.ml[g][1] = sum;
-      }
-    }
-    __syncthreads();
-    // pass 2: weighted V rows
-    float acc[G][EPL];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
-#pragma unroll
-    for (int k = 0; k < NL; ++k) {
-      const int r = (k * 4 + wave) * RPW + rsub;
-      float vf[EPL];
-      unpack16<KVT>(vr[k], vf);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float wgt = S.w[r][g];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(wgt, vf[e], acc[g][e]);
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] = sum_across_groups<LR>(acc[g][e]);
-    if (lane < LR) {
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) S.acc[wave][g][p * EPL + e] = acc[g][e];
-    }
-    __syncthreads();
-    for (int j = threadIdx.x; j < G * D; j += 256) {
-      const int g = j / D, dd = j - g * D;
-      const float v = (S.acc[0][g][dd] + S.acc[1][g][dd]) + (S.acc[2][g][dd] + S.acc[3][g][dd]);
-      if (MERGE) publish(&pacc[j], v);
-      else pacc[j] = v;
-      if (dd == 0) {
-        if (MERGE) {
-          publish(&pml[2 * g], S.ml[g][0]);
-          publish(&pml[2 * g + 1], S.ml[g][1]);
-        } else {
-          pml[2 * g] = S.ml[g][0];
-          pml[2 * g + 1] = S.ml[g][1];
-        }
-      }
-    }
-  }
-  if (!MERGE) return false;
-  uint32_t* rstate = a.row_state + size_t(row) * kRowStateWords;
-  if (!last_arrival(&rstate[RS_TICKET_ATTN], uint32_t(a.n_chunks))) return false;
-  combine_chunks<D, G>(a, row, b, h, n, &S.acc[0][0][0]);
-  return true;
-}
-
-// Merge of one (row, head) in a launch after the chunks' (plain-stored)
-// partials: thread dd owns output element dd; every chunk's max, sum and
-// partial are read in batches of kMergeBatch loads issued together, folded
-// into a running log-sum-exp in chunk order.  The first batch is requested
-// together with the row's n_sel (the partial buffers hold n_chunks chunks per
-// row, so the loads stay in bounds; chunks past the row's live count are
-// discarded once n_sel arrives): one memory round trip for rows of at most
-// kMergeBatch chunks.  blockDim.x == D.
+// Folds a batch of kMergeBatch chunk partials (max m, sum l, value v; chunks
+// past the live count carry m = -inf) into a running log-sum-exp (M, L, A).
 constexpr int kMergeBatch = 16;
 
 template <int D, int G>
@@ -490,42 +330,29 @@ __device__ __forceinline__ void merge_fold(float& M, float& L, float& A, const f
   M = Mb;
 }
 
+// The merge of a row's n_live parts by the last part to finish, in the same
+// launch (the partials were published with device-scope stores before the
+// ticket): thread j < G * D owns output element j; every part's (m, l, acc) is
+// requested in batches of kMergeBatch device-scope loads and folded in part
+// order.
 template <int D, int G>
-__device__ __forceinline__ void merge_rows(const AttnArgs& a, int row, int g) {
+__device__ __forceinline__ void merge_row_in_launch(const AttnArgs& a, int row, int n_live) {
+  const int j = threadIdx.x;
+  if (j >= G * D) return;
   const int b = row / a.Hkv, h = row - b * a.Hkv;
-  const int dd = threadIdx.x;
+  const int g = j / D, dd = j - g * D;
   const size_t oi = (size_t(b) * a.Hq + size_t(h) * G + g) * D + dd;
   const float* racc = a.part_acc + size_t(row) * a.n_chunks * G * D + size_t(g) * D + dd;
   const float* rml = a.part_ml + size_t(row) * a.n_chunks * G * 2 + size_t(g) * 2;
-  const int pre = min(kMergeBatch, a.n_chunks);
-  float m[kMergeBatch], l[kMergeBatch], v[kMergeBatch];
-#pragma unroll
-  for (int i = 0; i < kMergeBatch; ++i) {  // issued before n_sel is known
-    const bool ok = i < pre;
-    m[i] = ok ? rml[size_t(i) * G * 2] : -INFINITY;
-    l[i] = ok ? rml[size_t(i) * G * 2 + 1] : 0.f;
-    v[i] = ok ? racc[size_t(i) * G * D] : 0.f;
-  }
-  int n = a.n_sel[row];
-  n = n < 0 ? 0 : (n > a.idx_stride ? a.idx_stride : n);
-  const int n_live = (n + a.chunk - 1) / a.chunk;
-#pragma unroll
-  for (int i = 0; i < kMergeBatch; ++i) {
-    if (i >= n_live) {
-      m[i] = -INFINITY;
-      l[i] = 0.f;
-      v[i] = 0.f;
-    }
-  }
   float M = -INFINITY, L = 0.f, A = 0.f;
-  merge_fold<D, G>(M, L, A, m, l, v);
-  for (int c0 = kMergeBatch; c0 < n_live; c0 += kMergeBatch) {
+  for (int c0 = 0; c0 < n_live; c0 += kMergeBatch) {
+    float m[kMergeBatch], l[kMergeBatch], v[kMergeBatch];
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
       const bool ok = c0 + i < n_live;
-      m[i] = ok ? rml[size_t(c0 + i) * G * 2] : -INFINITY;
-      l[i] = ok ? rml[size_t(c0 + i) * G * 2 + 1] : 0.f;
-      v[i] = ok ? racc[size_t(c0 + i) * G * D] : 0.f;
+      m[i] = ok ? consume(&rml[size_t(c0 + i) * G * 2]) : -INFINITY;
+      l[i] = ok ? consume(&rml[size_t(c0 + i) * G * 2 + 1]) : 0.f;
+      v[i] = ok ? consume(&racc[size_t(c0 + i) * G * D]) : 0.f;
     }
     merge_fold<D, G>(M, L, A, m, l, v);
   }
@@ -555,7 +382,8 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, int row, int g) {
 //           its rows' weighted V.
 // At the end the row groups of each wave are summed through lane swaps and
 // the NW waves through shared memory, and the portion's partial (M, L, acc)
-// is written with plain stores for the merge launch (merge_rows).
+// is written with device-scope stores for the merge by the row's last part
+// (merge_row_in_launch).
 template <int KVT, int D, int NW, int NL>
 struct PortionShape {
   static constexpr int EB = Elem<KVT>::bytes;
@@ -580,7 +408,7 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-template <int KVT, int D, int G, int NW, int NL>
+template <int KVT, int D, int G, int NW, int NL, bool PUBLISH = false>
 __device__ __forceinline__ void attend_portion(const AttnArgs& a, PortionSmem<KVT, D, G, NW, NL>& S,
                                                const int* sidx, int row, int b, int h, int part, int cnt) {
   using SH = PortionShape<KVT, D, NW, NL>;
@@ -720,10 +548,18 @@ __device__ __forceinline__ void attend_portion(const AttnArgs& a, PortionSmem<KV
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; w += 2) v += S.acc[w][g][dd] + S.acc[w + 1][g][dd];
-    pacc[j] = v;
-    if (dd == 0) {
-      pml[2 * g] = S.ml[g][0];
-      pml[2 * g + 1] = S.ml[g][1];
+    if (PUBLISH) {  // read by the row's last part in this launch
+      publish(&pacc[j], v);
+      if (dd == 0) {
+        publish(&pml[2 * g], S.ml[g][0]);
+        publish(&pml[2 * g + 1], S.ml[g][1]);
+      }
+    } else {
+      pacc[j] = v;
+      if (dd == 0) {
+        pml[2 * g] = S.ml[g][0];
+        pml[2 * g + 1] = S.ml[g][1];
+      }
     }
   }
 }

@@ -1,5 +1,5 @@
-// Sparse decode step in three launches (JSSA summary Figure 1 and section
-// E.1: subspace score scan, per-KV-head top-k selection, gather-free indexed
+// Sparse decode step in two launches (JSSA summary Figure 1 and section E.1:
+// subspace score scan, per-KV-head top-k selection, gather-free indexed
 // attention).
 //
 // Scan launch, items in order (workgroup i takes items i, i + grid, ...):
@@ -18,15 +18,16 @@
 //   each part finds the exact k-th key and tie cut among the row's candidates
 //   (the same selection in every part of the row), keeps its own positions of
 //   the ascending index list plus window (writing them to the output list),
-//   and attends over them.  If fewer than k tokens reached L (the sample
-//   misled), the row is redone exactly: its scores are recomputed, first for
-//   the exact top radix digit of the k-th key, then to rewrite the candidate
-//   slots from that digit (every part writes the same values).
-// Merge launch, one workgroup per row and query head: the log-sum-exp
-//   combine of the parts' partials.
+//   and attends over them; the row's last part to finish (a ticket) merges
+//   the parts' partials with a log-sum-exp combine.  If fewer than k tokens
+//   reached L (the sample misled), the row is redone exactly: its scores are
+//   recomputed, first for the exact top radix digit of the k-th key, then to
+//   rewrite the candidate slots from that digit (every part writes the same
+//   values).
 // Data passes between launches through plain stores and loads; the only wait
 // inside a launch is a score run's on its row's sample (an item of a lower
-// workgroup index), bounded in time.
+// workgroup index), bounded in time (the merge takes no wait: the last ticket
+// holder reads the others' device-scope partials).
 #include <math.h>
 
 #include <type_traits>
@@ -1099,7 +1100,15 @@ struct Pipe {
       if constexpr (KVT == 1) reinterpret_cast<uint4*>(sm.at.q)[threadIdx.x] = qp;
       else sm.at.q[threadIdx.x] = qp.x;
     }
-    attend_portion<KVT, D, G, kAttnNW, kPortionNL>(a.at, sm.at, sm.sidx, row, b, h, part, cnt);
+    attend_portion<KVT, D, G, kAttnNW, kPortionNL, true>(a.at, sm.at, sm.sidx, row, b, h, part, cnt);
+  }
+  // Every part of the row takes a ticket once its partial is stored (device
+  // scope); the last merges the row's n_live parts.  (A merge launch of its
+  // own after this one measured 1.2 us slower per 128K step.)
+  static __device__ __forceinline__ void finish_row(const PipeArgs& a, int row, int n_list) {
+    uint32_t* ticket = a.at.row_state + size_t(row) * kRowStateWords + RS_TICKET_ATTN;
+    if (last_arrival(ticket, uint32_t(a.at.n_chunks)))
+      merge_row_in_launch<D, G>(a.at, row, (n_list + a.at.chunk - 1) / a.at.chunk);
   }
   static __device__ __forceinline__ void select_attend(const PipeArgs& a, int row, int part, SelSmem& sm) {
     const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
@@ -1133,6 +1142,7 @@ struct Pipe {
     }
     __syncthreads();  // the part's list is complete; the selection's shared memory is free
     attend_part(a, sm, row, b, h, part, cnt, qp);
+    finish_row(a, row, md.kk + md.nW);
   }
   // The same parts over a caller's index lists (n_sel[row] entries of idx).
   static __device__ __forceinline__ void list_attend(const PipeArgs& a, int row, int part, SelSmem& sm) {
@@ -1146,9 +1156,7 @@ struct Pipe {
     for (int i = threadIdx.x; i < cnt; i += RT) sm.sidx[i] = src[i];
     __syncthreads();
     attend_part(a, sm, row, b, h, part, cnt, qp);
-  }
-  static __device__ __forceinline__ void merge(const PipeArgs& a, int row, int g) {
-    merge_rows<D, G>(a.at, row, g);
+    finish_row(a, row, n);
   }
 };
 
@@ -1229,12 +1237,6 @@ __global__ __launch_bounds__(kResolveThreads, 1) void list_attend_kernel(PipeArg
   Pp::list_attend(a, row, part, *reinterpret_cast<typename Pp::SelSmem*>(smem));
 }
 
-// Merge launch: one workgroup of D threads per (row, query head).
-template <int KPT, int R, int GE, int D, int G, int KVT>
-__global__ __launch_bounds__(D) void merge_kernel(PipeArgs a) {
-  using Pp = Pipe<KPT, R, GE, D, G, KVT>;
-  Pp::merge(a, blockIdx.x / G, blockIdx.x % G);
-}
 
 // ---- host side ------------------------------------------------------------------------------
 // Shapes with a fused build: (kv dtype, kp dtype, d, rank, G).  Others run the staged launches.
@@ -1330,9 +1332,6 @@ static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
     return hipErrorInvalidValue;
   if (a.attend_only) {  // caller-provided index lists: the attention and merge launches only
     hipLaunchKernelGGL((list_attend_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_attn), dim3(kResolveThreads), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((merge_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_rows * G), dim3(D), 0, s, a);
     return hipGetLastError();
   }
   // score runs sized so that the samples and one run per resident workgroup
@@ -1365,8 +1364,6 @@ static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((select_attend_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_attn), dim3(kResolveThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess) return e;
-  hipLaunchKernelGGL((merge_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_rows * G), dim3(D), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   return mark(3);
 }
 
