@@ -91,3 +91,52 @@ def test_decode_step_graph_replays_equal_eager(name):
         assert np.array_equal(got[4], ref[4]), rep
         other.run()  # eager decode work on other buffers and workspace between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["128k", "hybrid"])
+def test_layer_stack_graph_replays_equal_eager(name):
+    """Three layers in one graph: an indexer layer (``jssa_decode_step``), a
+    layer reusing its lists (``jssa_reuse_step``), another indexer layer;
+    each with its own query and caches, one workspace for all."""
+    w, kpt = CASES[name]
+    layers = [_Step(w, kpt, w.seed + 10 * l) for l in range(3)]
+    other = _Step(w, kpt, w.seed + 100)
+    ws = layers[0].ws
+
+    def stack():
+        for l, y in enumerate(layers):
+            if l % 2 == 0:
+                J.decode_step(y.desc, y.kn, y.vn, y.pos, y.q, y.P, y.kp, y.K, y.V, y.seq, y.out, y.lse, ws,
+                              idx_out=y.idx, n_sel_out=y.n_sel)
+            else:
+                src = layers[l - 1]
+                J.reuse_step(y.desc, y.kn, y.vn, y.pos, y.q, y.K, y.V, src.idx, src.n_sel, y.out, y.lse, ws)
+
+    stack()
+    other.run()
+    torch.cuda.synchronize()
+    ref = [y.result() for y in layers]
+    for y in layers:
+        y.out.fill_(float("nan"))
+        y.lse.fill_(float("nan"))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            stack()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        for l, y in enumerate(layers):
+            got = y.result()
+            assert np.array_equal(got[0], ref[l][0], equal_nan=True), (rep, l)
+            assert np.array_equal(got[1], ref[l][1], equal_nan=True), (rep, l)
+            if l % 2 == 0:
+                assert np.array_equal(got[3], ref[l][3]), (rep, l)
+            assert np.array_equal(got[4], ref[l][4]), (rep, l)
+        other.run()
+        torch.cuda.synchronize()

@@ -18,7 +18,7 @@ __all__ = [
     "OP_TOPK", "OP_ATTN", "OP_DECODE", "OP_DENSE", "OP_SCORE", "OP_VOTE", "lib", "abi_version", "check_desc",
     "workspace_bytes", "workspace", "workspace_status", "STATUS_WAIT_TIMEOUT", "STATUS_EXACT_REDO",
     "STATUS_SHARED_CLAIMS", "STATUS_GLOBAL_CUT", "append_kv", "append_projection", "score", "topk", "indexed_attn", "decode", "decode_profiled",
-    "decode_step", "decode_step_static", "vote_select", "gather_kv", "dense_decode",
+    "decode_step", "decode_step_static", "reuse_step", "vote_select", "gather_kv", "dense_decode",
 ]
 
 # FP8 E4M3 projected keys travel as their byte codes
@@ -144,8 +144,9 @@ def decode_profiled(desc: Desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out,
                     idx_out=None, n_sel_out=None, stream=None):
     """``jssa_decode_profiled``: :func:`decode` recording four stage events
     (``torch.cuda.Event(enable_timing=True)``) around its launches; the fused
-    build records them before the scan, after it, after the resolve and after
-    the attention (the header lists the staged shapes' points)."""
+    build records them as the scan launch's own start and end, then after the
+    select/attend launch and right after that (the header lists the staged
+    shapes' points)."""
     arr = _event_array(events, stream)
     kv = _TORCH_DTYPE[desc.kv_dtype]
     call("jssa_decode_profiled", desc.c(), _ptr(q, kv, "q"), _ptr(P, torch.float32, "P"),
