@@ -176,11 +176,12 @@ def test_full_mla_step():
 
 def test_full_ctx128k_step_k8192():
     """The budget swept up to k = 8192: about 13,000 tokens pass the sampled
-    threshold, more than the selection holds in shared memory, so every row's
-    exact cut runs over global memory."""
+    threshold (about 100 per score tile, read two slot groups at a time); the
+    selection holds up to 16,384 in shared memory, so nearly every row is cut
+    there (a row past that takes the global cut, covered on its own)."""
     w = scaled(WORKLOADS["ctx128k"], topk=8192)
     st = _run_full(w, [(0, 0), (1, 6), (3, 3)])
-    assert st[J.STATUS_GLOBAL_CUT] == 3 * w.batch * w.n_kv_heads, st  # the helper decodes three times
+    assert st[J.STATUS_GLOBAL_CUT] <= 3 * w.batch * w.n_kv_heads // 4, st  # the helper decodes three times
 
 
 def test_full_ctx128k_step_k512():

@@ -8,12 +8,16 @@
   workgroup count (below 1152), and every row is longer than 8 tiles; the
   step's new token sits in the last candidate tile, a shared one.  The
   library's claim counter proves the claims happened.
-* Cut in global memory.  With k = 8192 of 32768 candidates the sampled
-  threshold passes about 10,500 tokens, more than the 8192 the selection holds
-  in shared memory, so the exact k-th key and tie cut run over the candidate
-  slots in global memory (the library counts these rows), also after an exact
-  re-selection (the sampled threshold admitted fewer than k tokens) and with
-  crowded bins of equal keys.
+* Cut in global memory.  With k = 16384 of 65536 candidates the sampled
+  threshold passes about 21,000 tokens, more than the 16,384 the selection
+  holds in shared memory, so the exact k-th key and tie cut run over the
+  candidate slots in global memory (the library counts these rows), also after
+  an exact re-selection (the sampled threshold admitted fewer than k tokens)
+  and with crowded bins of equal keys.
+* Every token a candidate.  A budget so close to the context (k = 30000 of
+  32768) that the sample cannot bound it: the threshold stays open, each
+  score tile keeps all its tokens and the selection reads the row's slots as
+  one run (in shared memory up to 16,384, the rest in place).
 
 Checks: the oracle on the same stored projected keys (set rule within 1e-4 of
 the k-th score, attention within 2e-3 relative L2), and the stand-alone entry
@@ -32,7 +36,8 @@ from _gpu_helpers import check_sets_within_tolerance, desc_for, oracle_kp, rel_l
 pytestmark = pytest.mark.gpu
 
 SHARED = scaled(WORKLOADS["hybrid_ragged"], batch=48, t_max=20000, t_min=12000, topk=2048)
-GLOBAL = scaled(WORKLOADS["ctx128k"], batch=2, t_max=32768, topk=8192)
+GLOBAL = scaled(WORKLOADS["ctx128k"], batch=2, t_max=65536, topk=16384)
+OPEN = scaled(WORKLOADS["ctx128k"], batch=2, t_max=32768, topk=30000)
 _CACHE = {}
 
 
@@ -218,3 +223,22 @@ def test_global_cut_after_exact_reselection():
     check_sets_within_tolerance(i1, n1, s64, n_cand, inp["seq_lens"], w.topk, w.window)
     ref, _ = O.attention(inp["q"], inp["k_cache"], inp["v_cache"], i1, n1, w.scale)
     assert rel_l2(o1, ref) <= 2e-3
+
+
+def test_open_threshold_every_token_a_candidate():
+    w = OPEN
+    inp = _inputs(w)
+    desc = desc_for(w)
+    kp_h = oracle_kp(inp, desc)
+    d = _dev(inp)
+    kp = to_dev(kp_h)
+    o1, l1, i1, n1, ws = _decode(desc, w, d, kp)
+    assert _status(ws)[J.STATUS_GLOBAL_CUT] == w.batch * w.n_kv_heads  # 32768 candidates per row
+    o2, i2, n2, _ = _composed(desc, w, d, kp)
+    assert np.array_equal(n1, n2) and np.array_equal(i1, i2)
+    assert rel_l2(o1, o2) <= 1e-5
+    s64, n_cand = O.subspace_scores(inp["q"], inp["P"], kp_h, inp["seq_lens"], w.window)
+    check_sets_within_tolerance(i1, n1, s64, n_cand, inp["seq_lens"], w.topk, w.window)
+    ref, ref_lse = O.attention(inp["q"], inp["k_cache"], inp["v_cache"], i1, n1, w.scale)
+    assert rel_l2(o1, ref) <= 2e-3
+    assert np.abs(l1 - ref_lse).max() <= 1e-4 * max(1.0, np.abs(ref_lse).max())

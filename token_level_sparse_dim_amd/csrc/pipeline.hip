@@ -49,7 +49,8 @@ constexpr int kPipeTileTokens = JSSA_PIPE_TILE_TOKENS;  // tokens per tile (at l
 constexpr int kPipeSampleTokens = 1024;                 // tokens of the threshold sample
 constexpr int kPipePF = 3;             // score-scan steps in flight per workgroup
 constexpr int kPipeMaxItem = 8192;     // tokens per score item at most (whole tiles)
-constexpr int kPipeCandLds = 8192;     // candidates resolved in shared memory
+constexpr int kPipeCandLds = 16384;    // candidates resolved in shared memory
+constexpr int kPipeSampleMin = 8192;   // candidate tokens above which a row's threshold is sampled
 constexpr int kPipeMaxTiles = 2048;    // tiles per row
 constexpr int kPipeCutList = 256;      // candidates of the cut's bin ranked directly (one per thread)
 constexpr int kPipeGatherTiles = 8;    // tiles per wave per gather round
@@ -481,6 +482,16 @@ struct Pipe {
   }
 
   // ---- SAMPLE -----------------------------------------------------------------------------
+  // The rank m of the row's threshold among NSAMP evenly strided tokens (the
+  // threshold is their m-th largest key: k's expected share of the sample
+  // plus four standard deviations and a margin), or 0 when every token is a
+  // candidate (a short row, or a budget the sample cannot usefully bound).
+  static __device__ __forceinline__ int sample_rank(const RowMode& md) {
+    if (md.n_cand <= kPipeSampleMin) return 0;
+    const double E = double(NSAMP) * md.kk / md.n_cand;  // expected sample tokens above the k-th score
+    const int m = int(ceil(E + 4.0 * sqrt(E) + 8.0));
+    return m < NSAMP ? m : 0;
+  }
   static __device__ __forceinline__ void sample(const PipeArgs& a, int row, SampleSmem& sm) {
     const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
     const RowMode md = row_mode(a, b);
@@ -490,12 +501,11 @@ struct Pipe {
       return;
     }
     uint32_t L = 0;  // every token is a candidate unless a sample allows a higher threshold
-    if (md.n_cand > kPipeCandLds) {
+    const int m = sample_rank(md);
+    if (m > 0) {
       const int n_samp = NSAMP;  // n_cand > NSAMP here
       const int stride = md.n_cand / n_samp;
-      const double E = double(n_samp) * md.kk / md.n_cand;  // expected sample tokens above the k-th score
-      const int m = int(ceil(E + 4.0 * sqrt(E) + 8.0));
-      if (m < n_samp) {
+      {
         // the sampled projected keys are requested before the query projection
         const char* kr = kp_row(a, row);
         constexpr int HALF = NIT_S / 2;  // steps per batch of loads
@@ -688,18 +698,38 @@ struct Pipe {
   // ---- SELECTION (second launch) ----------------------------------------------------------
   // Gathers the row's candidates into shared memory by ordinal (token order).
   // Each wave takes kPipeGatherTiles tiles a round and issues every load of the
-  // round at once: the tiles' counts (one per lane) and their first 64 slots
-  // (one 8-byte load per lane and tile: a tile's candidates are contiguous
-  // from the start of its slot, about 40 at 128K context and k = 2048; slots
-  // past the count are read but not used, and the candidate buffer has
-  // kCandPad slots past its last row, so no load needs a bound; a tile with
-  // more than 64 takes a second round trip).  A shuffle scan of the counts and
-  // the wave totals give the tiles' first ordinals, kept in sm.tab.  Stores of unused lanes go to a
-  // dummy slot.  Returns the number of candidates C; *kmin / *kmax: their
-  // smallest / largest key (C > 0).  FRESH: the slots and counts were
-  // rewritten by this workgroup after an earlier gather, so they are read
-  // with device-scope loads.
-  template <bool FRESH>
+  // round at once: the tiles' counts (one per lane) and their first 64 SL slots
+  // (SL 8-byte loads per lane and tile: a tile's candidates are contiguous
+  // from the start of its slot; about 40 at 128K context and k = 2048, about
+  // 100 at k = 8192 or at 32K context, where SL = 2; slots past the count are
+  // read but not used, and the candidate buffer has kCandPad slots past its
+  // last row, so no load needs a bound; a tile with more takes further round
+  // trips).  A shuffle scan of the counts and the wave totals give the tiles'
+  // first ordinals, kept in sm.tab.  Stores of unused lanes go to a dummy
+  // slot.  Returns the number of candidates C; *kmin / *kmax: their smallest /
+  // largest key (C > 0).  FRESH: the slots and counts were rewritten by this
+  // workgroup after an earlier gather, so they are read with device-scope
+  // loads.
+  static_assert(kCandPad >= 128, "the gather reads up to 128 slots from a tile's start");
+  static __device__ __forceinline__ void minmax_block(ResolveSmem& sm, uint32_t lo, uint32_t hi, uint32_t* kmin,
+                                                      uint32_t* kmax) {
+    const int wave = threadIdx.x >> 6;
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    sm.wmin[wave] = lo;
+    sm.wmax[wave] = hi;
+    __syncthreads();  // also: every gathered candidate is in shared memory
+    lo = 0xffffffffu;
+    hi = 0u;
+#pragma unroll
+    for (int w = 0; w < RW; ++w) {
+      lo = min(lo, sm.wmin[w]);
+      hi = max(hi, sm.wmax[w]);
+    }
+    *kmin = lo;
+    *kmax = hi;
+  }
+  template <bool FRESH, int SL>
   static __device__ __forceinline__ uint32_t gather(const PipeArgs& a, int row, int n_tiles_row, ResolveSmem& sm,
                                                     uint32_t* kmin, uint32_t* kmax) {
     constexpr int UB = kPipeGatherTiles;
@@ -721,12 +751,15 @@ struct Pipe {
       const bool own = lane < uint32_t(UB) && t0 + int(lane) < n_tiles_row;
       uint32_t my_cnt = FRESH ? consume(cnt_row + tl) : cnt_row[tl];
       my_cnt = own ? my_cnt : 0u;
-      uint64_t v0[UB];
+      uint64_t v0[UB][SL];
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         const int t = min(t0 + u, n_tiles_row - 1);  // past the row's tiles: count 0
-        const uint64_t* src = slots + size_t(t) * TS + lane;
-        v0[u] = FRESH ? consume(src) : *src;
+#pragma unroll
+        for (int q = 0; q < SL; ++q) {
+          const uint64_t* src = slots + size_t(t) * TS + q * 64 + lane;
+          v0[u][q] = FRESH ? consume(src) : *src;
+        }
       }
       const uint32_t incl = wave_scan_incl(my_cnt);  // over the lanes that own tiles
       sm.wsum[parity][wave] = uint32_t(__builtin_amdgcn_readlane(int(incl), UB - 1));
@@ -744,29 +777,45 @@ struct Pipe {
       for (int u = 0; u < UB; ++u) {
         const uint32_t cnt_u = uint32_t(__builtin_amdgcn_readlane(int(my_cnt), u));
         const uint32_t base_u = wbase + uint32_t(__builtin_amdgcn_readlane(int(excl), u));
-        put(lane < cnt_u, base_u + lane, v0[u]);
-        if (cnt_u > 64u) {  // a crowded tile: the rest of its slot
+#pragma unroll
+        for (int q = 0; q < SL; ++q) put(q * 64 + lane < cnt_u, base_u + q * 64 + lane, v0[u][q]);
+        if (cnt_u > 64u * SL) {  // a crowded tile: the rest of its slot
           const uint64_t* src = slots + size_t(t0 + u) * TS;
-          for (uint32_t i = lane + 64u; i < cnt_u; i += 64u) put(true, base_u + i, FRESH ? consume(src + i) : src[i]);
+          for (uint32_t i = lane + 64u * SL; i < cnt_u; i += 64u) put(true, base_u + i, FRESH ? consume(src + i) : src[i]);
         }
       }
       run += rtot;
     }
-    lo = wave_min_u32(lo);
-    hi = wave_max_u32(hi);
-    sm.wmin[wave] = lo;
-    sm.wmax[wave] = hi;
-    __syncthreads();  // also: every gathered candidate is in shared memory
-    lo = 0xffffffffu;
-    hi = 0u;
-#pragma unroll
-    for (int w = 0; w < RW; ++w) {
-      lo = min(lo, sm.wmin[w]);
-      hi = max(hi, sm.wmax[w]);
-    }
-    *kmin = lo;
-    *kmax = hi;
+    minmax_block(sm, lo, hi, kmin, kmax);
     return run;
+  }
+  // A row whose every token is a candidate (no sampled threshold): each tile
+  // holds all of its tokens, so the row's slots are one contiguous run of
+  // n_cand candidates in token order, copied with coalesced loads.  Only the
+  // first kPipeCandLds go to shared memory (more are cut in place, through
+  // sm.tab, which holds the tiles' first ordinals here too).
+  static __device__ __forceinline__ uint32_t gather_all(const PipeArgs& a, int row, int n_cand, int n_tiles_row,
+                                                        ResolveSmem& sm, uint32_t* kmin, uint32_t* kmax) {
+    constexpr int B = 8;
+    const uint64_t* slots = a.cand + size_t(row) * a.at.t_max;
+    for (int t = threadIdx.x; t < n_tiles_row; t += RT) sm.tab[t] = uint32_t(t) * TS;
+    uint32_t lo = 0xffffffffu, hi = 0u;
+    for (int o0 = 0; o0 < n_cand; o0 += B * RT) {
+      uint64_t v[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) v[u] = slots[min(o0 + u * RT + int(threadIdx.x), n_cand - 1)];
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int o = o0 + u * RT + int(threadIdx.x);
+        const bool ok = o < n_cand;
+        const uint32_t key = uint32_t(v[u]);
+        lo = min(lo, ok ? key : 0xffffffffu);
+        hi = max(hi, ok ? key : 0u);
+        if (ok && o < kPipeCandLds) sm.cand[o] = v[u];
+      }
+    }
+    minmax_block(sm, lo, hi, kmin, kmax);
+    return uint32_t(n_cand);
   }
 
   // The sampled threshold let fewer than kk tokens through: rebuild the row's
@@ -836,15 +885,25 @@ struct Pipe {
       sm.wcnt[buf][RW * i + wave] = uint32_t(__popcll(__ballot(flag(i))));  // every lane: the same word
     }
     __syncthreads();
-    const int nw = RW * nper;  // <= kPipeCandLds / 64: two words per lane at most
-    const uint32_t c0 = int(2 * lane) < nw ? sm.wcnt[buf][2 * lane] : 0u;
-    const uint32_t c1 = int(2 * lane + 1) < nw ? sm.wcnt[buf][2 * lane + 1] : 0u;
-    const uint32_t incl = wave_scan_incl(c0 + c1);
-    const uint32_t ex = (wave & 1) ? incl - c1 : incl - c0 - c1;  // this wave's words have its parity
+    // lane l holds words WPL l .. WPL l + WPL - 1; word RW i + wave sits at
+    // place wave mod WPL of its lane for every round i
+    constexpr int WPL = (RW * MAXPER + 63) / 64;
+    static_assert(RW % WPL == 0 && WPL * 64 >= RW * MAXPER && RW * MAXPER <= kPipeCandLds / 64, "flag words per lane");
+    const int nw = RW * nper;  // <= RW * MAXPER
+    uint32_t c[WPL], sum = 0u;
+#pragma unroll
+    for (int k = 0; k < WPL; ++k) {
+      c[k] = int(WPL * lane + k) < nw ? sm.wcnt[buf][WPL * lane + k] : 0u;
+      sum += c[k];
+    }
+    uint32_t ex = wave_scan_incl(sum) - sum;
+    const int kw = wave % WPL;
+#pragma unroll
+    for (int k = 0; k < WPL; ++k) ex += k < kw ? c[k] : 0u;
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
       if (i >= nper) break;
-      off[i] = uint32_t(__builtin_amdgcn_readlane(int(ex), (RW * i + wave) >> 1));
+      off[i] = uint32_t(__builtin_amdgcn_readlane(int(ex), (RW * i + wave) / WPL));
     }
   }
 
@@ -894,6 +953,120 @@ struct Pipe {
     *istar_out = sm.out[1];
   }
 
+  // The exact cut among C <= MAXPER * RT candidates held in shared memory,
+  // then the emission of the selected ones.  Ordinal RT i + threadIdx.x in
+  // round i; its key stays in kv[i].  Candidates are in token order, so
+  // ranking equal keys by ordinal ranks them by token index.  (Instantiated
+  // for half and all of kPipeCandLds: the common budgets keep the smaller
+  // register and code footprint.)
+  template <int MAXPER, typename Emit>
+  static __device__ __forceinline__ void cut_in_lds(ResolveSmem& sm, uint32_t C, uint32_t need, uint32_t kmin,
+                                                    uint32_t kmax, Emit emit) {
+    const uint32_t tid = threadIdx.x, lane = tid & 63;
+    const int nper = int((C + RT - 1) / RT);
+    uint32_t kv[MAXPER];
+    uint32_t kstar, istar;
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+      const uint32_t o = uint32_t(i) * RT + tid;
+      kv[i] = i < nper ? uint32_t(sm.cand[min(o, uint32_t(kPipeCandLds))]) : 0u;
+    }
+    auto live = [&](int i) { return uint32_t(i) * RT + tid < C; };
+    // One digit: the top 11 bits of d = key - kmin (the candidates sit in a
+    // narrow band at the top, so digits of the key itself would pile them
+    // into a few bins).  Everything above the k-th key's bin is taken; the
+    // bin's own candidates are ranked directly, by key and then ordinal.
+    const int nbits = kmax > kmin ? 32 - __clz(kmax - kmin) : 1;
+    const int sh = nbits > 11 ? nbits - 11 : 0;
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+      if (i >= nper) break;
+      atomicAdd(&sm.hist[live(i) ? (kv[i] - kmin) >> sh : 2048u], 1u);  // dead lanes: the dummy bin
+    }
+    __syncthreads();
+    if (tid < 64) top_bin_wave(sm.hist, need, sm.out);
+    __syncthreads();
+    const uint32_t bin = sm.out[0];
+    const uint32_t need_bin = need - sm.out[1];  // 1 <= need_bin <= the bin's count
+    // the bin's candidates, listed a wave at a time
+    const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+      if (i >= nper) break;
+      const bool inb = live(i) && ((kv[i] - kmin) >> sh) == bin;
+      const uint64_t mk = __ballot(inb);
+      if (mk) {
+        uint32_t b0 = 0;
+        if (lane == 0) b0 = atomicAdd(&sm.n_bin, uint32_t(__popcll(mk)));
+        b0 = uint32_t(__builtin_amdgcn_readfirstlane(int(b0))) + uint32_t(__popcll(mk & below));
+        if (inb && b0 < uint32_t(kPipeCutList)) {
+          sm.bin_key[b0] = kv[i];
+          sm.bin_ord[b0] = uint32_t(i) * RT + tid;
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t m = uint32_t(__builtin_amdgcn_readfirstlane(int(sm.n_bin)));
+    if (m <= 64u) {
+      // one wave: lane j holds the bin's j-th candidate and counts those
+      // ranked above it, four at a time (shared-memory broadcasts)
+      if (tid < 64) {
+        const uint32_t k = lane < m ? sm.bin_key[lane] : 0u;
+        const uint32_t o = lane < m ? sm.bin_ord[lane] : 0xffffffffu;
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < m; j += 4) {
+          const uint4 k4 = *reinterpret_cast<const uint4*>(&sm.bin_key[j]);
+          const uint4 o4 = *reinterpret_cast<const uint4*>(&sm.bin_ord[j]);
+          auto above = [&](uint32_t q, uint32_t kj, uint32_t oj) {
+            return (j + q < m && (kj > k || (kj == k && oj < o))) ? 1u : 0u;
+          };
+          rank += above(0, k4.x, o4.x) + above(1, k4.y, o4.y) + above(2, k4.z, o4.z) + above(3, k4.w, o4.w);
+        }
+        if (lane < m && rank == need_bin - 1u) {
+          sm.out[0] = k;
+          sm.out[1] = o;
+        }
+      }
+      __syncthreads();
+      kstar = sm.out[0];
+      istar = sm.out[1];
+    } else if (m <= uint32_t(kPipeCutList)) {
+      if (tid < m) {
+        const uint32_t k = sm.bin_key[tid], o = sm.bin_ord[tid];
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < m; ++j) {
+          const uint32_t kj = sm.bin_key[j], oj = sm.bin_ord[j];
+          rank += (kj > k || (kj == k && oj < o)) ? 1u : 0u;
+        }
+        if (rank == need_bin - 1u) {
+          sm.out[0] = k;
+          sm.out[1] = o;
+        }
+      }
+      __syncthreads();
+      kstar = sm.out[0];
+      istar = sm.out[1];
+    } else {
+      cut_by_passes<MAXPER>(sm, kv, nper, C, kmin, kmax, need, &kstar, &istar);
+    }
+    // emission in token order: a ballot per 64 ordinals places each taken
+    // candidate, so each wave store covers one run of consecutive positions
+    auto take = [&](int i) {
+      const uint32_t o = uint32_t(i) * RT + tid;
+      return o < C && (kv[i] > kstar || (kv[i] == kstar && o <= istar));
+    };
+    uint32_t off[MAXPER];
+    word_offsets<MAXPER>(sm, nper, 1, take, off);
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+      if (i >= nper) break;
+      const bool t = take(i);
+      const uint64_t mk = __ballot(t);
+      const uint32_t pos = off[i] + uint32_t(__popcll(mk & below));
+      if (t && pos < need) emit(pos, uint32_t(sm.cand[uint32_t(i) * RT + tid] >> 32));
+    }
+  }
+
   // The row's exact selection among its candidates: the k-th key K* and the
   // tie cut I*, then emit(pos, token) for each selected candidate, pos its
   // place in the ascending list (0 <= pos < kk).  Several workgroups may
@@ -917,123 +1090,26 @@ struct Pipe {
     for (int i = threadIdx.x; i < 2048; i += RT) sm.hist[i] = 0u;
     if (threadIdx.x == 0) sm.n_bin = 0u;
     uint32_t kmin, kmax;
-    uint32_t C = gather<false>(a, row, n_tiles_row, sm, &kmin, &kmax);
-    const bool fresh = C < uint32_t(md.kk);  // the slots are rewritten below (read back device-scope)
+    // the sample's rank sets the expected candidates per tile: m / NSAMP of its tokens
+    const int m = sample_rank(md);
+    const bool wide = m * TS > 48 * NSAMP;
+    uint32_t C = m == 0 ? gather_all(a, row, md.n_cand, n_tiles_row, sm, &kmin, &kmax)
+                 : wide ? gather<false, 2>(a, row, n_tiles_row, sm, &kmin, &kmax)
+                        : gather<false, 1>(a, row, n_tiles_row, sm, &kmin, &kmax);
+    const bool fresh = C < uint32_t(md.kk);  // (m > 0) the slots are rewritten below (read back device-scope)
     if (fresh) {
       exact_candidates(a, row, md, smem, leader);
       for (int i = threadIdx.x; i < 2048; i += RT) sm.hist[i] = 0u;
       if (threadIdx.x == 0) sm.n_bin = 0u;
-      C = gather<true>(a, row, n_tiles_row, sm, &kmin, &kmax);
+      C = wide ? gather<true, 2>(a, row, n_tiles_row, sm, &kmin, &kmax)
+               : gather<true, 1>(a, row, n_tiles_row, sm, &kmin, &kmax);
     }
     const uint32_t need = uint32_t(md.kk);  // 1 <= need <= C
     uint32_t kstar, istar;
-    if (C <= uint32_t(kPipeCandLds)) {
-      // Ordinal RT i + threadIdx.x in round i; its key stays in kv[i].
-      // Candidates are in token order, so ranking equal keys by ordinal ranks
-      // them by token index.
-      constexpr int MAXPER = kPipeCandLds / RT;
-      const uint32_t tid = threadIdx.x, lane = tid & 63;
-      const int nper = int((C + RT - 1) / RT);
-      uint32_t kv[MAXPER];
-#pragma unroll
-      for (int i = 0; i < MAXPER; ++i) {
-        const uint32_t o = uint32_t(i) * RT + tid;
-        kv[i] = i < nper ? uint32_t(sm.cand[min(o, uint32_t(kPipeCandLds))]) : 0u;
-      }
-      auto live = [&](int i) { return uint32_t(i) * RT + tid < C; };
-      // One digit: the top 11 bits of d = key - kmin (the candidates sit in a
-      // narrow band at the top, so digits of the key itself would pile them
-      // into a few bins).  Everything above the k-th key's bin is taken; the
-      // bin's own candidates are ranked directly, by key and then ordinal.
-      const int nbits = kmax > kmin ? 32 - __clz(kmax - kmin) : 1;
-      const int sh = nbits > 11 ? nbits - 11 : 0;
-#pragma unroll
-      for (int i = 0; i < MAXPER; ++i) {
-        if (i >= nper) break;
-        atomicAdd(&sm.hist[live(i) ? (kv[i] - kmin) >> sh : 2048u], 1u);  // dead lanes: the dummy bin
-      }
-      __syncthreads();
-      if (tid < 64) top_bin_wave(sm.hist, need, sm.out);
-      __syncthreads();
-      const uint32_t bin = sm.out[0];
-      const uint32_t need_bin = need - sm.out[1];  // 1 <= need_bin <= the bin's count
-      // the bin's candidates, listed a wave at a time
-      const uint64_t below = (1ull << lane) - 1ull;
-#pragma unroll
-      for (int i = 0; i < MAXPER; ++i) {
-        if (i >= nper) break;
-        const bool inb = live(i) && ((kv[i] - kmin) >> sh) == bin;
-        const uint64_t mk = __ballot(inb);
-        if (mk) {
-          uint32_t b0 = 0;
-          if (lane == 0) b0 = atomicAdd(&sm.n_bin, uint32_t(__popcll(mk)));
-          b0 = uint32_t(__builtin_amdgcn_readfirstlane(int(b0))) + uint32_t(__popcll(mk & below));
-          if (inb && b0 < uint32_t(kPipeCutList)) {
-            sm.bin_key[b0] = kv[i];
-            sm.bin_ord[b0] = uint32_t(i) * RT + tid;
-          }
-        }
-      }
-      __syncthreads();
-      const uint32_t m = uint32_t(__builtin_amdgcn_readfirstlane(int(sm.n_bin)));
-      if (m <= 64u) {
-        // one wave: lane j holds the bin's j-th candidate and counts those
-        // ranked above it, four at a time (shared-memory broadcasts)
-        if (tid < 64) {
-          const uint32_t k = lane < m ? sm.bin_key[lane] : 0u;
-          const uint32_t o = lane < m ? sm.bin_ord[lane] : 0xffffffffu;
-          uint32_t rank = 0;
-          for (uint32_t j = 0; j < m; j += 4) {
-            const uint4 k4 = *reinterpret_cast<const uint4*>(&sm.bin_key[j]);
-            const uint4 o4 = *reinterpret_cast<const uint4*>(&sm.bin_ord[j]);
-            auto above = [&](uint32_t q, uint32_t kj, uint32_t oj) {
-              return (j + q < m && (kj > k || (kj == k && oj < o))) ? 1u : 0u;
-            };
-            rank += above(0, k4.x, o4.x) + above(1, k4.y, o4.y) + above(2, k4.z, o4.z) + above(3, k4.w, o4.w);
-          }
-          if (lane < m && rank == need_bin - 1u) {
-            sm.out[0] = k;
-            sm.out[1] = o;
-          }
-        }
-        __syncthreads();
-        kstar = sm.out[0];
-        istar = sm.out[1];
-      } else if (m <= uint32_t(kPipeCutList)) {
-        if (tid < m) {
-          const uint32_t k = sm.bin_key[tid], o = sm.bin_ord[tid];
-          uint32_t rank = 0;
-          for (uint32_t j = 0; j < m; ++j) {
-            const uint32_t kj = sm.bin_key[j], oj = sm.bin_ord[j];
-            rank += (kj > k || (kj == k && oj < o)) ? 1u : 0u;
-          }
-          if (rank == need_bin - 1u) {
-            sm.out[0] = k;
-            sm.out[1] = o;
-          }
-        }
-        __syncthreads();
-        kstar = sm.out[0];
-        istar = sm.out[1];
-      } else {
-        cut_by_passes<MAXPER>(sm, kv, nper, C, kmin, kmax, need, &kstar, &istar);
-      }
-      // emission in token order: a ballot per 64 ordinals places each taken
-      // candidate, so each wave store covers one run of consecutive positions
-      auto take = [&](int i) {
-        const uint32_t o = uint32_t(i) * RT + tid;
-        return o < C && (kv[i] > kstar || (kv[i] == kstar && o <= istar));
-      };
-      uint32_t off[MAXPER];
-      word_offsets<MAXPER>(sm, nper, 1, take, off);
-#pragma unroll
-      for (int i = 0; i < MAXPER; ++i) {
-        if (i >= nper) break;
-        const bool t = take(i);
-        const uint64_t mk = __ballot(t);
-        const uint32_t pos = off[i] + uint32_t(__popcll(mk & below));
-        if (t && pos < need) emit(pos, uint32_t(sm.cand[uint32_t(i) * RT + tid] >> 32));
-      }
+    if (C <= uint32_t(kPipeCandLds / 2)) {
+      cut_in_lds<kPipeCandLds / 2 / RT>(sm, C, need, kmin, kmax, emit);
+    } else if (C <= uint32_t(kPipeCandLds)) {
+      cut_in_lds<kPipeCandLds / RT>(sm, C, need, kmin, kmax, emit);
     } else {
       // more candidates than shared memory holds: every pass reads them in place
       if (leader && threadIdx.x == 0)
@@ -1079,6 +1155,7 @@ struct Pipe {
     };
     int sidx[kPipeMaxPortion];  // the part's token indices
   };
+  static_assert(sizeof(SelSmem) <= 160 * 1024, "select/attend shared memory exceeds a compute unit's 160 KiB");
   // The group's queries, requested before the selection and staged in shared
   // memory after it: bf16 as stored, in 16-byte pieces (thread i holds piece
   // i of the G rows); fp32 one element per thread, scaled to base-2 logits.
