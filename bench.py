@@ -316,7 +316,7 @@ def main():
         "stage_events_us": {n: round(float(v), 2) for n, v in zip(names, stage_us)},
         "device_status": {"wait_timeouts": dstat[J.STATUS_WAIT_TIMEOUT],
                           "exact_reselections": dstat[J.STATUS_EXACT_REDO],
-                          "shared_tile_claims": dstat[J.STATUS_SHARED_CLAIMS],
+                          "range_split_scans": dstat[J.STATUS_RANGE_SPLIT],
                           "global_cut_rows": dstat[J.STATUS_GLOBAL_CUT],
                           "steps": args.warmup + args.steps},
         "roofline": {"kernel": "mla_score_kernel (MFMA projected-key scan + histogram)" if w.mla
@@ -655,7 +655,7 @@ def sweep(J, case, stream, args, reduce, kpt):
                      "scan_kernel_us": round(float(st[0]), 2),
                      "scan_GBps": round(kp_b / (float(st[0]) * 1e-6) / 1e9, 1),
                      "select_attend_us": round(float(st[1]), 2),
-                     "device_status": dict(zip(["wait_timeouts", "exact_reselections", "shared_tile_claims",
+                     "device_status": dict(zip(["wait_timeouts", "exact_reselections", "range_split_scans",
                                                 "global_cut_rows"], dstat)), "steps": steps}
         log(f"sweep {name}: {us:.2f} us/step, {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}%), scan "
             f"{st[0]:.2f} us, select/attend {st[1]:.2f} us")

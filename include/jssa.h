@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define JSSA_ABI_VERSION 9
+#define JSSA_ABI_VERSION 10
 
 typedef enum {
   JSSA_OK = 0,
@@ -151,9 +151,10 @@ int32_t jssa_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *   status_out[JSSA_STATUS_EXACT_REDO]    rows re-selected exactly because the
  *       sampled threshold of the fused decode admitted fewer than k tokens
  *       (results stay exact; a count only).
- *   status_out[JSSA_STATUS_SHARED_CLAIMS] claims of shared score tiles made by
- *       the fused decode's scan when a row's static runs do not cover it (a
- *       count only).
+ *   status_out[JSSA_STATUS_RANGE_SPLIT]   fused decode scans that had fewer
+ *       score workgroups than rows to score, so that the rows' tiles were
+ *       split into contiguous ranges across rows instead of per row (a count
+ *       only).
  *   status_out[JSSA_STATUS_GLOBAL_CUT]    rows of the fused decode whose
  *       candidates exceeded shared memory, so that the exact cut ran over
  *       global memory (a count only).
@@ -162,7 +163,7 @@ int32_t jssa_workspace_init(void* ws, size_t ws_bytes, void* stream);
 #define JSSA_STATUS_WORDS 4
 #define JSSA_STATUS_WAIT_TIMEOUT 0
 #define JSSA_STATUS_EXACT_REDO 1
-#define JSSA_STATUS_SHARED_CLAIMS 2
+#define JSSA_STATUS_RANGE_SPLIT 2
 #define JSSA_STATUS_GLOBAL_CUT 3
 int32_t jssa_workspace_status(void* ws, size_t ws_bytes, uint32_t* status_out, int32_t clear,
                               void* stream);

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert J.abi_version() == 9
+    assert J.abi_version() == 10
     lib = J.lib()
     assert lib.jssa_status_str(0) == b"JSSA_OK"
     for code, name in _lib.STATUS.items():
@@ -168,7 +168,7 @@ def test_status_words_match_header():
     src = open(HEADER).read()
     for name, val in (("JSSA_STATUS_WORDS", 4), ("JSSA_STATUS_WAIT_TIMEOUT", J.STATUS_WAIT_TIMEOUT),
                       ("JSSA_STATUS_EXACT_REDO", J.STATUS_EXACT_REDO),
-                      ("JSSA_STATUS_SHARED_CLAIMS", J.STATUS_SHARED_CLAIMS),
+                      ("JSSA_STATUS_RANGE_SPLIT", J.STATUS_RANGE_SPLIT),
                       ("JSSA_STATUS_GLOBAL_CUT", J.STATUS_GLOBAL_CUT)):
         assert re.search(rf"#define {name} {val}\b", src), name
 

@@ -1,13 +1,13 @@
 """GPU parity on the selection paths that only large launches reach.
 
-* Shared score tiles.  The decode's scan gives each (sequence, KV head) row a
-  few static runs of at most 8 tiles; when a row has more tiles than its runs
-  cover (many rows, long rows: the ragged hybrid batch at full size), the
-  row's runs claim the remaining tiles one at a time.  The case here has 384
-  rows, so each row gets one static run whatever the device's resident
-  workgroup count (below 1152), and every row is longer than 8 tiles; the
-  step's new token sits in the last candidate tile, a shared one.  The
-  library's claim counter proves the claims happened.
+* More rows than scan workgroups.  The decode's scan normally gives every
+  (sequence, KV head) row its own score workgroups, in proportion to the
+  row's length.  With more rows than the device holds resident scan
+  workgroups (1024 rows here), the rows' samples run in a launch of their
+  own and the score work is split into equal contiguous ranges of the rows'
+  tiles laid end to end, so ranges start and end inside rows.  The step's
+  new token sits in the last candidate tile of every sequence.  The library's
+  range-split counter proves the path ran.
 * Cut in global memory.  With k = 16384 of 65536 candidates the sampled
   threshold passes about 21,000 tokens, more than the 16,384 the selection
   holds in shared memory, so the exact k-th key and tie cut run over the
@@ -35,7 +35,7 @@ from _gpu_helpers import check_sets_within_tolerance, desc_for, oracle_kp, rel_l
 
 pytestmark = pytest.mark.gpu
 
-SHARED = scaled(WORKLOADS["hybrid_ragged"], batch=48, t_max=20000, t_min=12000, topk=2048)
+MANY = scaled(WORKLOADS["hybrid_ragged"], batch=128, t_max=12000, t_min=9000, topk=1024)
 GLOBAL = scaled(WORKLOADS["ctx128k"], batch=2, t_max=65536, topk=16384)
 OPEN = scaled(WORKLOADS["ctx128k"], batch=2, t_max=32768, topk=30000)
 _CACHE = {}
@@ -80,17 +80,17 @@ def _dev(inp):
     return {k: to_dev(inp[k]) for k in ("q", "P", "k_cache", "v_cache", "seq_lens")}
 
 
-def test_shared_tiles_step_with_new_token_in_a_shared_tile():
-    w = SHARED
+def test_more_rows_than_scan_workgroups_with_new_tokens():
+    w = MANY
     inp = _inputs(w)
     desc = desc_for(w)
     B, Hkv, T, r, G = w.batch, w.n_kv_heads, w.t_max, w.rank, w.group
     L = inp["seq_lens"]
-    assert (L - w.window > 8 * 1024).all()  # every row is longer than its one static run
+    assert (L - w.window > 8192).all()  # every row takes a sampled threshold
     d = _dev(inp)
     kp = torch.empty((B, Hkv, T, r), dtype=torch.bfloat16, device="cuda")
     J.append_projection(desc, T, torch.zeros(B, dtype=torch.int32, device="cuda"), d["P"], d["k_cache"], kp)
-    samples = [(0, 0), (7, 3), (23, 5), (47, 7)]
+    samples = [(0, 0), (37, 3), (90, 5), (127, 7)]
     for b, h in samples:  # the oracle scores its own projection of the sampled rows
         n = int(L[b])
         kp[b, h, :n] = to_dev(O.project_keys(inp["k_cache"][b:b + 1, :n, h:h + 1], inp["P"][h:h + 1],
@@ -109,7 +109,7 @@ def test_shared_tiles_step_with_new_token_in_a_shared_tile():
                   d["seq_lens"], out, lse, ws, idx_out=idx, n_sel_out=n_sel)
     torch.cuda.synchronize()
     st = _status(ws)
-    assert st[J.STATUS_SHARED_CLAIMS] > 0, st  # the rows' shared tiles were claimed
+    assert st[J.STATUS_RANGE_SPLIT] == 1, st  # the score work was split into ranges across rows
     gi, gn, go, gl = to_host(idx), to_host(n_sel), to_host(out), to_host(lse)
     assert np.isfinite(go).all() and np.isfinite(gl).all()
     # every row: the stand-alone entry points on the updated caches select the same lists

@@ -17,7 +17,7 @@ __all__ = [
     "Desc", "JssaError", "F32", "BF16", "FP8_E4M3", "REDUCE_MAX", "REDUCE_MEAN", "LAYOUT_GQA", "LAYOUT_MLA",
     "OP_TOPK", "OP_ATTN", "OP_DECODE", "OP_DENSE", "OP_SCORE", "OP_VOTE", "lib", "abi_version", "check_desc",
     "workspace_bytes", "workspace", "workspace_status", "STATUS_WAIT_TIMEOUT", "STATUS_EXACT_REDO",
-    "STATUS_SHARED_CLAIMS", "STATUS_GLOBAL_CUT", "append_kv", "append_projection", "score", "topk", "indexed_attn", "decode", "decode_profiled",
+    "STATUS_RANGE_SPLIT", "STATUS_GLOBAL_CUT", "append_kv", "append_projection", "score", "topk", "indexed_attn", "decode", "decode_profiled",
     "decode_step", "decode_step_static", "reuse_step", "vote_select", "gather_kv", "dense_decode",
 ]
 
@@ -69,7 +69,7 @@ def workspace(desc: Desc, op: int, device="cuda", stream=None) -> torch.Tensor:
     return ws
 
 
-STATUS_WAIT_TIMEOUT, STATUS_EXACT_REDO, STATUS_SHARED_CLAIMS, STATUS_GLOBAL_CUT = 0, 1, 2, 3
+STATUS_WAIT_TIMEOUT, STATUS_EXACT_REDO, STATUS_RANGE_SPLIT, STATUS_GLOBAL_CUT = 0, 1, 2, 3
 
 
 def workspace_status(ws, clear: bool = True, out=None, stream=None) -> torch.Tensor:
@@ -77,7 +77,7 @@ def workspace_status(ws, clear: bool = True, out=None, stream=None) -> torch.Ten
     4-element int32 device tensor (``out`` or a new one) on the stream and, with
     ``clear``, reset.  Index with ``STATUS_WAIT_TIMEOUT`` (nonzero: a bounded
     in-kernel wait gave up, results since the last clear are wrong),
-    ``STATUS_EXACT_REDO``, ``STATUS_SHARED_CLAIMS`` and ``STATUS_GLOBAL_CUT`` (counts)."""
+    ``STATUS_EXACT_REDO``, ``STATUS_RANGE_SPLIT`` and ``STATUS_GLOBAL_CUT`` (counts)."""
     if out is None:
         out = torch.zeros(4, dtype=torch.int32, device=ws.device)
     call("jssa_workspace_status", _ptr(ws, torch.uint8, "ws"), ws.numel(), _ptr(out, torch.int32, "out"),

@@ -408,6 +408,22 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// The group's queries in S.q: bf16 as stored, in 16-byte pieces (thread i
+// < G D / 8 holds piece i of the G rows); fp32 one element per thread (i < G
+// D), scaled to base-2 logits.  Requested here with the first sub-chunk's
+// K/V rows, so their latencies overlap.
+template <int KVT, int D, int G>
+__device__ __forceinline__ uint4 load_query_piece(const AttnArgs& a, int b, int h) {
+  constexpr int NP = KVT == 1 ? G * D / 8 : G * D;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  const size_t q0 = (size_t(b) * a.Hq + size_t(h) * G) * D;
+  if (threadIdx.x < NP) {
+    if constexpr (KVT == 1) v = load16(reinterpret_cast<const uint16_t*>(a.q) + q0 + threadIdx.x * 8);
+    else v.x = __float_as_uint(reinterpret_cast<const float*>(a.q)[q0 + threadIdx.x] * a.qscale);
+  }
+  return v;
+}
+
 template <int KVT, int D, int G, int NW, int NL, bool PUBLISH = false>
 __device__ __forceinline__ void attend_portion(const AttnArgs& a, PortionSmem<KVT, D, G, NW, NL>& S,
                                                const int* sidx, int row, int b, int h, int part, int cnt) {
@@ -437,8 +453,15 @@ __device__ __forceinline__ void attend_portion(const AttnArgs& a, PortionSmem<KV
       vr[k] = load16_nt(vbase + off);
     }
   };
+  const uint4 qpiece = load_query_piece<KVT, D, G>(a, b, h);
   uint4 kA[NL], vA[NL];
   load_sub(0, kA, vA);
+  constexpr int NQP = KVT == 1 ? G * D / 8 : G * D;
+  static_assert(NQP <= NW * 64, "query staging");
+  if (threadIdx.x < NQP) {
+    if constexpr (KVT == 1) reinterpret_cast<uint4*>(S.q)[threadIdx.x] = qpiece;
+    else S.q[threadIdx.x] = qpiece.x;
+  }
   if (threadIdx.x < G) {
     S.ml[threadIdx.x][0] = -INFINITY;
     S.ml[threadIdx.x][1] = 0.f;

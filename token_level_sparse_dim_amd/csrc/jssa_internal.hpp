@@ -61,7 +61,7 @@ enum QueueWord : int {
   QW_DONE = 1,    // finished items of that launch
   QW_ERR = 2,     // nonzero: a bounded wait gave up (that call's results are unreliable)
   QW_REDO = 3,    // rows re-selected exactly (the sampled threshold admitted fewer than k tokens)
-  QW_CLAIMS = 4,  // claims of shared score tiles made by the fused scan
+  QW_RANGE = 4,   // fused scans that split the score work into ranges across rows (fewer workgroups than rows)
   QW_BIG = 5,     // rows whose candidates exceeded shared memory (cut in global memory)
 };
 constexpr int kQueueWords = 64;

@@ -51,6 +51,16 @@ constexpr int kPipePF = 3;             // score-scan steps in flight per workgro
 constexpr int kPipeMaxItem = 8192;     // tokens per score item at most (whole tiles)
 constexpr int kPipeCandLds = 16384;    // candidates resolved in shared memory
 constexpr int kPipeSampleMin = 8192;   // candidate tokens above which a row's threshold is sampled
+// Leaves the remaining rounds of a loop over MAXPER rounds of candidates:
+// `break` where the loop still unrolls fully with it (MAXPER <= 8), else
+// `continue` (the unroller gives up on the larger loops with a second exit,
+// and their register arrays would go to scratch).
+#define JSSA_ROUNDS_END \
+  if constexpr (MAXPER <= 8) {  \
+    break;                      \
+  } else {                      \
+    continue;                   \
+  }
 constexpr int kPipeMaxTiles = 2048;    // tiles per row
 constexpr int kPipeCutList = 256;      // candidates of the cut's bin ranked directly (one per thread)
 constexpr int kPipeGatherTiles = 8;    // tiles per wave per gather round
@@ -69,13 +79,8 @@ constexpr int kPipePartTarget = 256;   // select/attend workgroups a launch aims
 constexpr int PW_L = 12;
 constexpr uint64_t kLwSet = uint64_t(1) << 32;
 constexpr uint64_t kLwAppended = uint64_t(1) << 33;
-// per-row state word of the scan: claims of the row's shared tiles (reset by the resolve)
-constexpr int PW_STEAL = 14;
 #ifndef JSSA_PIPE_PER_CU
 #define JSSA_PIPE_PER_CU 3  // scan workgroups per compute unit at most (0: as many as fit)
-#endif
-#ifndef JSSA_PIPE_STATIC_PCT
-#define JSSA_PIPE_STATIC_PCT 100  // share of a row's tiles covered by the static score runs
 #endif
 
 struct PipeArgs {
@@ -93,8 +98,8 @@ struct PipeArgs {
   void* kp_w;
   int attend_only;     // host side: launch the attention and merge only, on caller lists
   uint32_t* tile_cnt;  // [rows][n_tiles]
-  int G, d_k, topk, window, q_dtype, ts, n_tiles, n_rows, n_main, n_attn;
-  int item, n_big, n_small;  // score runs: n_big runs of `item` tokens per row, then n_small single tiles
+  int G, d_k, topk, window, q_dtype, ts, n_tiles, n_rows, n_attn;
+  int samples_in_scan;  // 1: scan workgroup r < n_rows samples row r; 0: a sample launch ran before the scan
   uint64_t spin_ticks;  // wall-clock ticks after the launch's start when every wait gives up
 };
 
@@ -630,68 +635,181 @@ struct Pipe {
     }
   }
 
-  // Scores tokens [t_begin, t_begin + len) of the row (whole tiles from t_begin).
-  static __device__ __forceinline__ void score_item(const PipeArgs& a, int row, int t_begin, int len, char* smem,
-                                                    uint64_t deadline) {
+  // Scores tokens [t_begin, t_end) of the row (t_begin on a tile boundary,
+  // t_end <= n_cand) with one query projection, in items of at most
+  // kPipeMaxItem tokens (the key buffer), and emits each item's candidates.
+  // The row's threshold is waited for after the first item's scan.
+  static __device__ void score_range(const PipeArgs& a, int row, int t_begin, int t_end, char* smem,
+                                     uint64_t deadline) {
     const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
-    const RowMode md = row_mode(a, b);
-    if (!md.select()) return;
-    if (t_begin >= md.n_cand) return;
-    const int t_end = min(t_begin + len, md.n_cand);
     ScoreSmem& sm = *reinterpret_cast<ScoreSmem*>(smem);
     const char* kr = kp_row(a, row);
     uint4 pre[kPipePF][S::U];
     uint64_t lw = 0;
+    int tb = t_begin, te = min(t_begin + kPipeMaxItem, t_end);
     project_query_staged<D, R, G>(a, b, h, sm.qp, [&] {
-      load_first(kr, t_begin, t_end, pre);  // in flight during the query projection
+      load_first(kr, tb, te, pre);  // in flight during the query projection
       if (threadIdx.x == 0) lw = consume(l_word(a, row));
     });
     QFrag<KPT, R, GE> qf;
     load_qfrag<KPT, R, GE>([&](int i) { return sm.qp.qp[i]; }, G, qf);
     __syncthreads();  // the projection's shared memory becomes the key buffer
-    scan_keys(kr, t_begin, t_end, qf, pre, sm.keys);
-    // the row's threshold (its sample item was handed out before this item)
-    if (threadIdx.x == 0) {
-      while ((lw >> 32) == 0 && !past(deadline)) {
-        __builtin_amdgcn_s_sleep(1);
-        lw = consume(l_word(a, row));
-      }
-      if ((lw >> 32) == 0) flag_error(a);
-      sm.l_key = uint32_t(lw);
-    }
-    __syncthreads();
-    rescore_new(a, row, b, kr, t_begin, t_end, qf, sm.keys, deadline);
-    __syncthreads();
-    // The row's shared tiles (those past the static runs): claimed one at a
-    // time from the row's counter by the row's runs as they finish, which
-    // evens out runs that stream at different rates.  A claim is requested
-    // before it is needed (the first one before this run's emission, the next
-    // one while the current tile is scanned), and no barrier waits on it
-    // before its use.  (Also draining other rows' tiles measured slower.)
-    const int pool0 = a.n_big * (a.item / TS);
-    const int n_tiles_row = (md.n_cand + TS - 1) / TS;
-    uint32_t* ctr = state(a, row) + PW_STEAL;
-    int first = 0;
-    if (threadIdx.x == 0 && pool0 < n_tiles_row)
-      first = int(__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    emit_keys(a, row, t_begin, t_end, sm.l_key, sm.keys);
-    if (pool0 >= n_tiles_row) return;
-    __syncthreads();  // every wave is done with keys[]
-    if (threadIdx.x == 0) sm.claim = first;
-    __syncthreads();
-    int c = sm.claim;
-    while (pool0 + c < n_tiles_row) {
-      const int tb = (pool0 + c) * TS, te = min(tb + TS, md.n_cand);
-      load_first(kr, tb, te, pre);
-      int nxt = 0;
-      if (threadIdx.x == 0) nxt = int(__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    for (;;) {
       scan_keys(kr, tb, te, qf, pre, sm.keys);
+      if (tb == t_begin) {  // the row's threshold (its sample was handed out before any score work)
+        if (threadIdx.x == 0) {
+          while ((lw >> 32) == 0 && !past(deadline)) {
+            __builtin_amdgcn_s_sleep(1);
+            lw = consume(l_word(a, row));
+          }
+          if ((lw >> 32) == 0) flag_error(a);
+          sm.l_key = uint32_t(lw);
+        }
+        __syncthreads();
+      }
       rescore_new(a, row, b, kr, tb, te, qf, sm.keys, deadline);
-      if (threadIdx.x == 0) sm.claim = nxt;
       __syncthreads();
       emit_keys(a, row, tb, te, sm.l_key, sm.keys);
-      c = sm.claim;
-      __syncthreads();  // keys[] and the claim are free again
+      if (te >= t_end) return;
+      tb = te;
+      te = min(tb + kPipeMaxItem, t_end);
+      load_first(kr, tb, te, pre);
+      __syncthreads();  // every wave is done with keys[]
+    }
+  }
+
+  // ---- SPLIT OF THE SCORE WORK -----------------------------------------------------------
+  // The rows' candidate tiles go to the score workgroups in proportion to the
+  // rows' lengths: sequence b's Hkv rows of tiles_of(b) tiles each get
+  // w(b) = floor(spare * tiles_of(b) / N) + 1 workgroups per row (N: the
+  // tiles of all rows; spare: the score workgroups beyond one per row), and
+  // workgroup j of a row scans its tiles [j T / w, (j + 1) T / w): one row and
+  // one query projection per workgroup, and about N / spare tiles each,
+  // whatever the mix of lengths.  With fewer score workgroups than rows, the
+  // rows' tiles are instead laid end to end (sequence b, then KV head, then
+  // tile) and split into equal contiguous ranges.
+  static __device__ __forceinline__ int tiles_of(const PipeArgs& a, int b) {
+    const RowMode md = row_mode(a, b);
+    return md.select() ? (md.n_cand + TS - 1) / TS : 0;
+  }
+  struct FlatSmem {
+    uint32_t wsum[256 / 64];
+    uint32_t found[2];
+  };
+  // Sum over sequences of cnt(b) (every thread gets it).
+  template <typename Cnt>
+  static __device__ __forceinline__ uint32_t seq_total(const PipeArgs& a, FlatSmem& fs, Cnt cnt) {
+    const int B = a.n_rows / a.at.Hkv;
+    uint32_t mine = 0;
+    for (int b = threadIdx.x; b < B; b += 256) mine += cnt(b);
+    uint32_t total;
+    block_exclusive_scan<4>(mine, fs.wsum, &total);
+    return total;
+  }
+  // The sequence b whose run of the sums of cnt holds g, and g's offset in it
+  // (g below the total).
+  template <typename Cnt>
+  static __device__ __forceinline__ void seq_locate(const PipeArgs& a, FlatSmem& fs, uint32_t g, Cnt cnt, int* b_out,
+                                                    uint32_t* o_out) {
+    const int B = a.n_rows / a.at.Hkv;
+    uint32_t base = 0;
+    for (int b0 = 0; b0 < B; b0 += 256) {
+      const int b = b0 + int(threadIdx.x);
+      const uint32_t c = b < B ? cnt(b) : 0u;
+      uint32_t chunk;
+      const uint32_t ex = base + block_exclusive_scan<4>(c, fs.wsum, &chunk);
+      if (c && g >= ex && g < ex + c) {  // one thread
+        fs.found[0] = uint32_t(b);
+        fs.found[1] = g - ex;
+      }
+      base += chunk;
+      __syncthreads();
+      if (g < base) break;  // uniform
+    }
+    __syncthreads();
+    *b_out = int(fs.found[0]);
+    *o_out = fs.found[1];
+    __syncthreads();  // found[] is reused
+  }
+  static __device__ void score_split(const PipeArgs& a, char* smem, FlatSmem& fs, uint64_t deadline) {
+    const int grid = int(gridDim.x);
+    // workgroups that sample sit out the split when the others are many enough
+    const int first = a.samples_in_scan && grid >= 2 * a.n_rows ? a.n_rows : 0;
+    const int s = int(blockIdx.x) - first;
+    if (s < 0) return;
+    const uint32_t W = uint32_t(grid - first);
+    const uint32_t Hkv = uint32_t(a.at.Hkv);
+    // Every sequence with the same tile count (the usual batch): the split in
+    // closed form, without the scans.  Runs of `it` tiles, ceil(nt / it) of
+    // them per row; run j of row r is score workgroup j n_rows + (r - j mod
+    // n_rows), so every row's first runs are dispatched first and a row's
+    // runs rotate over the XCDs.
+    {
+      const int B = a.n_rows / a.at.Hkv, lane = int(threadIdx.x & 63);
+      const int nt0 = tiles_of(a, 0);
+      bool same = true;  // a wave vote: every wave reads every length, no barrier
+      int lane_cand = 0;  // candidates of sequence `lane` (B <= 64)
+      for (int b = lane; b < B; b += 64) {
+        const RowMode mb = row_mode(a, b);
+        same = same && (mb.select() ? (mb.n_cand + TS - 1) / TS : 0) == nt0;
+        if (b == lane) lane_cand = mb.n_cand;
+      }
+      if (__all(same)) {
+        if (nt0 == 0) return;
+        const int per_row = int(W) / a.n_rows;
+        if (per_row >= 1) {
+          const int it = (nt0 + per_row - 1) / per_row, runs = (nt0 + it - 1) / it;
+          if (s >= a.n_rows * runs) return;
+          const int j = s / a.n_rows, r = (s - j * a.n_rows + j) % a.n_rows;
+          const int bq = r / a.at.Hkv;
+          const int n_cand = B <= 64 ? __shfl(lane_cand, bq) : row_mode(a, bq).n_cand;
+          score_range(a, r, j * it * TS, min(min(j * it + it, nt0) * TS, n_cand), smem, deadline);
+          return;
+        }
+      }
+    }
+    const uint32_t N = seq_total(a, fs, [&](int b) { return Hkv * uint32_t(tiles_of(a, b)); });
+    const uint32_t rows_live = seq_total(a, fs, [&](int b) { return tiles_of(a, b) ? Hkv : 0u; });
+    if (N == 0) return;
+    if (W >= rows_live) {
+      const uint64_t spare = W - rows_live;
+      auto per_row = [&](int b) -> uint32_t {
+        const uint32_t t = uint32_t(tiles_of(a, b));
+        return t ? uint32_t(spare * t / N) + 1u : 0u;
+      };
+      if (uint32_t(s) >= seq_total(a, fs, [&](int b) { return Hkv * per_row(b); })) return;
+      int b;
+      uint32_t o;
+      seq_locate(a, fs, uint32_t(s), [&](int b) { return Hkv * per_row(b); }, &b, &o);
+      const uint32_t w = per_row(b), h = o / w, j = o - h * w;
+      const RowMode md = row_mode(a, b);
+      const uint32_t nt = uint32_t(tiles_of(a, b));
+      const int t0 = int(uint64_t(nt) * j / w), t1 = int(uint64_t(nt) * (j + 1) / w);
+      if (t1 > t0) score_range(a, b * a.at.Hkv + int(h), t0 * TS, min(t1 * TS, md.n_cand), smem, deadline);
+      return;
+    }
+    // fewer score workgroups than rows: equal contiguous ranges of the rows' tiles laid end to end
+    if (s == 0 && threadIdx.x == 0) __hip_atomic_fetch_add(a.at.queue + QW_RANGE, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t g = uint32_t(uint64_t(N) * uint32_t(s) / W);
+    const uint32_t g1 = uint32_t(uint64_t(N) * uint32_t(s + 1) / W);
+    if (g >= g1) return;
+    int b;
+    uint32_t o;
+    seq_locate(a, fs, g, [&](int b) { return Hkv * uint32_t(tiles_of(a, b)); }, &b, &o);
+    while (g < g1) {  // one row segment at a time (sequences with nothing to score hold no tiles)
+      const RowMode md = row_mode(a, b);
+      const uint32_t nt = uint32_t(tiles_of(a, b));
+      if (nt == 0 || o >= Hkv * nt) {
+        ++b;
+        o = 0;
+        continue;
+      }
+      const uint32_t h = o / nt, t0 = o - h * nt;
+      const uint32_t seg = min(nt - t0, g1 - g);
+      score_range(a, b * a.at.Hkv + int(h), int(t0) * TS, min(int(t0 + seg) * TS, md.n_cand), smem, deadline);
+      __syncthreads();
+      g += seg;
+      o += seg;
     }
   }
 
@@ -881,7 +999,7 @@ struct Pipe {
     const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
-      if (i >= nper) break;
+      if (i >= nper) { JSSA_ROUNDS_END; }
       sm.wcnt[buf][RW * i + wave] = uint32_t(__popcll(__ballot(flag(i))));  // every lane: the same word
     }
     __syncthreads();
@@ -902,7 +1020,7 @@ struct Pipe {
     for (int k = 0; k < WPL; ++k) ex += k < kw ? c[k] : 0u;
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
-      if (i >= nper) break;
+      if (i >= nper) { JSSA_ROUNDS_END; }
       off[i] = uint32_t(__builtin_amdgcn_readlane(int(ex), (RW * i + wave) / WPL));
     }
   }
@@ -924,7 +1042,7 @@ struct Pipe {
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < MAXPER; ++i) {
-        if (i >= nper) break;
+        if (i >= nper) { JSSA_ROUNDS_END; }
         const uint32_t dv = kv[i] - kmin;
         const bool in = uint32_t(i) * RT + tid < C && (hi >= 32 || (dv >> hi) == (prefix >> hi));
         atomicAdd(&sm.hist[in ? (dv >> sh) & 0x7ffu : 2048u], 1u);
@@ -943,7 +1061,7 @@ struct Pipe {
     const uint64_t below = (1ull << (tid & 63)) - 1ull;
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
-      if (i >= nper) break;
+      if (i >= nper) { JSSA_ROUNDS_END; }
       const bool e = eq(i);
       const uint64_t mk = __ballot(e);
       if (e && off[i] + uint32_t(__popcll(mk & below)) == need - 1u) sm.out[1] = uint32_t(i) * RT + tid;
@@ -980,7 +1098,7 @@ struct Pipe {
     const int sh = nbits > 11 ? nbits - 11 : 0;
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
-      if (i >= nper) break;
+      if (i >= nper) { JSSA_ROUNDS_END; }
       atomicAdd(&sm.hist[live(i) ? (kv[i] - kmin) >> sh : 2048u], 1u);  // dead lanes: the dummy bin
     }
     __syncthreads();
@@ -992,7 +1110,7 @@ struct Pipe {
     const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
-      if (i >= nper) break;
+      if (i >= nper) { JSSA_ROUNDS_END; }
       const bool inb = live(i) && ((kv[i] - kmin) >> sh) == bin;
       const uint64_t mk = __ballot(inb);
       if (mk) {
@@ -1059,7 +1177,7 @@ struct Pipe {
     word_offsets<MAXPER>(sm, nper, 1, take, off);
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
-      if (i >= nper) break;
+      if (i >= nper) { JSSA_ROUNDS_END; }
       const bool t = take(i);
       const uint64_t mk = __ballot(t);
       const uint32_t pos = off[i] + uint32_t(__popcll(mk & below));
@@ -1078,11 +1196,6 @@ struct Pipe {
     ResolveSmem& sm = *reinterpret_cast<ResolveSmem*>(smem);
     if (leader && threadIdx.x == 0) {  // read again only by the next call's scan
       *l_word(a, row) = 0;
-      const uint32_t claims = state(a, row)[PW_STEAL];
-      if (claims) {
-        __hip_atomic_fetch_add(a.at.queue + QW_CLAIMS, claims, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        state(a, row)[PW_STEAL] = 0;
-      }
       const_cast<int32_t*>(a.at.n_sel)[row] = md.kk + md.nW;
     }
     const int n_tiles_row = (md.n_cand + TS - 1) / TS;
@@ -1156,27 +1269,9 @@ struct Pipe {
     int sidx[kPipeMaxPortion];  // the part's token indices
   };
   static_assert(sizeof(SelSmem) <= 160 * 1024, "select/attend shared memory exceeds a compute unit's 160 KiB");
-  // The group's queries, requested before the selection and staged in shared
-  // memory after it: bf16 as stored, in 16-byte pieces (thread i holds piece
-  // i of the G rows); fp32 one element per thread, scaled to base-2 logits.
-  static constexpr int kQPieces = KVT == 1 ? G * D / 8 : G * D;
-  static_assert(kQPieces <= kResolveThreads, "query staging");
-  static __device__ __forceinline__ uint4 query_piece(const PipeArgs& a, int b, int h) {
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    const size_t q0 = (size_t(b) * a.at.Hq + size_t(h) * G) * D;
-    if (threadIdx.x < kQPieces) {
-      if constexpr (KVT == 1) v = load16(reinterpret_cast<const uint16_t*>(a.at.q) + q0 + threadIdx.x * 8);
-      else v.x = __float_as_uint(reinterpret_cast<const float*>(a.at.q)[q0 + threadIdx.x] * a.at.qscale);
-    }
-    return v;
-  }
   static __device__ __forceinline__ void attend_part(const PipeArgs& a, SelSmem& sm, int row, int b, int h, int part,
-                                                     int cnt, const uint4& qp) {
+                                                     int cnt) {
     if (cnt <= 0) return;  // uniform over the workgroup
-    if (threadIdx.x < kQPieces) {
-      if constexpr (KVT == 1) reinterpret_cast<uint4*>(sm.at.q)[threadIdx.x] = qp;
-      else sm.at.q[threadIdx.x] = qp.x;
-    }
     attend_portion<KVT, D, G, kAttnNW, kPortionNL, true>(a.at, sm.at, sm.sidx, row, b, h, part, cnt);
   }
   // Every part of the row takes a ticket once its partial is stored (device
@@ -1190,7 +1285,6 @@ struct Pipe {
   static __device__ __forceinline__ void select_attend(const PipeArgs& a, int row, int part, SelSmem& sm) {
     const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
     const RowMode md = row_mode(a, b);
-    const uint4 qp = query_piece(a, b, h);
     const int p0 = part * a.at.chunk;
     const int p1 = min(p0 + a.at.chunk, md.kk + md.nW);
     const int cnt = p1 > p0 ? p1 - p0 : 0;
@@ -1218,13 +1312,12 @@ struct Pipe {
       }
     }
     __syncthreads();  // the part's list is complete; the selection's shared memory is free
-    attend_part(a, sm, row, b, h, part, cnt, qp);
+    attend_part(a, sm, row, b, h, part, cnt);
     finish_row(a, row, md.kk + md.nW);
   }
   // The same parts over a caller's index lists (n_sel[row] entries of idx).
   static __device__ __forceinline__ void list_attend(const PipeArgs& a, int row, int part, SelSmem& sm) {
     const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
-    const uint4 qp = query_piece(a, b, h);
     int n = a.at.n_sel[row];
     n = n < 0 ? 0 : (n > a.at.idx_stride ? a.at.idx_stride : n);
     const int p0 = part * a.at.chunk;
@@ -1232,55 +1325,37 @@ struct Pipe {
     const int32_t* src = a.at.idx + size_t(row) * a.at.idx_stride + p0;
     for (int i = threadIdx.x; i < cnt; i += RT) sm.sidx[i] = src[i];
     __syncthreads();
-    attend_part(a, sm, row, b, h, part, cnt, qp);
+    attend_part(a, sm, row, b, h, part, cnt);
     finish_row(a, row, n);
   }
 };
 
-// Scan launch: items in order are the samples (one per row), one long score
-// run per resident workgroup (long enough that its row's threshold is known
-// when it finishes), then single-tile runs that balance the end.  Workgroup i
-// takes items i, i + grid, i + 2 grid, ...: the samples go to the lowest
-// workgroup indices, which the dispatcher starts first, and no shared counter
-// is contended.  A score run waits for its row's threshold only after its
-// scan, under a deadline (a missing threshold is flagged, never waited for
-// forever).
+// Scan launch: workgroup r < n_rows first samples row r (when the grid
+// covers every row; the grid never exceeds the resident workgroups, and the
+// samples wait for nothing, so every row's threshold gets published), then
+// each workgroup takes its share of the split of the score work.  A score range waits for its row's threshold only after its
+// first scan, under a deadline (a missing threshold is flagged, never waited
+// for forever).
 template <int KPT, int R, int GE, int D, int G, int KVT>
 __global__ __launch_bounds__(256, 3) void scan_kernel(PipeArgs a) {
   using Pp = Pipe<KPT, R, GE, D, G, KVT>;
   __shared__ __align__(16) char smem[Pp::kSmemScan];
+  __shared__ typename Pp::FlatSmem fs;
   const uint64_t deadline = wall_clock64() + a.spin_ticks;
-  const int n_big_all = a.n_rows * a.n_big;
-  int t = blockIdx.x;
-  // at most one sample per workgroup (the grid covers every row), outside the
-  // loop of score runs: in a loop, each item type's invariants would stay live
-  // across the other's code
-  if (t < a.n_rows) {
-    Pp::sample(a, t, *reinterpret_cast<typename Pp::SampleSmem*>(smem));
-    __syncthreads();
-    t += gridDim.x;
-  }
-  for (; t < a.n_main; t += gridDim.x) {
-    int r, t_begin, len;
-    if (t < a.n_rows + n_big_all) {
-      // run `run` of row r at i = run * n_rows + (r - run mod n_rows): a row's
-      // runs are spread over the dispatch order and, rotating by one per
-      // round, over the XCDs (workgroup i goes to XCD i mod 8), so its shared
-      // tiles can even out slower XCDs
-      const int i = t - a.n_rows;
-      const int run = i / a.n_rows;
-      r = (i - run * a.n_rows + run) % a.n_rows;
-      t_begin = run * a.item;
-      len = a.item;
-    } else {
-      const int i = t - a.n_rows - n_big_all;
-      r = i / a.n_small;
-      t_begin = a.n_big * a.item + (i - r * a.n_small) * Pp::TS;
-      len = Pp::TS;
-    }
-    Pp::score_item(a, r, t_begin, len, smem, deadline);
+  if (a.samples_in_scan && int(blockIdx.x) < a.n_rows) {  // one sample per workgroup at most
+    Pp::sample(a, blockIdx.x, *reinterpret_cast<typename Pp::SampleSmem*>(smem));
     __syncthreads();
   }
+  Pp::score_split(a, smem, fs, deadline);
+}
+
+// More rows than the scan's resident workgroups: the samples (and the
+// step's appends) run in a launch of their own first, one row per workgroup.
+template <int KPT, int R, int GE, int D, int G, int KVT>
+__global__ __launch_bounds__(256, 3) void sample_kernel(PipeArgs a) {
+  using Pp = Pipe<KPT, R, GE, D, G, KVT>;
+  __shared__ __align__(16) char smem[sizeof(typename Pp::SampleSmem)];
+  Pp::sample(a, blockIdx.x, *reinterpret_cast<typename Pp::SampleSmem*>(smem));
 }
 
 // Workgroup i of the select/attend launches runs on XCD i mod 8: the parts of
@@ -1411,27 +1486,27 @@ static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
     hipLaunchKernelGGL((list_attend_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_attn), dim3(kResolveThreads), 0, s, a);
     return hipGetLastError();
   }
-  // score runs sized so that the samples and one run per resident workgroup
-  // fit; a run streams long enough that its row's threshold is known when it
-  // finishes, and the row's remaining tiles are shared by its runs as they
-  // finish
+  // At most one workgroup per resident slot: the samples, then as many score
+  // workgroups as the closed-form split of rows of t_max tokens uses (the
+  // split of shorter or ragged rows adapts to whatever grid it gets).
   const int resident = scan_per_cu<KPT, R, GE, D, G, KVT>() * compute_units();
   const int n_tiles_max = (a.at.t_max + Pp::TS - 1) / Pp::TS;
-  const int per_row = resident > 2 * a.n_rows ? (resident - a.n_rows) / a.n_rows : 1;
-  // static runs cover JSSA_PIPE_STATIC_PCT% of a row's tiles (whole tiles per run, rounded
-  // up); the rest, and whatever the longest run (kPipeMaxItem tokens) leaves, are shared
-  int big_tiles = (JSSA_PIPE_STATIC_PCT * n_tiles_max + 100 * per_row - 1) / (100 * per_row);
-  if (big_tiles < 1) big_tiles = 1;
-  if (big_tiles > kPipeMaxItem / Pp::TS) big_tiles = kPipeMaxItem / Pp::TS;
-  a.item = big_tiles * Pp::TS;
-  a.n_big = (n_tiles_max + big_tiles - 1) / big_tiles;
-  if (a.n_big > per_row) a.n_big = per_row;
-  a.n_small = 0;
-  a.n_main = a.n_rows + a.n_rows * a.n_big;
-  int grid = resident < a.n_main ? resident : a.n_main;
-  if (grid < a.n_rows) grid = a.n_rows;  // one sample per workgroup at most
+  int grid = resident;
+  if (resident >= 2 * a.n_rows) {
+    const int per_row = (resident - a.n_rows) / a.n_rows;
+    const int it = (n_tiles_max + per_row - 1) / per_row, runs = (n_tiles_max + it - 1) / it;
+    grid = a.n_rows * (1 + runs);
+  } else {
+    const int64_t useful = int64_t(a.n_rows) * (1 + n_tiles_max);
+    if (useful < grid) grid = int(useful);
+  }
+  a.samples_in_scan = a.n_rows <= grid;
   auto mark = [&](int i) { return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
   hipError_t e = hipSuccess;
+  if (!a.samples_in_scan) {
+    hipLaunchKernelGGL((sample_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_rows), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (ev) {  // events [0] and [1] take the scan kernel's own start and end
     hipExtLaunchKernelGGL((scan_kernel<KPT, R, GE, D, G, KVT>), dim3(grid), dim3(256), 0, s,
                           static_cast<hipEvent_t>(ev[0]), static_cast<hipEvent_t>(ev[1]), 0u, a);
