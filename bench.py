@@ -325,6 +325,20 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "bytes_per_launch": kp_bytes, "avg_launch_us": round(scan_us, 2)},
     }
+    if w.mla:
+        # the score scan runs on the matrix cores: each projected query is split
+        # into bf16 hi + lo terms, so the executed products are twice the
+        # algorithmic 2 Hq r flops per candidate (MEAN: one query row in a
+        # 16-row M-tile)
+        rows_m = w.n_q_heads if reduce == J.REDUCE_MAX else 16
+        n_cand = int(np.maximum(case.sets[0]["seq_lens"].cpu().numpy().astype(np.int64) - w.window, 0).sum())
+        flops = 2 * 2 * rows_m * w.rank * n_cand
+        tf = flops / (scan_us * 1e-6) / 1e12
+        result["mfma_util"] = {"kernel": "mla_score_kernel", "executed_flops_per_launch": flops,
+                               "algorithmic_flops_per_launch": flops // 2, "achieved_tflops": round(tf, 1),
+                               "peak_tflops": 2500.0, "frac": round(tf / 2500.0, 4),
+                               "counters": "profiles/mla_kernels_mfma.txt (SQ_VALU_MFMA_BUSY_CYCLES)"}
+        log(f"mla_score_kernel: {tf:.0f} TFLOP/s bf16 MFMA ({100 * tf / 2500:.1f}% of the dense peak)")
     if args.quick:
         print(json.dumps(result), flush=True)
         return
