@@ -441,21 +441,20 @@ __device__ __forceinline__ void attend_portion(const AttnArgs& a, PortionSmem<KV
   const size_t row_stride = size_t(a.Hkv) * D * EB;
   const size_t head_off = (size_t(b) * a.t_max * a.Hkv + h) * D * EB + size_t(p) * EPL * EB;
   const int n_sub = (cnt + CH - 1) / CH;
-  // K and V rows of sub-chunk c (rows past cnt re-read a valid row and get weight 0)
-  auto load_sub = [&](int c, uint4 (&kr)[NL], uint4 (&vr)[NL]) {
+  // K or V rows of sub-chunk c (rows past cnt re-read a valid row and get weight 0)
+  auto load_rows = [&](int c, const char* base, uint4 (&rr)[NL]) {
     const int c0 = min(c, n_sub - 1) * CH;
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
       const int r = (k * NW + wave) * RPW + rsub;
       const int t = min(max(sidx[min(c0 + r, cnt - 1)], 0), a.t_max - 1);  // indices are clamped
-      const size_t off = head_off + size_t(t) * row_stride;
-      kr[k] = load16_nt(kbase + off);
-      vr[k] = load16_nt(vbase + off);
+      rr[k] = load16_nt(base + head_off + size_t(t) * row_stride);
     }
   };
   const uint4 qpiece = load_query_piece<KVT, D, G>(a, b, h);
   uint4 kA[NL], vA[NL];
-  load_sub(0, kA, vA);
+  load_rows(0, kbase, kA);
+  load_rows(0, vbase, vA);
   constexpr int NQP = KVT == 1 ? G * D / 8 : G * D;
   static_assert(NQP <= NW * 64, "query staging");
   if (threadIdx.x < NQP) {
@@ -476,7 +475,8 @@ __device__ __forceinline__ void attend_portion(const AttnArgs& a, PortionSmem<KV
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
   }
-  auto sub_chunk = [&](int c, const uint4 (&kr)[NL], const uint4 (&vr)[NL]) {
+  // pass 1: the sub-chunk's logits into S.w
+  auto logits = [&](int c, const uint4 (&kr)[NL]) {
     const int n = min(CH, cnt - c * CH);
     // pass 1: logits
 #pragma unroll
@@ -498,6 +498,9 @@ __device__ __forceinline__ void attend_portion(const AttnArgs& a, PortionSmem<KV
         if (p == 0) S.w[r][g] = (r < n) ? s : -INFINITY;
       }
     }
+  };
+  // the running max and sum per head (one wave per head), this sub-chunk's weights
+  auto weights = [&]() {
     __syncthreads();
     if (wave < G) {
       const int g = wave;
@@ -522,6 +525,8 @@ __device__ __forceinline__ void attend_portion(const AttnArgs& a, PortionSmem<KV
       }
     }
     __syncthreads();
+  };
+  auto weigh_values = [&](int c, const uint4 (&vr)[NL]) {
     // pass 2: weighted V rows (the running sums rescaled first, after the first sub-chunk)
     if (c > 0) {
 #pragma unroll
@@ -551,10 +556,20 @@ __device__ __forceinline__ void attend_portion(const AttnArgs& a, PortionSmem<KV
     }
     __syncthreads();  // S.w and the factors are rewritten by the next sub-chunk
   };
-  for (int c = 0; c < n_sub; ++c) {
-    sub_chunk(c, kA, vA);
-    if (c + 1 < n_sub) load_sub(c + 1, kA, vA);
+  // The next sub-chunk's K rows are requested as soon as this one's logits
+  // are formed, its V rows as soon as this one's values are weighed: no
+  // extra registers, and the waits count the loads in issue order (K then
+  // V).  The last sub-chunk is peeled so that nothing is requested past it.
+  for (int c = 0; c + 1 < n_sub; ++c) {
+    logits(c, kA);
+    load_rows(c + 1, kbase, kA);
+    weights();
+    weigh_values(c, vA);
+    load_rows(c + 1, vbase, vA);
   }
+  logits(n_sub - 1, kA);
+  weights();
+  weigh_values(n_sub - 1, vA);
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
