@@ -5,11 +5,12 @@ caches.
 
 In the fused build the append runs inside the scan launch and the scan
 re-scores the step that holds the new token, so the cases put the token where
-that matters: early in a row (the start of a static scan run), near the end
-of the candidates (the last tile of a row's last static run: at these sizes
-the static runs cover every row, so no tile is shared; the shared-tile case
-is in test_gpu_select_paths.py and the full-size hybrid step), in the
-trailing window, past the cache (not written), and mixed over the batch.  The new key is either a needle (aligned
+that matters: early in a row (inside the range of the row's first score
+workgroup), near the end of the candidates (the last tile of the row's last
+score workgroup; ranges that cross rows, with the new token in every
+sequence, are in test_gpu_select_paths.py, and the ragged split in the
+full-size hybrid step), in the trailing window, past the cache (not
+written), and mixed over the batch.  The new key is either a needle (aligned
 with its query head's projection and long: selected if it is scored from the
 stored row) or a zero row written over a planted needle (selected only if a
 stale projected row were scored).  Everything is compared bit for bit: the
