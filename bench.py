@@ -271,8 +271,8 @@ def main():
     stage_us = stage_events(J, case, min(args.steps, 100), stream)
     # fused GQA build: the scan launch, the select/attend launch (its in-launch
     # merge included), the two back-to-back closing events (their own cost);
-    # MLA: score scan, candidate pass, resolve + attention + merge
-    names = ["score_scan", "candidates", "resolve+attention"] if w.mla else \
+    # MLA: score scan, candidate pass, selection + attention + merge
+    names = ["score_scan", "candidates", "select+attention+merge"] if w.mla else \
         ["scan", "select_attend_merge", "event_pair"]
     log("stage events (us): " + ", ".join(f"{n}={v:.2f}" for n, v in zip(names, stage_us)))
 

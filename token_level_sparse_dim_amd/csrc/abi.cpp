@@ -120,7 +120,11 @@ bool workspace_layout(const jssa_desc& d, int op, Workspace* ws) {
   // the fused decode uses its own tile counts and candidate slots only; the
   // staged selection also needs the first-digit histogram and tile tables
   const bool staged = op == JSSA_OP_TOPK || (op == JSSA_OP_DECODE && !ws->pipe);
-  const int cnt_tiles = staged ? ws->n_sel_tiles : ws->pipe_tiles;
+  // the MLA decode's candidate pass counts per kSubTile tokens (its selection
+  // is the fused decode's); the staged top-k per kSelTile
+  const int cnt_tiles = !staged ? ws->pipe_tiles
+                        : (mla && op == JSSA_OP_DECODE) ? ws->n_sel_tiles * (kSelTile / kSubTile)
+                                                        : ws->n_sel_tiles;
   ws->queue = take(kQueueWords * 4);  // first: jssa_workspace_status finds it at offset 0
   ws->row_state = take(rows * kRowStateWords * 4);
   if (ws->pipe) ws->pipe_qp = take(rows * size_t(G) * d.rank * 4);
@@ -386,11 +390,9 @@ int32_t decode_launch(const jssa_desc* desc, const void* q, const float* P, cons
     hipError_t e = launch_mla_qproj(*desc, q, P, base, lay, s);
     // events [0] and [1] take the score scan kernel's own start and end
     if (e == hipSuccess) e = launch_mla_scan(*desc, kp_cache, seq_lens, scores, true, base, lay, s, ev);
-    if (e == hipSuccess) e = launch_candidates(*desc, scores, seq_lens, base, lay, s);
+    if (e == hipSuccess) e = launch_candidates(*desc, scores, seq_lens, base, lay, s, true);
     if (e == hipSuccess) e = mark(2);
-    if (e == hipSuccess)
-      e = launch_resolve_attend(*desc, true, false, nullptr, nullptr, nullptr, idx, n_sel, seq_lens, nullptr,
-                                nullptr, base, lay, s);
+    if (e == hipSuccess) e = launch_select_rows(*desc, seq_lens, idx, n_sel, base, lay, s);
     if (e == hipSuccess) e = launch_mla_attend(*desc, q, k_cache, idx, n_sel, nullptr, out, lse, base, lay, s);
     if (e == hipSuccess) e = mark(3);
     return to_status(e);

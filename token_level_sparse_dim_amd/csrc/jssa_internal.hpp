@@ -24,6 +24,7 @@ namespace jssa {
 #endif
 constexpr int kScoreTile = JSSA_SCORE_TILE;  // candidate tokens per score workgroup
 constexpr int kSelTile = 4096;               // keys per selection workgroup
+constexpr int kSubTile = 1024;               // tokens per tile of the fused selection's candidate slots
 constexpr int kDigit1Bits = 12;      // first radix digit: key bits 31..20
 constexpr int kDigit1Bins = 1 << kDigit1Bits;
 constexpr int kMaxSelTiles = 4096;   // t_max <= kMaxSelTiles * kSelTile
@@ -123,8 +124,10 @@ hipError_t launch_hist(const jssa_desc& d, const float* scores, const int32_t* s
 
 // Candidate pass of the selection: every key in or above the first-digit
 // threshold bin, written in token order to its tile's slot.
+// sub_tiles: slots and counts per kSubTile tokens (the fused selection's
+// tiles) instead of per kSelTile
 hipError_t launch_candidates(const jssa_desc& d, const float* scores, const int32_t* seq_lens,
-                             char* ws_base, const Workspace& ws, hipStream_t s);
+                             char* ws_base, const Workspace& ws, hipStream_t s, bool sub_tiles = false);
 
 // One launch with a work queue: a resolve item per row (exact k-th key, tie
 // cut, emission of idx / n_sel in ascending order plus the window), and, when
@@ -197,6 +200,8 @@ hipError_t launch_pipeline(const jssa_desc& d, const void* q, const float* P, co
 // The fused decode's attention and chunk-merge launches on caller-provided
 // index lists (stride topk + window), with the decode workspace (pipeline
 // shapes only).
+hipError_t launch_select_rows(const jssa_desc& d, const int32_t* seq_lens, int32_t* idx, int32_t* n_sel,
+                              char* ws_base, const Workspace& ws, hipStream_t s);
 hipError_t launch_pipe_attend(const jssa_desc& d, const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* idx, const int32_t* n_sel, void* out, float* lse, char* ws_base,
                               const Workspace& ws, hipStream_t s);

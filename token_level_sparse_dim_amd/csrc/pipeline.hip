@@ -1190,7 +1190,11 @@ struct Pipe {
   // place in the ascending list (0 <= pos < kk).  Several workgroups may
   // select the same row (each emits its own part); only the `leader` resets
   // the row's state for the next call, writes n_sel and counts diagnostics.
-  template <typename Emit>
+  // REDO: the slots come from this decode's sampled threshold, so fewer than
+  // k candidates mean an exact re-selection; without REDO (slots from the
+  // candidate pass of an exact first-digit threshold) that cannot happen, and
+  // is flagged as an error if it does.
+  template <bool REDO = true, typename Emit>
   static __device__ __forceinline__ void select_row(const PipeArgs& a, int row, const RowMode& md, char* smem,
                                                     bool leader, Emit emit) {
     ResolveSmem& sm = *reinterpret_cast<ResolveSmem*>(smem);
@@ -1211,11 +1215,16 @@ struct Pipe {
                         : gather<false, 1>(a, row, n_tiles_row, sm, &kmin, &kmax);
     const bool fresh = C < uint32_t(md.kk);  // (m > 0) the slots are rewritten below (read back device-scope)
     if (fresh) {
-      exact_candidates(a, row, md, smem, leader);
-      for (int i = threadIdx.x; i < 2048; i += RT) sm.hist[i] = 0u;
-      if (threadIdx.x == 0) sm.n_bin = 0u;
-      C = wide ? gather<true, 2>(a, row, n_tiles_row, sm, &kmin, &kmax)
-               : gather<true, 1>(a, row, n_tiles_row, sm, &kmin, &kmax);
+      if constexpr (REDO) {
+        exact_candidates(a, row, md, smem, leader);
+        for (int i = threadIdx.x; i < 2048; i += RT) sm.hist[i] = 0u;
+        if (threadIdx.x == 0) sm.n_bin = 0u;
+        C = wide ? gather<true, 2>(a, row, n_tiles_row, sm, &kmin, &kmax)
+                 : gather<true, 1>(a, row, n_tiles_row, sm, &kmin, &kmax);
+      } else {
+        if (threadIdx.x == 0) flag_error(a);
+        return;  // uniform
+      }
     }
     const uint32_t need = uint32_t(md.kk);  // 1 <= need <= C
     uint32_t kstar, istar;
@@ -1315,6 +1324,20 @@ struct Pipe {
     attend_part(a, sm, row, b, h, part, cnt);
     finish_row(a, row, md.kk + md.nW);
   }
+  // One row's whole list from candidate slots of a previous launch (the MLA
+  // decode's candidate pass): the exact cut, the ascending list and the window.
+  static __device__ __forceinline__ void select_list(const PipeArgs& a, int row, char* smem) {
+    const int b = row / a.at.Hkv;
+    const RowMode md = row_mode(a, b);
+    int32_t* out = a.at.idx + size_t(row) * a.at.idx_stride;
+    if (md.select()) {
+      select_row<false>(a, row, md, smem, true, [&](uint32_t pos, uint32_t tok) { out[pos] = int(tok); });
+    } else {  // every candidate or none
+      for (int t = threadIdx.x; t < md.kk; t += RT) out[t] = t;
+      if (threadIdx.x == 0) const_cast<int32_t*>(a.at.n_sel)[row] = md.kk + md.nW;
+    }
+    for (int j = threadIdx.x; j < md.nW; j += RT) out[md.kk + j] = md.Tb - md.nW + j;
+  }
   // The same parts over a caller's index lists (n_sel[row] entries of idx).
   static __device__ __forceinline__ void list_attend(const PipeArgs& a, int row, int part, SelSmem& sm) {
     const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
@@ -1377,6 +1400,14 @@ __global__ __launch_bounds__(kResolveThreads, 1) void select_attend_kernel(PipeA
   int row, part;
   if (!part_of(a, blockIdx.x, &row, &part)) return;
   Pp::select_attend(a, row, part, *reinterpret_cast<typename Pp::SelSmem*>(smem));
+}
+
+// Selection only, one workgroup per row (the MLA decode's rows).
+template <int KPT, int R, int GE, int D, int G, int KVT>
+__global__ __launch_bounds__(kResolveThreads, 1) void select_only_kernel(PipeArgs a) {
+  using Pp = Pipe<KPT, R, GE, D, G, KVT>;
+  __shared__ __align__(16) char smem[sizeof(typename Pp::SelSmem)];
+  Pp::select_list(a, blockIdx.x, smem);
 }
 
 // Attention over caller lists: the same parts and arithmetic.
@@ -1577,6 +1608,31 @@ hipError_t launch_pipeline(const jssa_desc& d, const void* q, const float* P, co
                            float* lse, int32_t* idx, int32_t* n_sel, char* ws_base, const Workspace& ws,
                            const NewToken* nt, void* const* ev, hipStream_t s) {
   return pipeline_impl(d, q, P, kp, k_cache, v_cache, seq_lens, out, lse, idx, n_sel, ws_base, ws, nt, ev, false, s);
+}
+
+// The exact selection of every row from the candidate pass's slots (per
+// kSubTile tokens, a count per tile, from a first-digit threshold that admits
+// at least k keys), with the fused decode's selection: one 1024-thread
+// workgroup per row.  Any fused shape's selection code serves (it reads only
+// keys and token indices); this one has kSubTile-token tiles.
+hipError_t launch_select_rows(const jssa_desc& d, const int32_t* seq_lens, int32_t* idx, int32_t* n_sel,
+                              char* ws_base, const Workspace& ws, hipStream_t s) {
+  using Pp = Pipe<1, 32, 4, 128, 4, 1>;
+  static_assert(Pp::TS == kSubTile, "the candidate pass's tiles");
+  PipeArgs a{};
+  AttnArgs& at = a.at;
+  at.seq_lens = seq_lens; at.idx = idx; at.n_sel = n_sel;
+  at.Hkv = d.n_kv_heads; at.t_max = d.t_max; at.idx_stride = d.topk + d.window;
+  at.queue = reinterpret_cast<uint32_t*>(ws_base + ws.queue);
+  at.row_state = reinterpret_cast<uint32_t*>(ws_base + ws.row_state);
+  a.cand = reinterpret_cast<uint64_t*>(ws_base + ws.cand);
+  a.tile_cnt = reinterpret_cast<uint32_t*>(ws_base + ws.tile_cnt);
+  a.n_tiles = ws.n_sel_tiles * (kSelTile / kSubTile);  // the counts' row stride
+  a.topk = d.topk; a.window = d.window; a.ts = kSubTile;
+  a.n_rows = d.batch * d.n_kv_heads;
+  if ((d.t_max + kSubTile - 1) / kSubTile > kPipeMaxTiles) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((select_only_kernel<1, 32, 4, 128, 4, 1>), dim3(a.n_rows), dim3(kResolveThreads), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_pipe_attend(const jssa_desc& d, const void* q, const void* k_cache, const void* v_cache,

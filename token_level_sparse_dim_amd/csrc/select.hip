@@ -3,7 +3,9 @@
 // bin D1 of each row, every workgroup takes one tile of kSelTile scores and
 // writes the keys whose top 12 bits are >= D1 -- every token that can be
 // selected -- in token order into the tile's slot, with the slot's count.
-// The exact cut is made by the resolve items (resolve.hpp).
+// The exact cut is made by the resolve items (resolve.hpp), or, with SUB = 4
+// (the MLA decode), by the fused decode's selection, which reads the same
+// slots per 1024-token sub-tile (counts in `tile_cnt` per sub-tile).
 #include "jssa_device.hpp"
 #include "jssa_internal.hpp"
 #include "select_common.hpp"
@@ -19,7 +21,10 @@ struct CandArgs {
   int Hkv, t_max, topk, window, n_sel_tiles;
 };
 
+template <int SUB>
 __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
+  constexpr int PER_SUB = kKeysPerThread / SUB;  // key rounds of 256 tokens per sub-tile
+  static_assert(PER_SUB * SUB == kKeysPerThread, "sub-tiles of whole rounds");
   __shared__ uint32_t s_wc[4][kKeysPerThread];
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int row = b * a.Hkv + h;
@@ -41,29 +46,34 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
     if (lane == 0) s_wc[wave][i] = uint32_t(__popcll(bal[i]));
   }
   __syncthreads();
-  uint64_t* slot = a.cand + size_t(row) * a.t_max + t0;
   const unsigned long long below = (1ull << lane) - 1ull;
-  uint32_t run = 0;
 #pragma unroll
-  for (int i = 0; i < kKeysPerThread; ++i) {
-    uint32_t before = 0, tot = 0;
+  for (int sub = 0; sub < SUB; ++sub) {
+    const int s0 = t0 + sub * PER_SUB * 256;  // the sub-tile's first token
+    if (s0 >= t_end) break;
+    uint64_t* slot = a.cand + size_t(row) * a.t_max + s0;
+    uint32_t run = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t c = s_wc[w][i];
-      before += (w < wave) ? c : 0u;
-      tot += c;
+    for (int i = sub * PER_SUB; i < (sub + 1) * PER_SUB; ++i) {
+      uint32_t before = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t c = s_wc[w][i];
+        before += (w < wave) ? c : 0u;
+        tot += c;
+      }
+      if ((bal[i] >> lane) & 1ull) {
+        const uint32_t t = uint32_t(t0 + i * 256 + int(threadIdx.x));
+        publish(&slot[run + before + uint32_t(__popcll(bal[i] & below))], (uint64_t(t) << 32) | key[i]);
+      }
+      run += tot;
     }
-    if ((bal[i] >> lane) & 1ull) {
-      const uint32_t t = uint32_t(t0 + i * 256 + int(threadIdx.x));
-      publish(&slot[run + before + uint32_t(__popcll(bal[i] & below))], (uint64_t(t) << 32) | key[i]);
-    }
-    run += tot;
+    if (threadIdx.x == 0) publish(&a.tile_cnt[size_t(row) * a.n_sel_tiles * SUB + tile * SUB + sub], run);
   }
-  if (threadIdx.x == 0) publish(&a.tile_cnt[size_t(row) * a.n_sel_tiles + tile], run);
 }
 
 hipError_t launch_candidates(const jssa_desc& d, const float* scores, const int32_t* seq_lens,
-                             char* ws_base, const Workspace& ws, hipStream_t s) {
+                             char* ws_base, const Workspace& ws, hipStream_t s, bool sub_tiles) {
   CandArgs a;
   a.scores = scores; a.seq_lens = seq_lens;
   a.row_state = reinterpret_cast<const uint32_t*>(ws_base + ws.row_state);
@@ -72,7 +82,8 @@ hipError_t launch_candidates(const jssa_desc& d, const float* scores, const int3
   a.Hkv = d.n_kv_heads; a.t_max = d.t_max; a.topk = d.topk; a.window = d.window;
   a.n_sel_tiles = ws.n_sel_tiles;
   dim3 grid(ws.n_sel_tiles, d.n_kv_heads, d.batch);
-  hipLaunchKernelGGL(cand_kernel, grid, dim3(256), 0, s, a);
+  if (sub_tiles) hipLaunchKernelGGL(cand_kernel<kSelTile / kSubTile>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(cand_kernel<1>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
