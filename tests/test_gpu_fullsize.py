@@ -7,7 +7,9 @@ benchmark, the GPU projects the whole key cache, then appends one new token at
 T_b - 1 and decodes in one call on the decode workspace (also with FP8
 projected keys).
 
-The oracle checks sampled (sequence, KV head) rows one at a time: it projects
+The oracle checks (sequence, KV head) rows one at a time (every row of the
+128K bf16 step and of the MLA step, 32 rows of the ragged batch, 8 of each
+other variant): it projects
 that row's keys itself, and the row's projected keys in the GPU cache are
 replaced by the oracle's before the decode, so both sides score the same
 input (rows are independent in the decode). Every other row is checked by
@@ -72,6 +74,11 @@ def _check_structure(gi, gn, L, w):
             assert (np.diff(sel) > 0).all() and sel[0] >= 0 and sel[-1] < L[b]
             if w.window:
                 assert np.array_equal(sel[n_exp - w.window:], np.arange(L[b] - w.window, L[b]))
+
+
+def _eight(w):
+    """Eight rows spread over the sequences and KV heads."""
+    return [(b % w.batch, (3 * b + 1) % w.n_kv_heads) for b in range(8)]
 
 
 def _run_full(w, samples, reduce=J.REDUCE_MAX, kp_dtype=J.BF16, pos_of=None):
@@ -159,19 +166,20 @@ def _run_full(w, samples, reduce=J.REDUCE_MAX, kp_dtype=J.BF16, pos_of=None):
 
 
 def test_full_ctx128k_step():
-    """All four sequences, first / middle / last KV heads."""
-    st = _run_full(WORKLOADS["ctx128k"], [(0, 0), (1, 3), (2, 7), (3, 4), (0, 7), (3, 0)])
+    """Every (sequence, KV head) row against the oracle."""
+    w = WORKLOADS["ctx128k"]
+    st = _run_full(w, [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)])
     assert st[J.STATUS_GLOBAL_CUT] == 0
 
 
 def test_full_ctx128k_step_fp8_keys():
     """The same step with the FP8 E4M3 projected-key cache (the bench's --kp fp8)."""
-    _run_full(WORKLOADS["ctx128k"], [(0, 0), (1, 5), (3, 7)], kp_dtype=J.FP8_E4M3)
+    _run_full(WORKLOADS["ctx128k"], _eight(WORKLOADS["ctx128k"]), kp_dtype=J.FP8_E4M3)
 
 
 def test_full_mla_step():
-    """Three of the eight sequences (one latent row per sequence)."""
-    _run_full(WORKLOADS["mla"], [(0, 0), (4, 0), (7, 0)])
+    """All eight sequences (one latent row per sequence)."""
+    _run_full(WORKLOADS["mla"], [(b, 0) for b in range(WORKLOADS["mla"].batch)])
 
 
 def test_full_ctx128k_step_k8192():
@@ -180,13 +188,14 @@ def test_full_ctx128k_step_k8192():
     selection holds up to 16,384 in shared memory, so nearly every row is cut
     there (a row past that takes the global cut, covered on its own)."""
     w = scaled(WORKLOADS["ctx128k"], topk=8192)
-    st = _run_full(w, [(0, 0), (1, 6), (3, 3)])
+    st = _run_full(w, _eight(w))
     assert st[J.STATUS_GLOBAL_CUT] <= 3 * w.batch * w.n_kv_heads // 4, st  # the helper decodes three times
 
 
 def test_full_ctx128k_step_k512():
     """The budget swept down to k = 512."""
-    _run_full(scaled(WORKLOADS["ctx128k"], topk=512), [(0, 2), (2, 0), (3, 7)])
+    w = scaled(WORKLOADS["ctx128k"], topk=512)
+    _run_full(w, _eight(w))
 
 
 def test_full_hybrid_ragged_step():
@@ -195,13 +204,8 @@ def test_full_hybrid_ragged_step():
     over score workgroups in proportion to its length (a 128K row gets about
     fifteen times the workgroups of an 8K row); the new token is the last
     candidate of each sequence (W + 1 from the end), in the last tile of its
-    row's last workgroup.  Sampled: the two longest and the shortest
-    sequence."""
+    row's last workgroup.  Checked: two KV heads of every sequence."""
     w = WORKLOADS["hybrid_ragged"]
-
-    def pick(L):
-        o = np.argsort(L)
-        return [(int(o[-1]), 0), (int(o[-2]), 5), (int(o[0]), 7)]
-
-    st = _run_full(w, pick, pos_of=lambda L: L - w.window - 1)
+    st = _run_full(w, [(b, h) for b in range(w.batch) for h in (b % 8, (b + 3) % 8)],
+                   pos_of=lambda L: L - w.window - 1)
     assert st[J.STATUS_RANGE_SPLIT] == 0, st  # one row per score workgroup
