@@ -242,7 +242,8 @@ int32_t jssa_indexed_attn(const jssa_desc* desc, const void* q, const void* k_ca
  * attention over a part is the one jssa_indexed_attn runs on these shapes, so
  * both give the same outputs for the same lists.  Other shapes run the
  * stand-alone kernels in sequence (MLA: query projection, score scan with the
- * first-digit histogram, candidate pass, resolve, attention, chunk merge).
+ * first-digit histogram, candidate pass, the exact selection of each row by
+ * one workgroup, attention, chunk merge).
  * idx_out / n_sel_out may be NULL; when given they receive the selection.
  * The new token is expected to be appended (jssa_append_kv) before this
  * call.  Workspace op JSSA_OP_DECODE. */
@@ -261,7 +262,7 @@ int32_t jssa_decode(const jssa_desc* desc, const void* q, const float* P, const 
  * merge), [3] right after [2].  Other GQA shapes: [0] before the score scan,
  * [1] after it, [2] after the candidate pass, [3] after the resolve +
  * attention.  MLA: [0] and [1] the score scan kernel's start and end, [2]
- * after the candidate pass, [3] after the resolve, the attention and the
+ * after the candidate pass, [3] after the selection, the attention and the
  * chunk merge. */
 int32_t jssa_decode_profiled(const jssa_desc* desc, const void* q, const float* P,
                              const void* kp_cache, const void* k_cache, const void* v_cache,

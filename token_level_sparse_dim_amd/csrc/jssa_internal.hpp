@@ -188,20 +188,24 @@ struct NewToken {
   void* kp_cache;
 };
 
-// The whole decode step in four launches (scan with sampled-threshold
-// candidate emission; resolve; attention chunks; chunk merge); requires
-// ws.pipe.  With `ev` (four events): recorded before the scan, after it, after
-// the resolve and after the merge.  With `nt`, the scan launch also appends
-// the new token first (the caches in `nt` are the decode's caches).
+// The whole decode step in two launches (the scan with sampled-threshold
+// candidate emission, preceded by a sample launch when the rows outnumber the
+// resident scan workgroups; then selection, attention and merge in one
+// launch); requires ws.pipe.  With `ev` (four events): [0] and [1] the scan
+// kernel's own start and end, [2] after the select/attend launch, [3] right
+// after.  With `nt`, the scan launch also appends the new token (the caches in
+// `nt` are the decode's caches).
 hipError_t launch_pipeline(const jssa_desc& d, const void* q, const float* P, const void* kp,
                            const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
                            float* lse, int32_t* idx, int32_t* n_sel, char* ws_base, const Workspace& ws,
                            const NewToken* nt, void* const* ev, hipStream_t s);
-// The fused decode's attention and chunk-merge launches on caller-provided
-// index lists (stride topk + window), with the decode workspace (pipeline
-// shapes only).
+// The exact selection of each row from the candidate pass's per-1024-token
+// slots (the MLA decode), one 1024-thread workgroup per row.
 hipError_t launch_select_rows(const jssa_desc& d, const int32_t* seq_lens, int32_t* idx, int32_t* n_sel,
                               char* ws_base, const Workspace& ws, hipStream_t s);
+// The fused decode's attention parts (and their in-launch merge) on
+// caller-provided index lists (stride topk + window), with the decode
+// workspace (pipeline shapes only).
 hipError_t launch_pipe_attend(const jssa_desc& d, const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* idx, const int32_t* n_sel, void* out, float* lse, char* ws_base,
                               const Workspace& ws, hipStream_t s);

@@ -525,7 +525,7 @@ struct Pipe {
         };
         uint4 v[HALF][S::U];
         project_query_staged<D, R, G>(a, b, h, sm.qp, [&] { load_half(0, v); });
-        // left for the resolve launch, in case the row has to be re-selected exactly
+        // left for the select/attend launch, in case the row has to be re-selected exactly
         for (int j = threadIdx.x; j < G * R; j += 256) a.qp_pub[size_t(row) * G * R + j] = sm.qp.qp[j];
         QFrag<KPT, R, GE> qf;
         load_qfrag<KPT, R, GE>([&](int i) { return sm.qp.qp[i]; }, G, qf);
@@ -1264,7 +1264,7 @@ struct Pipe {
   // the same selection; part 0 also writes n_sel and resets the row's state),
   // keeps the positions [part * chunk, (part + 1) * chunk) of the ascending
   // list plus window (and writes them to the output list), then attends over
-  // them and leaves the part's partial for the merge launch.  Rows with
+  // them and leaves the part's partial for the row's last part to merge.  Rows with
   // nothing to choose got their list from the scan launch; their parts derive
   // their tokens from the positions.
   static constexpr int kAttnNW = kResolveThreads / 64;
@@ -1513,7 +1513,7 @@ static hipError_t launch_pipe_t(PipeArgs a, void* const* ev, hipStream_t s) {
   using Pp = Pipe<KPT, R, GE, D, G, KVT>;
   if (Pp::TS != a.ts || a.at.chunk % 64 != 0 || a.at.chunk > kPipeMaxPortion || a.at.n_chunks > kPipeMaxParts)
     return hipErrorInvalidValue;
-  if (a.attend_only) {  // caller-provided index lists: the attention and merge launches only
+  if (a.attend_only) {  // caller-provided index lists: the attention parts (with their merge) only
     hipLaunchKernelGGL((list_attend_kernel<KPT, R, GE, D, G, KVT>), dim3(a.n_attn), dim3(kResolveThreads), 0, s, a);
     return hipGetLastError();
   }
