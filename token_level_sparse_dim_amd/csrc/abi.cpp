@@ -117,6 +117,7 @@ bool workspace_layout(const jssa_desc& d, int op, Workspace* ws) {
     ws->pipe_chunk = pipe_chunk;
     ws->pipe_n_chunks = int((n_max + pipe_chunk - 1) / pipe_chunk);
   }
+  if (op == JSSA_OP_DENSE && dense_pipe_layout(d, &ws->pipe_chunk, &ws->pipe_n_chunks)) ws->pipe = true;
   // the fused decode uses its own tile counts and candidate slots only; the
   // staged selection also needs the first-digit histogram and tile tables
   const bool staged = op == JSSA_OP_TOPK || (op == JSSA_OP_DECODE && !ws->pipe);
@@ -493,6 +494,9 @@ int32_t jssa_dense_decode(const jssa_desc* desc, const void* q, const void* k_ca
   if (mla)
     return to_status(launch_mla_attend(*desc, q, k_cache, nullptr, nullptr, seq_lens, out, lse,
                                        static_cast<char*>(ws), lay, as_stream(stream)));
+  if (lay.pipe)
+    return to_status(launch_pipe_dense(*desc, q, k_cache, v_cache, seq_lens, out, lse, static_cast<char*>(ws), lay,
+                                       as_stream(stream)));
   return to_status(launch_resolve_attend(*desc, false, true, q, k_cache, v_cache, nullptr, nullptr, seq_lens,
                                          out, lse, static_cast<char*>(ws), lay, as_stream(stream)));
 }

@@ -365,11 +365,12 @@ __device__ __forceinline__ void merge_row_in_launch(const AttnArgs& a, int row, 
 // ---- one row's portion of its index list, by NW waves --------------------------------
 // The fused decode's attention: the workgroup that selected a row's tokens (or
 // read them from a caller's list) attends over its portion of the list, `cnt`
-// token indices in sidx[].  Sub-chunks of CH = NW * RPW * NL tokens: every K
-// and V row of a sub-chunk is requested at once (NL 16-byte loads of each per
-// lane, lane (p, rsub) taking elements EPL p .. EPL p + EPL - 1 of rows rsub,
-// rsub + RPW, ...), the next sub-chunk's as soon as this one is done (two
-// sub-chunks in flight measured slower: more barriers for the same transfer).
+// token indices in sidx[].  Sub-chunks of CH = NW * RPW * NL tokens: the K
+// and V rows of a sub-chunk are requested with NL 16-byte loads of each per
+// lane (lane (p, rsub) taking elements EPL p .. EPL p + EPL - 1 of rows rsub,
+// rsub + RPW, ...); the next sub-chunk's K rows as soon as this one's logits
+// are formed, its V rows as soon as this one's values are weighed.  (The
+// dense decode runs the same portions over every position.)
 // Per sub-chunk:
 //   pass 1: the G heads' logits -> shared memory (bf16: v_dot2c_f32_bf16 on
 //           the packed bf16 pairs of K and of the unscaled query, products

@@ -176,6 +176,9 @@ hipError_t launch_mla_attend(const jssa_desc& d, const void* q, const void* k_ca
 // Fused decode: whether a build exists for the descriptor's shape, its tile
 // size, tiles per row and attention chunk (tokens).
 bool pipeline_layout(const jssa_desc& d, int* ts, int* n_tiles, int* chunk);
+// The dense decode on the fused shapes: the decode's attention parts over
+// every position, `chunk` positions per part, n_chunks parts per row.
+bool dense_pipe_layout(const jssa_desc& d, int* chunk, int* n_chunks);
 
 // The step's new token (one row per sequence and KV head, at t = pos[b]) and
 // the caches it is written to, for a decode that appends it itself.
@@ -206,6 +209,9 @@ hipError_t launch_select_rows(const jssa_desc& d, const int32_t* seq_lens, int32
 // The fused decode's attention parts (and their in-launch merge) on
 // caller-provided index lists (stride topk + window), with the decode
 // workspace (pipeline shapes only).
+hipError_t launch_pipe_dense(const jssa_desc& d, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* seq_lens, void* out, float* lse, char* ws_base, const Workspace& ws,
+                             hipStream_t s);
 hipError_t launch_pipe_attend(const jssa_desc& d, const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* idx, const int32_t* n_sel, void* out, float* lse, char* ws_base,
                               const Workspace& ws, hipStream_t s);

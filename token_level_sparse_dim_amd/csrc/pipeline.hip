@@ -1324,6 +1324,19 @@ struct Pipe {
     attend_part(a, sm, row, b, h, part, cnt);
     finish_row(a, row, md.kk + md.nW);
   }
+  // The dense decode: part `part` of the row attends over positions
+  // [part * chunk, (part + 1) * chunk) of the sequence (all of them selected).
+  static __device__ __forceinline__ void dense_attend(const PipeArgs& a, int row, int part, SelSmem& sm) {
+    const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
+    int n = a.at.seq_lens[b];
+    n = n < 0 ? 0 : (n > a.at.t_max ? a.at.t_max : n);
+    const int p0 = part * a.at.chunk;
+    const int cnt = p0 < n ? min(a.at.chunk, n - p0) : 0;
+    for (int i = threadIdx.x; i < cnt; i += RT) sm.sidx[i] = p0 + i;
+    __syncthreads();
+    attend_part(a, sm, row, b, h, part, cnt);
+    finish_row(a, row, n);
+  }
   // One row's whole list from candidate slots of a previous launch (the MLA
   // decode's candidate pass): the exact cut, the ascending list and the window.
   static __device__ __forceinline__ void select_list(const PipeArgs& a, int row, char* smem) {
@@ -1402,6 +1415,16 @@ __global__ __launch_bounds__(kResolveThreads, 1) void select_attend_kernel(PipeA
   Pp::select_attend(a, row, part, *reinterpret_cast<typename Pp::SelSmem*>(smem));
 }
 
+// The dense decode's parts (the decode's attention over every position).
+template <int KPT, int R, int GE, int D, int G, int KVT>
+__global__ __launch_bounds__(kResolveThreads, 1) void dense_attend_kernel(PipeArgs a) {
+  using Pp = Pipe<KPT, R, GE, D, G, KVT>;
+  __shared__ __align__(16) char smem[sizeof(typename Pp::SelSmem)];
+  int row, part;
+  if (!part_of(a, blockIdx.x, &row, &part)) return;
+  Pp::dense_attend(a, row, part, *reinterpret_cast<typename Pp::SelSmem*>(smem));
+}
+
 // Selection only, one workgroup per row (the MLA decode's rows).
 template <int KPT, int R, int GE, int D, int G, int KVT>
 __global__ __launch_bounds__(kResolveThreads, 1) void select_only_kernel(PipeArgs a) {
@@ -1461,6 +1484,17 @@ bool pipeline_layout(const jssa_desc& d, int* ts, int* n_tiles, int* chunk) {
   c = (c + 63) / 64 * 64;
   *chunk = int(c);  // list positions per part; ceil(n_max / chunk) <= kPipeMaxParts parts
   return *n_tiles <= kPipeMaxTiles;
+}
+
+bool dense_pipe_layout(const jssa_desc& d, int* chunk, int* n_chunks) {
+  const int G = d.n_q_heads / d.n_kv_heads;
+  bool ok = false;
+  for (const PipeShape& s : kPipeShapes)
+    ok |= (d.kv_dtype == s.kv && d.kp_dtype == s.kp && d.d_k == s.d && d.rank == s.r && G == s.g);
+  if (!ok || d.layout != JSSA_LAYOUT_GQA || d.t_max < 1) return false;
+  *chunk = kPipeMaxPortion;
+  *n_chunks = (d.t_max + kPipeMaxPortion - 1) / kPipeMaxPortion;
+  return true;
 }
 
 // Ticks of the device wall clock in 4 seconds (the bound on every wait).
@@ -1633,6 +1667,47 @@ hipError_t launch_select_rows(const jssa_desc& d, const int32_t* seq_lens, int32
   if ((d.t_max + kSubTile - 1) / kSubTile > kPipeMaxTiles) return hipErrorInvalidValue;
   hipLaunchKernelGGL((select_only_kernel<1, 32, 4, 128, 4, 1>), dim3(a.n_rows), dim3(kResolveThreads), 0, s, a);
   return hipGetLastError();
+}
+
+// The dense decode on the fused shapes: every position of every row, in
+// parts of kPipeMaxPortion positions, with the decode's attention and
+// in-launch merge (one 1024-thread workgroup per part, a row's parts on one
+// XCD).
+template <int KPT, int R, int D, int G, int KVT>
+static hipError_t launch_dense_t(const PipeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((dense_attend_kernel<KPT, R, G, D, G, KVT>), dim3(a.n_attn), dim3(kResolveThreads), 0, s, a);
+  return hipGetLastError();
+}
+hipError_t launch_pipe_dense(const jssa_desc& d, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* seq_lens, void* out, float* lse, char* ws_base, const Workspace& ws,
+                             hipStream_t s) {
+  if (!ws.pipe || ws.pipe_chunk != kPipeMaxPortion) return hipErrorInvalidValue;
+  PipeArgs a{};
+  AttnArgs& at = a.at;
+  at.q = q; at.k = k_cache; at.v = v_cache; at.seq_lens = seq_lens; at.out = out; at.lse = lse;
+  at.part_acc = reinterpret_cast<float*>(ws_base + ws.part_acc);
+  at.part_ml = reinterpret_cast<float*>(ws_base + ws.part_ml);
+  at.row_state = reinterpret_cast<uint32_t*>(ws_base + ws.row_state);
+  at.queue = reinterpret_cast<uint32_t*>(ws_base + ws.queue);
+  at.Hq = d.n_q_heads; at.Hkv = d.n_kv_heads; at.t_max = d.t_max;
+  at.chunk = ws.pipe_chunk; at.n_chunks = ws.pipe_n_chunks;
+  at.out_dtype = d.out_dtype; at.qscale = d.scale * kLog2e;
+  at.attend = 1;
+  a.G = d.n_q_heads / d.n_kv_heads; a.d_k = d.d_k;
+  a.n_rows = d.batch * d.n_kv_heads;
+  a.n_attn = 8 * ((a.n_rows + 7) / 8) * ws.pipe_n_chunks;
+  a.spin_ticks = wait_ticks();
+  // the attention depends on the K/V type, d and G only: one instantiation each
+  const int G = a.G;
+  if (d.kv_dtype == JSSA_BF16) {
+    if (d.d_k == 128 && G == 4) return launch_dense_t<1, 32, 128, 4, 1>(a, s);
+    if (d.d_k == 128 && G == 1) return launch_dense_t<1, 64, 128, 1, 1>(a, s);
+    if (d.d_k == 64 && G == 4) return launch_dense_t<1, 16, 64, 4, 1>(a, s);
+  } else {
+    if (d.d_k == 64 && G == 4) return launch_dense_t<0, 16, 64, 4, 0>(a, s);
+    if (d.d_k == 128 && G == 2) return launch_dense_t<0, 32, 128, 2, 0>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_pipe_attend(const jssa_desc& d, const void* q, const void* k_cache, const void* v_cache,
