@@ -565,14 +565,20 @@ struct Pipe {
   // stay in flight, step st + kPipePF being requested as soon as step st is
   // scored.  Loads carry no per-lane branch (tokens past the end re-read the
   // last one).
+  // `late()` runs once, before the last whole group of steps (or before the
+  // remaining steps when there is no whole group): a load it issues is in
+  // flight behind the range's last key loads.
+  template <typename Late>
   static __device__ void scan_keys(const char* kr, int t_begin, int t_end, const QFrag<KPT, R, GE>& qf,
-                                   uint4 (&pre)[kPipePF][S::U], uint32_t* keys) {
+                                   uint4 (&pre)[kPipePF][S::U], uint32_t* keys, Late late) {
     const int n_steps = (t_end - t_begin + S::PER_ITER - 1) / S::PER_ITER;
     // whole groups of kPipePF steps with every reload unconditional (past the
     // end they re-read the last token), so the wait before each step's use
     // counts the same loads on every path; then the remaining steps
     int st0 = 0;
+    if (n_steps < kPipePF) late();
     for (; st0 + kPipePF <= n_steps; st0 += kPipePF) {
+      if (st0 + 2 * kPipePF > n_steps) late();
 #pragma unroll
       for (int j = 0; j < kPipePF; ++j) {
         uint32_t* kst = keys + (st0 + j) * S::PER_ITER;
@@ -607,7 +613,10 @@ struct Pipe {
   // the tile counts (plain stores: read after the launch boundary, or by the
   // workgroup that wrote them).  Each wave compacts whole tiles in rounds of 64
   // tokens (lane l takes token 64 k + l of round k, so the key reads are
-  // conflict-free); a ballot per round gives the positions.
+  // conflict-free); a ballot per round gives the positions.  A tile's keys
+  // are all read into registers before its first round: each round's store
+  // sits behind a branch, and a shared-memory read issued after one would
+  // wait out its full latency in every round.
   template <int NW = 4>
   static __device__ void emit_keys(const PipeArgs& a, int row, int t_begin, int t_end, uint32_t thr,
                                    const uint32_t* keys) {
@@ -621,11 +630,14 @@ struct Pipe {
       const int n_tok = min(TS, t_end - t0);
       const uint32_t* kk = keys + s * TS;
       uint64_t* slot = a.cand + size_t(row) * a.at.t_max + size_t(tile0 + s) * TS;
+      uint32_t kv[PL];
+#pragma unroll
+      for (int k = 0; k < PL; ++k) kv[k] = kk[k * 64 + lane];
       uint32_t pos = 0;
 #pragma unroll
       for (int k = 0; k < PL; ++k) {
         const int i = k * 64 + lane;
-        const uint32_t key = kk[i];
+        const uint32_t key = kv[k];
         const bool take = i < n_tok && key >= thr;
         const unsigned long long m = __ballot(take);
         if (take) slot[pos + uint32_t(__popcll(m & below))] = (uint64_t(uint32_t(t0 + i)) << 32) | key;
@@ -655,7 +667,11 @@ struct Pipe {
     load_qfrag<KPT, R, GE>([&](int i) { return sm.qp.qp[i]; }, G, qf);
     __syncthreads();  // the projection's shared memory becomes the key buffer
     for (;;) {
-      scan_keys(kr, tb, te, qf, pre, sm.keys);
+      // the row's threshold is read again behind the first item's last key
+      // loads, so it is usually in hand when the item's keys are
+      scan_keys(kr, tb, te, qf, pre, sm.keys, [&] {
+        if (tb == t_begin && threadIdx.x == 0 && (lw >> 32) == 0) lw = consume(l_word(a, row));
+      });
       if (tb == t_begin) {  // the row's threshold (its sample was handed out before any score work)
         if (threadIdx.x == 0) {
           while ((lw >> 32) == 0 && !past(deadline)) {
@@ -1492,8 +1508,17 @@ bool dense_pipe_layout(const jssa_desc& d, int* chunk, int* n_chunks) {
   for (const PipeShape& s : kPipeShapes)
     ok |= (d.kv_dtype == s.kv && d.kp_dtype == s.kp && d.d_k == s.d && d.rank == s.r && G == s.g);
   if (!ok || d.layout != JSSA_LAYOUT_GQA || d.t_max < 1) return false;
-  *chunk = kPipeMaxPortion;
-  *n_chunks = (d.t_max + kPipeMaxPortion - 1) / kPipeMaxPortion;
+  // parts of at most kPipeMaxPortion positions, and about kPipePartTarget
+  // workgroups in all when the rows are short (a cache of a few thousand
+  // positions, such as the packed rows of the gather-then-attend baseline,
+  // gets the sparse decode's part size instead of one workgroup per row)
+  const int64_t rows = int64_t(d.batch) * d.n_kv_heads;
+  const int64_t parts = (kPipePartTarget + rows - 1) / rows;
+  int64_t c = (int64_t(d.t_max) + parts - 1) / parts;
+  c = (c + 63) / 64 * 64;
+  if (c > kPipeMaxPortion) c = kPipeMaxPortion;
+  *chunk = int(c);
+  *n_chunks = int((d.t_max + c - 1) / c);
   return true;
 }
 
@@ -1681,7 +1706,7 @@ static hipError_t launch_dense_t(const PipeArgs& a, hipStream_t s) {
 hipError_t launch_pipe_dense(const jssa_desc& d, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* seq_lens, void* out, float* lse, char* ws_base, const Workspace& ws,
                              hipStream_t s) {
-  if (!ws.pipe || ws.pipe_chunk != kPipeMaxPortion) return hipErrorInvalidValue;
+  if (!ws.pipe || ws.pipe_chunk < 1 || ws.pipe_chunk > kPipeMaxPortion) return hipErrorInvalidValue;
   PipeArgs a{};
   AttnArgs& at = a.at;
   at.q = q; at.k = k_cache; at.v = v_cache; at.seq_lens = seq_lens; at.out = out; at.lse = lse;
