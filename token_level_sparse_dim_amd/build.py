@@ -67,7 +67,7 @@ def source_digest(name: str) -> str:
     import hashlib
     h = hashlib.sha256()
     for f in (name, "jssa_device.hpp", "jssa_internal.hpp", "select_common.hpp", "score_core.hpp",
-              "attn_core.hpp", "resolve.hpp"):
+              "attn_core.hpp", "resolve.hpp", "append_core.hpp"):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -381,14 +381,17 @@ int32_t decode_launch(const jssa_desc* desc, const void* q, const float* P, cons
   if (lay.pipe)
     return to_status(launch_pipeline(*desc, q, P, kp_cache, k_cache, v_cache, seq_lens, out, lse, idx, n_sel,
                                      base, lay, nt, ev, s));
-  if (nt) {  // the staged launches: the append is a launch of its own, first
+  // MLA (MAX): the step's append and the query projection share the first launch
+  const bool prep = mla && nt && mla_prep_fusable(*desc);
+  if (nt && !prep) {  // the staged launches: the append is a launch of its own, first
     const hipError_t ea = launch_append(*desc, nt->k_new, nt->v_new, 1, nt->pos, P, nt->k_cache, nt->v_cache,
                                         nt->kp_cache, s);
     if (ea != hipSuccess) return to_status(ea);
   }
   auto mark = [&](int i) { return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess; };
   if (mla) {
-    hipError_t e = launch_mla_qproj(*desc, q, P, base, lay, s);
+    hipError_t e = prep ? launch_mla_prep(*desc, nt->k_new, nt->pos, P, nt->k_cache, nt->kp_cache, q, base, lay, s)
+                        : launch_mla_qproj(*desc, q, P, base, lay, s);
     // events [0] and [1] take the score scan kernel's own start and end
     if (e == hipSuccess) e = launch_mla_scan(*desc, kp_cache, seq_lens, scores, true, base, lay, s, ev);
     if (e == hipSuccess) e = launch_candidates(*desc, scores, seq_lens, base, lay, s, true);

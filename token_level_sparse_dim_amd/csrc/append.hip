@@ -4,24 +4,13 @@
 // the lane walks its key row in 16-byte pieces and accumulates the rank-R
 // projection in fp32; the basis rows are wave-uniform, so they come through
 // the scalar cache.
+#include "append_core.hpp"
 #include "jssa_device.hpp"
 #include "jssa_internal.hpp"
 
 namespace jssa {
 
 constexpr int kAppendRowsMax = 64;  // up to this many new rows: one workgroup per row
-
-struct AppendArgs {
-  const void* k_new;
-  const void* v_new;
-  const int32_t* pos;
-  const float* P;
-  void* k_cache;
-  void* v_cache;
-  void* kp;
-  int n_new, Hkv, d_k, d_v, t_max;
-  int mla;
-};
 
 template <int KVT, int KPT, int R>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
@@ -201,49 +190,12 @@ __global__ __launch_bounds__(256) void append_new_kernel(AppendArgs a) {
   }
 }
 
-// Few new rows of a wide key (the MLA latent row, D = 576): one workgroup of
-// R * PARTS = 1024 threads per row, thread (o, part) with an fma chain over its
-// D / PARTS slice of d, every load of the slice requested at once; the parts
-// are then summed in order.  (A 256-thread workgroup walks 144 dependent basis
-// loads per thread.)
+// Few new rows of a wide key (the MLA latent row): one workgroup per row
+// (append_wide_row).
 template <int KVT, int KPT, int R, int D, int PARTS>
 __global__ __launch_bounds__(R * PARTS) void append_wide_kernel(AppendArgs a) {
-  constexpr int EB = Elem<KVT>::bytes, NT = R * PARTS, DPER = D / PARTS;
-  static_assert(D % PARTS == 0 && NT <= 1024, "slices");
-  __shared__ float s_part[NT];
-  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int o = threadIdx.x % R, part = threadIdx.x / R;
-  const int d0 = part * DPER;
-  const char* src = reinterpret_cast<const char*>(a.k_new) + ((size_t(b) * a.n_new + j) * a.Hkv + h) * D * EB;
-  const float* Pc = a.P + size_t(h) * D * R + o;
-  float kv[DPER], pv[DPER];
-#pragma unroll
-  for (int i = 0; i < DPER; ++i) {
-    if constexpr (KVT == 1) kv[i] = bf16_lo(uint32_t(reinterpret_cast<const uint16_t*>(src)[d0 + i]));
-    else kv[i] = reinterpret_cast<const float*>(src)[d0 + i];
-    pv[i] = Pc[size_t(d0 + i) * R];
-  }
-  constexpr int N16 = D * EB / 16;
-  uint4 kc16 = make_uint4(0u, 0u, 0u, 0u);
-  if (int(threadIdx.x) < N16) kc16 = load16(src + size_t(threadIdx.x) * 16);
-  const int t = a.pos[b] + j;
-  const bool ok = t >= 0 && t < a.t_max;
-  float acc = 0.f;
-#pragma unroll
-  for (int i = 0; i < DPER; ++i) acc = fmaf(kv[i], pv[i], acc);
-  s_part[threadIdx.x] = acc;
-  if (ok && int(threadIdx.x) < N16)
-    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(a.k_cache) + ((size_t(b) * a.t_max + t) * a.Hkv + h) * D * EB +
-                              size_t(threadIdx.x) * 16) = kc16;
-  __syncthreads();
-  if (ok && int(threadIdx.x) < R) {
-    float sum = 0.f;
-    for (int pp = 0; pp < PARTS; ++pp) sum += s_part[pp * R + threadIdx.x];
-    char* kprow = reinterpret_cast<char*>(a.kp) + ((size_t(b) * a.Hkv + h) * a.t_max + t) * R * Elem<KPT>::bytes;
-    if constexpr (KPT == 1) reinterpret_cast<uint16_t*>(kprow)[threadIdx.x] = f32_to_bf16_rne(sum);
-    else if constexpr (KPT == 2) reinterpret_cast<uint8_t*>(kprow)[threadIdx.x] = uint8_t(f32_to_e4m3_sat(sum));
-    else reinterpret_cast<float*>(kprow)[threadIdx.x] = sum;
-  }
+  __shared__ float s_part[R * PARTS];
+  append_wide_row<KVT, KPT, R, D, PARTS>(a, blockIdx.x, blockIdx.y, blockIdx.z, s_part);
 }
 
 template <int KVT, int KPT>

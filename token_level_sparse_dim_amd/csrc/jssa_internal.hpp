@@ -163,6 +163,10 @@ hipError_t launch_gather_kv(const jssa_desc& d, const void* k_cache, const void*
 // first-digit histogram and threshold state.
 hipError_t launch_mla_qproj(const jssa_desc& d, const void* q, const float* P, char* ws_base, const Workspace& ws,
                             hipStream_t s);
+bool mla_prep_fusable(const jssa_desc& d);
+hipError_t launch_mla_prep(const jssa_desc& d, const void* k_new, const int32_t* pos, const float* P,
+                           void* k_cache, void* kp_cache, const void* q, char* ws_base, const Workspace& ws,
+                           hipStream_t s);
 hipError_t launch_mla_scan(const jssa_desc& d, const void* kp, const int32_t* seq_lens, float* scores, bool hist,
                            char* ws_base, const Workspace& ws, hipStream_t s,
                            void* const* ev = nullptr);

@@ -19,6 +19,7 @@
 // (Operand layout of v_mfma_f32_16x16x32_bf16: see mfma16 in jssa_device.hpp.)
 #include <hip/hip_ext.h>
 
+#include "append_core.hpp"
 #include "jssa_device.hpp"
 #include "jssa_internal.hpp"
 #include "select_common.hpp"
@@ -67,10 +68,9 @@ __device__ __forceinline__ size_t qfrag_at(int b, int MT, int mt, int m, int r, 
 // accumulation (|P - P_hi - P_lo| <= 2^-17 |P|).  All loads are issued
 // before the first product.
 template <int R>
-__global__ __launch_bounds__(64) void mla_qproj_kernel(MlaQArgs a) {
+__device__ __forceinline__ void qproj_wave(const MlaQArgs& a, int mt, int nt, int b, int lane) {
   constexpr int KS = kMlaDk / 32;
-  const int mt = blockIdx.x, nt = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x, g = lane >> 4, n16 = lane & 15;
+  const int g = lane >> 4, n16 = lane & 15;
   const uint16_t* qrow = a.q + (size_t(b) * a.Hq + 16 * mt + n16) * kMlaDk + 8 * g;
   const float* pcol = a.P + 16 * nt + n16;
   u32x4_t qa[KS];
@@ -98,6 +98,35 @@ __global__ __launch_bounds__(64) void mla_qproj_kernel(MlaQArgs a) {
     a.qf[qfrag_at<R>(b, a.MT, mt, 4 * g + i, 16 * nt + n16, 0)] = hi;
     a.qf[qfrag_at<R>(b, a.MT, mt, 4 * g + i, 16 * nt + n16, 1)] = lo;
   }
+}
+template <int R>
+__global__ __launch_bounds__(64) void mla_qproj_kernel(MlaQArgs a) {
+  qproj_wave<R>(a, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x);
+}
+
+// The one-call step's first launch (MAX): workgroups 0 .. B-1 append sequence
+// b's new latent row (the arithmetic of the stand-alone append), the others
+// run the query projection's waves, qw per workgroup (wave w: M-tile w % MT,
+// coordinate tile (w / MT) % (R / 16), sequence w / (MT R / 16)); the rest of
+// their waves exit at once.  The two are independent, so one launch replaces
+// two.  (Two projection waves per workgroup spread them over about 128
+// compute units; sixteen queued their 162 loads each on 16 compute units and
+// made the launch slower than the two it replaces.)
+constexpr int kMlaPrepWaves = 2;
+template <int R, int PARTS>
+__global__ __launch_bounds__(R * PARTS) void mla_prep_kernel(AppendArgs ap, MlaQArgs qa, int n_append, int qw) {
+  static_assert(R * PARTS == 1024, "one 1024-thread workgroup per appended row");
+  __shared__ float s_part[R * PARTS];
+  if (int(blockIdx.x) < n_append) {
+    append_wide_row<1, 1, R, kMlaDk, PARTS>(ap, 0, 0, blockIdx.x, s_part);
+    return;
+  }
+  if (int(threadIdx.x >> 6) >= qw) return;
+  const int w = (int(blockIdx.x) - n_append) * qw + int(threadIdx.x >> 6);
+  const int NT = R / 16, per_b = qa.MT * NT;
+  const int b = w / per_b, rem = w - b * per_b;
+  if (b >= n_append) return;  // the last workgroup's spare waves (B sequences)
+  qproj_wave<R>(qa, rem % qa.MT, rem / qa.MT, b, int(threadIdx.x & 63));
 }
 
 // MEAN: the group-mean query (1/Hq) sum_h q_h, projected once (linearity:
@@ -545,7 +574,11 @@ __global__ __launch_bounds__(256, 1) void mla_attn_kernel(MlaAttnArgs a) {
 }
 
 // Log-sum-exp merge of the chunk partials of one (sequence, head), in chunk
-// order; out = 0 and lse = -inf when the sequence attends over nothing.
+// order; out = 0 and lse = -inf when the sequence attends over nothing.  The
+// partials are read in batches of kMlaMergeBatch chunks with every load of a
+// batch issued at once (chunks past the live count re-read the last live one
+// and carry weight 0), and each batch is folded into a running (M, L, o).
+constexpr int kMlaMergeBatch = 16;
 template <bool INDEXED>
 __global__ __launch_bounds__(128) void mla_combine_kernel(MlaAttnArgs a) {
   const int h = blockIdx.x, b = blockIdx.y;
@@ -557,18 +590,35 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(MlaAttnArgs a) {
   if (n_live > 0) {
     const float* ml = a.part_ml + (size_t(b) * a.n_chunks * a.Hq + h) * 2;
     const size_t cstride = size_t(a.Hq) * 2;
-    float M = -INFINITY;
-    for (int c = 0; c < n_live; ++c) M = fmaxf(M, ml[c * cstride]);
-    float L = 0.f;
     const float* po = a.part_o + (size_t(b) * a.n_chunks * a.Hq + h) * kMlaDv + 4 * threadIdx.x;
-    for (int c = 0; c < n_live; ++c) {
-      const float w = mla_exp2(ml[c * cstride] - M);
-      L = fmaf(w, ml[c * cstride + 1], L);
-      const float4 v = *reinterpret_cast<const float4*>(po + size_t(c) * a.Hq * kMlaDv);
-      o[0] = fmaf(w, v.x, o[0]);
-      o[1] = fmaf(w, v.y, o[1]);
-      o[2] = fmaf(w, v.z, o[2]);
-      o[3] = fmaf(w, v.w, o[3]);
+    float M = -INFINITY, L = 0.f;
+    for (int c0 = 0; c0 < n_live; c0 += kMlaMergeBatch) {
+      float m[kMlaMergeBatch], l[kMlaMergeBatch];
+      float4 v[kMlaMergeBatch];
+#pragma unroll
+      for (int i = 0; i < kMlaMergeBatch; ++i) {
+        const int c = min(c0 + i, n_live - 1);
+        m[i] = ml[c * cstride];
+        l[i] = ml[c * cstride + 1];
+        v[i] = *reinterpret_cast<const float4*>(po + size_t(c) * a.Hq * kMlaDv);
+      }
+      float Mb = M;
+#pragma unroll
+      for (int i = 0; i < kMlaMergeBatch; ++i) Mb = c0 + i < n_live ? fmaxf(Mb, m[i]) : Mb;
+      const float sc = (M == -INFINITY) ? 0.f : mla_exp2(M - Mb);
+      L *= sc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] *= sc;
+#pragma unroll
+      for (int i = 0; i < kMlaMergeBatch; ++i) {
+        const float w = (c0 + i < n_live) ? mla_exp2(m[i] - Mb) : 0.f;
+        L = fmaf(w, l[i], L);
+        o[0] = fmaf(w, v[i].x, o[0]);
+        o[1] = fmaf(w, v[i].y, o[1]);
+        o[2] = fmaf(w, v[i].z, o[2]);
+        o[3] = fmaf(w, v[i].w, o[3]);
+      }
+      M = Mb;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] /= L;
@@ -607,6 +657,30 @@ hipError_t launch_mla_qproj(const jssa_desc& d, const void* q, const float* P, c
     if (mean) hipLaunchKernelGGL(mla_qproj_mean_kernel<32>, dim3(1, d.batch), dim3(256), 0, s, qa);
     else hipLaunchKernelGGL(mla_qproj_kernel<32>, dim3(d.n_q_heads / 16, 2, d.batch), dim3(64), 0, s, qa);
   }
+  return hipGetLastError();
+}
+
+// The step's new latent rows and the query projection in one launch (MAX
+// reduction, bf16 rows, one new row per sequence); false when the shape takes
+// the separate launches.
+bool mla_prep_fusable(const jssa_desc& d) {
+  return d.layout == JSSA_LAYOUT_MLA && d.reduce == JSSA_REDUCE_MAX && d.kv_dtype == JSSA_BF16 &&
+         d.kp_dtype == JSSA_BF16 && d.d_k == kMlaDk && d.n_kv_heads == 1 && (d.rank == 64 || d.rank == 32);
+}
+hipError_t launch_mla_prep(const jssa_desc& d, const void* k_new, const int32_t* pos, const float* P,
+                           void* k_cache, void* kp_cache, const void* q, char* ws_base, const Workspace& ws,
+                           hipStream_t s) {
+  if (!mla_prep_fusable(d)) return hipErrorInvalidValue;
+  AppendArgs ap;
+  ap.k_new = k_new; ap.v_new = nullptr; ap.pos = pos; ap.P = P;
+  ap.k_cache = k_cache; ap.v_cache = nullptr; ap.kp = kp_cache;
+  ap.n_new = 1; ap.Hkv = 1; ap.d_k = d.d_k; ap.d_v = d.d_v; ap.t_max = d.t_max; ap.mla = 1;
+  const MlaQArgs qa = qproj_args(d, q, P, ws_base, ws);
+  const int q_waves = d.batch * qa.MT * (d.rank / 16);
+  const int qw = kMlaPrepWaves;
+  const dim3 grid(unsigned(d.batch + (q_waves + qw - 1) / qw));
+  if (d.rank == 64) hipLaunchKernelGGL((mla_prep_kernel<64, 16>), grid, dim3(1024), 0, s, ap, qa, d.batch, qw);
+  else hipLaunchKernelGGL((mla_prep_kernel<32, 32>), grid, dim3(1024), 0, s, ap, qa, d.batch, qw);
   return hipGetLastError();
 }
 
