@@ -14,7 +14,10 @@ written), and mixed over the batch.  The new key is either a needle (aligned
 with its query head's projection and long: selected if it is scored from the
 stored row) or a zero row written over a planted needle (selected only if a
 stale projected row were scored).  Everything is compared bit for bit: the
-caches, the index lists, the outputs and the log-sum-exp values."""
+caches, the index lists, the outputs and the log-sum-exp values.  In the MLA
+layout (MAX) the step's first launch appends the new latent rows and projects
+the queries together; the two MLA cases take both of its shapes (rank 64 with
+64 heads, rank 32 with 128 heads)."""
 import numpy as np
 import pytest
 import torch
@@ -39,6 +42,9 @@ CASES = {
     "staged": scaled(WORKLOADS["llama8b_32k"], batch=2, n_q_heads=16, n_kv_heads=8, t_max=5000,
                      topk=128),  # G = 2 in bf16: no fused build
     "mla": scaled(WORKLOADS["mla"], batch=2, n_q_heads=64, t_max=6000, topk=256, n_needles=8),
+    # 128 heads at rank 32: the step's first launch with two coordinate tiles
+    # per M-tile and an odd batch (the projection waves end mid-workgroup)
+    "mla_r32": scaled(WORKLOADS["mla"], batch=3, rank=32, t_max=5000, topk=200, n_needles=8),
 }
 WHERE = ["early", "late", "last", "mixed"]
 _CACHE = {}

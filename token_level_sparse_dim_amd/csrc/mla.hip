@@ -432,13 +432,16 @@ __global__ __launch_bounds__(256, 1) void mla_attn_kernel(MlaAttnArgs a) {
   __syncthreads();
 
   const uint16_t* kvb = a.kv + size_t(b) * a.t_max * kMlaDk;
-  // rows: A operand; row m = row 16 wave + n16 of the sub-block
+  // rows: A operand; row m = row 16 wave + n16 of the sub-block.  Plain
+  // (temporal) loads: the four head groups of a chunk run on one XCD and read
+  // the same rows, so three of the four find them in its L2 (non-temporal
+  // loads, which do not keep them there, made the launch about 4 us slower).
   auto load_rows = [&](int sb, u32x4_t (&kf)[KS]) {
     const int p = min(sb * 64 + 16 * wave + n16, cnt - 1);
     const int t = INDEXED ? S.idx[p] : c0 + p;
     const uint16_t* row = kvb + size_t(t) * kMlaDk + 8 * g;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) kf[s] = ld16_nt(row + 32 * s);
+    for (int s = 0; s < KS; ++s) kf[s] = ld16(row + 32 * s);
   };
 
   f32x4_t acc[2][8];

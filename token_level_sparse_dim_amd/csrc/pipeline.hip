@@ -69,6 +69,10 @@ constexpr int kResolveThreads = 1024;  // threads of a resolve workgroup
 #define JSSA_PORTION_NL 2
 #endif
 constexpr int kPortionNL = JSSA_PORTION_NL;  // K and V row loads per lane per attention sub-chunk
+#ifndef JSSA_DENSE_NL
+#define JSSA_DENSE_NL 2
+#endif
+constexpr int kDenseNL = JSSA_DENSE_NL;  // the same for the dense decode's parts
 constexpr int kPipeMaxPortion = 2048;  // list positions per select/attend workgroup at most
 constexpr int kPipeMaxParts = 16;      // select/attend workgroups per row at most
 constexpr int kPipePartTarget = 256;   // select/attend workgroups a launch aims for (one per CU)
@@ -1342,7 +1346,13 @@ struct Pipe {
   }
   // The dense decode: part `part` of the row attends over positions
   // [part * chunk, (part + 1) * chunk) of the sequence (all of them selected).
-  static __device__ __forceinline__ void dense_attend(const PipeArgs& a, int row, int part, SelSmem& sm) {
+  // (It needs no selection state: its own shared memory is the attention's
+  // and the positions'.)
+  struct DenseSmem {
+    PortionSmem<KVT, D, G, kAttnNW, kDenseNL> at;
+    int sidx[kPipeMaxPortion];
+  };
+  static __device__ __forceinline__ void dense_attend(const PipeArgs& a, int row, int part, DenseSmem& sm) {
     const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
     int n = a.at.seq_lens[b];
     n = n < 0 ? 0 : (n > a.at.t_max ? a.at.t_max : n);
@@ -1350,7 +1360,8 @@ struct Pipe {
     const int cnt = p0 < n ? min(a.at.chunk, n - p0) : 0;
     for (int i = threadIdx.x; i < cnt; i += RT) sm.sidx[i] = p0 + i;
     __syncthreads();
-    attend_part(a, sm, row, b, h, part, cnt);
+    if (cnt > 0)  // uniform over the workgroup
+      attend_portion<KVT, D, G, kAttnNW, kDenseNL, true>(a.at, sm.at, sm.sidx, row, b, h, part, cnt);
     finish_row(a, row, n);
   }
   // One row's whole list from candidate slots of a previous launch (the MLA
@@ -1435,10 +1446,10 @@ __global__ __launch_bounds__(kResolveThreads, 1) void select_attend_kernel(PipeA
 template <int KPT, int R, int GE, int D, int G, int KVT>
 __global__ __launch_bounds__(kResolveThreads, 1) void dense_attend_kernel(PipeArgs a) {
   using Pp = Pipe<KPT, R, GE, D, G, KVT>;
-  __shared__ __align__(16) char smem[sizeof(typename Pp::SelSmem)];
+  __shared__ __align__(16) char smem[sizeof(typename Pp::DenseSmem)];
   int row, part;
   if (!part_of(a, blockIdx.x, &row, &part)) return;
-  Pp::dense_attend(a, row, part, *reinterpret_cast<typename Pp::SelSmem*>(smem));
+  Pp::dense_attend(a, row, part, *reinterpret_cast<typename Pp::DenseSmem*>(smem));
 }
 
 // Selection only, one workgroup per row (the MLA decode's rows).
