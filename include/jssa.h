@@ -151,10 +151,11 @@ int32_t jssa_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *   status_out[JSSA_STATUS_EXACT_REDO]    rows re-selected exactly because the
  *       sampled threshold of the fused decode admitted fewer than k tokens
  *       (results stay exact; a count only).
- *   status_out[JSSA_STATUS_RANGE_SPLIT]   fused decode scans that had fewer
- *       score workgroups than rows to score, so that the rows' tiles were
- *       split into contiguous ranges across rows instead of per row (a count
- *       only).
+ *   status_out[JSSA_STATUS_RANGE_SPLIT]   fused decode scans whose rows'
+ *       tiles were split into equal contiguous ranges across rows instead of
+ *       per row: fewer score workgroups than rows, or rows of unequal lengths
+ *       whose per-row split would leave some runs more than a tile longer
+ *       than the even share (a count only).
  *   status_out[JSSA_STATUS_GLOBAL_CUT]    rows of the fused decode whose
  *       candidates exceeded shared memory, so that the exact cut ran over
  *       global memory (a count only).

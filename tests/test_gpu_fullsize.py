@@ -200,12 +200,13 @@ def test_full_ctx128k_step_k512():
 
 def test_full_hybrid_ragged_step():
     """The hybrid workload at full size: 16 sequences of 8K..128K tokens, the
-    last 512 always attended, k = 2048 of the rest.  Each row's tiles are split
-    over score workgroups in proportion to its length (a 128K row gets about
-    fifteen times the workgroups of an 8K row); the new token is the last
-    candidate of each sequence (W + 1 from the end), in the last tile of its
-    row's last workgroup.  Checked: two KV heads of every sequence."""
+    last 512 always attended, k = 2048 of the rest.  Whole score workgroups per
+    row would give a 128K row's runs 16 tiles against an even share of 14, so
+    the rows' tiles are laid end to end and split into equal contiguous ranges
+    (some workgroups score the end of one row and the start of the next); the
+    new token is the last candidate of each sequence (W + 1 from the end), in
+    the last tile of its row.  Checked: two KV heads of every sequence."""
     w = WORKLOADS["hybrid_ragged"]
     st = _run_full(w, [(b, h) for b in range(w.batch) for h in (b % 8, (b + 3) % 8)],
                    pos_of=lambda L: L - w.window - 1)
-    assert st[J.STATUS_RANGE_SPLIT] == 0, st  # one row per score workgroup
+    assert st[J.STATUS_RANGE_SPLIT] > 0, st  # ranges across rows

@@ -791,12 +791,24 @@ struct Pipe {
     const uint32_t N = seq_total(a, fs, [&](int b) { return Hkv * uint32_t(tiles_of(a, b)); });
     const uint32_t rows_live = seq_total(a, fs, [&](int b) { return tiles_of(a, b) ? Hkv : 0u; });
     if (N == 0) return;
-    if (W >= rows_live) {
-      const uint64_t spare = W - rows_live;
-      auto per_row = [&](int b) -> uint32_t {
-        const uint32_t t = uint32_t(tiles_of(a, b));
-        return t ? uint32_t(spare * t / N) + 1u : 0u;
-      };
+    const uint64_t spare = W >= rows_live ? W - rows_live : 0u;
+    auto per_row = [&](int b) -> uint32_t {
+      const uint32_t t = uint32_t(tiles_of(a, b));
+      return t ? uint32_t(spare * t / N) + 1u : 0u;
+    };
+    // Whole workgroups per row round each row's share: a long row's runs can
+    // end up several tiles longer than the even share ceil(N / W) (16 against
+    // 14 tiles in a batch of 8K..128K rows), and the scan lasts as long as its
+    // longest run.  Then the equal contiguous ranges below serve better, at
+    // the cost of a second query projection in the workgroups whose range
+    // crosses a row boundary.
+    const uint32_t even = (N + W - 1) / W;
+    const bool uneven =
+        W >= rows_live && seq_total(a, fs, [&](int b) {
+          const uint32_t t = uint32_t(tiles_of(a, b)), w = per_row(b);
+          return t && (t + w - 1) / w > even + 1u ? 1u : 0u;
+        }) != 0u;
+    if (W >= rows_live && !uneven) {
       if (uint32_t(s) >= seq_total(a, fs, [&](int b) { return Hkv * per_row(b); })) return;
       int b;
       uint32_t o;
@@ -808,7 +820,8 @@ struct Pipe {
       if (t1 > t0) score_range(a, b * a.at.Hkv + int(h), t0 * TS, min(t1 * TS, md.n_cand), smem, deadline);
       return;
     }
-    // fewer score workgroups than rows: equal contiguous ranges of the rows' tiles laid end to end
+    // fewer score workgroups than rows, or an uneven per-row split: equal
+    // contiguous ranges of the rows' tiles laid end to end
     if (s == 0 && threadIdx.x == 0) __hip_atomic_fetch_add(a.at.queue + QW_RANGE, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t g = uint32_t(uint64_t(N) * uint32_t(s) / W);
     const uint32_t g1 = uint32_t(uint64_t(N) * uint32_t(s + 1) / W);
