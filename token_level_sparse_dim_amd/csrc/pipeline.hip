@@ -656,13 +656,23 @@ struct Pipe {
   // kPipeMaxItem tokens (the key buffer), and emits each item's candidates.
   // The row's threshold is waited for after the first item's scan.
   static __device__ void score_range(const PipeArgs& a, int row, int t_begin, int t_end, char* smem,
-                                     uint64_t deadline) {
+                                     uint64_t deadline, bool split_tail) {
     const int b = row / a.at.Hkv, h = row - b * a.at.Hkv;
     ScoreSmem& sm = *reinterpret_cast<ScoreSmem*>(smem);
     const char* kr = kp_row(a, row);
     uint4 pre[kPipePF][S::U];
     uint64_t lw = 0;
-    int tb = t_begin, te = min(t_begin + kPipeMaxItem, t_end);
+    // With split_tail, a range of four tiles or more keeps its last two
+    // tiles for an item of their own: the items before emit their candidates
+    // while the next item's first keys are in flight, so only two tiles'
+    // emission follows the range's last key loads.  (The segments of the
+    // range split, already cut at row boundaries, keep whole items: each
+    // extra item boundary drains the load pipeline once.  So do FP8 keys,
+    // whose scan is bound by instruction issue rather than by the tail.)
+    const int n_t = (t_end - t_begin + TS - 1) / TS;
+    const int tail0 = split_tail && !S::F8 && n_t >= 4 ? t_begin + (n_t - 2) * TS : t_end;
+    auto item_end = [&](int x) { return x < tail0 ? min(x + kPipeMaxItem, tail0) : t_end; };
+    int tb = t_begin, te = item_end(t_begin);
     project_query_staged<D, R, G>(a, b, h, sm.qp, [&] {
       load_first(kr, tb, te, pre);  // in flight during the query projection
       if (threadIdx.x == 0) lw = consume(l_word(a, row));
@@ -689,11 +699,12 @@ struct Pipe {
       }
       rescore_new(a, row, b, kr, tb, te, qf, sm.keys, deadline);
       __syncthreads();
+      const int nb = te, ne = te < t_end ? item_end(te) : t_end;
+      if (nb < t_end) load_first(kr, nb, ne, pre);  // in flight during the emission
       emit_keys(a, row, tb, te, sm.l_key, sm.keys);
-      if (te >= t_end) return;
-      tb = te;
-      te = min(tb + kPipeMaxItem, t_end);
-      load_first(kr, tb, te, pre);
+      if (nb >= t_end) return;
+      tb = nb;
+      te = ne;
       __syncthreads();  // every wave is done with keys[]
     }
   }
@@ -783,7 +794,7 @@ struct Pipe {
           const int j = s / a.n_rows, r = (s - j * a.n_rows + j) % a.n_rows;
           const int bq = r / a.at.Hkv;
           const int n_cand = B <= 64 ? __shfl(lane_cand, bq) : row_mode(a, bq).n_cand;
-          score_range(a, r, j * it * TS, min(min(j * it + it, nt0) * TS, n_cand), smem, deadline);
+          score_range(a, r, j * it * TS, min(min(j * it + it, nt0) * TS, n_cand), smem, deadline, true);
           return;
         }
       }
@@ -817,7 +828,7 @@ struct Pipe {
       const RowMode md = row_mode(a, b);
       const uint32_t nt = uint32_t(tiles_of(a, b));
       const int t0 = int(uint64_t(nt) * j / w), t1 = int(uint64_t(nt) * (j + 1) / w);
-      if (t1 > t0) score_range(a, b * a.at.Hkv + int(h), t0 * TS, min(t1 * TS, md.n_cand), smem, deadline);
+      if (t1 > t0) score_range(a, b * a.at.Hkv + int(h), t0 * TS, min(t1 * TS, md.n_cand), smem, deadline, true);
       return;
     }
     // fewer score workgroups than rows, or an uneven per-row split: equal
@@ -839,7 +850,8 @@ struct Pipe {
       }
       const uint32_t h = o / nt, t0 = o - h * nt;
       const uint32_t seg = min(nt - t0, g1 - g);
-      score_range(a, b * a.at.Hkv + int(h), int(t0) * TS, min(int(t0 + seg) * TS, md.n_cand), smem, deadline);
+      score_range(a, b * a.at.Hkv + int(h), int(t0) * TS, min(int(t0 + seg) * TS, md.n_cand), smem, deadline,
+                  false);
       __syncthreads();
       g += seg;
       o += seg;
