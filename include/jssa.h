@@ -281,8 +281,9 @@ int32_t jssa_decode_profiled(const jssa_desc* desc, const void* q, const float* 
  * row's threshold, then writes the new K/V rows and the projected key and
  * marks the row as appended; the score run whose range holds pos[b] waits for
  * that mark and re-scores the one step that holds pos[b] from the stored row;
- * no launch of its own.  Other shapes launch the append first (before
- * stage_events[0]).  k_new / v_new: [B, 1, Hkv, d] (MLA: [B, 1, 1, d_k], v_new
+ * no launch of its own.  Other shapes launch the append first, before
+ * stage_events[0] (the MLA layout with the MAX reduction in one launch with
+ * the query projection).  k_new / v_new: [B, 1, Hkv, d] (MLA: [B, 1, 1, d_k], v_new
  * and v_cache unused, may be NULL); pos: int32 [B] device array; positions
  * outside [0, t_max) are not written.  The caches are read and written in
  * place.  stage_events may be NULL, else as for jssa_decode_profiled.
